@@ -1,0 +1,129 @@
+"""Gated linear attention (GLA) for AMD MI355X: Python binding of libgla.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libgla.so (see include/gla.h for the C ABI). PyTorch supplies
+device memory and the current HIP stream.
+
+    o, S_T = fwd_chunked(q, k, v, g, S0=None, cu_seqlens=None, chunk_size=64)
+    o = decode_step(q, k, v, g, S)          # S updated in place
+
+Shapes follow the C ABI: q, k [B, T, H, dk]; v [B, T, H, dv]; g [B, T, H]
+fp32 natural-log gates; S0 / S_T [N, H, dk, dv] fp32; cu_seqlens int32 [N+1]
+on the device (packed batch, B == 1).
+"""
+from __future__ import annotations
+
+from . import _lib
+from ._lib import GLAError, GLA_BF16, GLA_F32
+
+__all__ = ["fwd_chunked", "decode_step", "workspace_size", "GLAError", "library_path"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t == torch.bfloat16:
+        return GLA_BF16
+    if t == torch.float32:
+        return GLA_F32
+    raise TypeError(f"unsupported dtype {t}; expected torch.bfloat16 or torch.float32")
+
+
+def _ptr(x):
+    return None if x is None else x.data_ptr()
+
+
+def _require(x, name, dtype=None, device=None):
+    if x is None:
+        return
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and x.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {x.dtype}")
+    if device is not None and x.device != device:
+        raise ValueError(f"{name} must be on {device}, got {x.device}")
+
+
+def workspace_size(B, T, H, dk, dv, num_seqs, chunk_size=64, has_cu_seqlens=False,
+                   in_dtype=None) -> int:
+    torch = _torch()
+    code = _dtype_code(torch.bfloat16 if in_dtype is None else in_dtype)
+    return int(_lib.load().gla_fwd_chunked_workspace_size(
+        B, T, H, dk, dv, num_seqs, chunk_size, int(bool(has_cu_seqlens)), code))
+
+
+def fwd_chunked(q, k, v, g, S0=None, cu_seqlens=None, chunk_size: int = 64, out_dtype=None,
+                output_final_state: bool = True, o=None, S_T=None, workspace=None):
+    """Chunked GLA forward. Returns (o, S_T) (S_T is None if not requested)."""
+    torch = _torch()
+    lib = _lib.load()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or g.dim() != 3:
+        raise ValueError("expected q, k, v [B, T, H, d] and g [B, T, H]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _require(q, "q", None, dev)
+    _require(k, "k", q.dtype, dev)
+    _require(v, "v", q.dtype, dev)
+    _require(g, "g", torch.float32, dev)
+    _require(S0, "S0", torch.float32, dev)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if tuple(k.shape) != (B, T, H, dk) or tuple(v.shape[:3]) != (B, T, H) or tuple(g.shape) != (B, T, H):
+        raise ValueError("inconsistent q/k/v/g shapes")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if S0 is not None and tuple(S0.shape) != (N, H, dk, dv):
+        raise ValueError(f"S0 must be [{N}, {H}, {dk}, {dv}]")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    _require(o, "o", out_dtype, dev)
+    if output_final_state and S_T is None:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _require(S_T, "S_T", torch.float32, dev)
+    in_code = _dtype_code(q.dtype)
+    ws_bytes = int(lib.gla_fwd_chunked_workspace_size(B, T, H, dk, dv, N, chunk_size,
+                                                      int(cu_seqlens is not None), in_code))
+    if ws_bytes > 0 and (workspace is None or workspace.numel() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.gla_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0), _ptr(cu_seqlens),
+                             _ptr(o), _ptr(S_T), B, T, H, dk, dv, N, chunk_size, in_code,
+                             _dtype_code(out_dtype), _ptr(workspace) if ws_bytes > 0 else None,
+                             ws_bytes, stream)
+    _lib.check(st, "gla_fwd_chunked")
+    return o, S_T
+
+
+def decode_step(q, k, v, g, S, out_dtype=None, o=None):
+    """One recurrent decode step; S [N, H, dk, dv] fp32 is updated in place. Returns o."""
+    torch = _torch()
+    lib = _lib.load()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or g.dim() != 2 or S.dim() != 4:
+        raise ValueError("expected q, k [N, H, dk], v [N, H, dv], g [N, H], S [N, H, dk, dv]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _require(q, "q", None, dev)
+    _require(k, "k", q.dtype, dev)
+    _require(v, "v", q.dtype, dev)
+    _require(g, "g", torch.float32, dev)
+    _require(S, "S", torch.float32, dev)
+    if tuple(S.shape) != (N, H, dk, dv) or tuple(g.shape) != (N, H):
+        raise ValueError("inconsistent decode shapes")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    _require(o, "o", out_dtype, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.gla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S), _ptr(o), N, H, dk, dv,
+                             _dtype_code(q.dtype), _dtype_code(out_dtype), stream)
+    _lib.check(st, "gla_decode_step")
+    return o

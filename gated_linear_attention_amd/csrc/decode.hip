@@ -1,0 +1,123 @@
+// One-token GLA decode step, streaming each fp32 state through HBM once.
+//
+// Laplace 3B on AWS Trainium2 (automationscribe.com/?p=7116), "GLA mixer":
+// per (sequence, head) the state decays, absorbs k^T v, and is read by q:
+//     S <- exp(l) S + k^T v  (in place),   o = q S.
+// The step is bandwidth-bound: 2 * d_k * d_v * 4 bytes of state move per
+// (sequence, head) against 4 d_k d_v flops, so the kernel is a coalesced
+// 128-bit read-modify-write stream with the d_k reduction for o done in
+// registers, a cross-lane shuffle and one LDS exchange.
+//
+// Mapping: one 256-thread workgroup per (sequence, head). Thread t owns the
+// four columns 4*(t % (dv/4)) .. +3 of the rows r0 + i*RP, r0 = t / (dv/4),
+// RP = 256 / (dv/4); a wavefront therefore reads whole 512-byte (dv = 128)
+// rows, and every thread issues all of its dk/RP 16-byte loads before using
+// any of them, so each CU keeps many bytes in flight.
+#include "gla_common.h"
+#include "gla_internal.h"
+
+namespace gla {
+
+template <int DK, int DV, typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void decode_step_kernel(const Tin *__restrict__ q,
+                                                          const Tin *__restrict__ k,
+                                                          const Tin *__restrict__ v,
+                                                          const float *__restrict__ g,
+                                                          float *__restrict__ S,
+                                                          Tout *__restrict__ o) {
+  constexpr int TPR = DV / 4;   // threads per state row
+  constexpr int RP = 256 / TPR; // rows per pass
+  constexpr int NP = DK / RP;   // passes
+  static_assert(DK % RP == 0, "d_k must be a multiple of the rows per pass");
+  __shared__ f32x4 red[4][TPR];
+
+  const size_t p = blockIdx.x;  // (sequence, head) pair
+  const int t = threadIdx.x;
+  const int c4 = t % TPR;
+  const int r0 = t / TPR;
+  f32x4 *Sp = reinterpret_cast<f32x4 *>(S + p * (size_t)(DK * DV));
+
+  f32x4 s[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) s[i] = __builtin_nontemporal_load(Sp + (r0 + i * RP) * TPR + c4);
+
+  const float gate = expf(g[p]);
+  f32x4 vv;
+  vv.x = load_as_f32(v, p * DV + 4 * c4 + 0);
+  vv.y = load_as_f32(v, p * DV + 4 * c4 + 1);
+  vv.z = load_as_f32(v, p * DV + 4 * c4 + 2);
+  vv.w = load_as_f32(v, p * DV + 4 * c4 + 3);
+  float kk[NP], qq[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    kk[i] = load_as_f32(k, p * DK + r0 + i * RP);
+    qq[i] = load_as_f32(q, p * DK + r0 + i * RP);
+  }
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    f32x4 x = gate * s[i] + kk[i] * vv;
+    __builtin_nontemporal_store(x, Sp + (r0 + i * RP) * TPR + c4);
+    acc += qq[i] * x;
+  }
+
+  // Sum the partial outputs of the threads that own the same columns: first
+  // across the lanes of a wavefront (lanes c4, c4 + TPR, ...), then across the
+  // four wavefronts through LDS.
+#pragma unroll
+  for (int off = TPR; off < 64; off *= 2) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
+  const int wave = t / 64, lane = t % 64;
+  if (lane < TPR) red[wave][lane] = acc;
+  __syncthreads();
+  if (t < TPR) {
+    f32x4 r = red[0][t] + red[1][t] + red[2][t] + red[3][t];
+    Tout *op = o + p * DV + 4 * t;
+    store_from_f32(op, 0, r.x);
+    store_from_f32(op, 1, r.y);
+    store_from_f32(op, 2, r.z);
+    store_from_f32(op, 3, r.w);
+  }
+}
+
+template <int DK, int DV, typename Tin, typename Tout>
+static hipError_t launch_decode_t(const void *q, const void *k, const void *v, const float *g,
+                                  float *S, void *o, int pairs, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_step_kernel<DK, DV, Tin, Tout>), dim3(pairs), dim3(256), 0, stream,
+                     static_cast<const Tin *>(q), static_cast<const Tin *>(k),
+                     static_cast<const Tin *>(v), g, S, static_cast<Tout *>(o));
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_decode_d(const void *q, const void *k, const void *v, const float *g,
+                                  float *S, void *o, int pairs, bool in_bf16, bool out_bf16,
+                                  hipStream_t stream) {
+  if (in_bf16) {
+    return out_bf16 ? launch_decode_t<DK, DV, uint16_t, uint16_t>(q, k, v, g, S, o, pairs, stream)
+                    : launch_decode_t<DK, DV, uint16_t, float>(q, k, v, g, S, o, pairs, stream);
+  }
+  return out_bf16 ? launch_decode_t<DK, DV, float, uint16_t>(q, k, v, g, S, o, pairs, stream)
+                  : launch_decode_t<DK, DV, float, float>(q, k, v, g, S, o, pairs, stream);
+}
+
+hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g, float *S,
+                         void *o, int N, int H, int dk, int dv, bool in_bf16, bool out_bf16,
+                         hipStream_t stream) {
+  const long pairs = (long)N * H;
+  if (pairs == 0) return hipSuccess;
+  if (dk == 128 && dv == 128)
+    return launch_decode_d<128, 128>(q, k, v, g, S, o, (int)pairs, in_bf16, out_bf16, stream);
+  if (dk == 128 && dv == 64)
+    return launch_decode_d<128, 64>(q, k, v, g, S, o, (int)pairs, in_bf16, out_bf16, stream);
+  if (dk == 64 && dv == 128)
+    return launch_decode_d<64, 128>(q, k, v, g, S, o, (int)pairs, in_bf16, out_bf16, stream);
+  return launch_decode_d<64, 64>(q, k, v, g, S, o, (int)pairs, in_bf16, out_bf16, stream);
+}
+
+}  // namespace gla

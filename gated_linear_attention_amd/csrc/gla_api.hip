@@ -1,0 +1,246 @@
+// C ABI of libgla.so: argument validation, work planning and kernel launches.
+#include <climits>
+#include <cstdlib>
+#include <cstring>
+
+#include "gla.h"
+#include "gla_internal.h"
+
+using namespace gla;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];  // cache of each device's CU count (a device constant)
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    g_cu_count[dev] = n;
+  }
+  return g_cu_count[dev];
+}
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int round_up(long x, int m) { return (int)(((x + m - 1) / m) * m); }
+
+// State columns one workgroup of the forward owns (the column "slice").
+int slice_width(gla_dtype in_dtype) { return in_dtype == GLA_BF16 ? 64 : 32; }
+
+// Tokens per work item. A dense batch with enough (sequence, head, slice)
+// work units to cover every CU runs each sequence whole; otherwise sequences
+// are split into about ceil(CUs / units) segments. A packed batch caps
+// segments at its per-CU share of the work, so no single long sequence sets
+// the critical path. GLA_SEG_LEN overrides the choice (tuning only; the
+// result does not depend on it beyond rounding).
+int choose_seg_len(int B, int T, int H, int dv, int N, int C, bool has_cu, gla_dtype in_dtype) {
+  long L;
+  const char *env = std::getenv("GLA_SEG_LEN");
+  const int n_slices = dv / slice_width(in_dtype);
+  if (env && std::atoi(env) > 0) {
+    L = std::atoi(env);
+  } else if (!has_cu) {
+    const long units = (long)B * H * n_slices;
+    const int ncu = cu_count();
+    if (units >= ncu) {
+      L = T;
+    } else {
+      const long nseg = (ncu + units - 1) / units;
+      L = (T + nseg - 1) / nseg;
+    }
+  } else {
+    const long work = (long)T * H * n_slices;
+    L = work / cu_count();
+    (void)N;
+  }
+  L = round_up(L < C ? C : L, C);
+  const long cap = round_up(T < C ? C : T, C);
+  if (L > cap) L = cap;
+  if (L > 65536) L = 65536;  // bounds the scheduler's sort buckets
+  return (int)L;
+}
+
+// Whether the forward needs the device-side planner, and its workspace layout.
+bool make_plan(int B, int T, int H, int dk, int dv, int N, int C, bool has_cu,
+               gla_dtype in_dtype, PlanLayout &lay) {
+  std::memset(&lay, 0, sizeof(lay));
+  const int L = choose_seg_len(B, T, H, dv, N, C, has_cu, in_dtype);
+  lay.seg_len = L;
+  if (!has_cu) {
+    const int nseg = T > 0 ? (T + L - 1) / L : 1;
+    if (nseg <= 1) return false;
+    lay.max_items = B * nseg;
+    lay.max_state_items = B * (nseg - 1);
+    lay.max_multi = B;
+    lay.max_slots = B * nseg;
+  } else {
+    const int full = T / L;  // segments that can be full length
+    lay.max_items = N + full;
+    lay.max_state_items = full;
+    lay.max_multi = full;
+    lay.max_slots = 2 * full;
+  }
+  size_t off = 0;
+  lay.off_header = off;
+  off = align256(off + sizeof(PlanHeader));
+  lay.off_items = off;
+  off = align256(off + sizeof(WorkItem) * (size_t)lay.max_items);
+  lay.off_state_items = off;
+  off = align256(off + sizeof(WorkItem) * (size_t)lay.max_state_items);
+  lay.off_multi = off;
+  off = align256(off + sizeof(MultiSeq) * (size_t)lay.max_multi);
+  lay.off_slots = off;
+  off = align256(off + sizeof(float) * (size_t)lay.max_slots * H * dk * dv);
+  lay.off_slot_gamma = off;
+  off = align256(off + sizeof(float) * (size_t)lay.max_slots * H);
+  lay.total_bytes = off;
+  return true;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+size_t dtype_size(gla_dtype t) { return t == GLA_BF16 ? 2 : 4; }
+
+bool valid_dtype(int t) { return t == GLA_F32 || t == GLA_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char *gla_status_string(gla_status s) {
+  switch (s) {
+    case GLA_OK: return "GLA_OK";
+    case GLA_ERR_INVALID_ARGUMENT: return "GLA_ERR_INVALID_ARGUMENT";
+    case GLA_ERR_UNSUPPORTED: return "GLA_ERR_UNSUPPORTED";
+    case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE";
+    case GLA_ERR_HIP: return "GLA_ERR_HIP";
+  }
+  return "GLA_UNKNOWN_STATUS";
+}
+
+size_t gla_fwd_chunked_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
+                                      int chunk_size, int has_cu_seqlens, gla_dtype in_dtype) {
+  if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !supported_head_dim(dk) ||
+      !supported_head_dim(dv) || (chunk_size != 64 && chunk_size != 128) ||
+      !valid_dtype(in_dtype))
+    return 0;
+  PlanLayout lay;
+  if (!make_plan(B, T, H, dk, dv, num_seqs, chunk_size, has_cu_seqlens != 0, in_dtype, lay))
+    return 0;
+  return lay.total_bytes;
+}
+
+gla_status gla_fwd_chunked(const void *q, const void *k, const void *v, const float *g,
+                           const float *S0, const int32_t *cu_seqlens, void *o, float *S_T,
+                           int B, int T, int H, int dk, int dv, int num_seqs, int chunk_size,
+                           gla_dtype in_dtype, gla_dtype out_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return GLA_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
+  const bool has_cu = cu_seqlens != nullptr;
+  if (has_cu ? (B != 1) : (num_seqs != B)) return GLA_ERR_INVALID_ARGUMENT;
+  if ((long)B * T > INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
+  if (!supported_head_dim(dk) || !supported_head_dim(dv)) return GLA_ERR_UNSUPPORTED;
+  if (chunk_size != 64 && chunk_size != 128) return GLA_ERR_UNSUPPORTED;
+  if (in_dtype == GLA_BF16 && chunk_size != 64) return GLA_ERR_UNSUPPORTED;
+  const int N = num_seqs;
+  if (H == 0 || N == 0) return GLA_OK;
+  const size_t ntok = (size_t)B * T * H;
+  const size_t es = dtype_size(in_dtype);
+  const size_t bytes_qk = ntok * dk * es, bytes_v = ntok * dv * es, bytes_g = ntok * 4;
+  const size_t bytes_o = ntok * dv * dtype_size(out_dtype);
+  const size_t bytes_S = (size_t)N * H * dk * dv * 4;
+  if (ntok > 0 && (!q || !k || !v || !g || !o)) return GLA_ERR_INVALID_ARGUMENT;
+  if (overlaps(o, bytes_o, q, bytes_qk) || overlaps(o, bytes_o, k, bytes_qk) ||
+      overlaps(o, bytes_o, v, bytes_v) || overlaps(o, bytes_o, g, bytes_g) ||
+      overlaps(o, bytes_o, S0, S0 ? bytes_S : 0) || overlaps(o, bytes_o, S_T, S_T ? bytes_S : 0))
+    return GLA_ERR_INVALID_ARGUMENT;
+  if (S_T && S_T != S0 &&
+      (overlaps(S_T, bytes_S, S0, S0 ? bytes_S : 0) || overlaps(S_T, bytes_S, q, bytes_qk) ||
+       overlaps(S_T, bytes_S, k, bytes_qk) || overlaps(S_T, bytes_S, v, bytes_v) ||
+       overlaps(S_T, bytes_S, g, bytes_g)))
+    return GLA_ERR_INVALID_ARGUMENT;
+
+  FwdDims d;
+  d.B = B;
+  d.T = T;
+  d.H = H;
+  d.dk = dk;
+  d.dv = dv;
+  d.N = N;
+  d.C = chunk_size;
+  PlanLayout lay;
+  const bool planned = make_plan(B, T, H, dk, dv, N, chunk_size, has_cu, in_dtype, lay);
+  if (planned && (!workspace || workspace_bytes < lay.total_bytes)) return GLA_ERR_WORKSPACE;
+
+  const bool bf = in_dtype == GLA_BF16, out_bf = out_dtype == GLA_BF16;
+  auto run_chunks = [&](const WorkItem *items, const int *n_items, int grid_items, float *slots,
+                        float *slot_gamma, bool state_pass) -> hipError_t {
+    if (bf)
+      return launch_chunk_bf16(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+                               static_cast<const uint16_t *>(v), g, S0, S_T, o, out_bf, d, items,
+                               n_items, grid_items, slots, slot_gamma, state_pass, stream);
+    return launch_chunk_f32(static_cast<const float *>(q), static_cast<const float *>(k),
+                            static_cast<const float *>(v), g, S0, S_T, o, out_bf, d, items,
+                            n_items, grid_items, slots, slot_gamma, state_pass, stream);
+  };
+
+  hipError_t err;
+  if (!planned) {
+    err = run_chunks(nullptr, nullptr, B, nullptr, nullptr, false);
+    return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+  }
+  char *ws = static_cast<char *>(workspace);
+  const PlanHeader *hdr = reinterpret_cast<const PlanHeader *>(ws + lay.off_header);
+  const WorkItem *items = reinterpret_cast<const WorkItem *>(ws + lay.off_items);
+  const WorkItem *sitems = reinterpret_cast<const WorkItem *>(ws + lay.off_state_items);
+  float *slots = reinterpret_cast<float *>(ws + lay.off_slots);
+  float *slot_gamma = reinterpret_cast<float *>(ws + lay.off_slot_gamma);
+  if ((err = launch_plan(cu_seqlens, d, lay, workspace, stream)) != hipSuccess) return GLA_ERR_HIP;
+  if (lay.max_state_items > 0) {
+    if ((err = run_chunks(sitems, &hdr->n_state_items, lay.max_state_items, slots, slot_gamma,
+                          true)) != hipSuccess)
+      return GLA_ERR_HIP;
+    if ((err = launch_combine(S0, d, lay, workspace, stream)) != hipSuccess) return GLA_ERR_HIP;
+  }
+  err = run_chunks(items, &hdr->n_items, lay.max_items, slots, slot_gamma, false);
+  return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
+gla_status gla_decode_step(const void *q, const void *k, const void *v, const float *g,
+                           float *S, void *o, int N, int H, int dk, int dv, gla_dtype in_dtype,
+                           gla_dtype out_dtype, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (N < 0 || H < 0) return GLA_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
+  if (!supported_head_dim(dk) || !supported_head_dim(dv)) return GLA_ERR_UNSUPPORTED;
+  const size_t pairs = (size_t)N * H;
+  if (pairs == 0) return GLA_OK;
+  if (pairs > (size_t)INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
+  if (!q || !k || !v || !g || !S || !o) return GLA_ERR_INVALID_ARGUMENT;
+  const size_t es = dtype_size(in_dtype);
+  const size_t bq = pairs * dk * es, bv = pairs * dv * es, bg = pairs * 4;
+  const size_t bS = pairs * dk * dv * 4, bo = pairs * dv * dtype_size(out_dtype);
+  if (overlaps(o, bo, q, bq) || overlaps(o, bo, k, bq) || overlaps(o, bo, v, bv) ||
+      overlaps(o, bo, g, bg) || overlaps(o, bo, S, bS) || overlaps(S, bS, q, bq) ||
+      overlaps(S, bS, k, bq) || overlaps(S, bS, v, bv) || overlaps(S, bS, g, bg))
+    return GLA_ERR_INVALID_ARGUMENT;
+  const hipError_t err = launch_decode(q, k, v, g, S, o, N, H, dk, dv, in_dtype == GLA_BF16,
+                                       out_dtype == GLA_BF16, stream);
+  return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
+}  // extern "C"

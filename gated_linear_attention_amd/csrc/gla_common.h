@@ -1,0 +1,65 @@
+// Device-side helpers shared by the GLA kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gla {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 is stored as the upper 16 bits of a binary32; widening is a shift.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even narrowing of a finite or infinite float to bf16 bits;
+// NaN maps to a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two bf16 (lo element first) packed in one 32-bit word.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+// Split x into hi + lo with hi = bf16(x) and lo = bf16(x - hi): the pair holds
+// about 16 significant bits, so products hi*y + lo*y on the bf16 matrix cores
+// keep fp32-level accuracy (x - hi is exact in fp32).
+__device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) {
+  hi = f32_to_bf16_bits(x);
+  lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+// 2^x on the hardware exp unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Load element i of a bf16 or fp32 array as float.
+template <typename T> __device__ __forceinline__ float load_as_f32(const T *p, size_t i);
+template <> __device__ __forceinline__ float load_as_f32<float>(const float *p, size_t i) {
+  return p[i];
+}
+template <> __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t *p, size_t i) {
+  return bf16_bits_to_f32(p[i]);
+}
+
+// Store a float as fp32 or bf16.
+template <typename T> __device__ __forceinline__ void store_from_f32(T *p, size_t i, float x);
+template <> __device__ __forceinline__ void store_from_f32<float>(float *p, size_t i, float x) {
+  p[i] = x;
+}
+template <> __device__ __forceinline__ void store_from_f32<uint16_t>(uint16_t *p, size_t i, float x) {
+  p[i] = (uint16_t)f32_to_bf16_bits(x);
+}
+
+}  // namespace gla

@@ -1,0 +1,83 @@
+// Host/device interfaces between the C ABI layer and the GLA kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gla {
+
+// One unit of chunked-forward work for one (head, dv-slice): a run of tokens
+// [tok_begin, tok_end) of sequence `seq` on the flattened time axis (row b of
+// a dense batch starts at b*T). `state_in` < 0 starts from S0[seq] (zeros if
+// S0 is NULL); otherwise from workspace state slot `state_in`. In the
+// output pass, `state_out` < 0 writes the final state to S_T[seq] and
+// `state_out` == kNoStateOut writes nothing; in the state pass it is the slot
+// that receives the segment's local state and total log-decay.
+struct WorkItem {
+  int tok_begin;
+  int tok_end;
+  int seq;
+  int state_in;
+  int state_out;
+  int pad0, pad1, pad2;
+};
+constexpr int kNoStateOut = -2;
+
+// A sequence split into `nseg` > 1 segments whose start states live in slots
+// slot_base .. slot_base + nseg - 1 (slot s holds the start state of segment s).
+struct MultiSeq {
+  int seq;
+  int slot_base;
+  int nseg;
+  int pad;
+};
+
+struct PlanHeader {
+  int n_items;        // output-pass items
+  int n_state_items;  // state-pass items (all non-last segments)
+  int n_multi;        // sequences with more than one segment
+  int pad;
+};
+
+// Workspace layout of a planned forward (all offsets 256-byte aligned).
+struct PlanLayout {
+  int seg_len;          // tokens per segment (multiple of the chunk size)
+  int max_items;        // bound on output-pass items
+  int max_state_items;  // bound on state-pass items
+  int max_multi;        // bound on split sequences
+  int max_slots;        // bound on state slots
+  size_t off_header, off_items, off_state_items, off_multi, off_slots, off_slot_gamma;
+  size_t total_bytes;
+};
+
+// dims of the flattened problem
+struct FwdDims {
+  int B, T, H, dk, dv, N, C;
+};
+
+hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g, float *S,
+                         void *o, int N, int H, int dk, int dv, bool in_bf16, bool out_bf16,
+                         hipStream_t stream);
+
+hipError_t launch_plan(const int32_t *cu_seqlens, const FwdDims &d, const PlanLayout &lay,
+                       void *workspace, hipStream_t stream);
+
+hipError_t launch_combine(const float *S0, const FwdDims &d, const PlanLayout &lay,
+                          void *workspace, hipStream_t stream);
+
+// fp32 inputs, fp32 arithmetic. state_pass: compute segment-local states only.
+hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, const float *g,
+                            const float *S0, float *S_T, void *o, bool out_bf16,
+                            const FwdDims &d, const WorkItem *items, const int *n_items,
+                            int grid_items, float *slots, float *slot_gamma, bool state_pass,
+                            hipStream_t stream);
+
+// bf16 inputs on the matrix cores, fp32 accumulation and state.
+hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const float *g, const float *S0, float *S_T, void *o, bool out_bf16,
+                             const FwdDims &d, const WorkItem *items, const int *n_items,
+                             int grid_items, float *slots, float *slot_gamma, bool state_pass,
+                             hipStream_t stream);
+
+}  // namespace gla

@@ -1,0 +1,123 @@
+/*
+ * gla.h - C ABI of libgla.so: gated linear attention (GLA) on AMD MI355X (gfx950).
+ *
+ * The method (Laplace 3B on AWS Trainium2, automationscribe.com/?p=7116,
+ * section "GLA mixer"): every head keeps a d_k x d_v matrix state that decays
+ * and absorbs the rank-1 outer product of the current key and value, and the
+ * output reads the state with the query. With a per-token, per-head gate
+ * g_t = exp(l_t):
+ *
+ *     S_t = g_t * S_{t-1} + k_t^T v_t          (S is d_k x d_v, row-major)
+ *     o_t = q_t S_t                            (after the update)
+ *
+ * No 1/sqrt(d_k) scale and no normaliser are applied: callers fold any scale
+ * into k (or q). The page's fixed per-head decay lambda_h is the special case
+ * l_t = ln(lambda_h).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (HBM of the current device),
+ *    dense and row-major in the layouts given, allocated and owned by the
+ *    caller. The library allocates no device memory and keeps no state
+ *    between calls; it is re-entrant, and calls on different streams do not
+ *    interact. Calls on the same buffers from two streams race.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it and the call returns without synchronising.
+ *  - Argument errors are detected on the host before anything is enqueued and
+ *    reported by the return value; nothing is written then. A failed kernel
+ *    launch returns GLA_ERR_HIP. Faults inside a kernel surface at the
+ *    caller's next synchronisation, as with any HIP library.
+ *  - Tensor values are not validated: NaN/Inf propagate, and l_t > 0 (a
+ *    growing state) is computed as given.
+ *  - Supported sizes: d_k, d_v in {64, 128}; chunk_size in {64, 128}.
+ *    Anything else returns GLA_ERR_UNSUPPORTED.
+ */
+#ifndef GLA_H_
+#define GLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GLA_OK = 0,
+  GLA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad dtype, o aliasing an input */
+  GLA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (head dims, chunk size) */
+  GLA_ERR_WORKSPACE = 3,        /* workspace NULL or smaller than the size query returns */
+  GLA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} gla_status;
+
+typedef enum {
+  GLA_F32 = 0, /* IEEE binary32 */
+  GLA_BF16 = 1 /* bfloat16 (upper half of binary32), round-to-nearest-even on output */
+} gla_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *gla_status_string(gla_status s);
+
+/*
+ * Chunked-parallel forward (prefill / training forward) over a dense or
+ * packed batch. Computes the recurrence above in its chunked form (Laplace 3B
+ * on AWS Trainium2, "Challenge 1": within each chunk of `chunk_size` tokens
+ * the output is decay-masked linear attention plus the query read of the
+ * running state; the state then advances by the decay compounded over the
+ * chunk). Chunks restart at every sequence start; the last chunk of a
+ * sequence may be partial.
+ *
+ *   q          [B, T, H, dk]  in_dtype
+ *   k          [B, T, H, dk]  in_dtype
+ *   v          [B, T, H, dv]  in_dtype
+ *   g          [B, T, H]      fp32 natural-log gates l_t (the gate is exp(l_t))
+ *   S0         [N, H, dk, dv] fp32 initial states, or NULL for zeros
+ *   cu_seqlens [N+1] int32 DEVICE array of sequence offsets into the time axis,
+ *              or NULL. With cu_seqlens, B must be 1, cu_seqlens[0] = 0,
+ *              offsets non-decreasing and cu_seqlens[N] = T (these values are
+ *              read on the device and are not checked). Without it, N = B and
+ *              every row of the batch is one sequence of length T.
+ *   o          [B, T, H, dv]  out_dtype (GLA_F32 carries full accuracy; GLA_BF16
+ *              rounds the fp32 result once). Must not overlap any input.
+ *   S_T        [N, H, dk, dv] fp32 final states, or NULL to skip. May be the
+ *              same pointer as S0 (each state is read before it is written);
+ *              any other overlap with an input is undefined.
+ *   num_seqs   N (must equal B when cu_seqlens is NULL).
+ *   chunk_size 64 or 128: the chunk length C of the chunked form. Results
+ *              agree across chunk sizes up to rounding.
+ *   in_dtype   GLA_BF16 (MFMA path, fp32 accumulation and fp32 state) or
+ *              GLA_F32 (fp32 arithmetic throughout).
+ *   workspace  device scratch of at least gla_fwd_chunked_workspace_size()
+ *              bytes (may be NULL when that size is 0); contents on entry do
+ *              not matter; it is in use until the enqueued work completes.
+ */
+size_t gla_fwd_chunked_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
+                                      int chunk_size, int has_cu_seqlens, gla_dtype in_dtype);
+
+gla_status gla_fwd_chunked(const void *q, const void *k, const void *v, const float *g,
+                           const float *S0, const int32_t *cu_seqlens, void *o, float *S_T,
+                           int B, int T, int H, int dk, int dv, int num_seqs, int chunk_size,
+                           gla_dtype in_dtype, gla_dtype out_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step for N independent sequences (Laplace 3B on AWS
+ * Trainium2, "GLA mixer" for the update and readout; "Inference optimization"
+ * for serving with one fixed-size state per sequence):
+ *
+ *   S[n,h] <- exp(g[n,h]) * S[n,h] + k[n,h]^T v[n,h]      (in place)
+ *   o[n,h]  = q[n,h] S[n,h]                              (updated state)
+ *
+ *   q [N, H, dk], k [N, H, dk], v [N, H, dv]   in_dtype (GLA_BF16 or GLA_F32)
+ *   g [N, H]           fp32 natural-log gates; -inf gives g = 0 (a reset)
+ *   S [N, H, dk, dv]   fp32 states, read and overwritten in place
+ *   o [N, H, dv]       out_dtype; must not overlap S or the inputs
+ */
+gla_status gla_decode_step(const void *q, const void *k, const void *v, const float *g,
+                           float *S, void *o, int N, int H, int dk, int dv, gla_dtype in_dtype,
+                           gla_dtype out_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H_ */

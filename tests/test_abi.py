@@ -1,0 +1,98 @@
+"""The C ABI library loads and exports every symbol include/gla.h declares;
+host-side argument checks return their status codes without touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_linear_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "gla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gla_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    assert header_functions() == ["gla_decode_step", "gla_fwd_chunked",
+                                  "gla_fwd_chunked_workspace_size", "gla_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code, name in [(0, "GLA_OK"), (1, "GLA_ERR_INVALID_ARGUMENT"), (2, "GLA_ERR_UNSUPPORTED"),
+                       (3, "GLA_ERR_WORKSPACE"), (4, "GLA_ERR_HIP")]:
+        assert _lib.status_string(code) == name
+    assert _lib.status_string(99) == "GLA_UNKNOWN_STATUS"
+
+
+def _fwd(**kw):
+    a = dict(q=None, k=None, v=None, g=None, S0=None, cu=None, o=None, ST=None, B=1, T=64, H=1,
+             dk=64, dv=64, N=1, C=64, ind=_lib.GLA_BF16, outd=_lib.GLA_F32, ws=None, wsb=0)
+    a.update(kw)
+    return _lib.load().gla_fwd_chunked(a["q"], a["k"], a["v"], a["g"], a["S0"], a["cu"], a["o"],
+                                       a["ST"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["N"],
+                                       a["C"], a["ind"], a["outd"], a["ws"], a["wsb"], None)
+
+
+FAKE = 1 << 40  # never dereferenced: every call below fails validation first
+
+
+def test_fwd_rejects_bad_arguments_before_launch():
+    P = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30),
+             o=FAKE + (4 << 30))
+    assert _fwd(B=-1, **P) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert _fwd(ind=7, **P) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert _fwd(N=2, **P) == _lib.GLA_ERR_INVALID_ARGUMENT            # N != B without cu
+    assert _fwd(dk=96, **P) == _lib.GLA_ERR_UNSUPPORTED
+    assert _fwd(dv=192, **P) == _lib.GLA_ERR_UNSUPPORTED
+    assert _fwd(C=32, **P) == _lib.GLA_ERR_UNSUPPORTED
+    assert _fwd(C=128, **P) == _lib.GLA_ERR_UNSUPPORTED                # bf16 path: C = 64
+    assert _fwd(**{**P, "q": None}) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert _fwd(**{**P, "o": P["q"] + 64}) == _lib.GLA_ERR_INVALID_ARGUMENT  # o overlaps q
+    assert _fwd(cu=FAKE + (5 << 30), B=2, N=2, **P) == _lib.GLA_ERR_INVALID_ARGUMENT
+    # zero heads or zero sequences: nothing to do
+    assert _fwd(H=0, **P) == _lib.GLA_OK
+    assert _fwd(B=0, N=0, **P) == _lib.GLA_OK
+
+
+def test_fwd_requires_workspace_when_planned():
+    lib = _lib.load()
+    n = lib.gla_fwd_chunked_workspace_size(1, 4096, 1, 64, 64, 3, 64, 1, _lib.GLA_BF16)
+    assert n > 0
+    P = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30),
+             o=FAKE + (4 << 30), cu=FAKE + (5 << 30))
+    assert _fwd(B=1, T=4096, N=3, ws=None, wsb=0, **P) == _lib.GLA_ERR_WORKSPACE
+    assert _fwd(B=1, T=4096, N=3, ws=FAKE + (6 << 30), wsb=n - 1, **P) == _lib.GLA_ERR_WORKSPACE
+
+
+def test_workspace_size_is_zero_for_whole_sequences():
+    lib = _lib.load()
+    # 8 x 16 heads x 2 slices = 256 work units covers the device: no split, no plan
+    assert lib.gla_fwd_chunked_workspace_size(8, 2048, 16, 128, 128, 8, 64, 0, _lib.GLA_BF16) == 0
+    assert lib.gla_fwd_chunked_workspace_size(1, 256, 2, 64, 64, 1, 64, 0, 7) == 0
+
+
+def test_decode_rejects_bad_arguments_before_launch():
+    lib = _lib.load()
+    base = [FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30),
+            FAKE + (5 << 30)]
+    call = lambda ptrs, N=4, H=2, dk=64, dv=64, ind=_lib.GLA_BF16: lib.gla_decode_step(
+        *ptrs, N, H, dk, dv, ind, _lib.GLA_F32, None)
+    assert call(base, N=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(base, dk=96) == _lib.GLA_ERR_UNSUPPORTED
+    assert call(base, ind=5) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call([None] + base[1:]) == _lib.GLA_ERR_INVALID_ARGUMENT
+    bad = list(base)
+    bad[5] = base[4] + 8  # o inside S
+    assert call(bad) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(base, N=0) == _lib.GLA_OK

@@ -1,0 +1,170 @@
+"""GPU parity of the chunked forward (gla_fwd_chunked) against the fp64 oracle.
+
+The oracle is the token-by-token recurrence of Laplace 3B on AWS Trainium2
+(automationscribe.com/?p=7116), "GLA mixer"; the kernels compute its chunked
+form ("Challenge 1"). Tolerances: max relative error (normwise per tensor)
+2e-3 for bf16 inputs with fp32 accumulation, 1e-5 for fp32 inputs.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import gpu_util as gu
+from gated_linear_attention_amd import synth
+from oracle import c_oracle
+from oracle import gla_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(q, k, v, lg, S0, cu, dtype, C=64, out_dtype=None, alias=False):
+    import torch
+    import gated_linear_attention_amd as gla
+    td = gu.in_dtype(dtype)
+    S0d = gu.dev(S0)
+    o, ST = gla.fwd_chunked(gu.dev(q, td), gu.dev(k, td), gu.dev(v, td), gu.dev(lg), S0d,
+                            gu.dev(cu), chunk_size=C, out_dtype=out_dtype,
+                            S_T=S0d if alias else None)
+    torch.cuda.synchronize()
+    return gu.host(o), gu.host(ST)
+
+
+def check(q, k, v, lg, S0, cu, dtype, C=64, heads=None, tol=None, out_dtype=None, alias=False,
+          tight=None):
+    o, ST = run_gpu(q, k, v, lg, S0, cu, dtype, C, out_dtype, alias)
+    if heads is not None:
+        sl = lambda a: None if a is None else np.ascontiguousarray(a[:, :, heads] if a.ndim >= 3 else a)
+        o_ref, S_ref, _ = c_oracle.fwd(sl(q), sl(k), sl(v), sl(lg),
+                                       None if S0 is None else np.ascontiguousarray(S0[:, heads]),
+                                       cu, nthreads=16)
+        o, ST = o[:, :, heads], ST[:, heads]
+    else:
+        o_ref, S_ref, _ = c_oracle.fwd(q, k, v, lg, S0, cu, nthreads=16)
+    if out_dtype is not None:
+        o_ref = synth.round_bf16(o_ref.astype(np.float32))
+    eo, eS = orc.normwise_error(o, o_ref), orc.normwise_error(ST, S_ref)
+    tol = tol if tol is not None else (gu.TOL_BF16 if dtype == "bf16" else gu.TOL_F32)
+    gu.say(f"   o err {eo:.3e}  S_T err {eS:.3e}  (tol {tol:.1e})")
+    assert eo <= tol and eS <= tol, (eo, eS)
+    if tight is not None:
+        assert eo <= tight and eS <= tight, (eo, eS)
+    return eo, eS
+
+
+W = synth.WORKLOADS
+
+
+@pytest.mark.parametrize("C", [64, 128])
+def test_tiny_f32_workload(C):
+    """B=1, H=2, T=256, d=64, fp32 inputs, S0 = 0."""
+    gu.say(f"tiny fp32 workload C={C}")
+    w = W["tiny_f32"]
+    check(*synth.make_forward_inputs(w), "f32", C=C)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("T", [64, 300, 1])
+def test_bf16_shapes(dk, dv, T):
+    """Several tiles, a ragged tail chunk, a single token; nonzero S0."""
+    gu.say(f"bf16 dk={dk} dv={dv} T={T}")
+    w = synth.Workload("t", B=2, T=T, H=3, dk=dk, dv=dv, dtype="bf16", gate_bias=3.0,
+                       s0_std=0.02, chunk=64, seed=11)
+    check(*synth.make_forward_inputs(w), "bf16", tight=2e-5)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
+@pytest.mark.parametrize("C", [64, 128])
+def test_f32_shapes(dk, dv, C):
+    gu.say(f"f32 dk={dk} dv={dv} C={C}")
+    w = synth.Workload("t", B=2, T=333, H=2, dk=dk, dv=dv, dtype="f32", gate_bias=2.0,
+                       s0_std=0.02, chunk=C, seed=12)
+    check(*synth.make_forward_inputs(w), "f32", C=C)
+
+
+def test_bf16_output_dtype():
+    import torch
+    gu.say("bf16 output")
+    w = synth.Workload("t", B=1, T=200, H=2, dk=128, dv=128, dtype="bf16", gate_bias=3.0,
+                       s0_std=0.02, chunk=64, seed=13)
+    check(*synth.make_forward_inputs(w), "bf16", out_dtype=torch.bfloat16, tol=gu.TOL_BF16_OUT)
+
+
+def test_state_aliasing_S0_S_T():
+    gu.say("S_T aliases S0")
+    w = synth.Workload("t", B=2, T=190, H=2, dk=128, dv=128, dtype="bf16", gate_bias=3.0,
+                       s0_std=0.05, chunk=64, seed=14)
+    check(*synth.make_forward_inputs(w), "bf16", alias=True)
+
+
+@pytest.mark.parametrize("gate", ["zero", "strong"])
+def test_gate_extremes(gate):
+    """l = 0 (no decay: plain causal linear attention) and l = -20 per token."""
+    gu.say(f"gate extreme {gate}")
+    w = synth.Workload("t", B=1, T=150, H=2, dk=64, dv=64, dtype="bf16", gate_bias=3.0,
+                       s0_std=0.02, chunk=64, seed=15)
+    q, k, v, lg, S0, cu = synth.make_forward_inputs(w)
+    lg = np.zeros_like(lg) if gate == "zero" else np.full_like(lg, -20.0)
+    check(q, k, v, lg, S0, cu, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_varlen_with_edge_lengths(dtype):
+    """Packed batch with empty, length-1, sub-chunk and multi-chunk sequences."""
+    gu.say(f"varlen edge lengths {dtype}")
+    w = synth.Workload("t", B=1, T=0, H=3, dk=128, dv=128, dtype=dtype, gate_bias=3.0,
+                       s0_std=0.02, chunk=64, seed=16)
+    q, k, v, lg, S0, cu = synth.make_forward_inputs(w, lengths=[0, 1, 63, 64, 65, 200, 0, 130, 7])
+    check(q, k, v, lg, S0, cu, dtype)
+
+
+@pytest.mark.parametrize("seg", [64, 128, 192])
+@pytest.mark.parametrize("varlen", [False, True])
+def test_forced_segment_split(seg, varlen, monkeypatch):
+    """Sequences split into segments: state pass, combine, output pass."""
+    gu.say(f"segment split seg_len={seg} varlen={varlen}")
+    monkeypatch.setenv("GLA_SEG_LEN", str(seg))
+    w = synth.Workload("t", B=2, T=500, H=2, dk=128, dv=128, dtype="bf16", gate_bias=3.0,
+                       s0_std=0.03, chunk=64, seed=17)
+    lengths = [500, 0, 37, 321, 129] if varlen else None
+    check(*synth.make_forward_inputs(w, lengths=lengths), "bf16")
+
+
+def test_forced_segment_split_f32(monkeypatch):
+    gu.say("segment split fp32")
+    monkeypatch.setenv("GLA_SEG_LEN", "128")
+    w = synth.Workload("t", B=1, T=450, H=2, dk=64, dv=64, dtype="f32", gate_bias=3.0,
+                       s0_std=0.03, chunk=64, seed=18)
+    check(*synth.make_forward_inputs(w), "f32")
+
+
+def test_chunk_size_independence_f32():
+    import torch
+    gu.say("C=64 vs C=128 (fp32)")
+    w = synth.Workload("t", B=1, T=400, H=2, dk=64, dv=64, dtype="f32", gate_bias=3.0,
+                       s0_std=0.02, chunk=64, seed=19)
+    q, k, v, lg, S0, cu = synth.make_forward_inputs(w)
+    o1, S1 = run_gpu(q, k, v, lg, S0, cu, "f32", C=64)
+    o2, S2 = run_gpu(q, k, v, lg, S0, cu, "f32", C=128)
+    assert orc.normwise_error(o1, o2) <= 1e-5 and orc.normwise_error(S1, S2) <= 1e-5
+
+
+# ----------------------------------------------------------- full-size workloads
+def test_train_2k_full_size_sampled_heads():
+    """B=8, H=16, T=2048, d=128, bf16, S0 = 0: all heads run on the GPU; the
+    oracle checks 3 heads of every sequence."""
+    gu.say("train_2k full size")
+    check(*synth.make_forward_inputs(W["train_2k"]), "bf16", heads=[0, 7, 15], tight=1e-4)
+
+
+def test_prefill_64k_full_size_sampled_heads():
+    """B=1, H=32, T=65536, d=128, bf16, nonzero S0, split into segments; the
+    oracle checks 2 heads over the whole sequence."""
+    gu.say("prefill_64k full size")
+    check(*synth.make_forward_inputs(W["prefill_64k"]), "bf16", heads=[3, 30], tight=1e-4)
+
+
+def test_varlen_64_full_size_sampled_heads():
+    """64 packed sequences, lengths uniform in [128, 8192], H=16, d=128, bf16."""
+    gu.say("varlen_64 full size")
+    check(*synth.make_forward_inputs(W["varlen_64"]), "bf16", heads=[1, 12], tight=1e-4)
