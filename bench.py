@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the GLA hot path on one MI355X.
+
+Headline: chunked forward on the training-shape workload (B=8, H=16, T=2048,
+d_k=d_v=128, bf16 q/k/v, fp32 log-gates, S0 = 0, fp32 o and S_T), reported as
+tokens/s of one GLA layer with all 16 heads, with its HBM roofline and the
+matrix-core utilisation. A second object reports the decode step on 1,280
+sequences x 16 heads (fp32 state 1.34 GB updated in place, 100 chained
+steps) as state GB/s against the HBM peak. The fp64 CPU oracle is timed on a
+bounded sample of the headline workload as the CPU baseline.
+
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+Three input sets rotate across steps so that q/k/v (201 MB per set) are not
+served from the 256 MB last-level cache.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_linear_attention_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, sources):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    if there are none or the kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = data.get(kernel_key)
+    if not rec or rec.get("source_hash") != kernel_source_hash(sources):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_launches(fn, steps, stream):
+    """Run fn(i) for i in range(steps) on `stream`; return (wall seconds, mean
+    per-launch GPU ms from HIP events recorded on that stream)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]
+    return wall, sum(per) / len(per)
+
+
+def bench_forward(args):
+    import numpy as np
+    import torch
+
+    import gated_linear_attention_amd as gla
+    from gated_linear_attention_amd import synth
+
+    w = synth.WORKLOADS["train_2k"]
+    C = args.chunk
+    dev = torch.device("cuda:0")
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    sets = []
+    host_set0 = None
+    for i in range(3):
+        q, k, v, lg, S0, cu = synth.make_forward_inputs(w, seed=w.seed + 100 * i)
+        if i == 0:
+            host_set0 = (q, k, v, lg)
+        bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+        sets.append((bf(q), bf(k), bf(v), torch.from_numpy(lg).to(dev)))
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        q, k, v, lg = sets[i % 3]
+        gla.fwd_chunked(q, k, v, lg, None, None, chunk_size=C, o=o, S_T=S_T)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    wall, kern_ms = time_launches(step, args.steps, stream)
+    ms_per_step = 1e3 * wall / args.steps
+    tokens = B * T
+    tok_heads = B * T * H
+    # algorithmic bytes: q, k, v (bf16) + log-gates (fp32) + o (fp32) + S_T (fp32)
+    alg_bytes = tok_heads * (2 * dk + 2 * dk + 2 * dv + 4 + 4 * dv) + B * H * dk * dv * 4
+    # algorithmic flops of the chunked form at chunk C: causal intra-chunk scores
+    # and P V, the state read Q S and the state update K^T V
+    alg_flops = tok_heads * ((C + 1) * (dk + dv) + 4 * dk * dv)
+    # flops the matrix cores issue (whole 16x16 tiles, bf16 hi/lo splits, the
+    # score tiles recomputed by each 64-column slice)
+    n_chunks = B * H * (T // C)
+    slices = dv // 64
+    nm, ntile = C // 16, (C // 16) * (C // 16 + 1) // 2
+    causal_pv = sum((16 * mi + 15) // 32 + 1 for mi in range(nm))
+    mfma_per_chunk = slices * (ntile * (dk // 32)                        # scores
+                               + 4 * (nm * (dk // 32) * 2                  # Q S hi/lo
+                                      + causal_pv * 2                      # P V hi/lo
+                                      + (dk // 16) * (C // 32) * 2))       # K^T V hi/lo
+    issued_flops = n_chunks * mfma_per_chunk * 16 * 16 * 32 * 2
+    achieved_gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic("chunk_fwd_bf16_train_2k", ["chunk_bf16.hip", "gla_common.h"])
+    res = {
+        "tokens": tokens,
+        "ms_per_step": ms_per_step,
+        "kernel_ms": kern_ms,
+        "value": tokens / (ms_per_step * 1e-3),
+        "config": {"workload": "train_2k chunked forward", "B": B, "T": T, "H": H, "dk": dk,
+                   "dv": dv, "chunk": C, "in_dtype": "bf16", "out_dtype": "f32", "S0": "zeros",
+                   "global_batch": B, "seq_len": T, "input_sets_rotated": 3},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": alg_bytes,
+                     "kernel": f"chunk_bf16_kernel<{C},128,float,false>"},
+        "mfma": {"algorithmic_tflops": round(alg_flops / (kern_ms * 1e-3) / 1e12, 1),
+                 "algorithmic_util": round(alg_flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "issued_tflops": round(issued_flops / (kern_ms * 1e-3) / 1e12, 1),
+                 "issued_util": round(issued_flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "algorithmic_flops": alg_flops, "issued_flops": issued_flops,
+                 "peak_tflops": BF16_PEAK_TFLOPS},
+    }
+    return res, host_set0
+
+
+def bench_decode(args):
+    import numpy as np
+    import torch
+
+    import gated_linear_attention_amd as gla
+    from gated_linear_attention_amd import synth
+
+    D = synth.DECODE
+    N, H, dk, dv, steps = D["N"], D["H"], D["dk"], D["dv"], D["steps"]
+    dev = torch.device("cuda:0")
+    S = torch.from_numpy(synth.make_decode_state(N, H, dk, dv, seed=D["state_seed"])).to(dev)
+    qs, ks, vs, gs = [], [], [], []
+    for s in range(steps):
+        q, k, v, lg = synth.make_decode_step_inputs(N, H, dk, dv, seed=D["step_seed_base"] + s)
+        qs.append(torch.from_numpy(q).to(torch.bfloat16).to(dev))
+        ks.append(torch.from_numpy(k).to(torch.bfloat16).to(dev))
+        vs.append(torch.from_numpy(v).to(torch.bfloat16).to(dev))
+        gs.append(torch.from_numpy(lg).to(dev))
+    o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        gla.decode_step(qs[i % steps], ks[i % steps], vs[i % steps], gs[i % steps], S, o=o)
+
+    for i in range(min(args.warmup, 10)):
+        step(i)
+    torch.cuda.synchronize()
+    wall, kern_ms = time_launches(step, steps, stream)
+    pairs = N * H
+    alg_bytes = pairs * (2 * dk * dv * 4 + 2 * dk + 2 * dk + 2 * dv + 4 + 4 * dv)
+    gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic("decode_step_1280x16", ["decode.hip", "gla_common.h"])
+    return {
+        "metric": "decode-step state HBM GB/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "ms_per_step": 1e3 * wall / steps,
+        "kernel_ms": kern_ms,
+        "tokens_per_s": N / (1e-3 * wall / steps),
+        "config": {"workload": "decode 1280 sequences x 16 heads", "N": N, "H": H, "dk": dk,
+                   "dv": dv, "chained_steps": steps, "in_dtype": "bf16", "state": "f32 in place"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes": alg_bytes,
+                     "kernel": "decode_step_kernel<128,128,bf16,float>"},
+    }
+
+
+def cpu_baseline(host_set, target_s=10.0):
+    """Time the fp64 C oracle on a bounded sample of the headline workload:
+    all 8 sequences over a subset of heads, sized to about target_s seconds."""
+    import numpy as np
+
+    from oracle import c_oracle
+
+    q, k, v, lg = host_set
+    B, T, H, dk = q.shape
+    pick = lambda a, hs: np.ascontiguousarray(a[:, :, hs])
+    # calibrate on one head of one sequence, single-threaded
+    t0 = time.perf_counter()
+    c_oracle.fwd(pick(q[:1], [0]), pick(k[:1], [0]), pick(v[:1], [0]), pick(lg[:1], [0]),
+                 nthreads=1)
+    t1 = time.perf_counter() - t0
+    _, _, cores = c_oracle.fwd(pick(q[:1], [0]), pick(k[:1], [0]), pick(v[:1], [0]),
+                               pick(lg[:1], [0]), nthreads=0)
+    n_heads = int(max(1, min(H, round(target_s * cores / max(t1, 1e-6) / B))))
+    hs = list(range(n_heads))
+    t0 = time.perf_counter()
+    _, _, used = c_oracle.fwd(pick(q, hs), pick(k, hs), pick(v, hs), pick(lg, hs), nthreads=0)
+    el = time.perf_counter() - t0
+    tok_heads = B * T * n_heads
+    return {"value": round(tok_heads / el / H, 1), "unit": "tokens/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"train_2k: all {B} sequences x {n_heads} of {H} heads x {T} tokens "
+                      f"({tok_heads} token-heads, {el:.1f} s); value scaled to tokens/s of a "
+                      f"{H}-head layer",
+            "seconds": round(el, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--chunk", type=int, default=64, choices=[64, 128])
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: the GLA kernels here are single-device and this "
+              f"build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    log("forward: building inputs")
+    fwd, host_set = bench_forward(args)
+    log(f"forward: {fwd['value']:.4g} tokens/s, kernel {fwd['kernel_ms']:.4f} ms")
+    dec = None
+    if not args.no_decode:
+        log("decode: building inputs")
+        dec = bench_decode(args)
+        log(f"decode: {dec['value']} GB/s, kernel {dec['kernel_ms']:.4f} ms")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the fp64 oracle")
+        cpu = cpu_baseline(host_set)
+        log(f"cpu baseline: {cpu['value']} tokens/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": "GLA chunked-fwd tokens/s + MFMA util; decode-step state HBM GB/s vs peak",
+        "value": round(fwd["value"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(fwd["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": fwd["config"],
+        "kernel_ms": round(fwd["kernel_ms"], 5),
+        "roofline": fwd["roofline"],
+        "mfma": fwd["mfma"],
+        "decode": dec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

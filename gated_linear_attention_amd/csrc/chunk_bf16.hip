@@ -12,30 +12,72 @@
 // Work decomposition (MI355X): one 256-thread workgroup (4 wavefronts) owns
 // one work item (a run of one sequence's tokens) for one head and a 64-wide
 // slice of the state's columns; it walks the item's chunks in order and keeps
-// its d_k x 64 fp32 state slice in the matrix-core accumulator registers for
-// the whole run. Wavefront w owns state and output columns 16w .. 16w+15.
+// its d_k x 64 fp32 state slice in the matrix-core accumulators for the whole
+// run. Wavefront w owns state and output columns 16w .. 16w+15.
+//
+// Data movement per chunk:
+//  * Q, K (C x d_k) and the V slice (C x 64) are copied HBM -> LDS with
+//    buffer loads that write LDS directly (16 bytes per lane, no register
+//    staging); rows past the end of the run fall outside the buffer
+//    descriptor's range and arrive as zeros. Tiles are row-major with the
+//    16-byte column chunks of row r XOR-swizzled by r, so that the matrix-core
+//    operand reads of 16 consecutive rows hit distinct LDS banks.
+//  * With chunk size 64 the tiles are double-buffered: chunk n+1 streams in
+//    while chunk n computes. A 128-token chunk's tiles and P fill LDS once,
+//    so that chunk size reloads after each chunk.
+//  * Operands that need the chunk dimension as the reduction index (K^T for
+//    the state update, V for P V and K^T V) are read with the LDS transpose
+//    read (ds_read_b64_tr_b16), so no transposed copies are kept.
+//  * A chunk's outputs are stored one chunk later, so their write latency
+//    overlaps the next chunk's compute instead of the next load wait.
 // Per chunk:
-//   1. the chunk's Q, K (row-major and transposed) and V (transposed) tiles
-//      sit in LDS as bf16, with the in-chunk log2-domain gate prefix sums;
+//   1. each wavefront scans the chunk's log-gates (log2 domain) into its own
+//      LDS arrays: b2_i, 2^(b2_i), 2^(b2_last - b2_j);
 //   2. the lower-triangular 16x16 tiles of K Q^T are spread over the four
-//      wavefronts (v_mfma_f32_16x16x32_bf16), masked by the decay
-//      D_ij = 2^(b2_i - b2_j) evaluated per element, split into bf16 hi + lo
-//      parts and written to LDS as P;
+//      wavefronts (v_mfma_f32_16x16x32_bf16), masked by 2^(b2_i - b2_j)
+//      evaluated per element, split into bf16 hi + lo and written to LDS as P;
 //   3. each wavefront computes Q S from its accumulator-resident state (the
-//      accumulator layout is used directly as the B operand by permuting the
-//      reduction order of Q to match), scales rows by e^{b_i}, adds P V, and
-//      stores its 16 output columns;
+//      accumulator layout is the B operand directly; the reduction order of Q
+//      is permuted to match), scales rows by 2^(b2_i), and adds P V;
 //   4. it advances its state: S <- gamma S + K^T (kappa . V).
 // Accuracy: bf16 inputs are exact operands; every value rounded on its way
 // into an MFMA (P, S, kappa . V) is split into hi = bf16(x) and
-// lo = bf16(x - hi) and both parts are multiplied, which keeps the products
-// at ~16 significant bits with fp32 accumulation.
+// lo = bf16(x - hi) and both parts are multiplied, which keeps ~16
+// significant bits with fp32 accumulation.
 #include "gla_common.h"
 #include "gla_internal.h"
 
 namespace gla {
 
 constexpr int kBfSlice = 64;  // state columns per workgroup (4 wavefronts x 16)
+
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// LLVM's raw buffer load that writes LDS (M0 + lane * size) instead of VGPRs.
+__device__ void buffer_load_to_lds(i32x4 rsrc, lds_u32 *lds, int size, int voffset, int soffset,
+                                   int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Raw buffer descriptor: 48-bit base, stride 0, range num_bytes (loads at or
+// beyond it return 0), gfx9 data format word.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)((a >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane((int32_t)num_bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+// Workgroup barrier that orders LDS only (outstanding global loads stay in flight).
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Barrier after this wavefront's global loads (including those into LDS) landed.
+__device__ __forceinline__ void barrier_all() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -54,179 +96,98 @@ __device__ __forceinline__ WorkItem bf_item_for(const WorkItem *items, int it, i
   return w;
 }
 
-// bf16 element e (0..7) of a 16-byte vector
-__device__ __forceinline__ uint32_t bf_elem(const u32x4 &x, int e) {
-  const uint32_t w = x[e >> 1];
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+template <int C, int DK, bool SP>
+struct BfLds {
+  static constexpr int NST = C == 64 ? 2 : 1;  // LDS stages of the Q/K/V tiles (fit in 160 KB)
+  static constexpr int QR = SP ? 1 : C;                       // the state pass keeps no Q, P
+  static constexpr int PP = C + 8;                            // row pitch (bf16) of P
+  uint16_t q[NST][QR * DK];
+  uint16_t k[NST][C * DK];
+  uint16_t v[NST][C * kBfSlice];
+  float lg[NST][C];
+  uint16_t phi[QR * PP];
+  uint16_t plo[QR * PP];
+  float gb2[4][C];   // per wavefront: in-chunk prefix sums of the log-gates, log2 units
+  float glam[4][C];  // 2^(b2_i)
+  float gkap[4][C];  // 2^(b2_last - b2_j)
+};
+
+// Element offsets in the swizzled tiles: 16-byte chunk c of row r sits at chunk
+// c ^ (r mod chunks-per-row).
+template <int DK>
+__device__ __forceinline__ int qk_off(int r, int col) {
+  constexpr int CPR = DK / 8;
+  return r * DK + ((((col >> 3) ^ r) & (CPR - 1)) << 3) + (col & 7);
+}
+__device__ __forceinline__ int v_off(int r, int col) {
+  return r * kBfSlice + ((((col >> 3) ^ r) & 7) << 3) + (col & 7);
 }
 
-template <int C, int DK>
-struct BfTile {
-  static constexpr int PQ = DK + 8;  // row pitch (bf16) of Q and K: 4-bank row skew
-  static constexpr int PT = C + 8;   // row pitch of K^T, V^T and P
-  static constexpr int NKB = (C / 4) * (DK / 8);           // 4x8 blocks of a Q/K tile
-  static constexpr int NVB = (C / 4) * (kBfSlice / 8);     // 4x8 blocks of the V slice
-  static constexpr int KPT = (NKB + 255) / 256;            // blocks per thread
-  static constexpr int VPT = (NVB + 255) / 256;
-};
+__device__ __forceinline__ u32x2 lds_tr16(const uint16_t *p) {
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+  return __builtin_bit_cast(u32x2, x);
+}
 
-template <int C, int DK>
-struct alignas(16) BfLds {
-  using L = BfTile<C, DK>;
-  uint16_t Q[C * L::PQ];
-  uint16_t K[C * L::PQ];
-  uint16_t Kt[DK * L::PT];
-  uint16_t Vt[kBfSlice * L::PT];
-  uint16_t Phi[C * L::PT];
-  uint16_t Plo[C * L::PT];
-  float b2[C];    // in-chunk inclusive prefix sum of the log-gates, in log2 units
-  float lam[C];   // 2^(b2_i)
-  float kap[C];   // 2^(b2_last - b2_j)
-  float gam;      // 2^(b2_last): decay over the chunk
-  float lsum;     // sum of the chunk's natural-log gates
-};
-
-template <int C, int DK, bool STATE_PASS>
-struct BfPrefetch {
-  using L = BfTile<C, DK>;
-  u32x4 q[STATE_PASS ? 1 : L::KPT][4];
-  u32x4 k[L::KPT][4];
-  u32x4 v[L::VPT][4];
-  float lg[C / 64];
-};
-
-template <int C, int DK, bool STATE_PASS>
-__device__ __forceinline__ void bf_load(BfPrefetch<C, DK, STATE_PASS> &pf, const uint16_t *q,
-                                        const uint16_t *k, const uint16_t *v, const float *lg,
-                                        int t0, int n, int H, int h, int DV, int col0) {
-  using L = BfTile<C, DK>;
-  const int tid = threadIdx.x;
-  const u32x4 z = {0u, 0u, 0u, 0u};
+// Issue the HBM -> LDS copies of one chunk (rows [t0, t0 + n) of the run) into
+// stage `st`. Every wavefront copies a quarter of each tile.
+template <int C, int DK, bool SP>
+__device__ __forceinline__ void issue_chunk_loads(BfLds<C, DK, SP> &s, int st,
+                                                  const uint16_t *q, const uint16_t *k,
+                                                  const uint16_t *v, const float *lg, int t0,
+                                                  int n, int H, int h, int DV, int col0,
+                                                  int wave, int lane) {
+  constexpr int CPR = DK / 8;                    // 16-byte chunks per Q/K row
+  constexpr int QB = C * DK * 2 / 1024;          // 1 KB blocks per Q/K tile
+  constexpr int RPB = 1024 / (DK * 2);           // rows per block
+  constexpr int VB = C * kBfSlice * 2 / 1024;    // 1 KB blocks of the V slice (8 rows each)
+  const size_t tok0 = (size_t)t0 * H + h;
+  const uint32_t qk_row = (uint32_t)H * DK * 2, v_row = (uint32_t)H * DV * 2;
+  const i32x4 rk = make_rsrc(k + tok0 * DK, (n - 1) * qk_row + DK * 2);
+  const i32x4 rv = make_rsrc(v + tok0 * DV + col0, (n - 1) * v_row + kBfSlice * 2);
 #pragma unroll
-  for (int m = 0; m < L::KPT; ++m) {
-    const int b = tid + 256 * m;
-    const int jb = b / (DK / 8), db = b % (DK / 8);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = 4 * jb + r;
-      const bool ok = (b < L::NKB) && (j < n);
-      const size_t off = ((size_t)(t0 + j) * H + h) * DK + 8 * db;
-      pf.k[m][r] = ok ? *reinterpret_cast<const u32x4 *>(k + off) : z;
-      if (!STATE_PASS) pf.q[m][r] = ok ? *reinterpret_cast<const u32x4 *>(q + off) : z;
+  for (int i = 0; i < QB / 4; ++i) {
+    const int blk = wave * (QB / 4) + i;
+    const int r = blk * RPB + lane / CPR;
+    const int c = (lane % CPR) ^ (r & (CPR - 1));
+    const int off = r * qk_row + c * 16;
+    buffer_load_to_lds(rk, (lds_u32 *)&s.k[st][blk * 512], 16, off, 0, 0, 0);
+    if (!SP) {
+      const i32x4 rq = make_rsrc(q + tok0 * DK, (n - 1) * qk_row + DK * 2);
+      buffer_load_to_lds(rq, (lds_u32 *)&s.q[st][blk * 512], 16, off, 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int m = 0; m < L::VPT; ++m) {
-    const int b = tid + 256 * m;
-    const int jb = b / (kBfSlice / 8), cb = b % (kBfSlice / 8);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = 4 * jb + r;
-      const bool ok = (b < L::NVB) && (j < n);
-      pf.v[m][r] = ok ? *reinterpret_cast<const u32x4 *>(
-                            v + ((size_t)(t0 + j) * H + h) * DV + col0 + 8 * cb)
-                      : z;
-    }
+  for (int i = 0; i < VB / 4; ++i) {
+    const int blk = wave * (VB / 4) + i;
+    const int r = blk * 8 + lane / 8;
+    const int c = (lane % 8) ^ (r & 7);
+    buffer_load_to_lds(rv, (lds_u32 *)&s.v[st][blk * 512], 16, r * v_row + c * 16, 0, 0, 0);
   }
-  if (tid < 64) {
+  if (wave == 0) {
+    const i32x4 rg = make_rsrc(lg + tok0, (n - 1) * (uint32_t)H * 4 + 4);
 #pragma unroll
-    for (int e = 0; e < C / 64; ++e) {
-      const int j = tid * (C / 64) + e;
-      pf.lg[e] = (j < n) ? lg[(size_t)(t0 + j) * H + h] : 0.f;
-    }
+    for (int i = 0; i < C / 64; ++i)
+      buffer_load_to_lds(rg, (lds_u32 *)&s.lg[st][64 * i], 4, (64 * i + lane) * H * 4, 0, 0, 0);
   }
 }
 
-// Write a prefetched chunk into LDS: Q and K row-major, K and V transposed, and
-// the gate prefix sums (wavefront 0).
-template <int C, int DK, bool STATE_PASS>
-__device__ __forceinline__ void bf_store(const BfPrefetch<C, DK, STATE_PASS> &pf,
-                                         BfLds<C, DK> &s) {
-  using L = BfTile<C, DK>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int m = 0; m < L::KPT; ++m) {
-    const int b = tid + 256 * m;
-    if (b < L::NKB) {
-      const int jb = b / (DK / 8), db = b % (DK / 8);
-      if (!STATE_PASS) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          *reinterpret_cast<u32x4 *>(&s.Q[(4 * jb + r) * L::PQ + 8 * db]) = pf.q[m][r];
-          *reinterpret_cast<u32x4 *>(&s.K[(4 * jb + r) * L::PQ + 8 * db]) = pf.k[m][r];
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u32x2 w;
-        w.x = bf_elem(pf.k[m][0], e) | (bf_elem(pf.k[m][1], e) << 16);
-        w.y = bf_elem(pf.k[m][2], e) | (bf_elem(pf.k[m][3], e) << 16);
-        *reinterpret_cast<u32x2 *>(&s.Kt[(8 * db + e) * L::PT + 4 * jb]) = w;
-      }
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < L::VPT; ++m) {
-    const int b = tid + 256 * m;
-    if (b < L::NVB) {
-      const int jb = b / (kBfSlice / 8), cb = b % (kBfSlice / 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u32x2 w;
-        w.x = bf_elem(pf.v[m][0], e) | (bf_elem(pf.v[m][1], e) << 16);
-        w.y = bf_elem(pf.v[m][2], e) | (bf_elem(pf.v[m][3], e) << 16);
-        *reinterpret_cast<u32x2 *>(&s.Vt[(8 * cb + e) * L::PT + 4 * jb]) = w;
-      }
-    }
-  }
-  if (tid < 64) {
-    // inclusive scan of the chunk's log-gates (lane owns C/64 consecutive ones)
-    constexpr int E = C / 64;
-    float part[E];
-    float run = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      run += pf.lg[e];
-      part[e] = run;
-    }
-    float incl = run;
-#pragma unroll
-    for (int off = 1; off < 64; off *= 2) {
-      const float y = __shfl_up(incl, off);
-      if (tid >= off) incl += y;
-    }
-    const float excl = incl - run;
-    const float total = __shfl(incl, 63);
-    const float b2last = total * kLog2e;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = tid * E + e;
-      const float b2 = (excl + part[e]) * kLog2e;
-      s.b2[j] = b2;
-      s.lam[j] = fast_exp2(b2);
-      s.kap[j] = fast_exp2(b2last - b2);
-    }
-    if (tid == 0) {
-      s.gam = fast_exp2(b2last);
-      s.lsum = total;
-    }
-  }
-}
-
-template <int C, int DK, typename Tout, bool STATE_PASS>
+template <int C, int DK, typename Tout, bool SP>
 __global__ __launch_bounds__(256) void chunk_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ lg, const float *__restrict__ S0,
     float *__restrict__ ST, Tout *__restrict__ o, const WorkItem *__restrict__ items,
     const int *__restrict__ n_items, float *__restrict__ slots, float *__restrict__ slot_gamma,
     int T, int H, int DV, int n_pairs) {
-  using L = BfTile<C, DK>;
-  constexpr int NM = C / 16;   // 16-row tiles of the chunk
-  constexpr int NKS = DK / 32; // 32-deep k-steps over d_k
-  constexpr int NT = DK / 16;  // 16-row tiles of the state
-  constexpr int NJS = C / 32;  // 32-deep k-steps over the chunk
+  using LDS = BfLds<C, DK, SP>;
+  constexpr int NST = LDS::NST;
+  constexpr int PP = LDS::PP;
+  constexpr int NM = C / 16;                // 16-row tiles of the chunk
+  constexpr int NKS = DK / 32;              // 32-deep k-steps over d_k
+  constexpr int NT = DK / 16;               // 16-row tiles of the state
+  constexpr int NJS = C / 32;               // 32-deep k-steps over the chunk
   constexpr int NTILE = NM * (NM + 1) / 2;  // lower-triangular score tiles
-  __shared__ BfLds<C, DK> s;
+  constexpr int E = C / 64;                 // gate positions per lane
+  __shared__ LDS s;
 
   // Block -> (pair = item * H + head, column slice). Slices of one pair are
   // placed on the same XCD (workgroups are dealt to the 8 XCDs round-robin),
@@ -249,7 +210,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
   const WorkItem w = bf_item_for(items, it, T);
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   const int ln = lane % 16, lg4 = lane / 16;  // MFMA lane coordinates
   const int col0 = slice * kBfSlice;          // first state column of the slice
   const int wcol = 16 * wave;                 // wavefront's columns within the slice
@@ -259,42 +220,97 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
   f32x4 S_acc[NT];
   {
     const float *sin = nullptr;
-    if (!STATE_PASS) {
+    if (!SP) {
       if (w.state_in >= 0) sin = slots + ((size_t)w.state_in * H + h) * dkdv;
       else if (S0) sin = S0 + ((size_t)w.seq * H + h) * dkdv;
     }
+    if (sin) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        S_acc[t][r] = sin ? sin[(size_t)(16 * t + 4 * lg4 + r) * DV + col0 + wcol + ln] : 0.f;
+        for (int r = 0; r < 4; ++r)
+          S_acc[t][r] = sin[(size_t)(16 * t + 4 * lg4 + r) * DV + col0 + wcol + ln];
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) S_acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   }
 
   // Score tiles above the diagonal are never written: zero P once.
-  if (!STATE_PASS) {
-    for (int i = tid; i < C * L::PT / 2; i += 256) {
-      reinterpret_cast<uint32_t *>(s.Phi)[i] = 0u;
-      reinterpret_cast<uint32_t *>(s.Plo)[i] = 0u;
+  if (!SP) {
+    for (int i = tid; i < C * PP / 2; i += 256) {
+      reinterpret_cast<uint32_t *>(s.phi)[i] = 0u;
+      reinterpret_cast<uint32_t *>(s.plo)[i] = 0u;
     }
   }
 
   float lsum = 0.f;
-  BfPrefetch<C, DK, STATE_PASS> pf;
+  f32x4 O_prev[SP ? 1 : NM];
+  int t_prev = -1, n_prev = 0;
   int t0 = w.tok_begin;
-  if (t0 < w.tok_end) {
-    bf_load<C, DK, STATE_PASS>(pf, q, k, v, lg, t0, min(C, w.tok_end - t0), H, h, DV, col0);
-    bf_store<C, DK, STATE_PASS>(pf, s);
-  }
-  __syncthreads();
+  if (t0 < w.tok_end)
+    issue_chunk_loads<C, DK, SP>(s, 0, q, k, v, lg, t0, min(C, w.tok_end - t0), H, h, DV, col0,
+                                 wave, lane);
 
-  for (; t0 < w.tok_end; t0 += C) {
+  for (int ci = 0; t0 < w.tok_end; t0 += C, ++ci) {
     const int n = min(C, w.tok_end - t0);
     const int t1 = t0 + C;
-    if (t1 < w.tok_end)  // prefetch the next chunk into registers
-      bf_load<C, DK, STATE_PASS>(pf, q, k, v, lg, t1, min(C, w.tok_end - t1), H, h, DV, col0);
+    const int st = (NST == 2) ? (ci & 1) : 0;
+    barrier_all();  // chunk ci's tiles are in LDS; every wavefront left chunk ci-1
 
-    f32x4 O_acc[STATE_PASS ? 1 : NM];
-    if (!STATE_PASS) {
+    // ---- outputs of the previous chunk (stored now so their latency overlaps)
+    if (!SP && t_prev >= 0) {
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * mi + 4 * lg4 + r;
+          if (i < n_prev)
+            store_from_f32(o, ((size_t)(t_prev + i) * H + h) * DV + col0 + wcol + ln,
+                           O_prev[mi][r]);
+        }
+    }
+    if (NST == 2 && t1 < w.tok_end)
+      issue_chunk_loads<C, DK, SP>(s, st ^ 1, q, k, v, lg, t1, min(C, w.tok_end - t1), H, h, DV,
+                                   col0, wave, lane);
+
+    const uint16_t *sq = s.q[SP ? 0 : st];
+    const uint16_t *sk = s.k[st];
+    const uint16_t *sv = s.v[st];
+
+    // ---- gates: each wavefront scans the chunk's log-gates into its own arrays
+    float gam;
+    {
+      float part[E];
+      float run = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        run += s.lg[st][lane * E + e];
+        part[e] = run;
+      }
+      float incl = run;
+#pragma unroll
+      for (int off = 1; off < 64; off *= 2) {
+        const float y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      const float excl = incl - run;
+      const float total = __shfl(incl, 63);
+      const float b2last = total * kLog2e;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int j = lane * E + e;
+        const float b2 = (excl + part[e]) * kLog2e;
+        s.gb2[wave][j] = b2;
+        s.glam[wave][j] = fast_exp2(b2);
+        s.gkap[wave][j] = fast_exp2(b2last - b2);
+      }
+      gam = fast_exp2(b2last);
+      lsum += total;
+    }
+
+    f32x4 O_acc[SP ? 1 : NM];
+    if (!SP) {
       // ---- scores: lower-triangular 16x16 tiles of A^T = K Q^T, dealt round-robin
       for (int tile = wave; tile < NTILE; tile += 4) {
         int ti = 0, rem = tile;  // tile -> (ti, tj) with tj <= ti
@@ -304,33 +320,28 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
         }
         const int tj = rem;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int rk = 16 * tj + ln, rq = 16 * ti + ln;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          const u32x4 a = *reinterpret_cast<const u32x4 *>(
-              &s.K[(16 * tj + ln) * L::PQ + 32 * ks + 8 * lg4]);
-          const u32x4 b = *reinterpret_cast<const u32x4 *>(
-              &s.Q[(16 * ti + ln) * L::PQ + 32 * ks + 8 * lg4]);
+          const u32x4 a = *reinterpret_cast<const u32x4 *>(&sk[qk_off<DK>(rk, 32 * ks + 8 * lg4)]);
+          const u32x4 b = *reinterpret_cast<const u32x4 *>(&sq[qk_off<DK>(rq, 32 * ks + 8 * lg4)]);
           acc = mfma16(a, b, acc);
         }
         // acc[r] = A^T[j][i] with j = 16 tj + 4 lg4 + r, i = 16 ti + ln
         const int i = 16 * ti + ln;
-        const float b2i = s.b2[i];
+        const float b2i = s.gb2[wave][i];
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = 16 * tj + 4 * lg4 + r;
-          p[r] = (j <= i) ? acc[r] * fast_exp2(b2i - s.b2[j]) : 0.f;
+          p[r] = (j <= i) ? acc[r] * fast_exp2(b2i - s.gb2[wave][j]) : 0.f;
         }
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) split_bf16(p[r], hi[r], lo[r]);
-        u32x2 wh, wl;
-        wh.x = hi[0] | (hi[1] << 16);
-        wh.y = hi[2] | (hi[3] << 16);
-        wl.x = lo[0] | (lo[1] << 16);
-        wl.y = lo[2] | (lo[3] << 16);
-        *reinterpret_cast<u32x2 *>(&s.Phi[i * L::PT + 16 * tj + 4 * lg4]) = wh;
-        *reinterpret_cast<u32x2 *>(&s.Plo[i * L::PT + 16 * tj + 4 * lg4]) = wl;
+        uint32_t h0, l0, h1, l1;
+        split_pk_bf16(p[0], p[1], h0, l0);
+        split_pk_bf16(p[2], p[3], h1, l1);
+        const u32x2 wh = {h0, h1}, wl = {l0, l1};
+        *reinterpret_cast<u32x2 *>(&s.phi[i * PP + 16 * tj + 4 * lg4]) = wh;
+        *reinterpret_cast<u32x2 *>(&s.plo[i * PP + 16 * tj + 4 * lg4]) = wl;
       }
 
       // ---- inter-chunk read of the state: O = Q S (before this chunk's update)
@@ -340,23 +351,18 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
       for (int ks = 0; ks < NKS; ++ks) {
         // B operand from the accumulators: slot 8*lg4 + r <-> d = 32ks + 4lg4 + r,
         // slot 8*lg4 + 4 + r <-> d = 32ks + 16 + 4lg4 + r.
-        uint32_t h0[8], l0[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          split_bf16(S_acc[2 * ks][r], h0[r], l0[r]);
-          split_bf16(S_acc[2 * ks + 1][r], h0[4 + r], l0[4 + r]);
-        }
-        u32x4 bh, bl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bh[e] = h0[2 * e] | (h0[2 * e + 1] << 16);
-          bl[e] = l0[2 * e] | (l0[2 * e + 1] << 16);
-        }
+        uint32_t sh[4], sl[4];
+        split_pk_bf16(S_acc[2 * ks][0], S_acc[2 * ks][1], sh[0], sl[0]);
+        split_pk_bf16(S_acc[2 * ks][2], S_acc[2 * ks][3], sh[1], sl[1]);
+        split_pk_bf16(S_acc[2 * ks + 1][0], S_acc[2 * ks + 1][1], sh[2], sl[2]);
+        split_pk_bf16(S_acc[2 * ks + 1][2], S_acc[2 * ks + 1][3], sh[3], sl[3]);
+        const u32x4 bh = {sh[0], sh[1], sh[2], sh[3]}, bl = {sl[0], sl[1], sl[2], sl[3]};
 #pragma unroll
         for (int mi = 0; mi < NM; ++mi) {
-          const uint16_t *qrow = &s.Q[(16 * mi + ln) * L::PQ + 32 * ks + 4 * lg4];
-          const u32x2 qa = *reinterpret_cast<const u32x2 *>(qrow);
-          const u32x2 qb = *reinterpret_cast<const u32x2 *>(qrow + 16);
+          const int r = 16 * mi + ln;
+          const u32x2 qa = *reinterpret_cast<const u32x2 *>(&sq[qk_off<DK>(r, 32 * ks + 4 * lg4)]);
+          const u32x2 qb =
+              *reinterpret_cast<const u32x2 *>(&sq[qk_off<DK>(r, 32 * ks + 16 + 4 * lg4)]);
           const u32x4 a = {qa.x, qa.y, qb.x, qb.y};
           O_acc[mi] = mfma16(a, bh, O_acc[mi]);
           O_acc[mi] = mfma16(a, bl, O_acc[mi]);
@@ -366,78 +372,93 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
 #pragma unroll
       for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) O_acc[mi][r] *= s.lam[16 * mi + 4 * lg4 + r];
+        for (int r = 0; r < 4; ++r) O_acc[mi][r] *= s.glam[wave][16 * mi + 4 * lg4 + r];
     }
-    __syncthreads();  // P complete
+    barrier_lds();  // P complete
 
-    // V fragments of this wavefront's 16 columns: slot 8 lg4 + e <-> j = 32 js + 8 lg4 + e
+    // V fragments of this wavefront's 16 columns (transpose reads):
+    // slot 8 lg4 + e <-> j = 32 js + 8 lg4 + e, column wcol + ln.
     u32x4 vf[NJS];
 #pragma unroll
-    for (int js = 0; js < NJS; ++js)
-      vf[js] = *reinterpret_cast<const u32x4 *>(&s.Vt[(wcol + ln) * L::PT + 32 * js + 8 * lg4]);
+    for (int js = 0; js < NJS; ++js) {
+      const int r0 = 32 * js + 8 * lg4 + (ln >> 2);
+      const int c = wcol + 4 * (ln & 3);
+      const u32x2 x0 = lds_tr16(&sv[v_off(r0, c)]);
+      const u32x2 x1 = lds_tr16(&sv[v_off(r0 + 4, c)]);
+      vf[js] = u32x4{x0.x, x0.y, x1.x, x1.y};
+    }
 
-    if (!STATE_PASS) {
+    if (!SP) {
       // ---- intra-chunk: O += P V over the causal k-steps
 #pragma unroll
       for (int mi = 0; mi < NM; ++mi) {
 #pragma unroll
         for (int js = 0; js < NJS; ++js) {
           if (32 * js <= 16 * mi + 15) {
-            const int off = (16 * mi + ln) * L::PT + 32 * js + 8 * lg4;
-            const u32x4 ph = *reinterpret_cast<const u32x4 *>(&s.Phi[off]);
-            const u32x4 pl = *reinterpret_cast<const u32x4 *>(&s.Plo[off]);
+            const int off = (16 * mi + ln) * PP + 32 * js + 8 * lg4;
+            const u32x4 ph = *reinterpret_cast<const u32x4 *>(&s.phi[off]);
+            const u32x4 pl = *reinterpret_cast<const u32x4 *>(&s.plo[off]);
             O_acc[mi] = mfma16(ph, vf[js], O_acc[mi]);
             O_acc[mi] = mfma16(pl, vf[js], O_acc[mi]);
           }
         }
       }
-      // ---- store this wavefront's 16 output columns of the valid rows
-#pragma unroll
-      for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * mi + 4 * lg4 + r;
-          if (i < n)
-            store_from_f32(o, ((size_t)(t0 + i) * H + h) * DV + col0 + wcol + ln, O_acc[mi][r]);
-        }
     }
 
     // ---- state advance: S <- gamma S + K^T (kappa . V)
-    const float gam = s.gam;
-    lsum += s.lsum;
 #pragma unroll
     for (int t = 0; t < NT; ++t) S_acc[t] *= gam;
 #pragma unroll
     for (int js = 0; js < NJS; ++js) {
-      u32x4 bh, bl;
+      uint32_t kh[4], kl[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        uint32_t h2[2], l2[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int e = 2 * e2 + x;
-          const float kv = s.kap[32 * js + 8 * lg4 + e] * bf16_bits_to_f32(bf_elem(vf[js], e));
-          split_bf16(kv, h2[x], l2[x]);
-        }
-        bh[e2] = h2[0] | (h2[1] << 16);
-        bl[e2] = l2[0] | (l2[1] << 16);
+        const int j = 32 * js + 8 * lg4 + 2 * e2;
+        const uint32_t vw = vf[js][e2];
+        const float v0 = __uint_as_float(vw << 16), v1 = __uint_as_float(vw & 0xffff0000u);
+        split_pk_bf16(s.gkap[wave][j] * v0, s.gkap[wave][j + 1] * v1, kh[e2], kl[e2]);
       }
+      const u32x4 bh = {kh[0], kh[1], kh[2], kh[3]}, bl = {kl[0], kl[1], kl[2], kl[3]};
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4 *>(&s.Kt[(16 * t + ln) * L::PT + 32 * js + 8 * lg4]);
+        // A operand K^T: slot 8 lg4 + e <-> j = 32 js + 8 lg4 + e, d = 16 t + ln
+        const int r0 = 32 * js + 8 * lg4 + (ln >> 2);
+        const int c = 16 * t + 4 * (ln & 3);
+        const u32x2 x0 = lds_tr16(&sk[qk_off<DK>(r0, c)]);
+        const u32x2 x1 = lds_tr16(&sk[qk_off<DK>(r0 + 4, c)]);
+        const u32x4 a = {x0.x, x0.y, x1.x, x1.y};
         S_acc[t] = mfma16(a, bh, S_acc[t]);
         S_acc[t] = mfma16(a, bl, S_acc[t]);
       }
     }
-    __syncthreads();  // everyone is done with this chunk's LDS
-    if (t1 < w.tok_end) bf_store<C, DK, STATE_PASS>(pf, s);
-    __syncthreads();
+
+    if (!SP) {
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi) O_prev[mi] = O_acc[mi];
+      t_prev = t0;
+      n_prev = n;
+    }
+    if (NST == 1 && t1 < w.tok_end) {
+      barrier_lds();  // every wavefront is done with the single stage
+      issue_chunk_loads<C, DK, SP>(s, 0, q, k, v, lg, t1, min(C, w.tok_end - t1), H, h, DV,
+                                   col0, wave, lane);
+    }
   }
 
-  // ---- final state of the run
+  // ---- last chunk's outputs, final state of the run
+  if (!SP && t_prev >= 0) {
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * mi + 4 * lg4 + r;
+        if (i < n_prev)
+          store_from_f32(o, ((size_t)(t_prev + i) * H + h) * DV + col0 + wcol + ln,
+                         O_prev[mi][r]);
+      }
+  }
   float *sout = nullptr;
-  if (STATE_PASS) {
+  if (SP) {
     sout = slots + ((size_t)w.state_out * H + h) * dkdv;
     if (slice == 0 && tid == 0) slot_gamma[(size_t)w.state_out * H + h] = lsum;
   } else if (w.state_out == -1 && ST) {
@@ -488,14 +509,18 @@ hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_
                              const FwdDims &d, const WorkItem *items, const int *n_items,
                              int grid_items, float *slots, float *slot_gamma, bool state_pass,
                              hipStream_t stream) {
-  // The C ABI admits chunk_size 64 only on this path: a 128-token chunk's
-  // bf16 tiles (Q, K, K^T, V^T, P hi/lo) would exceed the 160 KB of LDS.
-  if (d.C != 64) return hipErrorInvalidValue;
+  if (d.C == 64) {
+    if (d.dk == 128)
+      return launch_bf_c<64, 128>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items,
+                                  grid_items, slots, slot_gamma, state_pass, stream);
+    return launch_bf_c<64, 64>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
+                               slots, slot_gamma, state_pass, stream);
+  }
   if (d.dk == 128)
-    return launch_bf_c<64, 128>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
-                                slots, slot_gamma, state_pass, stream);
-  return launch_bf_c<64, 64>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
-                             slots, slot_gamma, state_pass, stream);
+    return launch_bf_c<128, 128>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items,
+                                 grid_items, slots, slot_gamma, state_pass, stream);
+  return launch_bf_c<128, 64>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
+                              slots, slot_gamma, state_pass, stream);
 }
 
 }  // namespace gla

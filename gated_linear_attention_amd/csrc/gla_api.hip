@@ -155,7 +155,6 @@ gla_status gla_fwd_chunked(const void *q, const void *k, const void *v, const fl
   if ((long)B * T > INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
   if (!supported_head_dim(dk) || !supported_head_dim(dv)) return GLA_ERR_UNSUPPORTED;
   if (chunk_size != 64 && chunk_size != 128) return GLA_ERR_UNSUPPORTED;
-  if (in_dtype == GLA_BF16 && chunk_size != 64) return GLA_ERR_UNSUPPORTED;
   const int N = num_seqs;
   if (H == 0 || N == 0) return GLA_OK;
   const size_t ntok = (size_t)B * T * H;

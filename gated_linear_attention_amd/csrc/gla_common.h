@@ -13,6 +13,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // bf16 is stored as the upper 16 bits of a binary32; widening is a shift.
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
@@ -39,6 +43,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) {
   hi = f32_to_bf16_bits(x);
   lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+// Two floats to packed bf16 (round to nearest even) with one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// hi/lo split of two floats at once: returns packed bf16 pairs hi = bf16(x),
+// lo = bf16(x - hi) (element 0 in the low half).
+__device__ __forceinline__ void split_pk_bf16(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = cvt_pk_bf16(a, b);
+  const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
+  lo = cvt_pk_bf16(a - ha, b - hb);
 }
 
 // 2^x on the hardware exp unit (v_exp_f32).

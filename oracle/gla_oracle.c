@@ -35,10 +35,13 @@ int gla_oracle_fwd(const float *q, const float *k, const float *v, const float *
                    int dv, int N, double *o, double *ST, int nthreads) {
   int used = 1;
 #ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
+  const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+  const int nt = 1;
+  (void)nthreads;
 #endif
   const long pairs = (long)N * H;
-#pragma omp parallel
+#pragma omp parallel num_threads(nt)
   {
 #ifdef _OPENMP
 #pragma omp single
@@ -94,10 +97,13 @@ int gla_oracle_decode(const float *q, const float *k, const float *v, const floa
                       double *S, double *o, int N, int H, int dk, int dv, int nthreads) {
   int used = 1;
 #ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
+  const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+  const int nt = 1;
+  (void)nthreads;
 #endif
   const long pairs = (long)N * H;
-#pragma omp parallel
+#pragma omp parallel num_threads(nt)
   {
 #ifdef _OPENMP
 #pragma omp single

@@ -56,7 +56,6 @@ def test_fwd_rejects_bad_arguments_before_launch():
     assert _fwd(dk=96, **P) == _lib.GLA_ERR_UNSUPPORTED
     assert _fwd(dv=192, **P) == _lib.GLA_ERR_UNSUPPORTED
     assert _fwd(C=32, **P) == _lib.GLA_ERR_UNSUPPORTED
-    assert _fwd(C=128, **P) == _lib.GLA_ERR_UNSUPPORTED                # bf16 path: C = 64
     assert _fwd(**{**P, "q": None}) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert _fwd(**{**P, "o": P["q"] + 64}) == _lib.GLA_ERR_INVALID_ARGUMENT  # o overlaps q
     assert _fwd(cu=FAKE + (5 << 30), B=2, N=2, **P) == _lib.GLA_ERR_INVALID_ARGUMENT

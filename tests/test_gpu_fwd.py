@@ -65,12 +65,13 @@ def test_tiny_f32_workload(C):
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
 @pytest.mark.parametrize("T", [64, 300, 1])
-def test_bf16_shapes(dk, dv, T):
+@pytest.mark.parametrize("C", [64, 128])
+def test_bf16_shapes(dk, dv, T, C):
     """Several tiles, a ragged tail chunk, a single token; nonzero S0."""
-    gu.say(f"bf16 dk={dk} dv={dv} T={T}")
+    gu.say(f"bf16 dk={dk} dv={dv} T={T} C={C}")
     w = synth.Workload("t", B=2, T=T, H=3, dk=dk, dv=dv, dtype="bf16", gate_bias=3.0,
-                       s0_std=0.02, chunk=64, seed=11)
-    check(*synth.make_forward_inputs(w), "bf16", tight=2e-5)
+                       s0_std=0.02, chunk=C, seed=11)
+    check(*synth.make_forward_inputs(w), "bf16", C=C, tight=2e-5)
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
@@ -118,16 +119,16 @@ def test_varlen_with_edge_lengths(dtype):
     check(q, k, v, lg, S0, cu, dtype)
 
 
-@pytest.mark.parametrize("seg", [64, 128, 192])
+@pytest.mark.parametrize("seg,C", [(64, 64), (128, 64), (192, 64), (256, 128)])
 @pytest.mark.parametrize("varlen", [False, True])
-def test_forced_segment_split(seg, varlen, monkeypatch):
+def test_forced_segment_split(seg, C, varlen, monkeypatch):
     """Sequences split into segments: state pass, combine, output pass."""
-    gu.say(f"segment split seg_len={seg} varlen={varlen}")
+    gu.say(f"segment split seg_len={seg} C={C} varlen={varlen}")
     monkeypatch.setenv("GLA_SEG_LEN", str(seg))
     w = synth.Workload("t", B=2, T=500, H=2, dk=128, dv=128, dtype="bf16", gate_bias=3.0,
-                       s0_std=0.03, chunk=64, seed=17)
+                       s0_std=0.03, chunk=C, seed=17)
     lengths = [500, 0, 37, 321, 129] if varlen else None
-    check(*synth.make_forward_inputs(w, lengths=lengths), "bf16")
+    check(*synth.make_forward_inputs(w, lengths=lengths), "bf16", C=C)
 
 
 def test_forced_segment_split_f32(monkeypatch):
@@ -150,21 +151,24 @@ def test_chunk_size_independence_f32():
 
 
 # ----------------------------------------------------------- full-size workloads
-def test_train_2k_full_size_sampled_heads():
+@pytest.mark.parametrize("C", [64, 128])
+def test_train_2k_full_size_sampled_heads(C):
     """B=8, H=16, T=2048, d=128, bf16, S0 = 0: all heads run on the GPU; the
     oracle checks 3 heads of every sequence."""
-    gu.say("train_2k full size")
-    check(*synth.make_forward_inputs(W["train_2k"]), "bf16", heads=[0, 7, 15], tight=1e-4)
+    gu.say(f"train_2k full size C={C}")
+    check(*synth.make_forward_inputs(W["train_2k"]), "bf16", C=C, heads=[0, 7, 15], tight=1e-4)
 
 
-def test_prefill_64k_full_size_sampled_heads():
+@pytest.mark.parametrize("C", [64, 128])
+def test_prefill_64k_full_size_sampled_heads(C):
     """B=1, H=32, T=65536, d=128, bf16, nonzero S0, split into segments; the
     oracle checks 2 heads over the whole sequence."""
-    gu.say("prefill_64k full size")
-    check(*synth.make_forward_inputs(W["prefill_64k"]), "bf16", heads=[3, 30], tight=1e-4)
+    gu.say(f"prefill_64k full size C={C}")
+    check(*synth.make_forward_inputs(W["prefill_64k"]), "bf16", C=C, heads=[3, 30], tight=1e-4)
 
 
-def test_varlen_64_full_size_sampled_heads():
+@pytest.mark.parametrize("C", [64, 128])
+def test_varlen_64_full_size_sampled_heads(C):
     """64 packed sequences, lengths uniform in [128, 8192], H=16, d=128, bf16."""
-    gu.say("varlen_64 full size")
-    check(*synth.make_forward_inputs(W["varlen_64"]), "bf16", heads=[1, 12], tight=1e-4)
+    gu.say(f"varlen_64 full size C={C}")
+    check(*synth.make_forward_inputs(W["varlen_64"]), "bf16", C=C, heads=[1, 12], tight=1e-4)
