@@ -25,6 +25,9 @@ FLAGS = [
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
+    # keep matrix-core accumulators in VGPRs (VALU work on them then needs no
+    # AGPR <-> VGPR copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -36,9 +36,12 @@
 //   2. the lower-triangular 16x16 tiles of K Q^T are spread over the four
 //      wavefronts (v_mfma_f32_16x16x32_bf16), masked by 2^(b2_i - b2_j)
 //      evaluated per element, split into bf16 hi + lo and written to LDS as P;
-//   3. each wavefront computes Q S from its accumulator-resident state (the
-//      accumulator layout is the B operand directly; the reduction order of Q
-//      is permuted to match), scales rows by 2^(b2_i), and adds P V;
+//   3. each wavefront computes its 16 output columns transposed,
+//      O^T = S^T Q^T + V^T P^T, so that each lane ends up holding four
+//      consecutive columns of one output row (one 16-byte store): the state
+//      accumulators serve directly as the S^T operand (the reduction order of
+//      Q is permuted to match their layout), and the rows of O (columns of
+//      O^T) are scaled by 2^(b2_i) before P V is added;
 //   4. it advances its state: S <- gamma S + K^T (kappa . V).
 // Accuracy: bf16 inputs are exact operands; every value rounded on its way
 // into an MFMA (P, S, kappa . V) is split into hi = bf16(x) and
@@ -258,17 +261,14 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
     const int st = (NST == 2) ? (ci & 1) : 0;
     barrier_all();  // chunk ci's tiles are in LDS; every wavefront left chunk ci-1
 
-    // ---- outputs of the previous chunk (stored now so their latency overlaps)
+    // ---- outputs of the previous chunk (stored now so their latency overlaps).
+    // O_prev[mi][r] = O[16 mi + ln][wcol + 4 lg4 + r]: one 16-byte row piece.
     if (!SP && t_prev >= 0) {
+      Tout *ob = o + ((size_t)(t_prev + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
+      const size_t rs16 = (size_t)16 * H * DV;  // 16 rows
 #pragma unroll
       for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * mi + 4 * lg4 + r;
-          if (i < n_prev)
-            store_from_f32(o, ((size_t)(t_prev + i) * H + h) * DV + col0 + wcol + ln,
-                           O_prev[mi][r]);
-        }
+        if (16 * mi + ln < n_prev) store4_from_f32(ob + mi * rs16, O_prev[mi]);
     }
     if (NST == 2 && t1 < w.tok_end)
       issue_chunk_loads<C, DK, SP>(s, st ^ 1, q, k, v, lg, t1, min(C, w.tok_end - t1), H, h, DV,
@@ -344,13 +344,14 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
         *reinterpret_cast<u32x2 *>(&s.plo[i * PP + 16 * tj + 4 * lg4]) = wl;
       }
 
-      // ---- inter-chunk read of the state: O = Q S (before this chunk's update)
+      // ---- inter-chunk read of the state: O^T = S^T Q^T (before this chunk's update)
 #pragma unroll
       for (int mi = 0; mi < NM; ++mi) O_acc[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        // B operand from the accumulators: slot 8*lg4 + r <-> d = 32ks + 4lg4 + r,
-        // slot 8*lg4 + 4 + r <-> d = 32ks + 16 + 4lg4 + r.
+        // S^T operand from the accumulators: lane (ln, lg4) supplies column
+        // wcol + ln with slot 8*lg4 + r <-> d = 32ks + 4lg4 + r and
+        // slot 8*lg4 + 4 + r <-> d = 32ks + 16 + 4lg4 + r; Q^T uses the same slots.
         uint32_t sh[4], sl[4];
         split_pk_bf16(S_acc[2 * ks][0], S_acc[2 * ks][1], sh[0], sl[0]);
         split_pk_bf16(S_acc[2 * ks][2], S_acc[2 * ks][3], sh[1], sl[1]);
@@ -364,15 +365,14 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
           const u32x2 qb =
               *reinterpret_cast<const u32x2 *>(&sq[qk_off<DK>(r, 32 * ks + 16 + 4 * lg4)]);
           const u32x4 a = {qa.x, qa.y, qb.x, qb.y};
-          O_acc[mi] = mfma16(a, bh, O_acc[mi]);
-          O_acc[mi] = mfma16(a, bl, O_acc[mi]);
+          O_acc[mi] = mfma16(bh, a, O_acc[mi]);
+          O_acc[mi] = mfma16(bl, a, O_acc[mi]);
         }
       }
-      // rows scale by 2^(b2_i): O_acc[mi][r] is row 16 mi + 4 lg4 + r
+      // O_acc[mi][r] = O^T[wcol + 4 lg4 + r][16 mi + ln]: row i = 16 mi + ln of O
+      // scales by 2^(b2_i)
 #pragma unroll
-      for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) O_acc[mi][r] *= s.glam[wave][16 * mi + 4 * lg4 + r];
+      for (int mi = 0; mi < NM; ++mi) O_acc[mi] *= s.glam[wave][16 * mi + ln];
     }
     barrier_lds();  // P complete
 
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
     }
 
     if (!SP) {
-      // ---- intra-chunk: O += P V over the causal k-steps
+      // ---- intra-chunk: O^T += V^T P^T over the causal k-steps
 #pragma unroll
       for (int mi = 0; mi < NM; ++mi) {
 #pragma unroll
@@ -398,8 +398,8 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
             const int off = (16 * mi + ln) * PP + 32 * js + 8 * lg4;
             const u32x4 ph = *reinterpret_cast<const u32x4 *>(&s.phi[off]);
             const u32x4 pl = *reinterpret_cast<const u32x4 *>(&s.plo[off]);
-            O_acc[mi] = mfma16(ph, vf[js], O_acc[mi]);
-            O_acc[mi] = mfma16(pl, vf[js], O_acc[mi]);
+            O_acc[mi] = mfma16(vf[js], ph, O_acc[mi]);
+            O_acc[mi] = mfma16(vf[js], pl, O_acc[mi]);
           }
         }
       }
@@ -447,15 +447,11 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
 
   // ---- last chunk's outputs, final state of the run
   if (!SP && t_prev >= 0) {
+    Tout *ob = o + ((size_t)(t_prev + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
+    const size_t rs16 = (size_t)16 * H * DV;
 #pragma unroll
     for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * mi + 4 * lg4 + r;
-        if (i < n_prev)
-          store_from_f32(o, ((size_t)(t_prev + i) * H + h) * DV + col0 + wcol + ln,
-                         O_prev[mi][r]);
-      }
+      if (16 * mi + ln < n_prev) store4_from_f32(ob + mi * rs16, O_prev[mi]);
   }
   float *sout = nullptr;
   if (SP) {

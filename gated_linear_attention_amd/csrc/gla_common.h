@@ -80,4 +80,15 @@ template <> __device__ __forceinline__ void store_from_f32<uint16_t>(uint16_t *p
   p[i] = (uint16_t)f32_to_bf16_bits(x);
 }
 
+// Store four consecutive floats as fp32 (one 16-byte store) or bf16 (8 bytes).
+__device__ __forceinline__ void store4_from_f32(float *p, const f32x4 &x) {
+  *reinterpret_cast<f32x4 *>(p) = x;
+}
+__device__ __forceinline__ void store4_from_f32(uint16_t *p, const f32x4 &x) {
+  u32x2 w;
+  w.x = cvt_pk_bf16(x[0], x[1]);
+  w.y = cvt_pk_bf16(x[2], x[3]);
+  *reinterpret_cast<u32x2 *>(p) = w;
+}
+
 }  // namespace gla
