@@ -236,6 +236,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--chunk", type=int, default=64, choices=[64, 128])
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy 5 times (the reference "
+                         "kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the GLA kernels here are single-device and this "
@@ -245,6 +248,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        n = 512 * 1024 * 1024 // 4
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n * 4, "copies": 5}), flush=True)
+        return
 
     log("forward: building inputs")
     fwd, host_set = bench_forward(args)
