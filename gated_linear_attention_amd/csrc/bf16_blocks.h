@@ -1,0 +1,102 @@
+// Building blocks shared by the bf16 chunked-forward kernels (gfx950).
+#pragma once
+
+#include "gla_common.h"
+#include "gla_internal.h"
+
+namespace gla {
+
+
+constexpr int kBfSlice = 64;  // state columns per workgroup (4 wavefronts x 16)
+
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// LLVM's raw buffer load that writes LDS (M0 + lane * size) instead of VGPRs.
+__device__ void buffer_load_to_lds(i32x4 rsrc, lds_u32 *lds, int size, int voffset, int soffset,
+                                   int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Raw buffer descriptor: 48-bit base, stride 0, range num_bytes (loads at or
+// beyond it return 0), gfx9 data format word.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)((a >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane((int32_t)num_bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+// Workgroup barrier that orders LDS only (outstanding global loads stay in flight).
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Barrier after this wavefront's global loads (including those into LDS) landed.
+__device__ __forceinline__ void barrier_all() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ WorkItem bf_item_for(const WorkItem *items, int it, int T) {
+  if (items) return items[it];
+  WorkItem w;
+  w.tok_begin = it * T;
+  w.tok_end = (it + 1) * T;
+  w.seq = it;
+  w.state_in = -1;
+  w.state_out = -1;
+  w.pad0 = w.pad1 = w.pad2 = 0;
+  return w;
+}
+
+// Element offsets in the swizzled tiles: 16-byte chunk c of row r sits at chunk
+// c ^ (r mod chunks-per-row).
+template <int DK>
+__device__ __forceinline__ int qk_off(int r, int col) {
+  constexpr int CPR = DK / 8;
+  return r * DK + ((((col >> 3) ^ r) & (CPR - 1)) << 3) + (col & 7);
+}
+__device__ __forceinline__ int v_off(int r, int col) {
+  return r * kBfSlice + ((((col >> 3) ^ r) & 7) << 3) + (col & 7);
+}
+
+__device__ __forceinline__ u32x2 lds_tr16(const uint16_t *p) {
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+  return __builtin_bit_cast(u32x2, x);
+}
+
+// Inclusive prefix sum across the 64 lanes of a wavefront with DPP row shifts
+// and row broadcasts (no LDS round trips).
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  int v = __float_as_int(x);
+  v = __float_as_int(__int_as_float(v) +
+                     __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true)));
+  v = __float_as_int(__int_as_float(v) +
+                     __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true)));
+  v = __float_as_int(__int_as_float(v) +
+                     __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true)));
+  v = __float_as_int(__int_as_float(v) +
+                     __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true)));
+  v = __float_as_int(__int_as_float(v) +
+                     __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false)));
+  v = __float_as_int(__int_as_float(v) +
+                     __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false)));
+  return __int_as_float(v);
+}
+
+// Score tile index -> (row tile ti, column tile tj), tj <= ti, row-major over
+// the lower triangle (t = ti (ti + 1) / 2 + tj). Branch-free so that it folds
+// to constants once the tile loop is unrolled.
+__host__ __device__ constexpr int tile_ti(int t) {
+  return (t >= 1) + (t >= 3) + (t >= 6) + (t >= 10) + (t >= 15) + (t >= 21) + (t >= 28);
+}
+__host__ __device__ constexpr int tile_tj(int t) { return t - tile_ti(t) * (tile_ti(t) + 1) / 2; }
+static_assert(tile_ti(9) == 3 && tile_tj(9) == 3 && tile_ti(35) == 7 && tile_tj(30) == 2,
+              "lower-triangle tile numbering");
+
+}  // namespace gla

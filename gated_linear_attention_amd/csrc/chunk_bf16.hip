@@ -47,57 +47,9 @@
 // into an MFMA (P, S, kappa . V) is split into hi = bf16(x) and
 // lo = bf16(x - hi) and both parts are multiplied, which keeps ~16
 // significant bits with fp32 accumulation.
-#include "gla_common.h"
-#include "gla_internal.h"
+#include "bf16_blocks.h"
 
 namespace gla {
-
-constexpr int kBfSlice = 64;  // state columns per workgroup (4 wavefronts x 16)
-
-typedef __attribute__((address_space(3))) uint32_t lds_u32;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// LLVM's raw buffer load that writes LDS (M0 + lane * size) instead of VGPRs.
-__device__ void buffer_load_to_lds(i32x4 rsrc, lds_u32 *lds, int size, int voffset, int soffset,
-                                   int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-
-// Raw buffer descriptor: 48-bit base, stride 0, range num_bytes (loads at or
-// beyond it return 0), gfx9 data format word.
-__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
-  r.y = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)((a >> 32) & 0xffffu));
-  r.z = __builtin_amdgcn_readfirstlane((int32_t)num_bytes);
-  r.w = 0x00020000;
-  return r;
-}
-
-// Workgroup barrier that orders LDS only (outstanding global loads stay in flight).
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-// Barrier after this wavefront's global loads (including those into LDS) landed.
-__device__ __forceinline__ void barrier_all() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ WorkItem bf_item_for(const WorkItem *items, int it, int T) {
-  if (items) return items[it];
-  WorkItem w;
-  w.tok_begin = it * T;
-  w.tok_end = (it + 1) * T;
-  w.seq = it;
-  w.state_in = -1;
-  w.state_out = -1;
-  w.pad0 = w.pad1 = w.pad2 = 0;
-  return w;
-}
 
 template <int C, int DK, bool SP>
 struct BfLds {
@@ -115,64 +67,173 @@ struct BfLds {
   float gkap[4][C];  // 2^(b2_last - b2_j)
 };
 
-// Element offsets in the swizzled tiles: 16-byte chunk c of row r sits at chunk
-// c ^ (r mod chunks-per-row).
-template <int DK>
-__device__ __forceinline__ int qk_off(int r, int col) {
-  constexpr int CPR = DK / 8;
-  return r * DK + ((((col >> 3) ^ r) & (CPR - 1)) << 3) + (col & 7);
-}
-__device__ __forceinline__ int v_off(int r, int col) {
-  return r * kBfSlice + ((((col >> 3) ^ r) & 7) << 3) + (col & 7);
-}
-
-__device__ __forceinline__ u32x2 lds_tr16(const uint16_t *p) {
-  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
-  return __builtin_bit_cast(u32x2, x);
-}
-
-// Issue the HBM -> LDS copies of one chunk (rows [t0, t0 + n) of the run) into
-// stage `st`. Every wavefront copies a quarter of each tile.
+// HBM -> LDS copies of one chunk (rows [t0, t0 + n) of the run) into stage
+// `st`; every wavefront copies a quarter of each tile. The copy is issued in
+// three parts (K; Q; V and the gates) spread over the previous chunk's
+// compute, so the four wavefronts do not queue all their memory instructions
+// on the CU's address unit at once.
 template <int C, int DK, bool SP>
-__device__ __forceinline__ void issue_chunk_loads(BfLds<C, DK, SP> &s, int st,
-                                                  const uint16_t *q, const uint16_t *k,
-                                                  const uint16_t *v, const float *lg, int t0,
-                                                  int n, int H, int h, int DV, int col0,
-                                                  int wave, int lane) {
-  constexpr int CPR = DK / 8;                    // 16-byte chunks per Q/K row
-  constexpr int QB = C * DK * 2 / 1024;          // 1 KB blocks per Q/K tile
-  constexpr int RPB = 1024 / (DK * 2);           // rows per block
-  constexpr int VB = C * kBfSlice * 2 / 1024;    // 1 KB blocks of the V slice (8 rows each)
-  const size_t tok0 = (size_t)t0 * H + h;
-  const uint32_t qk_row = (uint32_t)H * DK * 2, v_row = (uint32_t)H * DV * 2;
-  const i32x4 rk = make_rsrc(k + tok0 * DK, (n - 1) * qk_row + DK * 2);
-  const i32x4 rv = make_rsrc(v + tok0 * DV + col0, (n - 1) * v_row + kBfSlice * 2);
+struct ChunkLoader {
+  static constexpr int CPR = DK / 8;                  // 16-byte chunks per Q/K row
+  static constexpr int QB = C * DK * 2 / 1024;        // 1 KB blocks per Q/K tile
+  static constexpr int RPB = 1024 / (DK * 2);         // rows per block
+  static constexpr int VB = C * kBfSlice * 2 / 1024;  // 1 KB blocks of the V slice (8 rows each)
+  i32x4 rq, rk, rv, rg;
+  uint32_t qk_row, v_row, g_row;
+  int st;
+  bool active;
+
+  __device__ __forceinline__ void setup(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                        const float *lg, int t0, int tok_end, int H, int h,
+                                        int DV, int col0, int stage) {
+    active = t0 < tok_end;
+    st = stage;
+    if (!active) return;
+    const int n = min(C, tok_end - t0);
+    const size_t tok0 = (size_t)t0 * H + h;
+    qk_row = (uint32_t)H * DK * 2;
+    v_row = (uint32_t)H * DV * 2;
+    g_row = (uint32_t)H * 4;
+    rk = make_rsrc(k + tok0 * DK, (n - 1) * qk_row + DK * 2);
+    if (!SP) rq = make_rsrc(q + tok0 * DK, (n - 1) * qk_row + DK * 2);
+    rv = make_rsrc(v + tok0 * DV + col0, (n - 1) * v_row + kBfSlice * 2);
+    rg = make_rsrc(lg + tok0, (n - 1) * g_row + 4);
+  }
+  template <typename Tiles>
+  __device__ __forceinline__ void qk_part(Tiles &dst, i32x4 r, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < QB / 4; ++i) {
-    const int blk = wave * (QB / 4) + i;
-    const int r = blk * RPB + lane / CPR;
-    const int c = (lane % CPR) ^ (r & (CPR - 1));
-    const int off = r * qk_row + c * 16;
-    buffer_load_to_lds(rk, (lds_u32 *)&s.k[st][blk * 512], 16, off, 0, 0, 0);
-    if (!SP) {
-      const i32x4 rq = make_rsrc(q + tok0 * DK, (n - 1) * qk_row + DK * 2);
-      buffer_load_to_lds(rq, (lds_u32 *)&s.q[st][blk * 512], 16, off, 0, 0, 0);
+    for (int i = 0; i < QB / 4; ++i) {
+      const int blk = wave * (QB / 4) + i;
+      const int row = blk * RPB + lane / CPR;
+      const int c = (lane % CPR) ^ (row & (CPR - 1));
+      buffer_load_to_lds(r, (lds_u32 *)&dst[st][blk * 512], 16, row * qk_row + c * 16, 0, 0, 0);
     }
   }
-#pragma unroll
-  for (int i = 0; i < VB / 4; ++i) {
-    const int blk = wave * (VB / 4) + i;
-    const int r = blk * 8 + lane / 8;
-    const int c = (lane % 8) ^ (r & 7);
-    buffer_load_to_lds(rv, (lds_u32 *)&s.v[st][blk * 512], 16, r * v_row + c * 16, 0, 0, 0);
+  __device__ __forceinline__ void k_part(BfLds<C, DK, SP> &s, int wave, int lane) {
+    if (active) qk_part(s.k, rk, wave, lane);
   }
-  if (wave == 0) {
-    const i32x4 rg = make_rsrc(lg + tok0, (n - 1) * (uint32_t)H * 4 + 4);
-#pragma unroll
-    for (int i = 0; i < C / 64; ++i)
-      buffer_load_to_lds(rg, (lds_u32 *)&s.lg[st][64 * i], 4, (64 * i + lane) * H * 4, 0, 0, 0);
+  __device__ __forceinline__ void q_part(BfLds<C, DK, SP> &s, int wave, int lane) {
+    if (!SP && active) qk_part(s.q, rq, wave, lane);
   }
-}
+  __device__ __forceinline__ void v_part(BfLds<C, DK, SP> &s, int wave, int lane) {
+    if (!active) return;
+#pragma unroll
+    for (int i = 0; i < VB / 4; ++i) {
+      const int blk = wave * (VB / 4) + i;
+      const int r = blk * 8 + lane / 8;
+      const int c = (lane % 8) ^ (r & 7);
+      buffer_load_to_lds(rv, (lds_u32 *)&s.v[st][blk * 512], 16, r * v_row + c * 16, 0, 0, 0);
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int i = 0; i < C / 64; ++i)
+        buffer_load_to_lds(rg, (lds_u32 *)&s.lg[st][64 * i], 4, (64 * i + lane) * g_row, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void all(BfLds<C, DK, SP> &s, int wave, int lane) {
+    k_part(s, wave, lane);
+    q_part(s, wave, lane);
+    v_part(s, wave, lane);
+  }
+};
+
+template <int C, int DK, typename Tout, bool SP>
+struct BfRun {
+  using LDS = BfLds<C, DK, SP>;
+  static constexpr int NST = LDS::NST;
+  static constexpr int PP = LDS::PP;
+  static constexpr int NM = C / 16;                // 16-row tiles of the chunk
+  static constexpr int NKS = DK / 32;              // 32-deep k-steps over d_k
+  static constexpr int NT = DK / 16;               // 16-row tiles of the state
+  static constexpr int NJS = C / 32;               // 32-deep k-steps over the chunk
+  static constexpr int NTILE = NM * (NM + 1) / 2;  // lower-triangular score tiles
+  static constexpr int E = C / 64;                 // gate positions per lane
+
+  LDS &s;
+  int wave, lane, ln, lg4, wcol;
+  __device__ __forceinline__ BfRun(LDS &s_, int wave_, int lane_)
+      : s(s_), wave(wave_), lane(lane_), ln(lane_ % 16), lg4(lane_ / 16), wcol(16 * wave_) {}
+
+  // Gates of the chunk in stage st: in-chunk prefix sums (log2 units) and the
+  // decay factors, into this wavefront's LDS arrays. Returns the chunk decay;
+  // adds the chunk's natural-log gate sum to lsum.
+  __device__ __forceinline__ float gates(int st, float &lsum) {
+    float part[E];
+    float run = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      run += s.lg[st][lane * E + e];
+      part[e] = run;
+    }
+    const float incl = wave_inclusive_scan(run);
+    const float excl = incl - run;
+    const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+    const float b2last = total * kLog2e;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = lane * E + e;
+      const float b2 = (excl + part[e]) * kLog2e;
+      s.gb2[wave][j] = b2;
+      s.glam[wave][j] = fast_exp2(b2);
+      s.gkap[wave][j] = fast_exp2(b2last - b2);
+    }
+    lsum += total;
+    return fast_exp2(b2last);
+  }
+
+  // Score tiles W, W+4, ... of A^T = K Q^T (compile-time list, so the tiles'
+  // operand reads and MFMA chains interleave), decay-masked, split into bf16
+  // hi/lo and written to P.
+  template <int W>
+  __device__ __forceinline__ void scores(const uint16_t *sq, const uint16_t *sk) {
+    constexpr int NW = (NTILE - W + 3) / 4;  // tiles of this wavefront
+    f32x4 acc[NW];
+#pragma unroll
+    for (int m = 0; m < NW; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int m = 0; m < NW; ++m) {
+        const int tile = W + 4 * m;
+        const int ti = tile_ti(tile), tj = tile_tj(tile);
+        const u32x4 a =
+            *reinterpret_cast<const u32x4 *>(&sk[qk_off<DK>(16 * tj + ln, 32 * ks + 8 * lg4)]);
+        const u32x4 b =
+            *reinterpret_cast<const u32x4 *>(&sq[qk_off<DK>(16 * ti + ln, 32 * ks + 8 * lg4)]);
+        acc[m] = mfma16(a, b, acc[m]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NW; ++m) {
+      const int tile = W + 4 * m;
+      const int ti = tile_ti(tile), tj = tile_tj(tile);
+      // acc[m][r] = A^T[j][i] with j = 16 tj + 4 lg4 + r, i = 16 ti + ln
+      const int i = 16 * ti + ln;
+      const float b2i = s.gb2[wave][i];
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * tj + 4 * lg4 + r;
+        const float d = fast_exp2(b2i - s.gb2[wave][j]);
+        p[r] = (ti > tj || j <= i) ? acc[m][r] * d : 0.f;
+      }
+      uint32_t h0, l0, h1, l1;
+      split_pk_bf16(p[0], p[1], h0, l0);
+      split_pk_bf16(p[2], p[3], h1, l1);
+      const u32x2 wh = {h0, h1}, wl = {l0, l1};
+      *reinterpret_cast<u32x2 *>(&s.phi[i * PP + 16 * tj + 4 * lg4]) = wh;
+      *reinterpret_cast<u32x2 *>(&s.plo[i * PP + 16 * tj + 4 * lg4]) = wl;
+    }
+  }
+  __device__ __forceinline__ void scores_dispatch(const uint16_t *sq, const uint16_t *sk) {
+    switch (wave) {
+      case 0: scores<0>(sq, sk); break;
+      case 1: scores<1>(sq, sk); break;
+      case 2: scores<2>(sq, sk); break;
+      default: scores<3>(sq, sk); break;
+    }
+  }
+};
 
 template <int C, int DK, typename Tout, bool SP>
 __global__ __launch_bounds__(256) void chunk_bf16_kernel(
@@ -181,15 +242,10 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
     float *__restrict__ ST, Tout *__restrict__ o, const WorkItem *__restrict__ items,
     const int *__restrict__ n_items, float *__restrict__ slots, float *__restrict__ slot_gamma,
     int T, int H, int DV, int n_pairs) {
-  using LDS = BfLds<C, DK, SP>;
-  constexpr int NST = LDS::NST;
-  constexpr int PP = LDS::PP;
-  constexpr int NM = C / 16;                // 16-row tiles of the chunk
-  constexpr int NKS = DK / 32;              // 32-deep k-steps over d_k
-  constexpr int NT = DK / 16;               // 16-row tiles of the state
-  constexpr int NJS = C / 32;               // 32-deep k-steps over the chunk
-  constexpr int NTILE = NM * (NM + 1) / 2;  // lower-triangular score tiles
-  constexpr int E = C / 64;                 // gate positions per lane
+  using Run = BfRun<C, DK, Tout, SP>;
+  using LDS = typename Run::LDS;
+  constexpr int NST = Run::NST, PP = Run::PP, NM = Run::NM, NKS = Run::NKS, NT = Run::NT,
+                NJS = Run::NJS;
   __shared__ LDS s;
 
   // Block -> (pair = item * H + head, column slice). Slices of one pair are
@@ -214,9 +270,9 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
-  const int ln = lane % 16, lg4 = lane / 16;  // MFMA lane coordinates
-  const int col0 = slice * kBfSlice;          // first state column of the slice
-  const int wcol = 16 * wave;                 // wavefront's columns within the slice
+  Run R(s, wave, lane);
+  const int ln = R.ln, lg4 = R.lg4, wcol = R.wcol;
+  const int col0 = slice * kBfSlice;  // first state column of the slice
   const size_t dkdv = (size_t)DK * DV;
 
   // State slice in accumulator layout: S_acc[t][r] = S[16t + 4*lg4 + r][col0 + wcol + ln].
@@ -250,10 +306,21 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
   float lsum = 0.f;
   f32x4 O_prev[SP ? 1 : NM];
   int t_prev = -1, n_prev = 0;
+  // Deferred output store of the previous chunk. O_prev[mi][r] holds
+  // O[16 mi + ln][wcol + 4 lg4 + r]: one 16-byte piece of a row.
+  auto store_prev = [&]() {
+    if (SP || t_prev < 0) return;
+    Tout *ob = o + ((size_t)(t_prev + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
+    const size_t rs16 = (size_t)16 * H * DV;  // 16 rows
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi)
+      if (16 * mi + ln < n_prev) store4_from_f32(ob + mi * rs16, O_prev[mi]);
+  };
+
+  ChunkLoader<C, DK, SP> ld;
   int t0 = w.tok_begin;
-  if (t0 < w.tok_end)
-    issue_chunk_loads<C, DK, SP>(s, 0, q, k, v, lg, t0, min(C, w.tok_end - t0), H, h, DV, col0,
-                                 wave, lane);
+  ld.setup(q, k, v, lg, t0, w.tok_end, H, h, DV, col0, 0);
+  ld.all(s, wave, lane);
 
   for (int ci = 0; t0 < w.tok_end; t0 += C, ++ci) {
     const int n = min(C, w.tok_end - t0);
@@ -261,88 +328,19 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
     const int st = (NST == 2) ? (ci & 1) : 0;
     barrier_all();  // chunk ci's tiles are in LDS; every wavefront left chunk ci-1
 
-    // ---- outputs of the previous chunk (stored now so their latency overlaps).
-    // O_prev[mi][r] = O[16 mi + ln][wcol + 4 lg4 + r]: one 16-byte row piece.
-    if (!SP && t_prev >= 0) {
-      Tout *ob = o + ((size_t)(t_prev + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
-      const size_t rs16 = (size_t)16 * H * DV;  // 16 rows
-#pragma unroll
-      for (int mi = 0; mi < NM; ++mi)
-        if (16 * mi + ln < n_prev) store4_from_f32(ob + mi * rs16, O_prev[mi]);
-    }
-    if (NST == 2 && t1 < w.tok_end)
-      issue_chunk_loads<C, DK, SP>(s, st ^ 1, q, k, v, lg, t1, min(C, w.tok_end - t1), H, h, DV,
-                                   col0, wave, lane);
-
     const uint16_t *sq = s.q[SP ? 0 : st];
     const uint16_t *sk = s.k[st];
     const uint16_t *sv = s.v[st];
+    if (NST == 2) ld.setup(q, k, v, lg, t1, w.tok_end, H, h, DV, col0, st ^ 1);
+    if (NST == 2) ld.k_part(s, wave, lane);
 
-    // ---- gates: each wavefront scans the chunk's log-gates into its own arrays
-    float gam;
-    {
-      float part[E];
-      float run = 0.f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        run += s.lg[st][lane * E + e];
-        part[e] = run;
-      }
-      float incl = run;
-#pragma unroll
-      for (int off = 1; off < 64; off *= 2) {
-        const float y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      const float excl = incl - run;
-      const float total = __shfl(incl, 63);
-      const float b2last = total * kLog2e;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int j = lane * E + e;
-        const float b2 = (excl + part[e]) * kLog2e;
-        s.gb2[wave][j] = b2;
-        s.glam[wave][j] = fast_exp2(b2);
-        s.gkap[wave][j] = fast_exp2(b2last - b2);
-      }
-      gam = fast_exp2(b2last);
-      lsum += total;
-    }
+    const float gam = R.gates(st, lsum);
 
     f32x4 O_acc[SP ? 1 : NM];
     if (!SP) {
-      // ---- scores: lower-triangular 16x16 tiles of A^T = K Q^T, dealt round-robin
-      for (int tile = wave; tile < NTILE; tile += 4) {
-        int ti = 0, rem = tile;  // tile -> (ti, tj) with tj <= ti
-        while (rem > ti) {
-          rem -= ti + 1;
-          ++ti;
-        }
-        const int tj = rem;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int rk = 16 * tj + ln, rq = 16 * ti + ln;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const u32x4 a = *reinterpret_cast<const u32x4 *>(&sk[qk_off<DK>(rk, 32 * ks + 8 * lg4)]);
-          const u32x4 b = *reinterpret_cast<const u32x4 *>(&sq[qk_off<DK>(rq, 32 * ks + 8 * lg4)]);
-          acc = mfma16(a, b, acc);
-        }
-        // acc[r] = A^T[j][i] with j = 16 tj + 4 lg4 + r, i = 16 ti + ln
-        const int i = 16 * ti + ln;
-        const float b2i = s.gb2[wave][i];
-        float p[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * tj + 4 * lg4 + r;
-          p[r] = (j <= i) ? acc[r] * fast_exp2(b2i - s.gb2[wave][j]) : 0.f;
-        }
-        uint32_t h0, l0, h1, l1;
-        split_pk_bf16(p[0], p[1], h0, l0);
-        split_pk_bf16(p[2], p[3], h1, l1);
-        const u32x2 wh = {h0, h1}, wl = {l0, l1};
-        *reinterpret_cast<u32x2 *>(&s.phi[i * PP + 16 * tj + 4 * lg4]) = wh;
-        *reinterpret_cast<u32x2 *>(&s.plo[i * PP + 16 * tj + 4 * lg4]) = wl;
-      }
+      // ---- scores -> P (LDS)
+      R.scores_dispatch(sq, sk);
+      if (NST == 2) ld.q_part(s, wave, lane);
 
       // ---- inter-chunk read of the state: O^T = S^T Q^T (before this chunk's update)
 #pragma unroll
@@ -374,7 +372,11 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
 #pragma unroll
       for (int mi = 0; mi < NM; ++mi) O_acc[mi] *= s.glam[wave][16 * mi + ln];
     }
+    if (NST == 2) ld.v_part(s, wave, lane);
     barrier_lds();  // P complete
+
+    // outputs of the previous chunk, stored now so their latency overlaps this chunk
+    store_prev();
 
     // V fragments of this wavefront's 16 columns (transpose reads):
     // slot 8 lg4 + e <-> j = 32 js + 8 lg4 + e, column wcol + ln.
@@ -440,19 +442,13 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
     }
     if (NST == 1 && t1 < w.tok_end) {
       barrier_lds();  // every wavefront is done with the single stage
-      issue_chunk_loads<C, DK, SP>(s, 0, q, k, v, lg, t1, min(C, w.tok_end - t1), H, h, DV,
-                                   col0, wave, lane);
+      ld.setup(q, k, v, lg, t1, w.tok_end, H, h, DV, col0, 0);
+      ld.all(s, wave, lane);
     }
   }
 
   // ---- last chunk's outputs, final state of the run
-  if (!SP && t_prev >= 0) {
-    Tout *ob = o + ((size_t)(t_prev + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
-    const size_t rs16 = (size_t)16 * H * DV;
-#pragma unroll
-    for (int mi = 0; mi < NM; ++mi)
-      if (16 * mi + ln < n_prev) store4_from_f32(ob + mi * rs16, O_prev[mi]);
-  }
+  store_prev();
   float *sout = nullptr;
   if (SP) {
     sout = slots + ((size_t)w.state_out * H + h) * dkdv;
@@ -505,13 +501,11 @@ hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_
                              const FwdDims &d, const WorkItem *items, const int *n_items,
                              int grid_items, float *slots, float *slot_gamma, bool state_pass,
                              hipStream_t stream) {
-  if (d.C == 64) {
-    if (d.dk == 128)
-      return launch_bf_c<64, 128>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items,
-                                  grid_items, slots, slot_gamma, state_pass, stream);
-    return launch_bf_c<64, 64>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
-                               slots, slot_gamma, state_pass, stream);
-  }
+  // 64-token chunks run on the eight-wavefront kernel; this file's four-wavefront
+  // kernel serves 128-token chunks (whose tiles leave no LDS for eight wavefronts).
+  if (d.C == 64)
+    return launch_chunk_bf16_c64(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
+                                 slots, slot_gamma, state_pass, stream);
   if (d.dk == 128)
     return launch_bf_c<128, 128>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items,
                                  grid_items, slots, slot_gamma, state_pass, stream);

@@ -73,6 +73,13 @@ hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, cons
                             int grid_items, float *slots, float *slot_gamma, bool state_pass,
                             hipStream_t stream);
 
+// bf16 inputs, 64-token chunks: eight-wavefront kernel (chunk_bf16_w8.hip).
+hipError_t launch_chunk_bf16_c64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                 const float *g, const float *S0, float *S_T, void *o,
+                                 bool out_bf16, const FwdDims &d, const WorkItem *items,
+                                 const int *n_items, int grid_items, float *slots,
+                                 float *slot_gamma, bool state_pass, hipStream_t stream);
+
 // bf16 inputs on the matrix cores, fp32 accumulation and state.
 hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                              const float *g, const float *S0, float *S_T, void *o, bool out_bf16,
