@@ -70,6 +70,31 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint16_t *p) {
   return __builtin_bit_cast(u32x2, x);
 }
 
+// The same transpose read issued as inline assembly. The compiler's wait
+// insertion treats the builtin above as a read that may overlap any LDS
+// direct load still in flight and waits for all outstanding global loads
+// before it; these reads never touch a tile that is being loaded. The result
+// is not ready until an lgkmcnt wait: pass it through lds_wait() (or
+// lds_after_wait() behind a barrier that waited) before use.
+__device__ __forceinline__ u32x2 lds_tr16_nowait(const uint16_t *p) {
+  const uint32_t a = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t *)p);
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+  return r;
+}
+// Wait for this wavefront's LDS reads; the operands are tied so that their
+// users cannot be scheduled above the wait.
+__device__ __forceinline__ void lds_wait(u32x4 &a, u32x4 &b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+}
+// Order values behind an lgkmcnt wait that already happened (e.g. in a barrier).
+__device__ __forceinline__ void lds_after_wait(u32x4 &a, u32x4 &b, u32x4 &c, u32x4 &d) {
+  asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+// Tell the compiler's wait insertion that every counter is drained (emits a
+// wait that is a no-op at run time when placed after barrier_all()).
+__device__ __forceinline__ void counters_drained() { __builtin_amdgcn_s_waitcnt(0); }
+
 // Inclusive prefix sum across the 64 lanes of a wavefront with DPP row shifts
 // and row broadcasts (no LDS round trips).
 __device__ __forceinline__ float wave_inclusive_scan(float x) {

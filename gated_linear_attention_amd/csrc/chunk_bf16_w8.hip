@@ -40,51 +40,81 @@ struct W8Lds {
   uint16_t q[2][QR * DK];
   uint16_t k[2][C * DK];
   uint16_t v[2][C * kBfSlice];
-  float lg[2][C];
   uint16_t phi[QR * PP];
   uint16_t plo[QR * PP];
   f32x4 xbuf[SP ? 1 : kW8Waves][2][64];  // partial outputs handed to the partner wavefront
+  u32x4 kvx[kW8Waves][2][64];            // kappa . V (hi, lo) for the partner's 32 keys
+  float lgb[3][C];                       // log-gates, loaded two chunks ahead
   float gb2[kW8Waves][C];   // per wavefront: in-chunk prefix sums of the log-gates, log2 units
   float glam[kW8Waves][C];  // 2^(b2_i)
   float gkap[kW8Waves][C];  // 2^(b2_last - b2_j)
 };
 
-// HBM -> LDS copy of one chunk into stage st, split in three parts over eight
-// wavefronts (see ChunkLoader in chunk_bf16.hip for the swizzle).
+// HBM -> LDS copy of one chunk into stage st, done by the four wavefronts of
+// row half 0 (the other four, whose chain per chunk is longer, only store
+// outputs). Tiles are swizzled as in ChunkLoader (chunk_bf16.hip). The row
+// pointers advance by one chunk per next() call, so a chunk costs a few scalar
+// adds and one clamp of the descriptor ranges. The log-gates go to a
+// three-slot ring two chunks ahead of their use.
 template <int DK, bool SP>
 struct W8Loader {
   static constexpr int C = kW8C;
+  static constexpr int LW = 4;  // loading wavefronts
   static constexpr int CPR = DK / 8;
   static constexpr int QB = C * DK * 2 / 1024;  // 1 KB blocks per Q/K tile (8 or 16)
   static constexpr int RPB = 1024 / (DK * 2);
   static constexpr int VB = C * kBfSlice * 2 / 1024;  // 8
-  static_assert(QB % kW8Waves == 0 && VB % kW8Waves == 0, "blocks per wavefront");
+  static_assert(QB % LW == 0 && VB % LW == 0, "blocks per loading wavefront");
+  const uint16_t *qp, *kp, *vp;  // first row (this head / slice) of the next chunk to load
+  const float *gp;               // first gate of the next gate chunk to load
+  size_t qk_step, v_step, g_step;  // elements per chunk
   i32x4 rq, rk, rv, rg;
-  uint32_t qk_row, v_row, g_row;
+  uint32_t qk_row, v_row, g_row;   // bytes per token
   int st;
-  bool active;
+  bool active, g_active;
 
-  __device__ __forceinline__ void setup(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                        const float *lg, int t0, int tok_end, int H, int h,
-                                        int DV, int col0, int stage) {
-    active = t0 < tok_end;
-    st = stage;
-    if (!active) return;
-    const int n = min(C, tok_end - t0);
+  __device__ __forceinline__ void init(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                       const float *lg, int t0, int H, int h, int DV, int col0) {
     const size_t tok0 = (size_t)t0 * H + h;
+    qp = q + tok0 * DK;
+    kp = k + tok0 * DK;
+    vp = v + tok0 * DV + col0;
+    gp = lg + tok0;
+    qk_step = (size_t)C * H * DK;
+    v_step = (size_t)C * H * DV;
+    g_step = (size_t)C * H;
     qk_row = (uint32_t)H * DK * 2;
     v_row = (uint32_t)H * DV * 2;
     g_row = (uint32_t)H * 4;
-    rk = make_rsrc(k + tok0 * DK, (n - 1) * qk_row + DK * 2);
-    if (!SP) rq = make_rsrc(q + tok0 * DK, (n - 1) * qk_row + DK * 2);
-    rv = make_rsrc(v + tok0 * DV + col0, (n - 1) * v_row + kBfSlice * 2);
-    rg = make_rsrc(lg + tok0, (n - 1) * g_row + 4);
+  }
+  // Descriptors for the tile chunk that starts at token t0 (the one after the
+  // previous call's), to be written into stage `stage`.
+  __device__ __forceinline__ void next(int t0, int tok_end, int stage) {
+    active = t0 < tok_end;
+    st = stage;
+    if (!active) return;
+    const uint32_t last = (uint32_t)(min(C, tok_end - t0) - 1);
+    rk = make_rsrc(kp, last * qk_row + DK * 2);
+    if (!SP) rq = make_rsrc(qp, last * qk_row + DK * 2);
+    rv = make_rsrc(vp, last * v_row + kBfSlice * 2);
+    qp += qk_step;
+    kp += qk_step;
+    vp += v_step;
+  }
+  // The same for the gate chunk starting at t0 (gates past the end read as 0).
+  __device__ __forceinline__ void gate_next(int t0, int tok_end) {
+    g_active = t0 < tok_end;
+    if (!g_active) return;
+    const uint32_t last = (uint32_t)(min(C, tok_end - t0) - 1);
+    rg = make_rsrc(gp, last * g_row + 4);
+    gp += g_step;
   }
   template <typename Tiles>
   __device__ __forceinline__ void qk_part(Tiles &dst, i32x4 r, int wave, int lane) {
+    if (wave >= LW) return;
 #pragma unroll
-    for (int i = 0; i < QB / kW8Waves; ++i) {
-      const int blk = wave * (QB / kW8Waves) + i;
+    for (int i = 0; i < QB / LW; ++i) {
+      const int blk = wave * (QB / LW) + i;
       const int row = blk * RPB + lane / CPR;
       const int c = (lane % CPR) ^ (row & (CPR - 1));
       buffer_load_to_lds(r, (lds_u32 *)&dst[st][blk * 512], 16, row * qk_row + c * 16, 0, 0, 0);
@@ -97,15 +127,18 @@ struct W8Loader {
     if (!SP && active) qk_part(s.q, rq, wave, lane);
   }
   __device__ __forceinline__ void v_part(W8Lds<DK, SP> &s, int wave, int lane) {
-    if (!active) return;
+    if (!active || wave >= LW) return;
 #pragma unroll
-    for (int i = 0; i < VB / kW8Waves; ++i) {
-      const int blk = wave * (VB / kW8Waves) + i;
+    for (int i = 0; i < VB / LW; ++i) {
+      const int blk = wave * (VB / LW) + i;
       const int r = blk * 8 + lane / 8;
       const int c = (lane % 8) ^ (r & 7);
       buffer_load_to_lds(rv, (lds_u32 *)&s.v[st][blk * 512], 16, r * v_row + c * 16, 0, 0, 0);
     }
-    if (wave == 0) buffer_load_to_lds(rg, (lds_u32 *)&s.lg[st][0], 4, lane * g_row, 0, 0, 0);
+  }
+  __device__ __forceinline__ void g_part(W8Lds<DK, SP> &s, int wave, int lane, int slot) {
+    if (g_active && wave == LW - 1)
+      buffer_load_to_lds(rg, (lds_u32 *)&s.lgb[slot][0], 4, lane * g_row, 0, 0, 0);
   }
 };
 
@@ -121,8 +154,8 @@ struct W8Wave {
   __device__ __forceinline__ W8Wave(LDS &s_, int w, int l)
       : s(s_), wave(w), lane(l), ln(l % 16), lg4(l / 16) {}
 
-  __device__ __forceinline__ float gates(int st, float &lsum) {
-    const float x = s.lg[st][lane];
+  // x = this lane's log-gate (0 past the end of the run); returns the chunk decay.
+  __device__ __forceinline__ float gates(float x, float &lsum) {
     const float incl = wave_inclusive_scan(x);
     const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
     const float b2last = total * kLog2e;
@@ -134,17 +167,18 @@ struct W8Wave {
     return fast_exp2(b2last);
   }
 
-  // Score tiles W and W + 8 of A^T = K Q^T -> decay mask -> bf16 hi/lo P.
+  // Score tile W (and W + 4 for W = 4, 5: the two tiles beyond eight go to the
+  // wavefronts of row half 1) of A^T = K Q^T -> decay mask -> bf16 hi/lo P.
   // All operand reads are issued before the first MFMA.
   template <int W>
   __device__ __forceinline__ void scores(const uint16_t *sq, const uint16_t *sk) {
-    constexpr int NW = W + 8 < NTILE ? 2 : 1;
+    constexpr int NW = (W == 4 || W == 5) ? 2 : 1;
     u32x4 a[NW][NKS], b[NW][NKS];
     f32x4 g4[NW];
     float b2i[NW];
 #pragma unroll
     for (int m = 0; m < NW; ++m) {
-      const int tile = W + 8 * m;
+      const int tile = W + 4 * m;
       const int ti = tile_ti(tile), tj = tile_tj(tile);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -166,7 +200,7 @@ struct W8Wave {
       for (int m = 0; m < NW; ++m) acc[m] = mfma16(a[m][ks], b[m][ks], acc[m]);
 #pragma unroll
     for (int m = 0; m < NW; ++m) {
-      const int tile = W + 8 * m;
+      const int tile = W + 4 * m;
       const int ti = tile_ti(tile), tj = tile_tj(tile);
       const int i = 16 * ti + ln;  // acc[m][r] = A^T[16 tj + 4 lg4 + r][i]
       float p[4];
@@ -215,7 +249,6 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
   constexpr int HALF = DK / 2;    // state rows per wavefront
   constexpr int NTH = DK / 32;    // 16-row state tiles per wavefront
   constexpr int NKH = DK / 64;    // 32-deep k-steps over the wavefront's half of d_k
-  constexpr int NJS = C / 32;     // 32-deep k-steps over the chunk
   __shared__ LDS s;
 
   // Block -> (pair = item * H + head, column slice); slices of a pair share an XCD.
@@ -273,37 +306,57 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
   }
 
   float lsum = 0.f;
-  // O_prev[m][r] = O[16 (2 rh + m) + ln][wcol + 4 lg4 + r] of the previous chunk.
+  // Output row blocks (16 rows) owned by this wavefront: rows 0..15 and
+  // 48..63 for row half 0, rows 16..47 for row half 1, so that both halves
+  // see the same number of key blocks in P V.
+  const int mi0 = rh, mi1 = 3 - rh;  // (0, 3) or (1, 2)
+  // O_prev[m][r] = O[16 mi_m + ln][wcol + 4 lg4 + r] of the previous chunk.
   f32x4 O_prev[2];
   int t_prev = -1, n_prev = 0;
   auto store_prev = [&]() {
     if (SP || t_prev < 0) return;
-    Tout *ob = o + ((size_t)(t_prev + 32 * rh + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
+    Tout *ob = o + ((size_t)(t_prev + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
     const size_t rs16 = (size_t)16 * H * DV;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-      if (32 * rh + 16 * m + ln < n_prev) store4_from_f32(ob + m * rs16, O_prev[m]);
+    if (16 * mi0 + ln < n_prev) store4_from_f32(ob + mi0 * rs16, O_prev[0]);
+    if (16 * mi1 + ln < n_prev) store4_from_f32(ob + mi1 * rs16, O_prev[1]);
   };
+
 
   W8Loader<DK, SP> ld;
   int t0 = w.tok_begin;
-  ld.setup(q, k, v, lg, t0, w.tok_end, H, h, DV, col0, 0);
+  ld.init(q, k, v, lg, t0, H, h, DV, col0);
+  ld.next(t0, w.tok_end, 0);
   ld.k_part(s, wave, lane);
   ld.q_part(s, wave, lane);
   ld.v_part(s, wave, lane);
+  ld.gate_next(t0, w.tok_end);
+  ld.g_part(s, wave, lane, 0);
+  ld.gate_next(t0 + C, w.tok_end);
+  ld.g_part(s, wave, lane, 1);
+  barrier_all();
+  // gates of the first chunk; each later chunk's are prepared at the end of
+  // the chunk before it, from the ring slot loaded two chunks ahead
+  float gam = t0 < w.tok_end ? R.gates(s.lgb[0][lane], lsum) : 1.f;
+  int g_rd = 1, g_ld = 2;  // ring slots of the next chunk's and of the far chunk's gates
+
+  // key rows of this wavefront's 32 keys (js = rh) and of the partner's
+  const int jo = 32 * rh, jx = 32 * (1 - rh);
 
   for (int ci = 0; t0 < w.tok_end; t0 += C, ++ci) {
     const int n = min(C, w.tok_end - t0);
     const int st = ci & 1;
     barrier_all();  // chunk ci's tiles are in LDS; every wavefront left chunk ci-1
+    counters_drained();
+    store_prev();   // outputs of chunk ci-1
 
     const uint16_t *sq = s.q[SP ? 0 : st];
     const uint16_t *sk = s.k[st];
     const uint16_t *sv = s.v[st];
-    ld.setup(q, k, v, lg, t0 + C, w.tok_end, H, h, DV, col0, st ^ 1);
+    const bool has_next = t0 + C < w.tok_end;
+    ld.next(t0 + C, w.tok_end, st ^ 1);
     ld.k_part(s, wave, lane);
-
-    const float gam = R.gates(st, lsum);
+    ld.gate_next(t0 + 2 * C, w.tok_end);
+    ld.g_part(s, wave, lane, g_ld);
 
     f32x4 own[2];
     if (!SP) {
@@ -343,63 +396,95 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16(bl, qf[ks][mi], part[mi]);
       }
-      // rows of the partner's half go through LDS
-#pragma unroll
-      for (int m = 0; m < 2; ++m) s.xbuf[wave][m][lane] = part[2 * (1 - rh) + m];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) own[m] = part[2 * rh + m];
+      // rows of the partner's blocks go through LDS (rh is wave-uniform: no
+      // register indexing)
+      if (rh) {
+        s.xbuf[wave][0][lane] = part[0];
+        s.xbuf[wave][1][lane] = part[3];
+        own[0] = part[1];
+        own[1] = part[2];
+      } else {
+        s.xbuf[wave][0][lane] = part[1];
+        s.xbuf[wave][1][lane] = part[2];
+        own[0] = part[0];
+        own[1] = part[3];
+      }
     }
-    ld.v_part(s, wave, lane);
-    barrier_lds();  // P and the partial outputs are complete
 
-    store_prev();
-
-    // V fragments (transpose reads): slot 8 lg4 + e <-> j = 32 js + 8 lg4 + e, column wcol + ln
-    u32x4 vf[NJS];
+    // ---- operands that need nothing computed in this chunk: K^T for the state
+    // update (A operand: slot 8 lg4 + e <-> key j0 + 8 lg4 + e, row d = drow0 + 16 t + ln)
+    // and V^T (slot 8 lg4 + e <-> key j0 + 8 lg4 + e, column wcol + ln)
+    u32x4 kt_o[NTH], kt_x[NTH];
 #pragma unroll
-    for (int js = 0; js < NJS; ++js) {
-      const int r0 = 32 * js + 8 * lg4 + (ln >> 2);
+    for (int t = 0; t < NTH; ++t) {
+      const int c = drow0 + 16 * t + 4 * (ln & 3);
+      const int ro = jo + 8 * lg4 + (ln >> 2), rx = jx + 8 * lg4 + (ln >> 2);
+      const u32x2 a0 = lds_tr16_nowait(&sk[qk_off<DK>(ro, c)]);
+      const u32x2 a1 = lds_tr16_nowait(&sk[qk_off<DK>(ro + 4, c)]);
+      const u32x2 b0 = lds_tr16_nowait(&sk[qk_off<DK>(rx, c)]);
+      const u32x2 b1 = lds_tr16_nowait(&sk[qk_off<DK>(rx + 4, c)]);
+      kt_o[t] = u32x4{a0.x, a0.y, a1.x, a1.y};
+      kt_x[t] = u32x4{b0.x, b0.y, b1.x, b1.y};
+    }
+    auto v_frag = [&](int j0) -> u32x4 {
+      const int r0 = j0 + 8 * lg4 + (ln >> 2);
       const int c = wcol + 4 * (ln & 3);
-      const u32x2 x0 = lds_tr16(&sv[v_off(r0, c)]);
-      const u32x2 x1 = lds_tr16(&sv[v_off(r0 + 4, c)]);
-      vf[js] = u32x4{x0.x, x0.y, x1.x, x1.y};
+      const u32x2 x0 = lds_tr16_nowait(&sv[v_off(r0, c)]);
+      const u32x2 x1 = lds_tr16_nowait(&sv[v_off(r0 + 4, c)]);
+      return u32x4{x0.x, x0.y, x1.x, x1.y};
+    };
+    u32x4 vf_0 = v_frag(0);   // keys 0..31
+    u32x4 vf_1 = v_frag(32);  // keys 32..63
+    lds_wait(vf_0, vf_1);
+    const u32x4 vf_o = rh ? vf_1 : vf_0;  // this wavefront's 32 keys
+    const f32x4 kap0 = *reinterpret_cast<const f32x4 *>(&s.gkap[wave][jo + 8 * lg4]);
+    const f32x4 kap1 = *reinterpret_cast<const f32x4 *>(&s.gkap[wave][jo + 8 * lg4 + 4]);
+
+    // kappa . V for this wavefront's keys, hi/lo; the partner does the other 32
+    u32x4 kv_h, kv_l;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const uint32_t vw = vf_o[e2];
+      const float v0 = __uint_as_float(vw << 16), v1 = __uint_as_float(vw & 0xffff0000u);
+      const f32x4 &kk = e2 < 2 ? kap0 : kap1;
+      uint32_t hh, ll;
+      split_pk_bf16(kk[2 * (e2 & 1)] * v0, kk[2 * (e2 & 1) + 1] * v1, hh, ll);
+      kv_h[e2] = hh;
+      kv_l[e2] = ll;
+    }
+    s.kvx[wave][0][lane] = kv_h;
+    s.kvx[wave][1][lane] = kv_l;
+
+    ld.v_part(s, wave, lane);
+    barrier_lds();  // P, the partial outputs and kappa . V are complete
+    static_assert(NTH == 4 || NTH == 2, "state tiles per wavefront");
+    if constexpr (NTH == 4) {
+      lds_after_wait(kt_o[0], kt_o[1], kt_o[2], kt_o[3]);
+      lds_after_wait(kt_x[0], kt_x[1], kt_x[2], kt_x[3]);
+    } else {
+      lds_after_wait(kt_o[0], kt_o[1], kt_x[0], kt_x[1]);
     }
 
-    // operands of P V and of the state update, all issued before the MFMAs
-    u32x4 pf_h[2][NJS], pf_l[2][NJS];
+    // operands of P V and of the rest of the state update
+    const u32x4 kx_h = s.kvx[wave ^ 4][0][lane];
+    const u32x4 kx_l = s.kvx[wave ^ 4][1][lane];
+    // P fragments: block mi0 (rows < 32) needs keys 0..31, block mi1 (rows >= 32) all 64
+    u32x4 pf_h[3], pf_l[3];
     f32x4 xp[2];
     float lam[2];
     if (!SP) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const int mi = 2 * rh + m;
+        const int mi = m ? mi1 : mi0;
         xp[m] = s.xbuf[wave ^ 4][m][lane];
         lam[m] = s.glam[wave][16 * mi + ln];
-#pragma unroll
-        for (int js = 0; js < NJS; ++js) {
-          if (32 * js <= 16 * mi + 15) {
-            const int off = (16 * mi + ln) * PP + 32 * js + 8 * lg4;
-            pf_h[m][js] = *reinterpret_cast<const u32x4 *>(&s.phi[off]);
-            pf_l[m][js] = *reinterpret_cast<const u32x4 *>(&s.plo[off]);
-          }
-        }
       }
-    }
-    u32x4 kt[NJS][NTH];
-    f32x4 kap[NJS][2];
 #pragma unroll
-    for (int js = 0; js < NJS; ++js) {
-#pragma unroll
-      for (int t = 0; t < NTH; ++t) {
-        // A operand K^T: slot 8 lg4 + e <-> j = 32 js + 8 lg4 + e, d = drow0 + 16 t + ln
-        const int r0 = 32 * js + 8 * lg4 + (ln >> 2);
-        const int c = drow0 + 16 * t + 4 * (ln & 3);
-        const u32x2 x0 = lds_tr16(&sk[qk_off<DK>(r0, c)]);
-        const u32x2 x1 = lds_tr16(&sk[qk_off<DK>(r0 + 4, c)]);
-        kt[js][t] = u32x4{x0.x, x0.y, x1.x, x1.y};
+      for (int e = 0; e < 3; ++e) {
+        const int off = (16 * (e ? mi1 : mi0) + ln) * PP + 32 * (e == 2) + 8 * lg4;
+        pf_h[e] = *reinterpret_cast<const u32x4 *>(&s.phi[off]);
+        pf_l[e] = *reinterpret_cast<const u32x4 *>(&s.plo[off]);
       }
-      kap[js][0] = *reinterpret_cast<const f32x4 *>(&s.gkap[wave][32 * js + 8 * lg4]);
-      kap[js][1] = *reinterpret_cast<const f32x4 *>(&s.gkap[wave][32 * js + 8 * lg4 + 4]);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -407,40 +492,25 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
       // own rows: partner's half of the state read, scale by 2^(b2_i), then V^T P^T
 #pragma unroll
       for (int m = 0; m < 2; ++m) own[m] = (own[m] + xp[m]) * lam[m];
-#pragma unroll
-      for (int js = 0; js < NJS; ++js) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const int mi = 2 * rh + m;
-          if (32 * js <= 16 * mi + 15) own[m] = mfma16(vf[js], pf_h[m][js], own[m]);
-        }
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const int mi = 2 * rh + m;
-          if (32 * js <= 16 * mi + 15) own[m] = mfma16(vf[js], pf_l[m][js], own[m]);
-        }
-      }
+      own[0] = mfma16(vf_0, pf_h[0], own[0]);
+      own[1] = mfma16(vf_0, pf_h[1], own[1]);
+      own[0] = mfma16(vf_0, pf_l[0], own[0]);
+      own[1] = mfma16(vf_0, pf_l[1], own[1]);
+      own[1] = mfma16(vf_1, pf_h[2], own[1]);
+      own[1] = mfma16(vf_1, pf_l[2], own[1]);
     }
 
     // ---- state advance for this half: S <- gamma S + K_half^T (kappa . V)
 #pragma unroll
     for (int t = 0; t < NTH; ++t) S_acc[t] *= gam;
 #pragma unroll
-    for (int js = 0; js < NJS; ++js) {
-      uint32_t kh[4], kl[4];
+    for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt_o[t], kv_h, S_acc[t]);
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t vw = vf[js][e2];
-        const float v0 = __uint_as_float(vw << 16), v1 = __uint_as_float(vw & 0xffff0000u);
-        const f32x4 &kk = kap[js][e2 >> 1];
-        split_pk_bf16(kk[2 * (e2 & 1)] * v0, kk[2 * (e2 & 1) + 1] * v1, kh[e2], kl[e2]);
-      }
-      const u32x4 bh = {kh[0], kh[1], kh[2], kh[3]}, bl = {kl[0], kl[1], kl[2], kl[3]};
+    for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt_o[t], kv_l, S_acc[t]);
 #pragma unroll
-      for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt[js][t], bh, S_acc[t]);
+    for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt_x[t], kx_h, S_acc[t]);
 #pragma unroll
-      for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt[js][t], bl, S_acc[t]);
-    }
+    for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt_x[t], kx_l, S_acc[t]);
 
     if (!SP) {
       O_prev[0] = own[0];
@@ -448,6 +518,9 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
       t_prev = t0;
       n_prev = n;
     }
+    if (has_next) gam = R.gates(s.lgb[g_rd][lane], lsum);
+    g_rd = g_rd == 2 ? 0 : g_rd + 1;
+    g_ld = g_ld == 2 ? 0 : g_ld + 1;
   }
 
   store_prev();
