@@ -36,6 +36,11 @@ __device__ __forceinline__ void barrier_lds() {
 __device__ __forceinline__ void barrier_all() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// The same, except that the last two vector-memory operations this wavefront
+// issued (two stores, by the caller's construction) may still be in flight.
+__device__ __forceinline__ void barrier_all_but_2() {
+  asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -94,6 +99,8 @@ __device__ __forceinline__ void lds_after_wait(u32x4 &a, u32x4 &b, u32x4 &c, u32
 // Tell the compiler's wait insertion that every counter is drained (emits a
 // wait that is a no-op at run time when placed after barrier_all()).
 __device__ __forceinline__ void counters_drained() { __builtin_amdgcn_s_waitcnt(0); }
+// gfx9 s_waitcnt immediate: vmcnt(2) expcnt(7) lgkmcnt(0).
+__device__ __forceinline__ void counters_drained_but_2() { __builtin_amdgcn_s_waitcnt(0x0072); }
 
 // Inclusive prefix sum across the 64 lanes of a wavefront with DPP row shifts
 // and row broadcasts (no LDS round trips).

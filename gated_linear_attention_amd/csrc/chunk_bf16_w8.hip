@@ -167,69 +167,51 @@ struct W8Wave {
     return fast_exp2(b2last);
   }
 
-  // Score tile W (and W + 4 for W = 4, 5: the two tiles beyond eight go to the
-  // wavefronts of row half 1) of A^T = K Q^T -> decay mask -> bf16 hi/lo P.
-  // All operand reads are issued before the first MFMA.
-  template <int W>
-  __device__ __forceinline__ void scores(const uint16_t *sq, const uint16_t *sk) {
-    constexpr int NW = (W == 4 || W == 5) ? 2 : 1;
-    u32x4 a[NW][NKS], b[NW][NKS];
-    f32x4 g4[NW];
-    float b2i[NW];
+  // One 16x16 score tile of A^T = K Q^T (rows: keys 16 tj.., columns: queries
+  // 16 ti..), in three stages so that a caller can interleave them with other
+  // work: operand reads, the MFMA chain, then decay mask -> bf16 hi/lo P.
+  struct TileOps {
+    u32x4 a[NKS], b[NKS];
+    float b2i;
+    f32x4 g4;
+  };
+  __device__ __forceinline__ void tile_read(TileOps &t, const uint16_t *sq, const uint16_t *sk,
+                                            int ti, int tj) {
 #pragma unroll
-    for (int m = 0; m < NW; ++m) {
-      const int tile = W + 4 * m;
-      const int ti = tile_ti(tile), tj = tile_tj(tile);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        a[m][ks] =
-            *reinterpret_cast<const u32x4 *>(&sk[qk_off<DK>(16 * tj + ln, 32 * ks + 8 * lg4)]);
-        b[m][ks] =
-            *reinterpret_cast<const u32x4 *>(&sq[qk_off<DK>(16 * ti + ln, 32 * ks + 8 * lg4)]);
-      }
-      b2i[m] = s.gb2[wave][16 * ti + ln];
-      g4[m] = *reinterpret_cast<const f32x4 *>(&s.gb2[wave][16 * tj + 4 * lg4]);
+    for (int ks = 0; ks < NKS; ++ks) {
+      t.a[ks] = *reinterpret_cast<const u32x4 *>(&sk[qk_off<DK>(16 * tj + ln, 32 * ks + 8 * lg4)]);
+      t.b[ks] = *reinterpret_cast<const u32x4 *>(&sq[qk_off<DK>(16 * ti + ln, 32 * ks + 8 * lg4)]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 acc[NW];
-#pragma unroll
-    for (int m = 0; m < NW; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int m = 0; m < NW; ++m) acc[m] = mfma16(a[m][ks], b[m][ks], acc[m]);
-#pragma unroll
-    for (int m = 0; m < NW; ++m) {
-      const int tile = W + 4 * m;
-      const int ti = tile_ti(tile), tj = tile_tj(tile);
-      const int i = 16 * ti + ln;  // acc[m][r] = A^T[16 tj + 4 lg4 + r][i]
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * tj + 4 * lg4 + r;
-        // masked entries (j > i) take 2^-inf = 0; the select is on the exponent
-        const float e = (ti > tj || j <= i) ? b2i[m] - g4[m][r] : -__builtin_huge_valf();
-        p[r] = acc[m][r] * fast_exp2(e);
-      }
-      uint32_t h0, l0, h1, l1;
-      split_pk_bf16(p[0], p[1], h0, l0);
-      split_pk_bf16(p[2], p[3], h1, l1);
-      const u32x2 wh = {h0, h1}, wl = {l0, l1};
-      *reinterpret_cast<u32x2 *>(&s.phi[i * PP + 16 * tj + 4 * lg4]) = wh;
-      *reinterpret_cast<u32x2 *>(&s.plo[i * PP + 16 * tj + 4 * lg4]) = wl;
-    }
+    t.b2i = s.gb2[wave][16 * ti + ln];
+    t.g4 = *reinterpret_cast<const f32x4 *>(&s.gb2[wave][16 * tj + 4 * lg4]);
   }
-  __device__ __forceinline__ void scores_dispatch(const uint16_t *sq, const uint16_t *sk) {
-    switch (wave) {
-      case 0: scores<0>(sq, sk); break;
-      case 1: scores<1>(sq, sk); break;
-      case 2: scores<2>(sq, sk); break;
-      case 3: scores<3>(sq, sk); break;
-      case 4: scores<4>(sq, sk); break;
-      case 5: scores<5>(sq, sk); break;
-      case 6: scores<6>(sq, sk); break;
-      default: scores<7>(sq, sk); break;
-    }
+  __device__ __forceinline__ f32x4 tile_mma(const TileOps &t) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) acc = mfma16(t.a[ks], t.b[ks], acc);
+    return acc;
+  }
+  // madd[r] = 0 where key 16 tj + 4 lg4 + r may attend (j <= i), -inf where masked;
+  // the decay factor is 2^(b2_i - b2_j + madd).
+  __device__ __forceinline__ f32x4 tile_mask(int ti, int tj) const {
+    f32x4 m;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      m[r] = (ti > tj || 16 * tj + 4 * lg4 + r <= 16 * ti + ln) ? 0.f : -__builtin_huge_valf();
+    return m;
+  }
+  __device__ __forceinline__ void tile_store(const f32x4 &acc, const TileOps &t, const f32x4 &madd,
+                                             int ti, int tj) {
+    const int i = 16 * ti + ln;  // acc[r] = A^T[16 tj + 4 lg4 + r][i]
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = acc[r] * fast_exp2(t.b2i - t.g4[r] + madd[r]);
+    uint32_t h0, l0, h1, l1;
+    split_pk_bf16(p[0], p[1], h0, l0);
+    split_pk_bf16(p[2], p[3], h1, l1);
+    const u32x2 wh = {h0, h1}, wl = {l0, l1};
+    *reinterpret_cast<u32x2 *>(&s.phi[i * PP + 16 * tj + 4 * lg4]) = wh;
+    *reinterpret_cast<u32x2 *>(&s.plo[i * PP + 16 * tj + 4 * lg4]) = wl;
   }
 };
 
@@ -310,16 +292,16 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
   // 48..63 for row half 0, rows 16..47 for row half 1, so that both halves
   // see the same number of key blocks in P V.
   const int mi0 = rh, mi1 = 3 - rh;  // (0, 3) or (1, 2)
-  // O_prev[m][r] = O[16 mi_m + ln][wcol + 4 lg4 + r] of the previous chunk.
-  f32x4 O_prev[2];
-  int t_prev = -1, n_prev = 0;
-  auto store_prev = [&]() {
-    if (SP || t_prev < 0) return;
-    Tout *ob = o + ((size_t)(t_prev + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
-    const size_t rs16 = (size_t)16 * H * DV;
-    if (16 * mi0 + ln < n_prev) store4_from_f32(ob + mi0 * rs16, O_prev[0]);
-    if (16 * mi1 + ln < n_prev) store4_from_f32(ob + mi1 * rs16, O_prev[1]);
+  // own[m][r] = O[16 mi_m + ln][wcol + 4 lg4 + r]: 16-byte row pieces, stored at
+  // the end of the chunk (the barrier that opens the next chunk lets them
+  // stay in flight)
+  const size_t rs16 = (size_t)16 * H * DV;
+  auto store_out = [&](int tc, int nc, const f32x4 (&own)[2]) {
+    Tout *ob = o + ((size_t)(tc + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
+    if (16 * mi0 + ln < nc) store4_from_f32(ob + mi0 * rs16, own[0]);
+    if (16 * mi1 + ln < nc) store4_from_f32(ob + mi1 * rs16, own[1]);
   };
+
 
 
   W8Loader<DK, SP> ld;
@@ -341,13 +323,27 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
 
   // key rows of this wavefront's 32 keys (js = rh) and of the partner's
   const int jo = 32 * rh, jx = 32 * (1 - rh);
+  // score tiles: tile `wave` for every wavefront, tiles 8 and 9 also for
+  // wavefronts 4 and 5 (lower triangle of 16x16 tiles, row-major)
+  const int ti1 = tile_ti(wave), tj1 = tile_tj(wave);
+  const bool two_tiles = wave == 4 || wave == 5;
+  const int ti2 = 3, tj2 = wave - 2;
+  const f32x4 madd1 = R.tile_mask(ti1, tj1), madd2 = R.tile_mask(ti2, tj2);
 
   for (int ci = 0; t0 < w.tok_end; t0 += C, ++ci) {
     const int n = min(C, w.tok_end - t0);
     const int st = ci & 1;
-    barrier_all();  // chunk ci's tiles are in LDS; every wavefront left chunk ci-1
-    counters_drained();
-    store_prev();   // outputs of chunk ci-1
+    // chunk ci's tiles are in LDS and every wavefront left chunk ci-1; the two
+    // output stores of chunk ci-1 (the last vector-memory operations issued,
+    // present whenever loads were issued after the previous barrier) may still
+    // be in flight. The state pass stores nothing and waits for everything.
+    if (SP) {
+      barrier_all();
+      counters_drained();
+    } else {
+      barrier_all_but_2();
+      counters_drained_but_2();
+    }
 
     const uint16_t *sq = s.q[SP ? 0 : st];
     const uint16_t *sk = s.k[st];
@@ -360,14 +356,11 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
 
     f32x4 own[2];
     if (!SP) {
-      R.scores_dispatch(sq, sk);
-      ld.q_part(s, wave, lane);
-
-      // ---- state read over this wavefront's half of d_k, all 64 rows:
+      // ---- score tile(s) and the state read over this wavefront's half of
+      // d_k for all 64 rows, scheduled together:
       // part[mi][r] = sum over d in the half of S[d][wcol + 4 lg4 + r] Q[16 mi + ln][d]
-      f32x4 part[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) part[mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+      typename Wv::TileOps t1;
+      R.tile_read(t1, sq, sk, ti1, tj1);
       u32x4 qf[NKH][4];
 #pragma unroll
       for (int ks = 0; ks < NKH; ++ks) {
@@ -381,21 +374,44 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+      // hi/lo bf16 of the state half (A operand), while the reads are in flight:
+      // slot 8 lg4 + r <-> d = drow0 + 32 ks + 4 lg4 + r,
+      // slot 8 lg4 + 4 + r <-> d = drow0 + 32 ks + 16 + 4 lg4 + r
+      u32x4 sh[NKH], sl[NKH];
 #pragma unroll
       for (int ks = 0; ks < NKH; ++ks) {
-        // slot 8 lg4 + r <-> d = drow0 + 32 ks + 4 lg4 + r,
-        // slot 8 lg4 + 4 + r <-> d = drow0 + 32 ks + 16 + 4 lg4 + r
-        uint32_t sh[4], sl[4];
-        split_pk_bf16(S_acc[2 * ks][0], S_acc[2 * ks][1], sh[0], sl[0]);
-        split_pk_bf16(S_acc[2 * ks][2], S_acc[2 * ks][3], sh[1], sl[1]);
-        split_pk_bf16(S_acc[2 * ks + 1][0], S_acc[2 * ks + 1][1], sh[2], sl[2]);
-        split_pk_bf16(S_acc[2 * ks + 1][2], S_acc[2 * ks + 1][3], sh[3], sl[3]);
-        const u32x4 bh = {sh[0], sh[1], sh[2], sh[3]}, bl = {sl[0], sl[1], sl[2], sl[3]};
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16(bh, qf[ks][mi], part[mi]);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16(bl, qf[ks][mi], part[mi]);
+        uint32_t h[4], l[4];
+        split_pk_bf16(S_acc[2 * ks][0], S_acc[2 * ks][1], h[0], l[0]);
+        split_pk_bf16(S_acc[2 * ks][2], S_acc[2 * ks][3], h[1], l[1]);
+        split_pk_bf16(S_acc[2 * ks + 1][0], S_acc[2 * ks + 1][1], h[2], l[2]);
+        split_pk_bf16(S_acc[2 * ks + 1][2], S_acc[2 * ks + 1][3], h[3], l[3]);
+        sh[ks] = u32x4{h[0], h[1], h[2], h[3]};
+        sl[ks] = u32x4{l[0], l[1], l[2], l[3]};
       }
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x4 acc1 = R.tile_mma(t1);
+      f32x4 part[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16(sh[0], qf[0][mi], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16(sl[0], qf[0][mi], part[mi]);
+      __builtin_amdgcn_sched_barrier(0);
+      // the tile's mask and P stores overlap the rest of the state read
+      R.tile_store(acc1, t1, madd1, ti1, tj1);
+#pragma unroll
+      for (int ks = 1; ks < NKH; ++ks) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16(sh[ks], qf[ks][mi], part[mi]);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16(sl[ks], qf[ks][mi], part[mi]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (two_tiles) {
+        typename Wv::TileOps t2;
+        R.tile_read(t2, sq, sk, ti2, tj2);
+        R.tile_store(R.tile_mma(t2), t2, madd2, ti2, tj2);
+      }
+      ld.q_part(s, wave, lane);
       // rows of the partner's blocks go through LDS (rh is wave-uniform: no
       // register indexing)
       if (rh) {
@@ -411,21 +427,11 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
       }
     }
 
-    // ---- operands that need nothing computed in this chunk: K^T for the state
-    // update (A operand: slot 8 lg4 + e <-> key j0 + 8 lg4 + e, row d = drow0 + 16 t + ln)
-    // and V^T (slot 8 lg4 + e <-> key j0 + 8 lg4 + e, column wcol + ln)
-    u32x4 kt_o[NTH], kt_x[NTH];
-#pragma unroll
-    for (int t = 0; t < NTH; ++t) {
-      const int c = drow0 + 16 * t + 4 * (ln & 3);
-      const int ro = jo + 8 * lg4 + (ln >> 2), rx = jx + 8 * lg4 + (ln >> 2);
-      const u32x2 a0 = lds_tr16_nowait(&sk[qk_off<DK>(ro, c)]);
-      const u32x2 a1 = lds_tr16_nowait(&sk[qk_off<DK>(ro + 4, c)]);
-      const u32x2 b0 = lds_tr16_nowait(&sk[qk_off<DK>(rx, c)]);
-      const u32x2 b1 = lds_tr16_nowait(&sk[qk_off<DK>(rx + 4, c)]);
-      kt_o[t] = u32x4{a0.x, a0.y, a1.x, a1.y};
-      kt_x[t] = u32x4{b0.x, b0.y, b1.x, b1.y};
-    }
+    // ---- kappa . V for this wavefront's 32 keys (js = rh), hi/lo; the partner
+    // does the other 32. V^T fragments: slot 8 lg4 + e <-> key j0 + 8 lg4 + e,
+    // column wcol + ln.
+    const f32x4 kap0 = *reinterpret_cast<const f32x4 *>(&s.gkap[wave][jo + 8 * lg4]);
+    const f32x4 kap1 = *reinterpret_cast<const f32x4 *>(&s.gkap[wave][jo + 8 * lg4 + 4]);
     auto v_frag = [&](int j0) -> u32x4 {
       const int r0 = j0 + 8 * lg4 + (ln >> 2);
       const int c = wcol + 4 * (ln & 3);
@@ -437,10 +443,6 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
     u32x4 vf_1 = v_frag(32);  // keys 32..63
     lds_wait(vf_0, vf_1);
     const u32x4 vf_o = rh ? vf_1 : vf_0;  // this wavefront's 32 keys
-    const f32x4 kap0 = *reinterpret_cast<const f32x4 *>(&s.gkap[wave][jo + 8 * lg4]);
-    const f32x4 kap1 = *reinterpret_cast<const f32x4 *>(&s.gkap[wave][jo + 8 * lg4 + 4]);
-
-    // kappa . V for this wavefront's keys, hi/lo; the partner does the other 32
     u32x4 kv_h, kv_l;
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
@@ -454,6 +456,21 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
     }
     s.kvx[wave][0][lane] = kv_h;
     s.kvx[wave][1][lane] = kv_l;
+
+    // ---- K^T for the state update, read now and used after the barrier
+    // (A operand: slot 8 lg4 + e <-> key j0 + 8 lg4 + e, row d = drow0 + 16 t + ln)
+    u32x4 kt_o[NTH], kt_x[NTH];
+#pragma unroll
+    for (int t = 0; t < NTH; ++t) {
+      const int c = drow0 + 16 * t + 4 * (ln & 3);
+      const int ro = jo + 8 * lg4 + (ln >> 2), rx = jx + 8 * lg4 + (ln >> 2);
+      const u32x2 a0 = lds_tr16_nowait(&sk[qk_off<DK>(ro, c)]);
+      const u32x2 a1 = lds_tr16_nowait(&sk[qk_off<DK>(ro + 4, c)]);
+      const u32x2 b0 = lds_tr16_nowait(&sk[qk_off<DK>(rx, c)]);
+      const u32x2 b1 = lds_tr16_nowait(&sk[qk_off<DK>(rx + 4, c)]);
+      kt_o[t] = u32x4{a0.x, a0.y, a1.x, a1.y};
+      kt_x[t] = u32x4{b0.x, b0.y, b1.x, b1.y};
+    }
 
     ld.v_part(s, wave, lane);
     barrier_lds();  // P, the partial outputs and kappa . V are complete
@@ -488,6 +505,16 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    // ---- state advance for this half, S <- gamma S + K_half^T (kappa . V):
+    // this wavefront's own 32 keys first (nothing read after the barrier)
+#pragma unroll
+    for (int t = 0; t < NTH; ++t) S_acc[t] *= gam;
+#pragma unroll
+    for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt_o[t], kv_h, S_acc[t]);
+#pragma unroll
+    for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt_o[t], kv_l, S_acc[t]);
+    __builtin_amdgcn_sched_barrier(0);
+
     if (!SP) {
       // own rows: partner's half of the state read, scale by 2^(b2_i), then V^T P^T
 #pragma unroll
@@ -499,31 +526,18 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
       own[1] = mfma16(vf_1, pf_h[2], own[1]);
       own[1] = mfma16(vf_1, pf_l[2], own[1]);
     }
-
-    // ---- state advance for this half: S <- gamma S + K_half^T (kappa . V)
-#pragma unroll
-    for (int t = 0; t < NTH; ++t) S_acc[t] *= gam;
-#pragma unroll
-    for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt_o[t], kv_h, S_acc[t]);
-#pragma unroll
-    for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt_o[t], kv_l, S_acc[t]);
+    // the partner's 32 keys
 #pragma unroll
     for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt_x[t], kx_h, S_acc[t]);
 #pragma unroll
     for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt_x[t], kx_l, S_acc[t]);
 
-    if (!SP) {
-      O_prev[0] = own[0];
-      O_prev[1] = own[1];
-      t_prev = t0;
-      n_prev = n;
-    }
+    if (!SP) store_out(t0, n, own);
     if (has_next) gam = R.gates(s.lgb[g_rd][lane], lsum);
     g_rd = g_rd == 2 ? 0 : g_rd + 1;
     g_ld = g_ld == 2 ? 0 : g_ld + 1;
   }
 
-  store_prev();
   float *sout = nullptr;
   if (SP) {
     sout = slots + ((size_t)w.state_out * H + h) * dkdv;
