@@ -58,21 +58,51 @@ def measured_traffic(kernel_key, sources):
 
 
 def time_launches(fn, steps, stream):
-    """Run fn(i) for i in range(steps) on `stream`; return (wall seconds, mean
-    per-launch GPU ms from HIP events recorded on that stream)."""
+    """Run fn(i) for i in range(steps) on `stream` twice: the timed pass (wall
+    clock between synchronisations, nothing else enqueued), then a pass with a
+    HIP event pair recorded on that stream around each launch. Returns (wall
+    seconds of the timed pass, mean per-launch GPU ms from the events)."""
     import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
     for i in range(steps):
         ev[i][0].record(stream)
         fn(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = [a.elapsed_time(b) for a, b in ev]
     return wall, sum(per) / len(per)
+
+
+def warm_up(fn, steps, seconds):
+    """At least `steps` calls and at least `seconds` of wall time, so that the
+    GPU clocks have settled before anything is timed."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while i < steps or time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
+
+
+# kernel that runs the headline forward at each chunk size, and the sources
+# whose hash keys its committed counter record
+FWD_KERNELS = {
+    64: ("chunk_bf16_w8_kernel<128,float,false>",
+         ["chunk_bf16_w8.hip", "bf16_blocks.h", "gla_common.h"]),
+    128: ("chunk_bf16_kernel<128,128,float,false>",
+          ["chunk_bf16.hip", "bf16_blocks.h", "gla_common.h"]),
+}
 
 
 def bench_forward(args):
@@ -98,13 +128,14 @@ def bench_forward(args):
     S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(i):
-        q, k, v, lg = sets[i % 3]
-        gla.fwd_chunked(q, k, v, lg, None, None, chunk_size=C, o=o, S_T=S_T)
+    def step_at(c):
+        def step(i):
+            q, k, v, lg = sets[i % 3]
+            gla.fwd_chunked(q, k, v, lg, None, None, chunk_size=c, o=o, S_T=S_T)
+        return step
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    step = step_at(C)
+    n_warm = warm_up(step, args.warmup, args.warm_seconds)
     wall, kern_ms = time_launches(step, args.steps, stream)
     ms_per_step = 1e3 * wall / args.steps
     tokens = B * T
@@ -126,7 +157,12 @@ def bench_forward(args):
                                       + (dk // 16) * (C // 32) * 2))       # K^T V hi/lo
     issued_flops = n_chunks * mfma_per_chunk * 16 * 16 * 32 * 2
     achieved_gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
-    traffic = measured_traffic("chunk_fwd_bf16_train_2k", ["chunk_bf16.hip", "gla_common.h"])
+    kname, ksrc = FWD_KERNELS[C]
+    traffic = measured_traffic(f"chunk_fwd_bf16_train_2k_c{C}", ksrc)
+    # the other chunk size, for reference (same inputs, same timing method)
+    C2 = 128 if C == 64 else 64
+    warm_up(step_at(C2), 10, 0.2)
+    wall2, kern_ms2 = time_launches(step_at(C2), args.steps, stream)
     res = {
         "tokens": tokens,
         "ms_per_step": ms_per_step,
@@ -135,10 +171,14 @@ def bench_forward(args):
         "config": {"workload": "train_2k chunked forward", "B": B, "T": T, "H": H, "dk": dk,
                    "dv": dv, "chunk": C, "in_dtype": "bf16", "out_dtype": "f32", "S0": "zeros",
                    "global_batch": B, "seq_len": T, "input_sets_rotated": 3},
+        "warmup_calls": n_warm,
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": alg_bytes,
-                     "kernel": f"chunk_bf16_kernel<{C},128,float,false>"},
+                     "traffic": traffic, "algorithmic_bytes": alg_bytes, "kernel": kname},
+        "other_chunk": {"chunk": C2, "kernel": FWD_KERNELS[C2][0],
+                        "kernel_ms": round(kern_ms2, 5),
+                        "tokens_per_s": round(tokens / (wall2 / args.steps), 1),
+                        "hbm_frac": round(alg_bytes / (kern_ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "mfma": {"algorithmic_tflops": round(alg_flops / (kern_ms * 1e-3) / 1e12, 1),
                  "algorithmic_util": round(alg_flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  "issued_tflops": round(issued_flops / (kern_ms * 1e-3) / 1e12, 1),
@@ -173,9 +213,7 @@ def bench_decode(args):
     def step(i):
         gla.decode_step(qs[i % steps], ks[i % steps], vs[i % steps], gs[i % steps], S, o=o)
 
-    for i in range(min(args.warmup, 10)):
-        step(i)
-    torch.cuda.synchronize()
+    warm_up(step, min(args.warmup, 10), min(args.warm_seconds, 0.5))
     wall, kern_ms = time_launches(step, steps, stream)
     pairs = N * H
     alg_bytes = pairs * (2 * dk * dv * 4 + 2 * dk + 2 * dk + 2 * dv + 4 + 4 * dv)
@@ -232,7 +270,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=10,
+                    help="minimum untimed calls before timing (see --warm-seconds)")
+    ap.add_argument("--warm-seconds", type=float, default=1.0,
+                    help="minimum wall time of the untimed warm-up, for the clocks to settle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--chunk", type=int, default=64, choices=[64, 128])
@@ -289,6 +330,7 @@ def main():
         "kernel_ms": round(fwd["kernel_ms"], 5),
         "roofline": fwd["roofline"],
         "mfma": fwd["mfma"],
+        "other_chunk": fwd["other_chunk"],
         "decode": dec,
         "cpu_baseline": cpu,
     }

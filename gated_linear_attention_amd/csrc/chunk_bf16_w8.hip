@@ -254,6 +254,13 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   Wv R(s, wave, lane);
+  // Row half 1 has the longer chain per chunk (wavefronts 4 and 5 also compute
+  // the two extra score tiles); let the SIMD arbiter prefer it over row half 0,
+  // which waits at the mid-chunk barrier otherwise.
+  if (wave >= 6)
+    __builtin_amdgcn_s_setprio(2);
+  else if (wave >= 4)
+    __builtin_amdgcn_s_setprio(3);
   const int ln = R.ln, lg4 = R.lg4;
   const int cg = wave & 3, rh = wave >> 2;  // column group, d_k half / row half
   const int wcol = 16 * cg;
@@ -349,10 +356,14 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
     const uint16_t *sk = s.k[st];
     const uint16_t *sv = s.v[st];
     const bool has_next = t0 + C < w.tok_end;
-    ld.next(t0 + C, w.tok_end, st ^ 1);
-    ld.k_part(s, wave, lane);
-    ld.gate_next(t0 + 2 * C, w.tok_end);
-    ld.g_part(s, wave, lane, g_ld);
+    if (wave < W8Loader<DK, SP>::LW) {  // only the loading wavefronts need descriptors
+      ld.next(t0 + C, w.tok_end, st ^ 1);
+      ld.k_part(s, wave, lane);
+      if (wave == W8Loader<DK, SP>::LW - 1) {
+        ld.gate_next(t0 + 2 * C, w.tok_end);
+        ld.g_part(s, wave, lane, g_ld);
+      }
+    }
 
     f32x4 own[2];
     if (!SP) {
