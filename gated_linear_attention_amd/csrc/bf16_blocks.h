@@ -36,8 +36,10 @@ __device__ __forceinline__ void barrier_lds() {
 __device__ __forceinline__ void barrier_all() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-// The same, except that the last two vector-memory operations this wavefront
-// issued (two stores, by the caller's construction) may still be in flight.
+// The same, except that up to two vector-memory operations may still be in
+// flight: for the caller to use only where those are stores issued after all
+// of this wavefront's loads had completed (loads and stores share the counter
+// and may complete out of order).
 __device__ __forceinline__ void barrier_all_but_2() {
   asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

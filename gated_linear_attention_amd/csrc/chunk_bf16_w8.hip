@@ -300,10 +300,13 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
   // see the same number of key blocks in P V.
   const int mi0 = rh, mi1 = 3 - rh;  // (0, 3) or (1, 2)
   // own[m][r] = O[16 mi_m + ln][wcol + 4 lg4 + r]: 16-byte row pieces, stored at
-  // the end of the chunk (the barrier that opens the next chunk lets them
-  // stay in flight)
+  // the end of the chunk. Loads and stores share one counter and need not
+  // complete in order, so this wavefront's loads are waited for first (issued
+  // long before, they have landed); the barrier that opens the next chunk then
+  // lets just these stores stay in flight.
   const size_t rs16 = (size_t)16 * H * DV;
   auto store_out = [&](int tc, int nc, const f32x4 (&own)[2]) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     Tout *ob = o + ((size_t)(tc + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
     if (16 * mi0 + ln < nc) store4_from_f32(ob + mi0 * rs16, own[0]);
     if (16 * mi1 + ln < nc) store4_from_f32(ob + mi1 * rs16, own[1]);
@@ -340,10 +343,10 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
   for (int ci = 0; t0 < w.tok_end; t0 += C, ++ci) {
     const int n = min(C, w.tok_end - t0);
     const int st = ci & 1;
-    // chunk ci's tiles are in LDS and every wavefront left chunk ci-1; the two
-    // output stores of chunk ci-1 (the last vector-memory operations issued,
-    // present whenever loads were issued after the previous barrier) may still
-    // be in flight. The state pass stores nothing and waits for everything.
+    // chunk ci's tiles are in LDS and every wavefront left chunk ci-1; the
+    // output stores of chunk ci-1 (at most two, issued after this wavefront's
+    // loads had all completed) may still be in flight. The state pass stores
+    // nothing and waits for everything.
     if (SP) {
       barrier_all();
       counters_drained();
@@ -543,8 +546,8 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
 #pragma unroll
     for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt_x[t], kx_l, S_acc[t]);
 
-    if (!SP) store_out(t0, n, own);
     if (has_next) gam = R.gates(s.lgb[g_rd][lane], lsum);
+    if (!SP) store_out(t0, n, own);
     g_rd = g_rd == 2 ? 0 : g_rd + 1;
     g_ld = g_ld == 2 ? 0 : g_ld + 1;
   }
