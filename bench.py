@@ -277,6 +277,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--chunk", type=int, default=64, choices=[64, 128])
+    ap.add_argument("--stream-reference", action="store_true",
+                    help="only time two plain streams over the decode state's size (1.342 GB "
+                         "fp32): a device copy and an in-place scale, as read+write GB/s")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes)")
@@ -289,6 +292,20 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.stream_reference:
+        from gated_linear_attention_amd import synth
+        D = synth.DECODE
+        n = D["N"] * D["H"] * D["dk"] * D["dv"]
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        res = {}
+        for name, fn in (("copy", lambda i: b.copy_(a)), ("inplace_scale", lambda i: a.mul_(0.999))):
+            warm_up(fn, 10, args.warm_seconds)
+            wall, kern_ms = time_launches(fn, 50, torch.cuda.current_stream())
+            res[name] = {"gbs": round(2 * n * 4 / (kern_ms * 1e-3) / 1e9, 1),
+                         "kernel_ms": round(kern_ms, 4)}
+        print(json.dumps({"stream_reference_bytes": 2 * n * 4, **res}), flush=True)
+        return
     if args.copy_calibration:
         n = 512 * 1024 * 1024 // 4
         a = torch.ones(n, device="cuda")
