@@ -28,12 +28,17 @@ All inputs are converted exactly to fp64 (bf16 and fp32 values embed in
 fp64 without rounding). Pins: tests/test_oracle_pins.py (brute-force masked
 sum, no-decay and fixed-decay closed forms, exact rationals, reset,
 continuation, linearity, chunked regrouping) and tests/test_oracle_mutants.py.
+
+The backward (recurrent_backward) is the reverse-mode adjoint of the same
+token-by-token recurrence, written out: it walks each sequence backwards
+carrying dL/dS_t. Its pins (tests/test_oracle_bwd_pins.py) are central finite
+differences and fp64 automatic differentiation of an independent forward.
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["recurrent_forward", "decode_step", "normwise_error"]
+__all__ = ["recurrent_forward", "recurrent_backward", "decode_step", "normwise_error"]
 
 
 def _seq_bounds(B: int, T: int, cu_seqlens):
@@ -81,6 +86,66 @@ def recurrent_forward(q, k, v, log_g, S0=None, cu_seqlens=None, heads=None):
             o[b, t] = np.einsum("hd,hde->he", qt, S)
         S_T[n] = S
     return o, S_T
+
+
+def recurrent_backward(q, k, v, log_g, dO, dS_T=None, S0=None, cu_seqlens=None, heads=None):
+    """Gradients of L = sum_t <dO_t, o_t> + sum_n <dS_T[n], S_T[n]> (the
+    backward of recurrent_forward for upstream gradients dO and dS_T), fp64.
+
+    dO: [B, T, H, dv]; dS_T: [N, H, dk, dv] or None (zeros). Other arguments
+    as recurrent_forward. Returns (dq [B,T,H',dk], dk [B,T,H',dk],
+    dv [B,T,H',dv], dlog_g [B,T,H'], dS0 [N,H',dk,dv]), all fp64.
+
+    Per sequence and head, walking t from the last token to the first with
+    A = dL/dS_t (starting from dS_T):
+        A      += q_t^T dO_t              (o_t = q_t S_t reads S_t)
+        dq_t    = dO_t S_t^T
+        dk_t    = A v_t^T,  dv_t = k_t A  (S_t gets k_t^T v_t)
+        dl_t    = g_t <A, S_{t-1}>        (S_t gets g_t S_{t-1}, g_t = exp(l_t))
+        A       = g_t A                   (now dL/dS_{t-1})
+    and dS0 = A after the first token. The forward states S_t of one head are
+    kept for the walk back.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    log_g = np.asarray(log_g)
+    dO = np.asarray(dO)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    hs = np.arange(H) if heads is None else np.asarray(heads, dtype=np.int64)
+    bounds = _seq_bounds(B, T, cu_seqlens)
+    dq = np.zeros((B, T, len(hs), dk), dtype=np.float64)
+    dkk = np.zeros((B, T, len(hs), dk), dtype=np.float64)
+    dvv = np.zeros((B, T, len(hs), dv), dtype=np.float64)
+    dl = np.zeros((B, T, len(hs)), dtype=np.float64)
+    dS0 = np.zeros((len(bounds), len(hs), dk, dv), dtype=np.float64)
+    for n, (b, start, end) in enumerate(bounds):
+        for i, h in enumerate(hs):
+            S = (np.zeros((dk, dv)) if S0 is None
+                 else np.asarray(S0)[n, h].astype(np.float64))
+            states = [S]  # states[j] = S after j tokens of this sequence
+            for t in range(start, end):
+                g = np.exp(np.float64(log_g[b, t, h]))
+                S = g * S + np.outer(k[b, t, h].astype(np.float64), v[b, t, h].astype(np.float64))
+                states.append(S)
+            A = (np.zeros((dk, dv)) if dS_T is None
+                 else np.asarray(dS_T)[n, h].astype(np.float64))
+            for t in range(end - 1, start - 1, -1):
+                j = t - start
+                qt = q[b, t, h].astype(np.float64)
+                kt = k[b, t, h].astype(np.float64)
+                vt = v[b, t, h].astype(np.float64)
+                dOt = dO[b, t, h].astype(np.float64)
+                g = np.exp(np.float64(log_g[b, t, h]))
+                A = A + np.outer(qt, dOt)
+                dq[b, t, i] = states[j + 1] @ dOt
+                dkk[b, t, i] = A @ vt
+                dvv[b, t, i] = kt @ A
+                dl[b, t, i] = g * np.sum(A * states[j])
+                A = g * A
+            dS0[n, i] = A
+    return dq, dkk, dvv, dl, dS0
 
 
 def decode_step(q, k, v, log_g, S):
