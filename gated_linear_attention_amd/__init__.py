@@ -5,6 +5,7 @@ kernels of libgla.so (see include/gla.h for the C ABI). PyTorch supplies
 device memory and the current HIP stream.
 
     o, S_T = fwd_chunked(q, k, v, g, S0=None, cu_seqlens=None, chunk_size=64)
+    dq, dk, dv, dg, dS0 = bwd_chunked(q, k, v, g, dO, S0=None, cu_seqlens=None, dS_T=None)
     o = decode_step(q, k, v, g, S)          # S updated in place
 
 Shapes follow the C ABI: q, k [B, T, H, dk]; v [B, T, H, dv]; g [B, T, H]
@@ -16,7 +17,8 @@ from __future__ import annotations
 from . import _lib
 from ._lib import GLAError, GLA_BF16, GLA_F32
 
-__all__ = ["fwd_chunked", "decode_step", "workspace_size", "GLAError", "library_path"]
+__all__ = ["fwd_chunked", "bwd_chunked", "decode_step", "workspace_size", "GLAError",
+           "library_path"]
 
 
 def library_path() -> str:
@@ -100,6 +102,53 @@ def fwd_chunked(q, k, v, g, S0=None, cu_seqlens=None, chunk_size: int = 64, out_
                              ws_bytes, stream)
     _lib.check(st, "gla_fwd_chunked")
     return o, S_T
+
+
+def bwd_chunked(q, k, v, g, dO, S0=None, cu_seqlens=None, dS_T=None, chunk_size: int = 64,
+                need_dS0: bool = True, workspace=None):
+    """Backward of fwd_chunked for upstream gradients dO (and dS_T of the final
+    state, None for zero). Returns fp32 (dq, dk, dv, dg, dS0); dS0 is None when
+    not requested."""
+    torch = _torch()
+    lib = _lib.load()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or g.dim() != 3 or dO.dim() != 4:
+        raise ValueError("expected q, k [B, T, H, dk], v, dO [B, T, H, dv] and g [B, T, H]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _require(q, "q", None, dev)
+    _require(k, "k", q.dtype, dev)
+    _require(v, "v", q.dtype, dev)
+    _require(dO, "dO", q.dtype, dev)
+    _require(g, "g", torch.float32, dev)
+    _require(S0, "S0", torch.float32, dev)
+    _require(dS_T, "dS_T", torch.float32, dev)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    if (tuple(k.shape) != (B, T, H, dk) or tuple(v.shape[:3]) != (B, T, H)
+            or tuple(g.shape) != (B, T, H) or tuple(dO.shape) != tuple(v.shape)):
+        raise ValueError("inconsistent q/k/v/g/dO shapes")
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    for name, x in (("S0", S0), ("dS_T", dS_T)):
+        if x is not None and tuple(x.shape) != (N, H, dk, dv):
+            raise ValueError(f"{name} must be [{N}, {H}, {dk}, {dv}]")
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((B, T, H, dk), **f32)
+    dkk = torch.empty((B, T, H, dk), **f32)
+    dvv = torch.empty((B, T, H, dv), **f32)
+    dg = torch.empty((B, T, H), **f32)
+    dS0 = torch.empty((N, H, dk, dv), **f32) if need_dS0 else None
+    in_code = _dtype_code(q.dtype)
+    ws_bytes = int(lib.gla_bwd_chunked_workspace_size(B, T, H, dk, dv, N, chunk_size,
+                                                      int(cu_seqlens is not None), in_code))
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.gla_bwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0), _ptr(cu_seqlens),
+                             _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg),
+                             _ptr(dS0), B, T, H, dk, dv, N, chunk_size, in_code,
+                             _ptr(workspace), ws_bytes, stream)
+    _lib.check(st, "gla_bwd_chunked")
+    return dq, dkk, dvv, dg, dS0
 
 
 def decode_step(q, k, v, g, S, out_dtype=None, o=None):

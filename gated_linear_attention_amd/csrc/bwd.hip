@@ -1,0 +1,212 @@
+// Device kernels of the chunked backward (gla_bwd_chunked).
+//
+// The backward of the recurrence S_t = g_t S_{t-1} + k_t^T v_t, o_t = q_t S_t
+// (Laplace 3B on AWS Trainium2, automationscribe.com/?p=7116, "GLA mixer";
+// training differentiates through the chunked state updates, "Challenge 1")
+// is computed from three runs of the chunked forward and the kernels below:
+//  * dq_t = dO_t S_t^T is the forward output for the transposed state
+//    S'_t = g_t S'_{t-1} + v_t^T k_t, i.e. the forward with (q, k, v) :=
+//    (dO, v, k) and initial state S0^T;
+//  * the adjoint A_u = dL/dS_u obeys A_u = g_{u+1} A_{u+1} + q_u^T dO_u from
+//    A_{end-1} = q^T dO + dS_T: a forward recurrence in reversed time whose
+//    gate at reversed position tau is l_{end-tau} (and 0 at tau = 0). With
+//    tokens reversed inside each sequence, dv_u = k_u A_u is the forward
+//    with (q, k, v) := (k, q, dO) from dS_T, and dk_u = v_u A_u^T the forward
+//    with (q, k, v) := (v, dO, q) from dS_T^T; the first of these ends in A_0,
+//    and dS0 = g_0 A_0;
+//  * with B_u the cumulative log-gate, dL/dB_u = q_u.dq_u - k_u.dk_u plus
+//    <dS_T, S_T> at a sequence's last token, and dl_t is the sum of dL/dB_u
+//    over u >= t in the same sequence.
+#include "gla_common.h"
+#include "gla_internal.h"
+
+namespace gla {
+
+namespace {
+
+// [start, end) of the sequence holding flattened token p.
+__device__ __forceinline__ void seq_of(int p, const int32_t *cu, int N, int T, int &s, int &e) {
+  if (!cu) {
+    s = (p / T) * T;
+    e = s + T;
+    return;
+  }
+  int lo = 0, hi = N;  // largest n with cu[n] <= p
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= p) lo = mid;
+    else hi = mid;
+  }
+  s = cu[lo];
+  e = cu[lo + 1];
+}
+
+// dst[p] = src[s + e - 1 - p] row by row (one token row = row_bytes, a
+// multiple of 16): tokens reversed inside every sequence. An involution.
+__global__ __launch_bounds__(256) void reverse_rows_kernel(const char *__restrict__ src,
+                                                           char *__restrict__ dst,
+                                                           const int32_t *__restrict__ cu, int N,
+                                                           int T, int n_tok, int row_bytes) {
+  const int p = blockIdx.x;
+  if (p >= n_tok) return;
+  int s, e;
+  seq_of(p, cu, N, T, s, e);
+  const int from = s + e - 1 - p;
+  const u32x4 *a = reinterpret_cast<const u32x4 *>(src + (size_t)from * row_bytes);
+  u32x4 *b = reinterpret_cast<u32x4 *>(dst + (size_t)p * row_bytes);
+  for (int i = threadIdx.x; i < row_bytes / 16; i += 256) b[i] = a[i];
+}
+
+// Gates of the reversed-time adjoint recurrence: at reversed position tau of
+// a sequence [s, e), l_hat = 0 for tau = 0 and l[e - tau] otherwise.
+__global__ __launch_bounds__(256) void reversed_gates_kernel(const float *__restrict__ lg,
+                                                             float *__restrict__ out,
+                                                             const int32_t *__restrict__ cu, int N,
+                                                             int T, int n_tok, int H) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)n_tok * H) return;
+  const int p = (int)(i / H), h = (int)(i % H);
+  int s, e;
+  seq_of(p, cu, N, T, s, e);
+  out[i] = p == s ? 0.f : lg[(size_t)(s + e - p) * H + h];
+}
+
+// out[m] = in[m]^T for m = 0 .. count-1 matrices of rows x cols (fp32).
+__global__ __launch_bounds__(256) void transpose_kernel(const float *__restrict__ in,
+                                                        float *__restrict__ out, int rows,
+                                                        int cols) {
+  __shared__ float tile[32][33];
+  const size_t m = blockIdx.z;
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;  // 32 x 8
+  const float *a = in + m * rows * cols;
+  float *b = out + m * rows * cols;
+  for (int r = ty; r < 32; r += 8)
+    if (r0 + r < rows && c0 + tx < cols) tile[r][tx] = a[(size_t)(r0 + r) * cols + c0 + tx];
+  __syncthreads();
+  for (int c = ty; c < 32; c += 8)
+    if (c0 + c < cols && r0 + tx < rows) b[(size_t)(c0 + c) * rows + r0 + tx] = tile[tx][c];
+}
+
+template <typename Tin>
+__device__ __forceinline__ float dot_row(const Tin *x, const float *y, int d) {
+  float acc = 0.f;
+  for (int i = 0; i < d; ++i) acc += load_as_f32(x, i) * y[i];
+  return acc;
+}
+
+// One workgroup per (sequence, head): dl (reverse cumulative sum of
+// q.dq - k.dk, plus <dS_T, S_T> at the last token) and dS0 = g_0 A_0.
+// ST_t and dST_t are S_T^T and dS_T^T ([dv][dk], either may be null for
+// dS_T = 0); A0 is the adjoint after the first token ([dk][dv]).
+template <typename Tin>
+__global__ __launch_bounds__(256) void dgate_kernel(
+    const Tin *__restrict__ q, const Tin *__restrict__ k, const float *__restrict__ dq,
+    const float *__restrict__ dk, const float *__restrict__ lg, const float *__restrict__ ST_t,
+    const float *__restrict__ dST_t, const float *__restrict__ A0, float *__restrict__ dl,
+    float *__restrict__ dS0, const int32_t *__restrict__ cu, int N, int T, int H, int DK, int DV) {
+  const int n = blockIdx.x / H, h = blockIdx.x % H;
+  const int tid = threadIdx.x;
+  const int s = cu ? cu[n] : n * T, e = cu ? cu[n + 1] : (n + 1) * T;
+  const int len = e - s;
+  const size_t mat = (size_t)DK * DV, base = ((size_t)n * H + h) * mat;
+  __shared__ float red[256];
+
+  // <dS_T, S_T>
+  float fro = 0.f;
+  if (dST_t)
+    for (size_t i = tid; i < mat; i += 256) fro += dST_t[base + i] * ST_t[base + i];
+  red[tid] = fro;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  fro = red[0];
+  __syncthreads();
+
+  // dS0 = g_0 A_0 (an empty sequence passes dS_T through: A_0 = dS_T)
+  if (dS0) {
+    const float g0 = len > 0 ? fast_exp2(lg[(size_t)s * H + h] * kLog2e) : 1.f;
+    for (size_t i = tid; i < mat; i += 256) dS0[base + i] = g0 * A0[base + i];
+  }
+  if (len <= 0) return;
+
+  // dL/dB_u over a contiguous block of tokens per thread, block totals
+  const int per = (len + 255) / 256;
+  const int t0 = s + tid * per, t1 = min(e, t0 + per);
+  float tot = 0.f;
+  for (int t = t0; t < t1; ++t) {
+    const size_t rq = ((size_t)t * H + h) * DK;
+    float db = dot_row(q + rq, dq + rq, DK) - dot_row(k + rq, dk + rq, DK);
+    if (t == e - 1) db += fro;
+    dl[(size_t)t * H + h] = db;
+    tot += db;
+  }
+  // suffix sums of the block totals (Hillis-Steele over 256 threads)
+  red[tid] = tot;
+  __syncthreads();
+  for (int w = 1; w < 256; w <<= 1) {
+    const float x = tid + w < 256 ? red[tid + w] : 0.f;
+    __syncthreads();
+    red[tid] += x;
+    __syncthreads();
+  }
+  float run = red[tid] - tot;  // sum over later blocks
+  for (int t = t1 - 1; t >= t0; --t) {
+    run += dl[(size_t)t * H + h];
+    dl[(size_t)t * H + h] = run;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_reverse_rows(const void *src, void *dst, const int32_t *cu, int N, int T,
+                               int n_tok, int row_bytes, hipStream_t stream) {
+  if (n_tok == 0) return hipSuccess;
+  hipLaunchKernelGGL(reverse_rows_kernel, dim3(n_tok), dim3(256), 0, stream,
+                     static_cast<const char *>(src), static_cast<char *>(dst), cu, N, T, n_tok,
+                     row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_reversed_gates(const float *lg, float *out, const int32_t *cu, int N, int T,
+                                 int n_tok, int H, hipStream_t stream) {
+  const long total = (long)n_tok * H;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(reversed_gates_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     stream, lg, out, cu, N, T, n_tok, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const float *in, float *out, int count, int rows, int cols,
+                            hipStream_t stream) {
+  const size_t mat = (size_t)rows * cols;
+  for (int m0 = 0; m0 < count; m0 += 65535) {  // grid z is at most 65535
+    const int n = count - m0 < 65535 ? count - m0 : 65535;
+    hipLaunchKernelGGL(transpose_kernel, dim3((cols + 31) / 32, (rows + 31) / 32, n), dim3(256),
+                       0, stream, in + m0 * mat, out + m0 * mat, rows, cols);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_dgate(const void *q, const void *k, const float *dq, const float *dk,
+                        const float *lg, const float *ST_t, const float *dST_t, const float *A0,
+                        float *dl, float *dS0, const int32_t *cu, int N, int T, int H, int DK,
+                        int DV, bool in_bf16, hipStream_t stream) {
+  if ((long)N * H == 0) return hipSuccess;
+  const dim3 grid((unsigned)(N * H)), block(256);
+  if (in_bf16)
+    hipLaunchKernelGGL(dgate_kernel<uint16_t>, grid, block, 0, stream,
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), dq, dk,
+                       lg, ST_t, dST_t, A0, dl, dS0, cu, N, T, H, DK, DV);
+  else
+    hipLaunchKernelGGL(dgate_kernel<float>, grid, block, 0, stream,
+                       static_cast<const float *>(q), static_cast<const float *>(k), dq, dk, lg,
+                       ST_t, dST_t, A0, dl, dS0, cu, N, T, H, DK, DV);
+  return hipGetLastError();
+}
+
+}  // namespace gla

@@ -117,62 +117,15 @@ bool valid_dtype(int t) { return t == GLA_F32 || t == GLA_BF16; }
 
 }  // namespace
 
-extern "C" {
+namespace gla {
 
-const char *gla_status_string(gla_status s) {
-  switch (s) {
-    case GLA_OK: return "GLA_OK";
-    case GLA_ERR_INVALID_ARGUMENT: return "GLA_ERR_INVALID_ARGUMENT";
-    case GLA_ERR_UNSUPPORTED: return "GLA_ERR_UNSUPPORTED";
-    case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE";
-    case GLA_ERR_HIP: return "GLA_ERR_HIP";
-  }
-  return "GLA_UNKNOWN_STATUS";
-}
-
-size_t gla_fwd_chunked_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
-                                      int chunk_size, int has_cu_seqlens, gla_dtype in_dtype) {
-  if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !supported_head_dim(dk) ||
-      !supported_head_dim(dv) || (chunk_size != 64 && chunk_size != 128) ||
-      !valid_dtype(in_dtype))
-    return 0;
-  PlanLayout lay;
-  if (!make_plan(B, T, H, dk, dv, num_seqs, chunk_size, has_cu_seqlens != 0, in_dtype, lay))
-    return 0;
-  return lay.total_bytes;
-}
-
-gla_status gla_fwd_chunked(const void *q, const void *k, const void *v, const float *g,
-                           const float *S0, const int32_t *cu_seqlens, void *o, float *S_T,
-                           int B, int T, int H, int dk, int dv, int num_seqs, int chunk_size,
-                           gla_dtype in_dtype, gla_dtype out_dtype, void *workspace,
-                           size_t workspace_bytes, void *stream_) {
-  hipStream_t stream = static_cast<hipStream_t>(stream_);
-  if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return GLA_ERR_INVALID_ARGUMENT;
-  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
+// The chunked forward after argument checks: plans (when the batch needs
+// splitting) and launches. Shared by gla_fwd_chunked and gla_bwd_chunked.
+gla_status fwd_core(const void *q, const void *k, const void *v, const float *g, const float *S0,
+                    const int32_t *cu_seqlens, void *o, float *S_T, int B, int T, int H, int dk,
+                    int dv, int N, int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
   const bool has_cu = cu_seqlens != nullptr;
-  if (has_cu ? (B != 1) : (num_seqs != B)) return GLA_ERR_INVALID_ARGUMENT;
-  if ((long)B * T > INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
-  if (!supported_head_dim(dk) || !supported_head_dim(dv)) return GLA_ERR_UNSUPPORTED;
-  if (chunk_size != 64 && chunk_size != 128) return GLA_ERR_UNSUPPORTED;
-  const int N = num_seqs;
-  if (H == 0 || N == 0) return GLA_OK;
-  const size_t ntok = (size_t)B * T * H;
-  const size_t es = dtype_size(in_dtype);
-  const size_t bytes_qk = ntok * dk * es, bytes_v = ntok * dv * es, bytes_g = ntok * 4;
-  const size_t bytes_o = ntok * dv * dtype_size(out_dtype);
-  const size_t bytes_S = (size_t)N * H * dk * dv * 4;
-  if (ntok > 0 && (!q || !k || !v || !g || !o)) return GLA_ERR_INVALID_ARGUMENT;
-  if (overlaps(o, bytes_o, q, bytes_qk) || overlaps(o, bytes_o, k, bytes_qk) ||
-      overlaps(o, bytes_o, v, bytes_v) || overlaps(o, bytes_o, g, bytes_g) ||
-      overlaps(o, bytes_o, S0, S0 ? bytes_S : 0) || overlaps(o, bytes_o, S_T, S_T ? bytes_S : 0))
-    return GLA_ERR_INVALID_ARGUMENT;
-  if (S_T && S_T != S0 &&
-      (overlaps(S_T, bytes_S, S0, S0 ? bytes_S : 0) || overlaps(S_T, bytes_S, q, bytes_qk) ||
-       overlaps(S_T, bytes_S, k, bytes_qk) || overlaps(S_T, bytes_S, v, bytes_v) ||
-       overlaps(S_T, bytes_S, g, bytes_g)))
-    return GLA_ERR_INVALID_ARGUMENT;
-
   FwdDims d;
   d.B = B;
   d.T = T;
@@ -217,6 +170,214 @@ gla_status gla_fwd_chunked(const void *q, const void *k, const void *v, const fl
   }
   err = run_chunks(items, &hdr->n_items, lay.max_items, slots, slot_gamma, false);
   return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
+// Workspace of fwd_core for these sizes (0 when it runs without a plan).
+size_t fwd_workspace(int B, int T, int H, int dk, int dv, int N, int chunk_size, bool has_cu,
+                     gla_dtype in_dtype) {
+  PlanLayout lay;
+  if (!make_plan(B, T, H, dk, dv, N, chunk_size, has_cu, in_dtype, lay)) return 0;
+  return lay.total_bytes;
+}
+
+}  // namespace gla
+
+extern "C" {
+
+const char *gla_status_string(gla_status s) {
+  switch (s) {
+    case GLA_OK: return "GLA_OK";
+    case GLA_ERR_INVALID_ARGUMENT: return "GLA_ERR_INVALID_ARGUMENT";
+    case GLA_ERR_UNSUPPORTED: return "GLA_ERR_UNSUPPORTED";
+    case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE";
+    case GLA_ERR_HIP: return "GLA_ERR_HIP";
+  }
+  return "GLA_UNKNOWN_STATUS";
+}
+
+size_t gla_fwd_chunked_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
+                                      int chunk_size, int has_cu_seqlens, gla_dtype in_dtype) {
+  if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !supported_head_dim(dk) ||
+      !supported_head_dim(dv) || (chunk_size != 64 && chunk_size != 128) ||
+      !valid_dtype(in_dtype))
+    return 0;
+  return fwd_workspace(B, T, H, dk, dv, num_seqs, chunk_size, has_cu_seqlens != 0, in_dtype);
+}
+
+gla_status gla_fwd_chunked(const void *q, const void *k, const void *v, const float *g,
+                           const float *S0, const int32_t *cu_seqlens, void *o, float *S_T,
+                           int B, int T, int H, int dk, int dv, int num_seqs, int chunk_size,
+                           gla_dtype in_dtype, gla_dtype out_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return GLA_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
+  const bool has_cu = cu_seqlens != nullptr;
+  if (has_cu ? (B != 1) : (num_seqs != B)) return GLA_ERR_INVALID_ARGUMENT;
+  if ((long)B * T > INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
+  if (!supported_head_dim(dk) || !supported_head_dim(dv)) return GLA_ERR_UNSUPPORTED;
+  if (chunk_size != 64 && chunk_size != 128) return GLA_ERR_UNSUPPORTED;
+  const int N = num_seqs;
+  if (H == 0 || N == 0) return GLA_OK;
+  const size_t ntok = (size_t)B * T * H;
+  const size_t es = dtype_size(in_dtype);
+  const size_t bytes_qk = ntok * dk * es, bytes_v = ntok * dv * es, bytes_g = ntok * 4;
+  const size_t bytes_o = ntok * dv * dtype_size(out_dtype);
+  const size_t bytes_S = (size_t)N * H * dk * dv * 4;
+  if (ntok > 0 && (!q || !k || !v || !g || !o)) return GLA_ERR_INVALID_ARGUMENT;
+  if (overlaps(o, bytes_o, q, bytes_qk) || overlaps(o, bytes_o, k, bytes_qk) ||
+      overlaps(o, bytes_o, v, bytes_v) || overlaps(o, bytes_o, g, bytes_g) ||
+      overlaps(o, bytes_o, S0, S0 ? bytes_S : 0) || overlaps(o, bytes_o, S_T, S_T ? bytes_S : 0))
+    return GLA_ERR_INVALID_ARGUMENT;
+  if (S_T && S_T != S0 &&
+      (overlaps(S_T, bytes_S, S0, S0 ? bytes_S : 0) || overlaps(S_T, bytes_S, q, bytes_qk) ||
+       overlaps(S_T, bytes_S, k, bytes_qk) || overlaps(S_T, bytes_S, v, bytes_v) ||
+       overlaps(S_T, bytes_S, g, bytes_g)))
+    return GLA_ERR_INVALID_ARGUMENT;
+
+  return fwd_core(q, k, v, g, S0, cu_seqlens, o, S_T, B, T, H, dk, dv, N, chunk_size, in_dtype,
+                  out_dtype, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace layout of the backward (all offsets 256-byte aligned).
+struct BwdLayout {
+  size_t rq, rk, rv, rdo, lhat, s0t, dstt, stt, a0, rdv, rdk, fws, total, fws_bytes;
+};
+
+BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int N, int C, bool has_cu,
+                     gla_dtype in_dtype) {
+  BwdLayout L;
+  const size_t ntok = (size_t)B * T * H, es = dtype_size(in_dtype);
+  const size_t mat = (size_t)N * H * dk * dv * 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L.rq = take(ntok * dk * es);
+  L.rk = take(ntok * dk * es);
+  L.rv = take(ntok * dv * es);
+  L.rdo = take(ntok * dv * es);
+  L.lhat = take(ntok * 4);
+  L.s0t = take(mat);
+  L.dstt = take(mat);
+  L.stt = take(mat);
+  L.a0 = take(mat);
+  L.rdv = take(ntok * dv * 4);
+  L.rdk = take(ntok * dk * 4);
+  const size_t f1 = fwd_workspace(B, T, H, dv, dk, N, C, has_cu, in_dtype);
+  const size_t f2 = fwd_workspace(B, T, H, dk, dv, N, C, has_cu, in_dtype);
+  L.fws_bytes = f1 > f2 ? f1 : f2;
+  L.fws = take(L.fws_bytes);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gla_bwd_chunked_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
+                                      int chunk_size, int has_cu_seqlens, gla_dtype in_dtype) {
+  if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !supported_head_dim(dk) ||
+      !supported_head_dim(dv) || (chunk_size != 64 && chunk_size != 128) ||
+      !valid_dtype(in_dtype))
+    return 0;
+  return bwd_layout(B, T, H, dk, dv, num_seqs, chunk_size, has_cu_seqlens != 0, in_dtype).total;
+}
+
+gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const float *g,
+                           const float *S0, const int32_t *cu_seqlens, const void *dO,
+                           const float *dS_T, float *dq, float *dk, float *dv, float *dg,
+                           float *dS0, int B, int T, int H, int dk_dim, int dv_dim, int num_seqs,
+                           int chunk_size, gla_dtype in_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const int DK = dk_dim, DV = dv_dim;
+  if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return GLA_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(in_dtype)) return GLA_ERR_INVALID_ARGUMENT;
+  const bool has_cu = cu_seqlens != nullptr;
+  if (has_cu ? (B != 1) : (num_seqs != B)) return GLA_ERR_INVALID_ARGUMENT;
+  if ((long)B * T > INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
+  if (!supported_head_dim(DK) || !supported_head_dim(DV)) return GLA_ERR_UNSUPPORTED;
+  if (chunk_size != 64 && chunk_size != 128) return GLA_ERR_UNSUPPORTED;
+  const int N = num_seqs;
+  if (H == 0 || N == 0) return GLA_OK;
+  const size_t ntok = (size_t)B * T * H;
+  const size_t es = dtype_size(in_dtype);
+  const size_t b_qk = ntok * DK * es, b_v = ntok * DV * es, b_g = ntok * 4;
+  const size_t b_dqk = ntok * DK * 4, b_dv = ntok * DV * 4;
+  const size_t b_S = (size_t)N * H * DK * DV * 4;
+  if (ntok > 0 && (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg))
+    return GLA_ERR_INVALID_ARGUMENT;
+  struct Buf {
+    const void *p;
+    size_t n;
+  };
+  const Buf ins[] = {{q, b_qk}, {k, b_qk}, {v, b_v}, {g, b_g}, {dO, b_v},
+                     {S0, S0 ? b_S : 0}, {dS_T, dS_T ? b_S : 0}};
+  const Buf outs[] = {{dq, b_dqk}, {dk, b_dqk}, {dv, b_dv}, {dg, b_g}, {dS0, dS0 ? b_S : 0}};
+  for (const Buf &o : outs) {
+    for (const Buf &i : ins)
+      if (overlaps(o.p, o.n, i.p, i.n)) return GLA_ERR_INVALID_ARGUMENT;
+    for (const Buf &o2 : outs)
+      if (&o2 != &o && overlaps(o.p, o.n, o2.p, o2.n)) return GLA_ERR_INVALID_ARGUMENT;
+  }
+  const BwdLayout L = bwd_layout(B, T, H, DK, DV, N, chunk_size, has_cu, in_dtype);
+  if (!workspace || workspace_bytes < L.total) return GLA_ERR_WORKSPACE;
+
+  char *ws = static_cast<char *>(workspace);
+  void *rq = ws + L.rq, *rk = ws + L.rk, *rv = ws + L.rv, *rdo = ws + L.rdo;
+  float *lhat = reinterpret_cast<float *>(ws + L.lhat);
+  float *s0t = S0 ? reinterpret_cast<float *>(ws + L.s0t) : nullptr;
+  float *dstt = dS_T ? reinterpret_cast<float *>(ws + L.dstt) : nullptr;
+  float *stt = reinterpret_cast<float *>(ws + L.stt);
+  float *a0 = reinterpret_cast<float *>(ws + L.a0);
+  float *rdv = reinterpret_cast<float *>(ws + L.rdv);
+  float *rdk = reinterpret_cast<float *>(ws + L.rdk);
+  void *fws = L.fws_bytes ? ws + L.fws : nullptr;
+  const int ntk = B * T;
+  const int row_qk = H * DK * (int)es, row_v = H * DV * (int)es;
+  hipError_t err = hipSuccess;
+  auto hip_ok = [&](hipError_t e) {
+    err = e;
+    return e == hipSuccess;
+  };
+  // inputs of the reversed-time passes; transposed initial states
+  if (!hip_ok(launch_reverse_rows(q, rq, cu_seqlens, N, T, ntk, row_qk, stream)) ||
+      !hip_ok(launch_reverse_rows(k, rk, cu_seqlens, N, T, ntk, row_qk, stream)) ||
+      !hip_ok(launch_reverse_rows(v, rv, cu_seqlens, N, T, ntk, row_v, stream)) ||
+      !hip_ok(launch_reverse_rows(dO, rdo, cu_seqlens, N, T, ntk, row_v, stream)) ||
+      !hip_ok(launch_reversed_gates(g, lhat, cu_seqlens, N, T, ntk, H, stream)) ||
+      (S0 && !hip_ok(launch_transpose(S0, s0t, N * H, DK, DV, stream))) ||
+      (dS_T && !hip_ok(launch_transpose(dS_T, dstt, N * H, DK, DV, stream))))
+    return GLA_ERR_HIP;
+  gla_status st;
+  // dq: forward with (q, k, v) = (dO, v, k) on the transposed state; its final
+  // state is S_T^T
+  st = fwd_core(dO, v, k, g, s0t, cu_seqlens, dq, stt, B, T, H, DV, DK, N, chunk_size, in_dtype,
+                GLA_F32, fws, L.fws_bytes, stream);
+  if (st != GLA_OK) return st;
+  // dv (reversed): (q, k, v) = (k, q, dO) reversed, from dS_T; ends in A_0
+  st = fwd_core(rk, rq, rdo, lhat, dS_T, cu_seqlens, rdv, a0, B, T, H, DK, DV, N, chunk_size,
+                in_dtype, GLA_F32, fws, L.fws_bytes, stream);
+  if (st != GLA_OK) return st;
+  // dk (reversed): (q, k, v) = (v, dO, q) reversed, from dS_T^T
+  st = fwd_core(rv, rdo, rq, lhat, dstt, cu_seqlens, rdk, nullptr, B, T, H, DV, DK, N, chunk_size,
+                in_dtype, GLA_F32, fws, L.fws_bytes, stream);
+  if (st != GLA_OK) return st;
+  if (!hip_ok(launch_reverse_rows(rdv, dv, cu_seqlens, N, T, ntk, H * DV * 4, stream)) ||
+      !hip_ok(launch_reverse_rows(rdk, dk, cu_seqlens, N, T, ntk, H * DK * 4, stream)) ||
+      !hip_ok(launch_dgate(q, k, dq, dk, g, stt, dstt, a0, dg, dS0, cu_seqlens, N, T, H, DK, DV,
+                           in_dtype == GLA_BF16, stream)))
+    return GLA_ERR_HIP;
+  (void)err;
+  return GLA_OK;
 }
 
 gla_status gla_decode_step(const void *q, const void *k, const void *v, const float *g,

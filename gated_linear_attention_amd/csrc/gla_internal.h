@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gla.h"
+
 namespace gla {
 
 // One unit of chunked-forward work for one (head, dv-slice): a run of tokens
@@ -86,5 +88,24 @@ hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_
                              const FwdDims &d, const WorkItem *items, const int *n_items,
                              int grid_items, float *slots, float *slot_gamma, bool state_pass,
                              hipStream_t stream);
+
+// The chunked forward after argument checks (gla_api.hip), and its workspace.
+gla_status fwd_core(const void *q, const void *k, const void *v, const float *g, const float *S0,
+                    const int32_t *cu_seqlens, void *o, float *S_T, int B, int T, int H, int dk,
+                    int dv, int N, int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+size_t fwd_workspace(int B, int T, int H, int dk, int dv, int N, int chunk_size, bool has_cu,
+                     gla_dtype in_dtype);
+// Backward helpers (bwd.hip).
+hipError_t launch_reverse_rows(const void *src, void *dst, const int32_t *cu, int N, int T,
+                               int n_tok, int row_bytes, hipStream_t stream);
+hipError_t launch_reversed_gates(const float *lg, float *out, const int32_t *cu, int N, int T,
+                                 int n_tok, int H, hipStream_t stream);
+hipError_t launch_transpose(const float *in, float *out, int count, int rows, int cols,
+                            hipStream_t stream);
+hipError_t launch_dgate(const void *q, const void *k, const float *dq, const float *dk,
+                        const float *lg, const float *ST_t, const float *dST_t, const float *A0,
+                        float *dl, float *dS0, const int32_t *cu, int N, int T, int H, int DK,
+                        int DV, bool in_bf16, hipStream_t stream);
 
 }  // namespace gla

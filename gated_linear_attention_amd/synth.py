@@ -152,6 +152,17 @@ def make_forward_inputs(w: Workload, *, seed: int | None = None, B: int | None =
     return q, k, v, log_g, S0, cu
 
 
+def make_backward_grads(w: Workload, B: int, T: int, H: int, N: int, *, seed: int,
+                        final_state: bool = True, s_std: float = 0.02):
+    """Upstream gradients for a backward run: dO [B, T, H, dv] ~ N(0, 1) in the
+    workload's dtype (bf16-exact values when bf16), and dS_T [N, H, dk, dv]
+    ~ N(0, s_std^2) fp32 (None when final_state is False)."""
+    rng = np.random.default_rng(seed)
+    dO = _store(_normal(rng, (B, T, H, w.dv)), w.dtype)
+    dS_T = _normal(rng, (N, H, w.dk, w.dv), s_std) if final_state else None
+    return dO, dS_T
+
+
 def make_decode_state(N: int, H: int, dk: int, dv: int, *, seed: int, std: float = 0.02):
     """Initial fp32 decode state S[N, H, dk, dv] ~ N(0, std^2)."""
     rng = np.random.default_rng(seed)

@@ -100,6 +100,39 @@ gla_status gla_fwd_chunked(const void *q, const void *k, const void *v, const fl
                            size_t workspace_bytes, void *stream);
 
 /*
+ * Backward of gla_fwd_chunked (training; Laplace 3B on AWS Trainium2,
+ * "Challenge 1": the training step differentiates through the chunk-by-chunk
+ * state updates). For upstream gradients dO of o and dS_T of S_T it returns
+ * the gradients of L = sum <dO, o> + sum <dS_T, S_T>:
+ *
+ *   dq, dk [B, T, H, dk] fp32;  dv [B, T, H, dv] fp32
+ *   dg     [B, T, H]     fp32   gradient with respect to the log-gates l_t
+ *   dS0    [N, H, dk, dv] fp32  gradient with respect to S0, or NULL to skip
+ *
+ * Inputs q, k, v, g, S0, cu_seqlens, B, T, H, dk, dv, num_seqs, chunk_size
+ * and in_dtype exactly as for the forward (the forward's results are not
+ * needed; the states are recomputed). dO [B, T, H, dv] is in_dtype; dS_T
+ * [N, H, dk, dv] fp32, or NULL for zero. Method: dq is a forward run on the
+ * transposed state; dk and dv are forward runs over each sequence reversed
+ * in time (the adjoint dL/dS_t obeys the same recurrence backwards, with the
+ * gates shifted by one token); dg follows from dL/dB_t = q_t.dq_t - k_t.dk_t
+ * (B the cumulative log-gate, plus <dS_T, S_T> at a sequence's last token)
+ * summed over later tokens of the sequence. Outputs must not overlap the
+ * inputs or each other. The workspace (gla_bwd_chunked_workspace_size bytes,
+ * never 0 for a non-empty batch) holds the reversed inputs and intermediate
+ * results; its contents on entry do not matter. Errors as gla_fwd_chunked.
+ */
+size_t gla_bwd_chunked_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
+                                      int chunk_size, int has_cu_seqlens, gla_dtype in_dtype);
+
+gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const float *g,
+                           const float *S0, const int32_t *cu_seqlens, const void *dO,
+                           const float *dS_T, float *dq, float *dk, float *dv, float *dg,
+                           float *dS0, int B, int T, int H, int dk_dim, int dv_dim, int num_seqs,
+                           int chunk_size, gla_dtype in_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent decode step for N independent sequences (Laplace 3B on AWS
  * Trainium2, "GLA mixer" for the update and readout; "Inference optimization"
  * for serving with one fixed-size state per sequence):

@@ -18,7 +18,8 @@ def header_functions():
 
 
 def test_header_declares_the_boundary():
-    assert header_functions() == ["gla_decode_step", "gla_fwd_chunked",
+    assert header_functions() == ["gla_bwd_chunked", "gla_bwd_chunked_workspace_size",
+                                  "gla_decode_step", "gla_fwd_chunked",
                                   "gla_fwd_chunked_workspace_size", "gla_status_string"]
 
 
@@ -95,3 +96,37 @@ def test_decode_rejects_bad_arguments_before_launch():
     bad[5] = base[4] + 8  # o inside S
     assert call(bad) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call(base, N=0) == _lib.GLA_OK
+
+
+def _bwd(**kw):
+    a = dict(q=None, k=None, v=None, g=None, S0=None, cu=None, dO=None, dST=None, dq=None,
+             dk=None, dv=None, dg=None, dS0=None, B=1, T=64, H=1, dkd=64, dvd=64, N=1, C=64,
+             ind=_lib.GLA_BF16, ws=None, wsb=0)
+    a.update(kw)
+    return _lib.load().gla_bwd_chunked(a["q"], a["k"], a["v"], a["g"], a["S0"], a["cu"], a["dO"],
+                                       a["dST"], a["dq"], a["dk"], a["dv"], a["dg"], a["dS0"],
+                                       a["B"], a["T"], a["H"], a["dkd"], a["dvd"], a["N"], a["C"],
+                                       a["ind"], a["ws"], a["wsb"], None)
+
+
+def test_bwd_rejects_bad_arguments_before_launch():
+    G = 1 << 30
+    P = dict(q=FAKE, k=FAKE + G, v=FAKE + 2 * G, g=FAKE + 3 * G, dO=FAKE + 4 * G,
+             dq=FAKE + 5 * G, dk=FAKE + 6 * G, dv=FAKE + 7 * G, dg=FAKE + 8 * G)
+    lib = _lib.load()
+    n = lib.gla_bwd_chunked_workspace_size(1, 64, 1, 64, 64, 1, 64, 0, _lib.GLA_BF16)
+    assert n > 0  # the reversed inputs live in the workspace
+    W = dict(ws=FAKE + 9 * G, wsb=n)
+    assert _bwd(B=-1, **P, **W) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert _bwd(ind=5, **P, **W) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert _bwd(N=2, **P, **W) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert _bwd(dkd=96, **P, **W) == _lib.GLA_ERR_UNSUPPORTED
+    assert _bwd(C=256, **P, **W) == _lib.GLA_ERR_UNSUPPORTED
+    assert _bwd(**{**P, "dO": None}, **W) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert _bwd(**{**P, "dg": None}, **W) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert _bwd(**{**P, "dq": P["q"] + 64}, **W) == _lib.GLA_ERR_INVALID_ARGUMENT  # output on input
+    assert _bwd(**{**P, "dk": P["dq"] + 64}, **W) == _lib.GLA_ERR_INVALID_ARGUMENT  # outputs overlap
+    assert _bwd(**P) == _lib.GLA_ERR_WORKSPACE
+    assert _bwd(**P, ws=FAKE + 9 * G, wsb=n - 1) == _lib.GLA_ERR_WORKSPACE
+    assert _bwd(H=0, **P) == _lib.GLA_OK
+    assert lib.gla_bwd_chunked_workspace_size(1, 64, 1, 96, 64, 1, 64, 0, _lib.GLA_BF16) == 0
