@@ -189,6 +189,55 @@ def bench_forward(args):
     return res, host_set0
 
 
+def bench_backward(args):
+    """The chunked backward on the training shape (dS_T = 0, S0 = 0)."""
+    import torch
+
+    import gated_linear_attention_amd as gla
+    from gated_linear_attention_amd import synth
+
+    w = synth.WORKLOADS["train_2k"]
+    C = args.chunk
+    dev = torch.device("cuda:0")
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    q, k, v, lg, S0, cu = synth.make_forward_inputs(w, seed=w.seed)
+    dO, _ = synth.make_backward_grads(w, B, T, H, B, seed=w.seed + 7, final_state=False)
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+    tq, tk, tv, tdo = bf(q), bf(k), bf(v), bf(dO)
+    tlg = torch.from_numpy(lg).to(dev)
+    ws = torch.empty(gla._lib.load().gla_bwd_chunked_workspace_size(B, T, H, dk, dv, B, C, 0,
+                                                                      gla.GLA_BF16),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        gla.bwd_chunked(tq, tk, tv, tlg, tdo, chunk_size=C, need_dS0=False, workspace=ws)
+
+    warm_up(step, 3, min(args.warm_seconds, 0.5))
+    steps = max(5, args.steps // 5)
+    wall, kern_ms = time_launches(step, steps, stream)
+    tok_heads = B * T * H
+    # read q, k, v, dO (bf16) and the gates once, write dq, dk, dv (fp32) and dg once
+    alg_bytes = tok_heads * (2 * dk + 2 * dk + 2 * dv + 2 * dv + 4 + 4 * dk + 4 * dk + 4 * dv + 4)
+    gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
+    return {
+        "metric": "chunked backward tokens/s",
+        "value": round(B * T / (wall / steps), 1),
+        "unit": "tokens/s",
+        "ms_per_step": round(1e3 * wall / steps, 4),
+        "kernel_ms": round(kern_ms, 4),
+        "steps": steps,
+        "config": {"workload": "train_2k chunked backward", "B": B, "T": T, "H": H, "dk": dk,
+                   "dv": dv, "chunk": C, "in_dtype": "bf16", "grad_dtype": "f32",
+                   "S0": "zeros", "dS_T": "zeros"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": alg_bytes,
+                     "note": "whole gla_bwd_chunked call: three chunked-forward runs plus "
+                             "reversal, transpose and gate-gradient kernels"},
+    }
+
+
 def bench_decode(args):
     import numpy as np
     import torch
@@ -282,6 +331,7 @@ def main():
                     help="minimum wall time of the untimed warm-up, for the clocks to settle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--chunk", type=int, default=64, choices=[64, 128])
     ap.add_argument("--stream-reference", action="store_true",
                     help="only time two plain streams over the decode state's size (1.342 GB "
@@ -325,6 +375,11 @@ def main():
     log("forward: building inputs")
     fwd, host_set = bench_forward(args)
     log(f"forward: {fwd['value']:.4g} tokens/s, kernel {fwd['kernel_ms']:.4f} ms")
+    bwd = None
+    if not args.no_backward:
+        log("backward: building inputs")
+        bwd = bench_backward(args)
+        log(f"backward: {bwd['value']:.4g} tokens/s, call {bwd['kernel_ms']:.4f} ms")
     dec = None
     if not args.no_decode:
         log("decode: building inputs")
@@ -354,6 +409,7 @@ def main():
         "roofline": fwd["roofline"],
         "mfma": fwd["mfma"],
         "other_chunk": fwd["other_chunk"],
+        "backward": bwd,
         "decode": dec,
         "cpu_baseline": cpu,
     }

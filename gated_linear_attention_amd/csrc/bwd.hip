@@ -88,27 +88,43 @@ __global__ __launch_bounds__(256) void transpose_kernel(const float *__restrict_
     if (c0 + c < cols && r0 + tx < rows) b[(size_t)(c0 + c) * rows + r0 + tx] = tile[tx][c];
 }
 
+// dB[p, h] = q.dq - k.dk for every token row (32 lanes per row, 4 elements
+// per lane per step, 8 rows per workgroup).
 template <typename Tin>
-__device__ __forceinline__ float dot_row(const Tin *x, const float *y, int d) {
+__global__ __launch_bounds__(256) void gate_dot_kernel(const Tin *__restrict__ q,
+                                                       const Tin *__restrict__ k,
+                                                       const float *__restrict__ dq,
+                                                       const float *__restrict__ dk,
+                                                       float *__restrict__ dB, long rows, int DK) {
+  const long row = (long)blockIdx.x * 8 + threadIdx.x / 32;
+  const int l = threadIdx.x % 32;
   float acc = 0.f;
-  for (int i = 0; i < d; ++i) acc += load_as_f32(x, i) * y[i];
-  return acc;
+  if (row < rows) {
+    const size_t base = (size_t)row * DK;
+    for (int i = 4 * l; i < DK; i += 128) {
+      const f32x4 a = load4_as_f32(q + base + i), b = *reinterpret_cast<const f32x4 *>(dq + base + i);
+      const f32x4 c = load4_as_f32(k + base + i), d = *reinterpret_cast<const f32x4 *>(dk + base + i);
+      acc += (a[0] * b[0] + a[1] * b[1]) + (a[2] * b[2] + a[3] * b[3]) -
+             ((c[0] * d[0] + c[1] * d[1]) + (c[2] * d[2] + c[3] * d[3]));
+    }
+  }
+#pragma unroll
+  for (int w = 16; w > 0; w >>= 1) acc += __shfl_xor(acc, w, 32);
+  if (row < rows && l == 0) dB[row] = acc;
 }
 
-// One workgroup per (sequence, head): dl (reverse cumulative sum of
-// q.dq - k.dk, plus <dS_T, S_T> at the last token) and dS0 = g_0 A_0.
-// ST_t and dST_t are S_T^T and dS_T^T ([dv][dk], either may be null for
-// dS_T = 0); A0 is the adjoint after the first token ([dk][dv]).
-template <typename Tin>
-__global__ __launch_bounds__(256) void dgate_kernel(
-    const Tin *__restrict__ q, const Tin *__restrict__ k, const float *__restrict__ dq,
-    const float *__restrict__ dk, const float *__restrict__ lg, const float *__restrict__ ST_t,
-    const float *__restrict__ dST_t, const float *__restrict__ A0, float *__restrict__ dl,
-    float *__restrict__ dS0, const int32_t *__restrict__ cu, int N, int T, int H, int DK, int DV) {
+// One workgroup per (sequence, head): dl = reverse cumulative sum of dB over
+// the sequence (plus <dS_T, S_T> at its last token), in tiles of 2048 tokens
+// from the end; and dS0 = g_0 A_0. ST_t and dST_t are S_T^T and dS_T^T
+// ([dv][dk]; dST_t null for dS_T = 0); A0 is the adjoint after the first
+// token ([dk][dv]). dB and dl may be the same array.
+__global__ __launch_bounds__(256) void gate_scan_kernel(
+    const float *dB, const float *__restrict__ lg, const float *__restrict__ ST_t,
+    const float *__restrict__ dST_t, const float *__restrict__ A0, float *dl,
+    float *__restrict__ dS0, const int32_t *__restrict__ cu, int T, int H, int DK, int DV) {
   const int n = blockIdx.x / H, h = blockIdx.x % H;
   const int tid = threadIdx.x;
   const int s = cu ? cu[n] : n * T, e = cu ? cu[n + 1] : (n + 1) * T;
-  const int len = e - s;
   const size_t mat = (size_t)DK * DV, base = ((size_t)n * H + h) * mat;
   __shared__ float red[256];
 
@@ -127,35 +143,41 @@ __global__ __launch_bounds__(256) void dgate_kernel(
 
   // dS0 = g_0 A_0 (an empty sequence passes dS_T through: A_0 = dS_T)
   if (dS0) {
-    const float g0 = len > 0 ? fast_exp2(lg[(size_t)s * H + h] * kLog2e) : 1.f;
+    const float g0 = e > s ? fast_exp2(lg[(size_t)s * H + h] * kLog2e) : 1.f;
     for (size_t i = tid; i < mat; i += 256) dS0[base + i] = g0 * A0[base + i];
   }
-  if (len <= 0) return;
 
-  // dL/dB_u over a contiguous block of tokens per thread, block totals
-  const int per = (len + 255) / 256;
-  const int t0 = s + tid * per, t1 = min(e, t0 + per);
-  float tot = 0.f;
-  for (int t = t0; t < t1; ++t) {
-    const size_t rq = ((size_t)t * H + h) * DK;
-    float db = dot_row(q + rq, dq + rq, DK) - dot_row(k + rq, dk + rq, DK);
-    if (t == e - 1) db += fro;
-    dl[(size_t)t * H + h] = db;
-    tot += db;
-  }
-  // suffix sums of the block totals (Hillis-Steele over 256 threads)
-  red[tid] = tot;
-  __syncthreads();
-  for (int w = 1; w < 256; w <<= 1) {
-    const float x = tid + w < 256 ? red[tid + w] : 0.f;
+  // tiles of 8 tokens per thread, last tile first; carry = sum over later tiles
+  float carry = fro;
+  for (int hi = e; hi > s; hi -= 2048) {
+    const int lo = hi - 2048 > s ? hi - 2048 : s;
+    const int t0 = lo + 8 * tid;
+    float x[8], tot = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = t0 + j;
+      x[j] = t < hi ? dB[(size_t)t * H + h] : 0.f;
+      tot += x[j];
+    }
+    // inclusive suffix sums of the per-thread totals
+    red[tid] = tot;
     __syncthreads();
-    red[tid] += x;
+    for (int w = 1; w < 256; w <<= 1) {
+      const float y = tid + w < 256 ? red[tid + w] : 0.f;
+      __syncthreads();
+      red[tid] += y;
+      __syncthreads();
+    }
+    float run = carry + red[tid] - tot;
+    const float tile_total = red[0];
     __syncthreads();
-  }
-  float run = red[tid] - tot;  // sum over later blocks
-  for (int t = t1 - 1; t >= t0; --t) {
-    run += dl[(size_t)t * H + h];
-    dl[(size_t)t * H + h] = run;
+#pragma unroll
+    for (int j = 7; j >= 0; --j) {
+      const int t = t0 + j;
+      run += x[j];
+      if (t < hi) dl[(size_t)t * H + h] = run;
+    }
+    carry += tile_total;
   }
 }
 
@@ -196,16 +218,23 @@ hipError_t launch_dgate(const void *q, const void *k, const float *dq, const flo
                         const float *lg, const float *ST_t, const float *dST_t, const float *A0,
                         float *dl, float *dS0, const int32_t *cu, int N, int T, int H, int DK,
                         int DV, bool in_bf16, hipStream_t stream) {
+  const long rows = (long)(cu ? T : (long)N * T) * H;  // token rows of the batch
+  if (rows > 0) {
+    const dim3 grid((unsigned)((rows + 7) / 8)), block(256);
+    if (in_bf16)
+      hipLaunchKernelGGL(gate_dot_kernel<uint16_t>, grid, block, 0, stream,
+                         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), dq,
+                         dk, dl, rows, DK);
+    else
+      hipLaunchKernelGGL(gate_dot_kernel<float>, grid, block, 0, stream,
+                         static_cast<const float *>(q), static_cast<const float *>(k), dq, dk, dl,
+                         rows, DK);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if ((long)N * H == 0) return hipSuccess;
-  const dim3 grid((unsigned)(N * H)), block(256);
-  if (in_bf16)
-    hipLaunchKernelGGL(dgate_kernel<uint16_t>, grid, block, 0, stream,
-                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), dq, dk,
-                       lg, ST_t, dST_t, A0, dl, dS0, cu, N, T, H, DK, DV);
-  else
-    hipLaunchKernelGGL(dgate_kernel<float>, grid, block, 0, stream,
-                       static_cast<const float *>(q), static_cast<const float *>(k), dq, dk, lg,
-                       ST_t, dST_t, A0, dl, dS0, cu, N, T, H, DK, DV);
+  hipLaunchKernelGGL(gate_scan_kernel, dim3((unsigned)(N * H)), dim3(256), 0, stream, dl, lg,
+                     ST_t, dST_t, A0, dl, dS0, cu, T, H, DK, DV);
   return hipGetLastError();
 }
 

@@ -71,6 +71,16 @@ template <> __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_
   return bf16_bits_to_f32(p[i]);
 }
 
+// Load four consecutive elements (16-byte aligned fp32, 8-byte aligned bf16) as floats.
+__device__ __forceinline__ f32x4 load4_as_f32(const float *p) {
+  return *reinterpret_cast<const f32x4 *>(p);
+}
+__device__ __forceinline__ f32x4 load4_as_f32(const uint16_t *p) {
+  const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
+  return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+               __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+}
+
 // Store a float as fp32 or bf16.
 template <typename T> __device__ __forceinline__ void store_from_f32(T *p, size_t i, float x);
 template <> __device__ __forceinline__ void store_from_f32<float>(float *p, size_t i, float x) {
