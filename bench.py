@@ -268,6 +268,21 @@ def bench_decode(args):
     alg_bytes = pairs * (2 * dk * dv * 4 + 2 * dk + 2 * dk + 2 * dv + 4 + 4 * dv)
     gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
     traffic = measured_traffic("decode_step_1280x16", ["decode.hip", "gla_common.h"])
+    # the same chain against a serving pool: the 1,280 requests on random,
+    # distinct slots of a 2,048-entry pool
+    P = 2048
+    del S
+    pool = torch.empty((P, H, dk, dv), dtype=torch.float32, device=dev).normal_(0.0, 0.02)
+    perm = np.random.default_rng(D["state_seed"]).permutation(P)[:N].astype(np.int32)
+    slots = torch.from_numpy(perm).to(dev)
+
+    def step_slots(i):
+        gla.decode_step_slots(qs[i % steps], ks[i % steps], vs[i % steps], gs[i % steps], pool,
+                              slots, o=o)
+
+    warm_up(step_slots, 10, min(args.warm_seconds, 0.5))
+    wall_s, kern_ms_s = time_launches(step_slots, steps, stream)
+    gbs_s = alg_bytes / (kern_ms_s * 1e-3) / 1e9
     return {
         "metric": "decode-step state HBM GB/s",
         "value": round(gbs, 1),
@@ -281,6 +296,9 @@ def bench_decode(args):
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes": alg_bytes,
                      "kernel": "decode_step_kernel<128,128,bf16,float>"},
+        "pool_slots": {"pool": P, "requests": N, "kernel_ms": round(kern_ms_s, 4),
+                       "gbs": round(gbs_s, 1), "frac": round(gbs_s / HBM_PEAK_GBS, 4),
+                       "entry": "gla_decode_step_slots"},
     }
 
 

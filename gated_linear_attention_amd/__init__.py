@@ -7,6 +7,7 @@ device memory and the current HIP stream.
     o, S_T = fwd_chunked(q, k, v, g, S0=None, cu_seqlens=None, chunk_size=64)
     dq, dk, dv, dg, dS0 = bwd_chunked(q, k, v, g, dO, S0=None, cu_seqlens=None, dS_T=None)
     o = decode_step(q, k, v, g, S)          # S updated in place
+    o = decode_step_slots(q, k, v, g, S_pool, slots)   # S_pool[slots] updated in place
 
 Shapes follow the C ABI: q, k [B, T, H, dk]; v [B, T, H, dv]; g [B, T, H]
 fp32 natural-log gates; S0 / S_T [N, H, dk, dv] fp32; cu_seqlens int32 [N+1]
@@ -17,8 +18,8 @@ from __future__ import annotations
 from . import _lib
 from ._lib import GLAError, GLA_BF16, GLA_F32
 
-__all__ = ["fwd_chunked", "bwd_chunked", "decode_step", "workspace_size", "GLAError",
-           "library_path"]
+__all__ = ["fwd_chunked", "bwd_chunked", "decode_step", "decode_step_slots", "workspace_size",
+           "GLAError", "library_path"]
 
 
 def library_path() -> str:
@@ -175,4 +176,36 @@ def decode_step(q, k, v, g, S, out_dtype=None, o=None):
     st = lib.gla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S), _ptr(o), N, H, dk, dv,
                              _dtype_code(q.dtype), _dtype_code(out_dtype), stream)
     _lib.check(st, "gla_decode_step")
+    return o
+
+
+def decode_step_slots(q, k, v, g, S_pool, slots, out_dtype=None, o=None):
+    """Decode step over a pool of states: request n reads and updates
+    S_pool[slots[n]] ([P, H, dk, dv] fp32, in place); slots (int32 [N], on the
+    device) outside [0, P) mark padded lanes (no state touched, o = 0). Returns o."""
+    torch = _torch()
+    lib = _lib.load()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or g.dim() != 2 or S_pool.dim() != 4:
+        raise ValueError("expected q, k [N, H, dk], v [N, H, dv], g [N, H], S_pool [P, H, dk, dv]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    P = S_pool.shape[0]
+    dev = q.device
+    _require(q, "q", None, dev)
+    _require(k, "k", q.dtype, dev)
+    _require(v, "v", q.dtype, dev)
+    _require(g, "g", torch.float32, dev)
+    _require(S_pool, "S_pool", torch.float32, dev)
+    _require(slots, "slots", torch.int32, dev)
+    if tuple(S_pool.shape[1:]) != (H, dk, dv) or tuple(g.shape) != (N, H) or slots.numel() != N:
+        raise ValueError("inconsistent decode shapes")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    _require(o, "o", out_dtype, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.gla_decode_step_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S_pool), _ptr(slots),
+                                   _ptr(o), N, P, H, dk, dv, _dtype_code(q.dtype),
+                                   _dtype_code(out_dtype), stream)
+    _lib.check(st, "gla_decode_step_slots")
     return o

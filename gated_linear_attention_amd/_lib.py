@@ -48,6 +48,8 @@ def load():
     lib.gla_bwd_chunked.restype = i
     lib.gla_decode_step.argtypes = [vp] * 6 + [i] * 4 + [i, i, vp]
     lib.gla_decode_step.restype = i
+    lib.gla_decode_step_slots.argtypes = [vp] * 7 + [i] * 5 + [i, i, vp]
+    lib.gla_decode_step_slots.restype = i
     _lib = lib
     return lib
 

@@ -13,6 +13,11 @@
 // RP = 256 / (dv/4); a wavefront therefore reads whole 512-byte (dv = 128)
 // rows, and every thread issues all of its dk/RP 16-byte loads before using
 // any of them, so each CU keeps many bytes in flight.
+//
+// Serving-pool variant (the page's "Inference optimization": one fixed-size
+// state per sequence, kept in the serving engine's pool): with `slots`, the
+// state of request n is S_pool[slots[n]]; a slot outside [0, P) marks a padded
+// lane of a fixed-width batch, which touches no state and outputs zeros.
 #include "gla_common.h"
 #include "gla_internal.h"
 
@@ -24,7 +29,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const Tin *__restrict_
                                                           const Tin *__restrict__ v,
                                                           const float *__restrict__ g,
                                                           float *__restrict__ S,
-                                                          Tout *__restrict__ o) {
+                                                          Tout *__restrict__ o,
+                                                          const int32_t *__restrict__ slots,
+                                                          int P, int H) {
   constexpr int TPR = DV / 4;   // threads per state row
   constexpr int RP = 256 / TPR; // rows per pass
   constexpr int NP = DK / RP;   // passes
@@ -35,7 +42,20 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const Tin *__restrict_
   const int t = threadIdx.x;
   const int c4 = t % TPR;
   const int r0 = t / TPR;
-  f32x4 *Sp = reinterpret_cast<f32x4 *>(S + p * (size_t)(DK * DV));
+  size_t sp = p;  // state of this pair
+  if (slots) {
+    const int slot = slots[p / H];
+    if (slot < 0 || slot >= P) {  // padded lane
+      if (t < TPR) {
+        Tout *op = o + p * DV + 4 * t;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) store_from_f32(op, j, 0.f);
+      }
+      return;
+    }
+    sp = (size_t)slot * H + p % H;
+  }
+  f32x4 *Sp = reinterpret_cast<f32x4 *>(S + sp * (size_t)(DK * DV));
 
   f32x4 s[NP];
 #pragma unroll
@@ -85,39 +105,45 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const Tin *__restrict_
   }
 }
 
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const float *g;
+  float *S;
+  void *o;
+  const int32_t *slots;
+  int P, H, pairs;
+};
+
 template <int DK, int DV, typename Tin, typename Tout>
-static hipError_t launch_decode_t(const void *q, const void *k, const void *v, const float *g,
-                                  float *S, void *o, int pairs, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_step_kernel<DK, DV, Tin, Tout>), dim3(pairs), dim3(256), 0, stream,
-                     static_cast<const Tin *>(q), static_cast<const Tin *>(k),
-                     static_cast<const Tin *>(v), g, S, static_cast<Tout *>(o));
+static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_step_kernel<DK, DV, Tin, Tout>), dim3(a.pairs), dim3(256), 0, stream,
+                     static_cast<const Tin *>(a.q), static_cast<const Tin *>(a.k),
+                     static_cast<const Tin *>(a.v), a.g, a.S, static_cast<Tout *>(a.o), a.slots,
+                     a.P, a.H);
   return hipGetLastError();
 }
 
 template <int DK, int DV>
-static hipError_t launch_decode_d(const void *q, const void *k, const void *v, const float *g,
-                                  float *S, void *o, int pairs, bool in_bf16, bool out_bf16,
+static hipError_t launch_decode_d(const DecodeArgs &a, bool in_bf16, bool out_bf16,
                                   hipStream_t stream) {
   if (in_bf16) {
-    return out_bf16 ? launch_decode_t<DK, DV, uint16_t, uint16_t>(q, k, v, g, S, o, pairs, stream)
-                    : launch_decode_t<DK, DV, uint16_t, float>(q, k, v, g, S, o, pairs, stream);
+    return out_bf16 ? launch_decode_t<DK, DV, uint16_t, uint16_t>(a, stream)
+                    : launch_decode_t<DK, DV, uint16_t, float>(a, stream);
   }
-  return out_bf16 ? launch_decode_t<DK, DV, float, uint16_t>(q, k, v, g, S, o, pairs, stream)
-                  : launch_decode_t<DK, DV, float, float>(q, k, v, g, S, o, pairs, stream);
+  return out_bf16 ? launch_decode_t<DK, DV, float, uint16_t>(a, stream)
+                  : launch_decode_t<DK, DV, float, float>(a, stream);
 }
 
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g, float *S,
                          void *o, int N, int H, int dk, int dv, bool in_bf16, bool out_bf16,
-                         hipStream_t stream) {
+                         const int32_t *slots, int P, hipStream_t stream) {
   const long pairs = (long)N * H;
   if (pairs == 0) return hipSuccess;
-  if (dk == 128 && dv == 128)
-    return launch_decode_d<128, 128>(q, k, v, g, S, o, (int)pairs, in_bf16, out_bf16, stream);
-  if (dk == 128 && dv == 64)
-    return launch_decode_d<128, 64>(q, k, v, g, S, o, (int)pairs, in_bf16, out_bf16, stream);
-  if (dk == 64 && dv == 128)
-    return launch_decode_d<64, 128>(q, k, v, g, S, o, (int)pairs, in_bf16, out_bf16, stream);
-  return launch_decode_d<64, 64>(q, k, v, g, S, o, (int)pairs, in_bf16, out_bf16, stream);
+  const DecodeArgs a{q, k, v, g, S, o, slots, P, H, (int)pairs};
+  if (dk == 128 && dv == 128) return launch_decode_d<128, 128>(a, in_bf16, out_bf16, stream);
+  if (dk == 128 && dv == 64) return launch_decode_d<128, 64>(a, in_bf16, out_bf16, stream);
+  if (dk == 64 && dv == 128) return launch_decode_d<64, 128>(a, in_bf16, out_bf16, stream);
+  return launch_decode_d<64, 64>(a, in_bf16, out_bf16, stream);
 }
 
 }  // namespace gla

@@ -399,7 +399,32 @@ gla_status gla_decode_step(const void *q, const void *k, const void *v, const fl
       overlaps(S, bS, k, bq) || overlaps(S, bS, v, bv) || overlaps(S, bS, g, bg))
     return GLA_ERR_INVALID_ARGUMENT;
   const hipError_t err = launch_decode(q, k, v, g, S, o, N, H, dk, dv, in_dtype == GLA_BF16,
-                                       out_dtype == GLA_BF16, stream);
+                                       out_dtype == GLA_BF16, nullptr, 0, stream);
+  return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
+gla_status gla_decode_step_slots(const void *q, const void *k, const void *v, const float *g,
+                                 float *S_pool, const int32_t *slots, void *o, int N, int P,
+                                 int H, int dk, int dv, gla_dtype in_dtype, gla_dtype out_dtype,
+                                 void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (N < 0 || P < 0 || H < 0) return GLA_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
+  if (!supported_head_dim(dk) || !supported_head_dim(dv)) return GLA_ERR_UNSUPPORTED;
+  const size_t pairs = (size_t)N * H;
+  if (pairs == 0) return GLA_OK;
+  if (pairs > (size_t)INT_MAX || (size_t)P * H > (size_t)INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
+  if (!q || !k || !v || !g || !slots || !o || (P > 0 && !S_pool)) return GLA_ERR_INVALID_ARGUMENT;
+  const size_t es = dtype_size(in_dtype);
+  const size_t bq = pairs * dk * es, bv = pairs * dv * es, bg = pairs * 4, bs = (size_t)N * 4;
+  const size_t bS = (size_t)P * H * dk * dv * 4, bo = pairs * dv * dtype_size(out_dtype);
+  if (overlaps(o, bo, q, bq) || overlaps(o, bo, k, bq) || overlaps(o, bo, v, bv) ||
+      overlaps(o, bo, g, bg) || overlaps(o, bo, S_pool, bS) || overlaps(o, bo, slots, bs) ||
+      overlaps(S_pool, bS, q, bq) || overlaps(S_pool, bS, k, bq) || overlaps(S_pool, bS, v, bv) ||
+      overlaps(S_pool, bS, g, bg) || overlaps(S_pool, bS, slots, bs))
+    return GLA_ERR_INVALID_ARGUMENT;
+  const hipError_t err = launch_decode(q, k, v, g, S_pool, o, N, H, dk, dv, in_dtype == GLA_BF16,
+                                       out_dtype == GLA_BF16, slots, P, stream);
   return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 

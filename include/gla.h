@@ -149,6 +149,26 @@ gla_status gla_decode_step(const void *q, const void *k, const void *v, const fl
                            float *S, void *o, int N, int H, int dk, int dv, gla_dtype in_dtype,
                            gla_dtype out_dtype, void *stream);
 
+/*
+ * The decode step over a serving pool of states (Laplace 3B on AWS Trainium2,
+ * "Inference optimization": the serving engine keeps one fixed-size state per
+ * sequence in its pool and decodes fixed-width, padded batches). Request n
+ * uses pool entry slots[n]:
+ *
+ *   S_pool[slots[n], h] <- exp(g[n,h]) * S_pool[slots[n], h] + k[n,h]^T v[n,h]
+ *   o[n, h]              = q[n,h] S_pool[slots[n], h]          (updated state)
+ *
+ *   S_pool [P, H, dk, dv] fp32, updated in place at the requested slots only
+ *   slots  [N] int32 DEVICE array; a slot outside [0, P) (e.g. -1) marks a
+ *          padded lane: no state is read or written and o[n] is set to 0.
+ *          Valid slots must be distinct (two requests on one slot race).
+ *   q, k, v, g, o, N, H, dk, dv, dtypes as gla_decode_step.
+ */
+gla_status gla_decode_step_slots(const void *q, const void *k, const void *v, const float *g,
+                                 float *S_pool, const int32_t *slots, void *o, int N, int P,
+                                 int H, int dk, int dv, gla_dtype in_dtype, gla_dtype out_dtype,
+                                 void *stream);
+
 #ifdef __cplusplus
 }
 #endif

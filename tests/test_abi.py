@@ -19,7 +19,7 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     assert header_functions() == ["gla_bwd_chunked", "gla_bwd_chunked_workspace_size",
-                                  "gla_decode_step", "gla_fwd_chunked",
+                                  "gla_decode_step", "gla_decode_step_slots", "gla_fwd_chunked",
                                   "gla_fwd_chunked_workspace_size", "gla_status_string"]
 
 
@@ -130,3 +130,21 @@ def test_bwd_rejects_bad_arguments_before_launch():
     assert _bwd(**P, ws=FAKE + 9 * G, wsb=n - 1) == _lib.GLA_ERR_WORKSPACE
     assert _bwd(H=0, **P) == _lib.GLA_OK
     assert lib.gla_bwd_chunked_workspace_size(1, 64, 1, 96, 64, 1, 64, 0, _lib.GLA_BF16) == 0
+
+
+def test_decode_slots_rejects_bad_arguments_before_launch():
+    G = 1 << 30
+    lib = _lib.load()
+    def call(q=FAKE, k=FAKE + G, v=FAKE + 2 * G, g=FAKE + 3 * G, S=FAKE + 4 * G,
+             slots=FAKE + 40 * G, o=FAKE + 41 * G, N=4, P=8, H=2, dk=64, dv=64,
+             ind=_lib.GLA_BF16, outd=_lib.GLA_F32):
+        return lib.gla_decode_step_slots(q, k, v, g, S, slots, o, N, P, H, dk, dv, ind, outd, None)
+    assert call(N=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(P=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(ind=3) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(dk=96) == _lib.GLA_ERR_UNSUPPORTED
+    assert call(slots=None) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(S=None) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(o=FAKE + 4 * G + 64) == _lib.GLA_ERR_INVALID_ARGUMENT   # o inside the pool
+    assert call(slots=FAKE + 4 * G + 64) == _lib.GLA_ERR_INVALID_ARGUMENT  # slots inside the pool
+    assert call(N=0) == _lib.GLA_OK
