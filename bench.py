@@ -302,6 +302,80 @@ def bench_decode(args):
     }
 
 
+def bench_laplace(args):
+    """Laplace 3B's mixer shape (16 heads of d_k = 96, d_v = 192, fixed
+    geometric decays): the fixed-decay forward on 8 x 2,048 tokens at both
+    chunk sizes, the per-token-gate forward on the same decays, and the decode
+    step on 1,280 sequences."""
+    import torch
+
+    import gated_linear_attention_amd as gla
+    from gated_linear_attention_amd import synth
+
+    w = synth.WORKLOADS["laplace_2k"]
+    dev = torch.device("cuda:0")
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    q, k, v, lg, _, _ = synth.make_forward_inputs(w)
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
+    tq, tk, tv = bf(q), bf(k), bf(v)
+    tlg = torch.from_numpy(lg).to(dev)
+    lam = torch.from_numpy(synth.fixed_log_decays(H)).to(dev)
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    tok_heads = B * T * H
+    # q, k, v (bf16) + o (fp32) + S_T (fp32); the per-token form also reads its gates
+    alg_fixed = tok_heads * (2 * dk + 2 * dk + 2 * dv + 4 * dv) + B * H * dk * dv * 4
+    alg_gates = alg_fixed + tok_heads * 4
+    steps = max(10, args.steps // 2)
+
+    def timed(fn, alg_bytes):
+        warm_up(fn, 5, min(args.warm_seconds, 0.3))
+        wall, kern_ms = time_launches(fn, steps, stream)
+        gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
+        return {"kernel_ms": round(kern_ms, 5), "tokens_per_s": round(B * T / (wall / steps), 1),
+                "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    fwd = {}
+    for C in (64, 128):
+        fwd[f"fixed_decay_c{C}"] = timed(
+            lambda i, C=C: gla.fwd_chunked_fixed_decay(tq, tk, tv, lam, chunk_size=C, o=o,
+                                                       S_T=S_T), alg_fixed)
+    fwd["token_gates_c64"] = timed(
+        lambda i: gla.fwd_chunked(tq, tk, tv, tlg, chunk_size=64, o=o, S_T=S_T), alg_gates)
+    del tq, tk, tv, tlg, o, S_T
+
+    # decode: 1,280 sequences x 16 heads of 96 x 192 fp32 state, in place
+    N, dsteps = 1280, 20
+    S = torch.from_numpy(synth.make_decode_state(N, H, dk, dv, seed=w.seed + 1)).to(dev)
+    lgd = lam.expand(N, H).contiguous()
+    ins = []
+    for s_ in range(dsteps):
+        dq, dkk, dvv, _ = synth.make_decode_step_inputs(N, H, dk, dv, seed=w.seed + 10 + s_)
+        ins.append((bf(dq), bf(dkk), bf(dvv)))
+    od = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+
+    def dstep(i):
+        a, b_, c = ins[i % dsteps]
+        gla.decode_step(a, b_, c, lgd, S, o=od)
+
+    warm_up(dstep, 10, min(args.warm_seconds, 0.3))
+    wall, kern_ms = time_launches(dstep, dsteps, stream)
+    alg_dec = N * H * (2 * dk * dv * 4 + 2 * dk + 2 * dk + 2 * dv + 4 + 4 * dv)
+    gbs = alg_dec / (kern_ms * 1e-3) / 1e9
+    return {
+        "config": {"workload": "laplace_2k forward and 1280-sequence decode", "B": B, "T": T,
+                   "H": H, "dk": dk, "dv": dv, "in_dtype": "bf16", "out_dtype": "f32",
+                   "decays": "fixed geometric schedule, half-lives 1 .. 2048 tokens"},
+        "forward": fwd,
+        "forward_kernel": "chunk_bf16_kernel<C,96,float,false>",
+        "forward_algorithmic_bytes": alg_fixed,
+        "decode": {"N": N, "kernel_ms": round(kern_ms, 5), "gbs": round(gbs, 1),
+                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg_dec,
+                   "kernel": "decode_step_rows_kernel<96,192,8,bf16,float>"},
+    }
+
+
 def cpu_baseline(host_set, target_s=10.0, min_wall=3.0):
     """Time the fp64 C oracle on a bounded sample of the headline workload:
     all 8 sequences over a subset of heads, sized to about target_s seconds."""
@@ -350,6 +424,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-laplace", action="store_true")
     ap.add_argument("--chunk", type=int, default=64, choices=[64, 128])
     ap.add_argument("--stream-reference", action="store_true",
                     help="only time two plain streams over the decode state's size (1.342 GB "
@@ -403,6 +478,11 @@ def main():
         log("decode: building inputs")
         dec = bench_decode(args)
         log(f"decode: {dec['value']} GB/s, kernel {dec['kernel_ms']:.4f} ms")
+    lap = None
+    if not args.no_laplace:
+        log("laplace shape: building inputs")
+        lap = bench_laplace(args)
+        log(f"laplace: fwd {lap['forward']} decode {lap['decode']['gbs']} GB/s")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the fp64 oracle")
@@ -429,6 +509,7 @@ def main():
         "other_chunk": fwd["other_chunk"],
         "backward": bwd,
         "decode": dec,
+        "laplace": lap,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -5,6 +5,7 @@ kernels of libgla.so (see include/gla.h for the C ABI). PyTorch supplies
 device memory and the current HIP stream.
 
     o, S_T = fwd_chunked(q, k, v, g, S0=None, cu_seqlens=None, chunk_size=64)
+    o, S_T = fwd_chunked_fixed_decay(q, k, v, log_lambda, S0=None, cu_seqlens=None)
     dq, dk, dv, dg, dS0 = bwd_chunked(q, k, v, g, dO, S0=None, cu_seqlens=None, dS_T=None)
     o = decode_step(q, k, v, g, S)          # S updated in place
     o = decode_step_slots(q, k, v, g, S_pool, slots)   # S_pool[slots] updated in place
@@ -18,7 +19,7 @@ from __future__ import annotations
 from . import _lib
 from ._lib import GLAError, GLA_BF16, GLA_F32
 
-__all__ = ["fwd_chunked", "bwd_chunked", "decode_step", "decode_step_slots", "workspace_size",
+__all__ = ["fwd_chunked", "fwd_chunked_fixed_decay", "bwd_chunked", "decode_step", "decode_step_slots", "workspace_size",
            "GLAError", "library_path"]
 
 
@@ -66,10 +67,26 @@ def workspace_size(B, T, H, dk, dv, num_seqs, chunk_size=64, has_cu_seqlens=Fals
 def fwd_chunked(q, k, v, g, S0=None, cu_seqlens=None, chunk_size: int = 64, out_dtype=None,
                 output_final_state: bool = True, o=None, S_T=None, workspace=None):
     """Chunked GLA forward. Returns (o, S_T) (S_T is None if not requested)."""
+    return _fwd(q, k, v, g, S0, cu_seqlens, chunk_size, out_dtype, output_final_state, o, S_T,
+                workspace, fixed_decay=False)
+
+
+def fwd_chunked_fixed_decay(q, k, v, log_lambda, S0=None, cu_seqlens=None, chunk_size: int = 64,
+                            out_dtype=None, output_final_state: bool = True, o=None, S_T=None,
+                            workspace=None):
+    """Chunked GLA forward with one fixed log-decay per head (log_lambda [H]
+    fp32): no per-token gate stream. Returns (o, S_T)."""
+    return _fwd(q, k, v, log_lambda, S0, cu_seqlens, chunk_size, out_dtype, output_final_state,
+                o, S_T, workspace, fixed_decay=True)
+
+
+def _fwd(q, k, v, g, S0, cu_seqlens, chunk_size, out_dtype, output_final_state, o, S_T,
+         workspace, fixed_decay):
     torch = _torch()
     lib = _lib.load()
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or g.dim() != 3:
-        raise ValueError("expected q, k, v [B, T, H, d] and g [B, T, H]")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or g.dim() != (1 if fixed_decay else 3):
+        raise ValueError("expected q, k, v [B, T, H, d] and "
+                         + ("log_lambda [H]" if fixed_decay else "g [B, T, H]"))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev = q.device
@@ -79,7 +96,8 @@ def fwd_chunked(q, k, v, g, S0=None, cu_seqlens=None, chunk_size: int = 64, out_
     _require(g, "g", torch.float32, dev)
     _require(S0, "S0", torch.float32, dev)
     _require(cu_seqlens, "cu_seqlens", torch.int32, dev)
-    if tuple(k.shape) != (B, T, H, dk) or tuple(v.shape[:3]) != (B, T, H) or tuple(g.shape) != (B, T, H):
+    g_shape = (H,) if fixed_decay else (B, T, H)
+    if tuple(k.shape) != (B, T, H, dk) or tuple(v.shape[:3]) != (B, T, H) or tuple(g.shape) != g_shape:
         raise ValueError("inconsistent q/k/v/g shapes")
     N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     if S0 is not None and tuple(S0.shape) != (N, H, dk, dv):
@@ -97,11 +115,11 @@ def fwd_chunked(q, k, v, g, S0=None, cu_seqlens=None, chunk_size: int = 64, out_
     if ws_bytes > 0 and (workspace is None or workspace.numel() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    st = lib.gla_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0), _ptr(cu_seqlens),
-                             _ptr(o), _ptr(S_T), B, T, H, dk, dv, N, chunk_size, in_code,
-                             _dtype_code(out_dtype), _ptr(workspace) if ws_bytes > 0 else None,
-                             ws_bytes, stream)
-    _lib.check(st, "gla_fwd_chunked")
+    fn = lib.gla_fwd_chunked_fixed_decay if fixed_decay else lib.gla_fwd_chunked
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T),
+            B, T, H, dk, dv, N, chunk_size, in_code, _dtype_code(out_dtype),
+            _ptr(workspace) if ws_bytes > 0 else None, ws_bytes, stream)
+    _lib.check(st, "gla_fwd_chunked_fixed_decay" if fixed_decay else "gla_fwd_chunked")
     return o, S_T
 
 

@@ -62,11 +62,22 @@ __device__ __forceinline__ WorkItem bf_item_for(const WorkItem *items, int it, i
 }
 
 // Element offsets in the swizzled tiles: 16-byte chunk c of row r sits at chunk
-// c ^ (r mod chunks-per-row).
+// c ^ qk_swz(r). With a power-of-two count of chunks per row the mask is
+// r mod chunks-per-row. A 96-wide row (12 chunks, a 48-dword pitch, so rows r
+// and r + 2 start on the same bank) keeps each chunk inside its group of four
+// and uses the mask (r / 2) mod 4: the 16-byte reads of 8 consecutive rows at
+// one logical chunk then cover all 32 banks.
+template <int DK>
+__device__ __forceinline__ int qk_swz(int r) {
+  constexpr int CPR = DK / 8;
+  static_assert(DK == 96 || (CPR & (CPR - 1)) == 0, "row width");
+  if constexpr (DK == 96) return (r >> 1) & 3;
+  else return r & (CPR - 1);
+}
 template <int DK>
 __device__ __forceinline__ int qk_off(int r, int col) {
-  constexpr int CPR = DK / 8;
-  return r * DK + ((((col >> 3) ^ r) & (CPR - 1)) << 3) + (col & 7);
+  if constexpr (DK == 96) return r * DK + (((col >> 3) ^ qk_swz<DK>(r)) << 3) + (col & 7);
+  else return r * DK + ((((col >> 3) ^ r) & (DK / 8 - 1)) << 3) + (col & 7);
 }
 __device__ __forceinline__ int v_off(int r, int col) {
   return r * kBfSlice + ((((col >> 3) ^ r) & 7) << 3) + (col & 7);

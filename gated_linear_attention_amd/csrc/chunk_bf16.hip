@@ -76,7 +76,7 @@ template <int C, int DK, bool SP>
 struct ChunkLoader {
   static constexpr int CPR = DK / 8;                  // 16-byte chunks per Q/K row
   static constexpr int QB = C * DK * 2 / 1024;        // 1 KB blocks per Q/K tile
-  static constexpr int RPB = 1024 / (DK * 2);         // rows per block
+  static_assert(QB % 4 == 0, "Q/K tile blocks split over four wavefronts");
   static constexpr int VB = C * kBfSlice * 2 / 1024;  // 1 KB blocks of the V slice (8 rows each)
   i32x4 rq, rk, rv, rg;
   uint32_t qk_row, v_row, g_row;
@@ -84,8 +84,8 @@ struct ChunkLoader {
   bool active;
 
   __device__ __forceinline__ void setup(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                        const float *lg, int t0, int tok_end, int H, int h,
-                                        int DV, int col0, int stage) {
+                                        const float *lg, int t0, int tok_end, int H, int gts,
+                                        int h, int DV, int col0, int stage) {
     active = t0 < tok_end;
     st = stage;
     if (!active) return;
@@ -93,19 +93,22 @@ struct ChunkLoader {
     const size_t tok0 = (size_t)t0 * H + h;
     qk_row = (uint32_t)H * DK * 2;
     v_row = (uint32_t)H * DV * 2;
-    g_row = (uint32_t)H * 4;
+    g_row = (uint32_t)gts * 4;
     rk = make_rsrc(k + tok0 * DK, (n - 1) * qk_row + DK * 2);
     if (!SP) rq = make_rsrc(q + tok0 * DK, (n - 1) * qk_row + DK * 2);
     rv = make_rsrc(v + tok0 * DV + col0, (n - 1) * v_row + kBfSlice * 2);
-    rg = make_rsrc(lg + tok0, (n - 1) * g_row + 4);
+    rg = make_rsrc(lg + (size_t)t0 * gts + h, (n - 1) * g_row + 4);
   }
   template <typename Tiles>
   __device__ __forceinline__ void qk_part(Tiles &dst, i32x4 r, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < QB / 4; ++i) {
       const int blk = wave * (QB / 4) + i;
-      const int row = blk * RPB + lane / CPR;
-      const int c = (lane % CPR) ^ (row & (CPR - 1));
+      // the lane's LDS slot is 16-byte chunk e of the row-major tile: row
+      // e / CPR, swizzled chunk e % CPR, filled from logical chunk c
+      const int e = blk * 64 + lane;
+      const int row = e / CPR;
+      const int c = (e % CPR) ^ qk_swz<DK>(row);
       buffer_load_to_lds(r, (lds_u32 *)&dst[st][blk * 512], 16, row * qk_row + c * 16, 0, 0, 0);
     }
   }
@@ -154,15 +157,17 @@ struct BfRun {
   __device__ __forceinline__ BfRun(LDS &s_, int wave_, int lane_)
       : s(s_), wave(wave_), lane(lane_), ln(lane_ % 16), lg4(lane_ / 16), wcol(16 * wave_) {}
 
-  // Gates of the chunk in stage st: in-chunk prefix sums (log2 units) and the
-  // decay factors, into this wavefront's LDS arrays. Returns the chunk decay;
-  // adds the chunk's natural-log gate sum to lsum.
-  __device__ __forceinline__ float gates(int st, float &lsum) {
+  // Gates of the chunk in stage st (n tokens): in-chunk prefix sums (log2
+  // units) and the decay factors, into this wavefront's LDS arrays. Positions
+  // past the end add 0 (a fixed decay loads its value into every position).
+  // Returns the chunk decay; adds the chunk's natural-log gate sum to lsum.
+  __device__ __forceinline__ float gates(int st, int n, float &lsum) {
     float part[E];
     float run = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      run += s.lg[st][lane * E + e];
+      const float x = s.lg[st][lane * E + e];
+      run += lane * E + e < n ? x : 0.f;
       part[e] = run;
     }
     const float incl = wave_inclusive_scan(run);
@@ -241,7 +246,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
     const uint16_t *__restrict__ v, const float *__restrict__ lg, const float *__restrict__ S0,
     float *__restrict__ ST, Tout *__restrict__ o, const WorkItem *__restrict__ items,
     const int *__restrict__ n_items, float *__restrict__ slots, float *__restrict__ slot_gamma,
-    int T, int H, int DV, int n_pairs) {
+    int T, int H, int gts, int DV, int n_pairs) {
   using Run = BfRun<C, DK, Tout, SP>;
   using LDS = typename Run::LDS;
   constexpr int NST = Run::NST, PP = Run::PP, NM = Run::NM, NKS = Run::NKS, NT = Run::NT,
@@ -319,7 +324,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
 
   ChunkLoader<C, DK, SP> ld;
   int t0 = w.tok_begin;
-  ld.setup(q, k, v, lg, t0, w.tok_end, H, h, DV, col0, 0);
+  ld.setup(q, k, v, lg, t0, w.tok_end, H, gts, h, DV, col0, 0);
   ld.all(s, wave, lane);
 
   for (int ci = 0; t0 < w.tok_end; t0 += C, ++ci) {
@@ -331,10 +336,10 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
     const uint16_t *sq = s.q[SP ? 0 : st];
     const uint16_t *sk = s.k[st];
     const uint16_t *sv = s.v[st];
-    if (NST == 2) ld.setup(q, k, v, lg, t1, w.tok_end, H, h, DV, col0, st ^ 1);
+    if (NST == 2) ld.setup(q, k, v, lg, t1, w.tok_end, H, gts, h, DV, col0, st ^ 1);
     if (NST == 2) ld.k_part(s, wave, lane);
 
-    const float gam = R.gates(st, lsum);
+    const float gam = R.gates(st, n, lsum);
 
     f32x4 O_acc[SP ? 1 : NM];
     if (!SP) {
@@ -442,7 +447,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
     }
     if (NST == 1 && t1 < w.tok_end) {
       barrier_lds();  // every wavefront is done with the single stage
-      ld.setup(q, k, v, lg, t1, w.tok_end, H, h, DV, col0, 0);
+      ld.setup(q, k, v, lg, t1, w.tok_end, H, gts, h, DV, col0, 0);
       ld.all(s, wave, lane);
     }
   }
@@ -476,7 +481,7 @@ static hipError_t launch_bf_t(const uint16_t *q, const uint16_t *k, const uint16
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((chunk_bf16_kernel<C, DK, Tout, SP>), dim3(blocks), dim3(256), 0, stream,
                      q, k, v, g, S0, S_T, static_cast<Tout *>(o), items, n_items, slots,
-                     slot_gamma, d.T, d.H, d.dv, (int)pairs);
+                     slot_gamma, d.T, d.H, d.gts, d.dv, (int)pairs);
   return hipGetLastError();
 }
 
@@ -502,7 +507,15 @@ hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_
                              int grid_items, float *slots, float *slot_gamma, bool state_pass,
                              hipStream_t stream) {
   // 64-token chunks run on the eight-wavefront kernel; this file's four-wavefront
-  // kernel serves 128-token chunks (whose tiles leave no LDS for eight wavefronts).
+  // kernel serves 128-token chunks (whose tiles leave no LDS for eight wavefronts)
+  // and the 96-wide key dimension.
+  if (d.dk == 96) {  // 96 x 192 heads run here at both chunk sizes
+    if (d.C == 64)
+      return launch_bf_c<64, 96>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
+                                 slots, slot_gamma, state_pass, stream);
+    return launch_bf_c<128, 96>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
+                                slots, slot_gamma, state_pass, stream);
+  }
   if (d.C == 64)
     return launch_chunk_bf16_c64(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
                                  slots, slot_gamma, state_pass, stream);

@@ -74,18 +74,19 @@ struct W8Loader {
   bool active, g_active;
 
   __device__ __forceinline__ void init(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                       const float *lg, int t0, int H, int h, int DV, int col0) {
+                                       const float *lg, int t0, int H, int gts, int h, int DV,
+                                       int col0) {
     const size_t tok0 = (size_t)t0 * H + h;
     qp = q + tok0 * DK;
     kp = k + tok0 * DK;
     vp = v + tok0 * DV + col0;
-    gp = lg + tok0;
+    gp = lg + (size_t)t0 * gts + h;
     qk_step = (size_t)C * H * DK;
     v_step = (size_t)C * H * DV;
-    g_step = (size_t)C * H;
+    g_step = (size_t)C * gts;
     qk_row = (uint32_t)H * DK * 2;
     v_row = (uint32_t)H * DV * 2;
-    g_row = (uint32_t)H * 4;
+    g_row = (uint32_t)gts * 4;
   }
   // Descriptors for the tile chunk that starts at token t0 (the one after the
   // previous call's), to be written into stage `stage`.
@@ -101,7 +102,9 @@ struct W8Loader {
     kp += qk_step;
     vp += v_step;
   }
-  // The same for the gate chunk starting at t0 (gates past the end read as 0).
+  // The same for the gate chunk starting at t0 (with a per-token gate stream,
+  // gates past the end read as 0; a fixed decay reads one value for all lanes
+  // and the scan masks the lanes past the end).
   __device__ __forceinline__ void gate_next(int t0, int tok_end) {
     g_active = t0 < tok_end;
     if (!g_active) return;
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
     const uint16_t *__restrict__ v, const float *__restrict__ lg, const float *__restrict__ S0,
     float *__restrict__ ST, Tout *__restrict__ o, const WorkItem *__restrict__ items,
     const int *__restrict__ n_items, float *__restrict__ slots, float *__restrict__ slot_gamma,
-    int T, int H, int DV, int n_pairs) {
+    int T, int H, int gts, int DV, int n_pairs) {
   using Wv = W8Wave<DK, SP>;
   using LDS = typename Wv::LDS;
   constexpr int C = kW8C;
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
 
   W8Loader<DK, SP> ld;
   int t0 = w.tok_begin;
-  ld.init(q, k, v, lg, t0, H, h, DV, col0);
+  ld.init(q, k, v, lg, t0, H, gts, h, DV, col0);
   ld.next(t0, w.tok_end, 0);
   ld.k_part(s, wave, lane);
   ld.q_part(s, wave, lane);
@@ -328,7 +331,11 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
   barrier_all();
   // gates of the first chunk; each later chunk's are prepared at the end of
   // the chunk before it, from the ring slot loaded two chunks ahead
-  float gam = t0 < w.tok_end ? R.gates(s.lgb[0][lane], lsum) : 1.f;
+  float gam = 1.f;
+  if (t0 < w.tok_end) {
+    const float x = s.lgb[0][lane];
+    gam = R.gates(lane < w.tok_end - t0 ? x : 0.f, lsum);
+  }
   int g_rd = 1, g_ld = 2;  // ring slots of the next chunk's and of the far chunk's gates
 
   // key rows of this wavefront's 32 keys (js = rh) and of the partner's
@@ -546,7 +553,10 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
 #pragma unroll
     for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt_x[t], kx_l, S_acc[t]);
 
-    if (has_next) gam = R.gates(s.lgb[g_rd][lane], lsum);
+    if (has_next) {
+      const float x = s.lgb[g_rd][lane];
+      gam = R.gates(lane < w.tok_end - t0 - C ? x : 0.f, lsum);
+    }
     if (!SP) store_out(t0, n, own);
     g_rd = g_rd == 2 ? 0 : g_rd + 1;
     g_ld = g_ld == 2 ? 0 : g_ld + 1;
@@ -579,7 +589,7 @@ static hipError_t launch_w8_t(const uint16_t *q, const uint16_t *k, const uint16
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((chunk_bf16_w8_kernel<DK, Tout, SP>), dim3(blocks), dim3(512), 0, stream,
                      q, k, v, g, S0, S_T, static_cast<Tout *>(o), items, n_items, slots,
-                     slot_gamma, d.T, d.H, d.dv, (int)pairs);
+                     slot_gamma, d.T, d.H, d.gts, d.dv, (int)pairs);
   return hipGetLastError();
 }
 

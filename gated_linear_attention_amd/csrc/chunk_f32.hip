@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ lg, const float *__restrict__ S0, float *__restrict__ ST,
     Tout *__restrict__ o, const WorkItem *__restrict__ items, const int *__restrict__ n_items,
-    float *__restrict__ slots, float *__restrict__ slot_gamma, int T, int H, int DV) {
+    float *__restrict__ slots, float *__restrict__ slot_gamma, int T, int H, int gts, int DV) {
   constexpr int DVS = kF32Slice, KB = kF32DkBlk;
   constexpr int NPE = C * C / 256;    // score entries per thread
   constexpr int NOE = C * DVS / 256;  // output entries per thread
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
     const int n = min(C, w.tok_end - t0);
     __syncthreads();
     // gates: inclusive scan of the chunk's log-gates (padding rows add 0)
-    if (tid < C) bcum[tid] = (tid < n) ? lg[(size_t)(t0 + tid) * H + h] : 0.f;
+    if (tid < C) bcum[tid] = (tid < n) ? lg[(size_t)(t0 + tid) * gts + h] : 0.f;
     for (int e = tid; e < C * DVS; e += 256) {
       const int j = e / DVS, c = e % DVS;
       Vs[j][c] = (j < n) ? v[((size_t)(t0 + j) * H + h) * DV + c0 + c] : 0.f;
@@ -200,7 +200,7 @@ static hipError_t launch_f32_t(const float *q, const float *k, const float *v, c
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((chunk_f32_kernel<C, DK, Tout, SP>), dim3(blocks), dim3(256), 0, stream, q,
                      k, v, g, S0, S_T, static_cast<Tout *>(o), items, n_items, slots, slot_gamma,
-                     d.T, d.H, d.dv);
+                     d.T, d.H, d.gts, d.dv);
   return hipGetLastError();
 }
 
@@ -225,6 +225,13 @@ hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, cons
                             const FwdDims &d, const WorkItem *items, const int *n_items,
                             int grid_items, float *slots, float *slot_gamma, bool state_pass,
                             hipStream_t stream) {
+  if (d.dk == 96) {
+    if (d.C == 64)
+      return launch_f32_c<64, 96>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
+                                  slots, slot_gamma, state_pass, stream);
+    return launch_f32_c<128, 96>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
+                                 slots, slot_gamma, state_pass, stream);
+  }
   if (d.C == 64) {
     if (d.dk == 128)
       return launch_f32_c<64, 128>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items,

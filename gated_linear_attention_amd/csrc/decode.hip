@@ -105,6 +105,75 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const Tin *__restrict_
   }
 }
 
+// The same step for row widths whose 4-column groups do not divide a
+// wavefront (d_v = 192 in Laplace 3B's 96 x 192 heads, "GLA mixer"): RP rows
+// per pass of TPR = d_v / 4 threads each, and the d_k reduction of o through
+// LDS (each thread's partial sum, then one thread per column group adds RP).
+template <int DK, int DV, int RP, typename Tin, typename Tout>
+__global__ __launch_bounds__(512) void decode_step_rows_kernel(const Tin *__restrict__ q,
+                                                               const Tin *__restrict__ k,
+                                                               const Tin *__restrict__ v,
+                                                               const float *__restrict__ g,
+                                                               float *__restrict__ S,
+                                                               Tout *__restrict__ o,
+                                                               const int32_t *__restrict__ slots,
+                                                               int P, int H) {
+  constexpr int TPR = DV / 4;
+  constexpr int NP = DK / RP;
+  static_assert(DK % RP == 0 && DV % 4 == 0, "row tiling");
+  __shared__ f32x4 red[RP][TPR];
+
+  const size_t p = blockIdx.x;
+  const int t = threadIdx.x;
+  const int c4 = t % TPR;
+  const int r0 = t / TPR;
+  size_t sp = p;
+  if (slots) {
+    const int slot = slots[p / H];
+    if (slot < 0 || slot >= P) {
+      if (t < TPR) {
+        Tout *op = o + p * DV + 4 * t;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) store_from_f32(op, j, 0.f);
+      }
+      return;
+    }
+    sp = (size_t)slot * H + p % H;
+  }
+  f32x4 *Sp = reinterpret_cast<f32x4 *>(S + sp * (size_t)(DK * DV));
+
+  f32x4 s[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) s[i] = __builtin_nontemporal_load(Sp + (r0 + i * RP) * TPR + c4);
+  const float gate = expf(g[p]);
+  f32x4 vv;
+  vv.x = load_as_f32(v, p * DV + 4 * c4 + 0);
+  vv.y = load_as_f32(v, p * DV + 4 * c4 + 1);
+  vv.z = load_as_f32(v, p * DV + 4 * c4 + 2);
+  vv.w = load_as_f32(v, p * DV + 4 * c4 + 3);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const float kk = load_as_f32(k, p * DK + r0 + i * RP);
+    const float qq = load_as_f32(q, p * DK + r0 + i * RP);
+    const f32x4 x = gate * s[i] + kk * vv;
+    __builtin_nontemporal_store(x, Sp + (r0 + i * RP) * TPR + c4);
+    acc += qq * x;
+  }
+  red[r0][c4] = acc;
+  __syncthreads();
+  if (t < TPR) {
+    f32x4 r = red[0][t];
+#pragma unroll
+    for (int i = 1; i < RP; ++i) r += red[i][t];
+    Tout *op = o + p * DV + 4 * t;
+    store_from_f32(op, 0, r.x);
+    store_from_f32(op, 1, r.y);
+    store_from_f32(op, 2, r.z);
+    store_from_f32(op, 3, r.w);
+  }
+}
+
 struct DecodeArgs {
   const void *q, *k, *v;
   const float *g;
@@ -121,6 +190,26 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
                      static_cast<const Tin *>(a.v), a.g, a.S, static_cast<Tout *>(a.o), a.slots,
                      a.P, a.H);
   return hipGetLastError();
+}
+
+template <int DK, int DV, int RP, typename Tin, typename Tout>
+static hipError_t launch_decode_rows_t(const DecodeArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_step_rows_kernel<DK, DV, RP, Tin, Tout>), dim3(a.pairs),
+                     dim3(RP * DV / 4), 0, stream, static_cast<const Tin *>(a.q),
+                     static_cast<const Tin *>(a.k), static_cast<const Tin *>(a.v), a.g, a.S,
+                     static_cast<Tout *>(a.o), a.slots, a.P, a.H);
+  return hipGetLastError();
+}
+
+template <int DK, int DV, int RP>
+static hipError_t launch_decode_rows_d(const DecodeArgs &a, bool in_bf16, bool out_bf16,
+                                       hipStream_t stream) {
+  if (in_bf16) {
+    return out_bf16 ? launch_decode_rows_t<DK, DV, RP, uint16_t, uint16_t>(a, stream)
+                    : launch_decode_rows_t<DK, DV, RP, uint16_t, float>(a, stream);
+  }
+  return out_bf16 ? launch_decode_rows_t<DK, DV, RP, float, uint16_t>(a, stream)
+                  : launch_decode_rows_t<DK, DV, RP, float, float>(a, stream);
 }
 
 template <int DK, int DV>
@@ -143,6 +232,7 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const floa
   if (dk == 128 && dv == 128) return launch_decode_d<128, 128>(a, in_bf16, out_bf16, stream);
   if (dk == 128 && dv == 64) return launch_decode_d<128, 64>(a, in_bf16, out_bf16, stream);
   if (dk == 64 && dv == 128) return launch_decode_d<64, 128>(a, in_bf16, out_bf16, stream);
+  if (dk == 96 && dv == 192) return launch_decode_rows_d<96, 192, 8>(a, in_bf16, out_bf16, stream);
   return launch_decode_d<64, 64>(a, in_bf16, out_bf16, stream);
 }
 

@@ -28,6 +28,12 @@ int cu_count() {
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
+// (d_k, d_v) pairs of the forward and decode: any of {64, 128} x {64, 128},
+// and Laplace 3B's 96 x 192 heads.
+bool fwd_dims(int dk, int dv) {
+  return (supported_head_dim(dk) && supported_head_dim(dv)) || (dk == 96 && dv == 192);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int round_up(long x, int m) { return (int)(((x + m - 1) / m) * m); }
@@ -124,7 +130,8 @@ namespace gla {
 gla_status fwd_core(const void *q, const void *k, const void *v, const float *g, const float *S0,
                     const int32_t *cu_seqlens, void *o, float *S_T, int B, int T, int H, int dk,
                     int dv, int N, int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
-                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                    void *workspace, size_t workspace_bytes, hipStream_t stream,
+                    bool fixed_decay) {
   const bool has_cu = cu_seqlens != nullptr;
   FwdDims d;
   d.B = B;
@@ -134,6 +141,7 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
   d.dv = dv;
   d.N = N;
   d.C = chunk_size;
+  d.gts = fixed_decay ? 0 : H;
   PlanLayout lay;
   const bool planned = make_plan(B, T, H, dk, dv, N, chunk_size, has_cu, in_dtype, lay);
   if (planned && (!workspace || workspace_bytes < lay.total_bytes)) return GLA_ERR_WORKSPACE;
@@ -197,31 +205,36 @@ const char *gla_status_string(gla_status s) {
 
 size_t gla_fwd_chunked_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
                                       int chunk_size, int has_cu_seqlens, gla_dtype in_dtype) {
-  if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !supported_head_dim(dk) ||
-      !supported_head_dim(dv) || (chunk_size != 64 && chunk_size != 128) ||
-      !valid_dtype(in_dtype))
+  if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !fwd_dims(dk, dv) ||
+      (chunk_size != 64 && chunk_size != 128) || !valid_dtype(in_dtype))
     return 0;
   return fwd_workspace(B, T, H, dk, dv, num_seqs, chunk_size, has_cu_seqlens != 0, in_dtype);
 }
 
-gla_status gla_fwd_chunked(const void *q, const void *k, const void *v, const float *g,
-                           const float *S0, const int32_t *cu_seqlens, void *o, float *S_T,
-                           int B, int T, int H, int dk, int dv, int num_seqs, int chunk_size,
-                           gla_dtype in_dtype, gla_dtype out_dtype, void *workspace,
-                           size_t workspace_bytes, void *stream_) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of both forward entry points, then the forward.
+gla_status fwd_checked(const void *q, const void *k, const void *v, const float *g,
+                       const float *S0, const int32_t *cu_seqlens, void *o, float *S_T, int B,
+                       int T, int H, int dk, int dv, int num_seqs, int chunk_size,
+                       gla_dtype in_dtype, gla_dtype out_dtype, void *workspace,
+                       size_t workspace_bytes, void *stream_, bool fixed_decay) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return GLA_ERR_INVALID_ARGUMENT;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
   const bool has_cu = cu_seqlens != nullptr;
   if (has_cu ? (B != 1) : (num_seqs != B)) return GLA_ERR_INVALID_ARGUMENT;
   if ((long)B * T > INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
-  if (!supported_head_dim(dk) || !supported_head_dim(dv)) return GLA_ERR_UNSUPPORTED;
+  if (!fwd_dims(dk, dv)) return GLA_ERR_UNSUPPORTED;
   if (chunk_size != 64 && chunk_size != 128) return GLA_ERR_UNSUPPORTED;
   const int N = num_seqs;
   if (H == 0 || N == 0) return GLA_OK;
   const size_t ntok = (size_t)B * T * H;
   const size_t es = dtype_size(in_dtype);
-  const size_t bytes_qk = ntok * dk * es, bytes_v = ntok * dv * es, bytes_g = ntok * 4;
+  const size_t bytes_qk = ntok * dk * es, bytes_v = ntok * dv * es;
+  const size_t bytes_g = fixed_decay ? (size_t)H * 4 : ntok * 4;
   const size_t bytes_o = ntok * dv * dtype_size(out_dtype);
   const size_t bytes_S = (size_t)N * H * dk * dv * 4;
   if (ntok > 0 && (!q || !k || !v || !g || !o)) return GLA_ERR_INVALID_ARGUMENT;
@@ -235,8 +248,31 @@ gla_status gla_fwd_chunked(const void *q, const void *k, const void *v, const fl
        overlaps(S_T, bytes_S, g, bytes_g)))
     return GLA_ERR_INVALID_ARGUMENT;
 
-  return fwd_core(q, k, v, g, S0, cu_seqlens, o, S_T, B, T, H, dk, dv, N, chunk_size, in_dtype,
-                  out_dtype, workspace, workspace_bytes, stream);
+  return gla::fwd_core(q, k, v, g, S0, cu_seqlens, o, S_T, B, T, H, dk, dv, N, chunk_size,
+                       in_dtype, out_dtype, workspace, workspace_bytes, stream, fixed_decay);
+}
+
+}  // namespace
+
+extern "C" {
+
+gla_status gla_fwd_chunked(const void *q, const void *k, const void *v, const float *g,
+                           const float *S0, const int32_t *cu_seqlens, void *o, float *S_T,
+                           int B, int T, int H, int dk, int dv, int num_seqs, int chunk_size,
+                           gla_dtype in_dtype, gla_dtype out_dtype, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  return fwd_checked(q, k, v, g, S0, cu_seqlens, o, S_T, B, T, H, dk, dv, num_seqs, chunk_size,
+                     in_dtype, out_dtype, workspace, workspace_bytes, stream, false);
+}
+
+gla_status gla_fwd_chunked_fixed_decay(const void *q, const void *k, const void *v,
+                                       const float *log_lambda, const float *S0,
+                                       const int32_t *cu_seqlens, void *o, float *S_T, int B,
+                                       int T, int H, int dk, int dv, int num_seqs,
+                                       int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
+                                       void *workspace, size_t workspace_bytes, void *stream) {
+  return fwd_checked(q, k, v, log_lambda, S0, cu_seqlens, o, S_T, B, T, H, dk, dv, num_seqs,
+                     chunk_size, in_dtype, out_dtype, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"
@@ -386,7 +422,7 @@ gla_status gla_decode_step(const void *q, const void *k, const void *v, const fl
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (N < 0 || H < 0) return GLA_ERR_INVALID_ARGUMENT;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
-  if (!supported_head_dim(dk) || !supported_head_dim(dv)) return GLA_ERR_UNSUPPORTED;
+  if (!fwd_dims(dk, dv)) return GLA_ERR_UNSUPPORTED;
   const size_t pairs = (size_t)N * H;
   if (pairs == 0) return GLA_OK;
   if (pairs > (size_t)INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
@@ -410,7 +446,7 @@ gla_status gla_decode_step_slots(const void *q, const void *k, const void *v, co
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (N < 0 || P < 0 || H < 0) return GLA_ERR_INVALID_ARGUMENT;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
-  if (!supported_head_dim(dk) || !supported_head_dim(dv)) return GLA_ERR_UNSUPPORTED;
+  if (!fwd_dims(dk, dv)) return GLA_ERR_UNSUPPORTED;
   const size_t pairs = (size_t)N * H;
   if (pairs == 0) return GLA_OK;
   if (pairs > (size_t)INT_MAX || (size_t)P * H > (size_t)INT_MAX) return GLA_ERR_INVALID_ARGUMENT;

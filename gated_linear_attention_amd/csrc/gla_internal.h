@@ -56,6 +56,7 @@ struct PlanLayout {
 // dims of the flattened problem
 struct FwdDims {
   int B, T, H, dk, dv, N, C;
+  int gts;  // gate token stride in floats: H (log_g [.., T, H]) or 0 (one fixed log-decay per head)
 };
 
 // slots == nullptr: state of pair (n, h) is S[n, h]; otherwise S[slots[n], h]
@@ -92,10 +93,12 @@ hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_
                              hipStream_t stream);
 
 // The chunked forward after argument checks (gla_api.hip), and its workspace.
+// g is log_g [.., T, H], or with fixed_decay one log-decay per head [H].
 gla_status fwd_core(const void *q, const void *k, const void *v, const float *g, const float *S0,
                     const int32_t *cu_seqlens, void *o, float *S_T, int B, int T, int H, int dk,
                     int dv, int N, int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
-                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+                    void *workspace, size_t workspace_bytes, hipStream_t stream,
+                    bool fixed_decay = false);
 size_t fwd_workspace(int B, int T, int H, int dk, int dv, int N, int chunk_size, bool has_cu,
                      gla_dtype in_dtype);
 // Backward helpers (bwd.hip).

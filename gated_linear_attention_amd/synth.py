@@ -35,6 +35,7 @@ __all__ = [
     "make_decode_step_inputs",
     "varlen_lengths",
     "laplace_decay_schedule",
+    "fixed_log_decays",
 ]
 
 
@@ -79,6 +80,7 @@ class Workload:
     len_lo: int = 0
     len_hi: int = 0
     seed: int = 0
+    fixed_decay: bool = False  # log g[b, t, h] = ln(lambda_h) of the geometric schedule
 
 
 WORKLOADS = {
@@ -91,6 +93,10 @@ WORKLOADS = {
     "varlen_64": Workload("varlen_64", B=1, T=0, H=16, dk=128, dv=128, dtype="bf16",
                           gate_bias=3.0, s0_std=0.02, chunk=128, num_seqs=64,
                           len_lo=128, len_hi=8192, seed=1004),
+    # Laplace 3B's mixer shape: 16 heads of d_k = 96, d_v = 192 with the
+    # fixed geometric decays, 8 sequences of 2,048 tokens.
+    "laplace_2k": Workload("laplace_2k", B=8, T=2048, H=16, dk=96, dv=192, dtype="bf16",
+                           gate_bias=0.0, s0_std=0.0, chunk=64, seed=1005, fixed_decay=True),
 }
 
 # Batched decode: 1,280 sequences x 16 heads, d_k = d_v = 128, fp32 state
@@ -146,6 +152,9 @@ def make_forward_inputs(w: Workload, *, seed: int | None = None, B: int | None =
     v = _store(_normal(rng, (B, T, H, w.dv)), w.dtype)
     pre = rng.standard_normal(size=(B, T, H)) + w.gate_bias
     log_g = log_sigmoid(pre).astype(np.float32)
+    if w.fixed_decay:
+        log_g = np.ascontiguousarray(
+            np.broadcast_to(fixed_log_decays(H), (B, T, H)), dtype=np.float32)
     S0 = None
     if w.s0_std > 0:
         S0 = _normal(rng, (N, H, w.dk, w.dv), w.s0_std)
@@ -178,6 +187,12 @@ def make_decode_step_inputs(N: int, H: int, dk: int, dv: int, *, seed: int,
     v = _store(_normal(rng, (N, H, dv)), dtype)
     log_g = log_sigmoid(rng.standard_normal(size=(N, H)) + gate_bias).astype(np.float32)
     return q, k, v, log_g
+
+
+def fixed_log_decays(H: int) -> np.ndarray:
+    """The schedule's ln(lambda_h) for H heads as the fp32 values a fixed-decay
+    forward takes (shape [H])."""
+    return laplace_decay_schedule(H=H).astype(np.float32)
 
 
 def laplace_decay_schedule(H: int = 16, t_min: float = 1.0, t_max: float = 2048.0) -> np.ndarray:

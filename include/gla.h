@@ -28,8 +28,10 @@
  *    caller's next synchronisation, as with any HIP library.
  *  - Tensor values are not validated: NaN/Inf propagate, and l_t > 0 (a
  *    growing state) is computed as given.
- *  - Supported sizes: d_k, d_v in {64, 128}; chunk_size in {64, 128}.
- *    Anything else returns GLA_ERR_UNSUPPORTED.
+ *  - Supported sizes: d_k, d_v in {64, 128}; chunk_size in {64, 128}. The
+ *    forward and the decode steps also take (d_k, d_v) = (96, 192), the head
+ *    shape of Laplace 3B ("GLA mixer"); the backward does not. Anything else
+ *    returns GLA_ERR_UNSUPPORTED.
  */
 #ifndef GLA_H_
 #define GLA_H_
@@ -98,6 +100,26 @@ gla_status gla_fwd_chunked(const void *q, const void *k, const void *v, const fl
                            int B, int T, int H, int dk, int dv, int num_seqs, int chunk_size,
                            gla_dtype in_dtype, gla_dtype out_dtype, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/*
+ * The same forward for fixed per-head decays (Laplace 3B on AWS Trainium2,
+ * "Decay schedule": each head's decay is set at initialisation on a
+ * geometric schedule and not learned), so there is no per-token gate stream:
+ * every token of head h has l_t = log_lambda[h].
+ *
+ *   log_lambda [H] fp32 device array of natural-log decays ln(lambda_h).
+ *
+ * Every other argument, the workspace (gla_fwd_chunked_workspace_size with
+ * the same sizes), the supported sizes and the errors are as in
+ * gla_fwd_chunked; results equal gla_fwd_chunked with g[b, t, h] =
+ * log_lambda[h] up to rounding.
+ */
+gla_status gla_fwd_chunked_fixed_decay(const void *q, const void *k, const void *v,
+                                       const float *log_lambda, const float *S0,
+                                       const int32_t *cu_seqlens, void *o, float *S_T, int B,
+                                       int T, int H, int dk, int dv, int num_seqs,
+                                       int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
+                                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Backward of gla_fwd_chunked (training; Laplace 3B on AWS Trainium2,

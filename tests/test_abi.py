@@ -20,7 +20,8 @@ def header_functions():
 def test_header_declares_the_boundary():
     assert header_functions() == ["gla_bwd_chunked", "gla_bwd_chunked_workspace_size",
                                   "gla_decode_step", "gla_decode_step_slots", "gla_fwd_chunked",
-                                  "gla_fwd_chunked_workspace_size", "gla_status_string"]
+                                  "gla_fwd_chunked_fixed_decay", "gla_fwd_chunked_workspace_size",
+                                  "gla_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -36,13 +37,15 @@ def test_status_strings():
     assert _lib.status_string(99) == "GLA_UNKNOWN_STATUS"
 
 
-def _fwd(**kw):
+def _fwd(fixed=False, **kw):
     a = dict(q=None, k=None, v=None, g=None, S0=None, cu=None, o=None, ST=None, B=1, T=64, H=1,
              dk=64, dv=64, N=1, C=64, ind=_lib.GLA_BF16, outd=_lib.GLA_F32, ws=None, wsb=0)
     a.update(kw)
-    return _lib.load().gla_fwd_chunked(a["q"], a["k"], a["v"], a["g"], a["S0"], a["cu"], a["o"],
-                                       a["ST"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["N"],
-                                       a["C"], a["ind"], a["outd"], a["ws"], a["wsb"], None)
+    lib = _lib.load()
+    fn = lib.gla_fwd_chunked_fixed_decay if fixed else lib.gla_fwd_chunked
+    return fn(a["q"], a["k"], a["v"], a["g"], a["S0"], a["cu"], a["o"], a["ST"], a["B"], a["T"],
+              a["H"], a["dk"], a["dv"], a["N"], a["C"], a["ind"], a["outd"], a["ws"], a["wsb"],
+              None)
 
 
 FAKE = 1 << 40  # never dereferenced: every call below fails validation first
@@ -56,6 +59,8 @@ def test_fwd_rejects_bad_arguments_before_launch():
     assert _fwd(N=2, **P) == _lib.GLA_ERR_INVALID_ARGUMENT            # N != B without cu
     assert _fwd(dk=96, **P) == _lib.GLA_ERR_UNSUPPORTED
     assert _fwd(dv=192, **P) == _lib.GLA_ERR_UNSUPPORTED
+    assert _fwd(dk=192, dv=96, **P) == _lib.GLA_ERR_UNSUPPORTED
+    assert _fwd(dk=96, dv=192, B=0, N=0, **P) == _lib.GLA_OK  # the Laplace head shape is accepted
     assert _fwd(C=32, **P) == _lib.GLA_ERR_UNSUPPORTED
     assert _fwd(**{**P, "q": None}) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert _fwd(**{**P, "o": P["q"] + 64}) == _lib.GLA_ERR_INVALID_ARGUMENT  # o overlaps q
@@ -63,6 +68,18 @@ def test_fwd_rejects_bad_arguments_before_launch():
     # zero heads or zero sequences: nothing to do
     assert _fwd(H=0, **P) == _lib.GLA_OK
     assert _fwd(B=0, N=0, **P) == _lib.GLA_OK
+
+
+def test_fixed_decay_fwd_rejects_bad_arguments_before_launch():
+    P = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30),
+             o=FAKE + (4 << 30), H=4)
+    assert _fwd(True, B=-1, **P) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert _fwd(True, dk=96, **P) == _lib.GLA_ERR_UNSUPPORTED
+    assert _fwd(True, C=256, **P) == _lib.GLA_ERR_UNSUPPORTED
+    assert _fwd(True, **{**P, "g": None}) == _lib.GLA_ERR_INVALID_ARGUMENT
+    # log_lambda holds H = 4 floats: an o that starts at its last one overlaps it
+    assert _fwd(True, **{**P, "o": P["g"] + 12}) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert _fwd(True, H=0, **{k: v for k, v in P.items() if k != "H"}) == _lib.GLA_OK
 
 
 def test_fwd_requires_workspace_when_planned():
@@ -90,6 +107,8 @@ def test_decode_rejects_bad_arguments_before_launch():
         *ptrs, N, H, dk, dv, ind, _lib.GLA_F32, None)
     assert call(base, N=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call(base, dk=96) == _lib.GLA_ERR_UNSUPPORTED
+    assert call(base, dk=192, dv=96) == _lib.GLA_ERR_UNSUPPORTED
+    assert call(base, dk=96, dv=192, N=0) == _lib.GLA_OK  # the Laplace head shape is accepted
     assert call(base, ind=5) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call([None] + base[1:]) == _lib.GLA_ERR_INVALID_ARGUMENT
     bad = list(base)

@@ -37,7 +37,7 @@ def _run_chain(N, H, dk, dv, steps, dtype, out_dtype, seed=7, sample=None):
     return worst_o, worst_S
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128), (96, 192)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_decode_small(dk, dv, dtype):
     import torch

@@ -51,7 +51,7 @@ def run_slots(P, H, dk, dv, slots, dtype, out_dtype=None, seed=3, steps=2):
     return worst_o, eS
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128), (96, 192)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_slots_match_dense_on_gathered_states(dk, dv, dtype):
     gu.say(f"decode slots dk={dk} dv={dv} {dtype}")
