@@ -98,7 +98,7 @@ def warm_up(fn, steps, seconds):
 # kernel that runs the headline forward at each chunk size, and the sources
 # whose hash keys its committed counter record
 FWD_KERNELS = {
-    64: ("chunk_bf16_w8_kernel<128,float,false>",
+    64: ("chunk_bf16_w8_kernel<128,4,float,false>",
          ["chunk_bf16_w8.hip", "bf16_blocks.h", "gla_common.h"]),
     128: ("chunk_bf16_kernel<128,128,float,false>",
           ["chunk_bf16.hip", "bf16_blocks.h", "gla_common.h"]),
@@ -368,7 +368,8 @@ def bench_laplace(args):
                    "H": H, "dk": dk, "dv": dv, "in_dtype": "bf16", "out_dtype": "f32",
                    "decays": "fixed geometric schedule, half-lives 1 .. 2048 tokens"},
         "forward": fwd,
-        "forward_kernel": "chunk_bf16_kernel<C,96,float,false>",
+        "forward_kernel": {"c64": "chunk_bf16_w8_kernel<96,6,float,false>",
+                           "c128": "chunk_bf16_kernel<128,96,float,false>"},
         "forward_algorithmic_bytes": alg_fixed,
         "decode": {"N": N, "kernel_ms": round(kern_ms, 5), "gbs": round(gbs, 1),
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg_dec,

@@ -48,6 +48,11 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f3
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+// 16 x 16 x 16 step: lane (m, g) holds k-slots 4g .. 4g+3 of A row m and of B column m.
+__device__ __forceinline__ f32x4 mfma16k16(const u32x2 &a, const u32x2 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                   __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
 
 __device__ __forceinline__ WorkItem bf_item_for(const WorkItem *items, int it, int T) {
   if (items) return items[it];
@@ -82,6 +87,14 @@ __device__ __forceinline__ int qk_off(int r, int col) {
 __device__ __forceinline__ int v_off(int r, int col) {
   return r * kBfSlice + ((((col >> 3) ^ r) & 7) << 3) + (col & 7);
 }
+// V tiles of SW columns: 64 as above; 96 (twelve chunks per row) swizzled like
+// the 96-wide Q/K rows.
+template <int SW>
+__device__ __forceinline__ int v_off_sw(int r, int col) {
+  static_assert(SW == 64 || SW == 96, "slice width");
+  if constexpr (SW == 64) return v_off(r, col);
+  else return r * SW + (((col >> 3) ^ qk_swz<96>(r)) << 3) + (col & 7);
+}
 
 __device__ __forceinline__ u32x2 lds_tr16(const uint16_t *p) {
   const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
@@ -105,9 +118,15 @@ __device__ __forceinline__ u32x2 lds_tr16_nowait(const uint16_t *p) {
 __device__ __forceinline__ void lds_wait(u32x4 &a, u32x4 &b) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
 }
+__device__ __forceinline__ void lds_wait(u32x4 &a, u32x4 &b, u32x4 &c) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c));
+}
 // Order values behind an lgkmcnt wait that already happened (e.g. in a barrier).
 __device__ __forceinline__ void lds_after_wait(u32x4 &a, u32x4 &b, u32x4 &c, u32x4 &d) {
   asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ void lds_after_wait(u32x4 &a, u32x4 &b, u32x4 &c) {
+  asm volatile("" : "+v"(a), "+v"(b), "+v"(c));
 }
 // Tell the compiler's wait insertion that every counter is drained (emits a
 // wait that is a no-op at run time when placed after barrier_all()).

@@ -506,19 +506,15 @@ hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_
                              const FwdDims &d, const WorkItem *items, const int *n_items,
                              int grid_items, float *slots, float *slot_gamma, bool state_pass,
                              hipStream_t stream) {
-  // 64-token chunks run on the eight-wavefront kernel; this file's four-wavefront
-  // kernel serves 128-token chunks (whose tiles leave no LDS for eight wavefronts)
-  // and the 96-wide key dimension.
-  if (d.dk == 96) {  // 96 x 192 heads run here at both chunk sizes
-    if (d.C == 64)
-      return launch_bf_c<64, 96>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
-                                 slots, slot_gamma, state_pass, stream);
-    return launch_bf_c<128, 96>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
-                                slots, slot_gamma, state_pass, stream);
-  }
+  // 64-token chunks run on the eight- (twelve-) wavefront kernel; this file's
+  // four-wavefront kernel serves 128-token chunks (whose tiles leave no LDS for
+  // more wavefronts).
   if (d.C == 64)
     return launch_chunk_bf16_c64(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
                                  slots, slot_gamma, state_pass, stream);
+  if (d.dk == 96)
+    return launch_bf_c<128, 96>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
+                                slots, slot_gamma, state_pass, stream);
   if (d.dk == 128)
     return launch_bf_c<128, 128>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items,
                                  grid_items, slots, slot_gamma, state_pass, stream);

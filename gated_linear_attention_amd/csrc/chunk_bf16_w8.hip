@@ -23,6 +23,12 @@
 // other's waits. Data movement (HBM -> LDS buffer loads into swizzled,
 // double-buffered tiles; LDS transpose reads; hi/lo bf16 splits of P, S and
 // kappa . V) is the same as in chunk_bf16.hip.
+//
+// The same kernel serves the 96 x 192 heads of Laplace 3B ("GLA mixer") with
+// six column groups: twelve wavefronts (three per SIMD) over a 96-column slice,
+// so a head is two slices. Each wavefront then holds 48 state rows, and the
+// state read over its half of d_k takes one 32-deep and one 16-deep
+// matrix-core step; ten wavefronts compute one score tile each.
 #include "bf16_blocks.h"
 
 namespace gla {
@@ -30,40 +36,43 @@ namespace gla {
 namespace {
 
 constexpr int kW8C = 64;      // chunk size of this kernel
-constexpr int kW8Waves = 8;
 
-template <int DK, bool SP>
+// NCG column groups of 16: 2 NCG wavefronts over a slice of 16 NCG state columns.
+template <int DK, int NCG, bool SP>
 struct W8Lds {
   static constexpr int C = kW8C;
+  static constexpr int NW = 2 * NCG;  // wavefronts
+  static constexpr int SW = 16 * NCG; // state columns of the slice
   static constexpr int QR = SP ? 1 : C;
   static constexpr int PP = C + 8;  // row pitch (bf16) of P
   uint16_t q[2][QR * DK];
   uint16_t k[2][C * DK];
-  uint16_t v[2][C * kBfSlice];
+  uint16_t v[2][C * SW];
   uint16_t phi[QR * PP];
   uint16_t plo[QR * PP];
-  f32x4 xbuf[SP ? 1 : kW8Waves][2][64];  // partial outputs handed to the partner wavefront
-  u32x4 kvx[kW8Waves][2][64];            // kappa . V (hi, lo) for the partner's 32 keys
-  float lgb[3][C];                       // log-gates, loaded two chunks ahead
-  float gb2[kW8Waves][C];   // per wavefront: in-chunk prefix sums of the log-gates, log2 units
-  float glam[kW8Waves][C];  // 2^(b2_i)
-  float gkap[kW8Waves][C];  // 2^(b2_last - b2_j)
+  f32x4 xbuf[SP ? 1 : NW][2][64];  // partial outputs handed to the partner wavefront
+  u32x4 kvx[NW][2][64];            // kappa . V (hi, lo) for the partner's 32 keys
+  float lgb[3][C];                 // log-gates, loaded two chunks ahead
+  float gb2[NW][C];   // per wavefront: in-chunk prefix sums of the log-gates, log2 units
+  float glam[NW][C];  // 2^(b2_i)
+  float gkap[NW][C];  // 2^(b2_last - b2_j)
 };
 
-// HBM -> LDS copy of one chunk into stage st, done by the four wavefronts of
-// row half 0 (the other four, whose chain per chunk is longer, only store
-// outputs). Tiles are swizzled as in ChunkLoader (chunk_bf16.hip). The row
+// HBM -> LDS copy of one chunk into stage st, done by the wavefronts of row
+// half 0 (the others, whose chain per chunk is longer, only store outputs). Tiles are swizzled as in ChunkLoader (chunk_bf16.hip). The row
 // pointers advance by one chunk per next() call, so a chunk costs a few scalar
 // adds and one clamp of the descriptor ranges. The log-gates go to a
 // three-slot ring two chunks ahead of their use.
-template <int DK, bool SP>
+template <int DK, int NCG, bool SP>
 struct W8Loader {
+  using LDS = W8Lds<DK, NCG, SP>;
   static constexpr int C = kW8C;
-  static constexpr int LW = 4;  // loading wavefronts
+  static constexpr int LW = NCG;  // loading wavefronts
+  static constexpr int SW = LDS::SW;
   static constexpr int CPR = DK / 8;
-  static constexpr int QB = C * DK * 2 / 1024;  // 1 KB blocks per Q/K tile (8 or 16)
+  static constexpr int QB = C * DK * 2 / 1024;  // 1 KB blocks per Q/K tile (8, 12 or 16)
   static constexpr int RPB = 1024 / (DK * 2);
-  static constexpr int VB = C * kBfSlice * 2 / 1024;  // 8
+  static constexpr int VB = C * SW * 2 / 1024;  // 8 or 12
   static_assert(QB % LW == 0 && VB % LW == 0, "blocks per loading wavefront");
   const uint16_t *qp, *kp, *vp;  // first row (this head / slice) of the next chunk to load
   const float *gp;               // first gate of the next gate chunk to load
@@ -97,7 +106,7 @@ struct W8Loader {
     const uint32_t last = (uint32_t)(min(C, tok_end - t0) - 1);
     rk = make_rsrc(kp, last * qk_row + DK * 2);
     if (!SP) rq = make_rsrc(qp, last * qk_row + DK * 2);
-    rv = make_rsrc(vp, last * v_row + kBfSlice * 2);
+    rv = make_rsrc(vp, last * v_row + SW * 2);
     qp += qk_step;
     kp += qk_step;
     vp += v_step;
@@ -118,36 +127,50 @@ struct W8Loader {
 #pragma unroll
     for (int i = 0; i < QB / LW; ++i) {
       const int blk = wave * (QB / LW) + i;
-      const int row = blk * RPB + lane / CPR;
-      const int c = (lane % CPR) ^ (row & (CPR - 1));
+      int row, c;
+      if constexpr (DK == 96) {  // rows straddle the 1 KB blocks: map the linear chunk index
+        const int e = blk * 64 + lane;
+        row = e / CPR;
+        c = (e % CPR) ^ qk_swz<DK>(row);
+      } else {
+        row = blk * RPB + lane / CPR;
+        c = (lane % CPR) ^ (row & (CPR - 1));
+      }
       buffer_load_to_lds(r, (lds_u32 *)&dst[st][blk * 512], 16, row * qk_row + c * 16, 0, 0, 0);
     }
   }
-  __device__ __forceinline__ void k_part(W8Lds<DK, SP> &s, int wave, int lane) {
+  __device__ __forceinline__ void k_part(LDS &s, int wave, int lane) {
     if (active) qk_part(s.k, rk, wave, lane);
   }
-  __device__ __forceinline__ void q_part(W8Lds<DK, SP> &s, int wave, int lane) {
+  __device__ __forceinline__ void q_part(LDS &s, int wave, int lane) {
     if (!SP && active) qk_part(s.q, rq, wave, lane);
   }
-  __device__ __forceinline__ void v_part(W8Lds<DK, SP> &s, int wave, int lane) {
+  __device__ __forceinline__ void v_part(LDS &s, int wave, int lane) {
     if (!active || wave >= LW) return;
 #pragma unroll
     for (int i = 0; i < VB / LW; ++i) {
       const int blk = wave * (VB / LW) + i;
-      const int r = blk * 8 + lane / 8;
-      const int c = (lane % 8) ^ (r & 7);
+      int r, c;
+      if constexpr (SW == 64) {
+        r = blk * 8 + lane / 8;
+        c = (lane % 8) ^ (r & 7);
+      } else {
+        const int e = blk * 64 + lane;
+        r = e / 12;
+        c = (e % 12) ^ qk_swz<96>(r);
+      }
       buffer_load_to_lds(rv, (lds_u32 *)&s.v[st][blk * 512], 16, r * v_row + c * 16, 0, 0, 0);
     }
   }
-  __device__ __forceinline__ void g_part(W8Lds<DK, SP> &s, int wave, int lane, int slot) {
+  __device__ __forceinline__ void g_part(LDS &s, int wave, int lane, int slot) {
     if (g_active && wave == LW - 1)
       buffer_load_to_lds(rg, (lds_u32 *)&s.lgb[slot][0], 4, lane * g_row, 0, 0, 0);
   }
 };
 
-template <int DK, bool SP>
+template <int DK, int NCG, bool SP>
 struct W8Wave {
-  using LDS = W8Lds<DK, SP>;
+  using LDS = W8Lds<DK, NCG, SP>;
   static constexpr int C = kW8C;
   static constexpr int PP = LDS::PP;
   static constexpr int NTILE = 10;     // lower-triangular 16x16 score tiles of a 64-token chunk
@@ -220,24 +243,27 @@ struct W8Wave {
 
 }  // namespace
 
-template <int DK, typename Tout, bool SP>
-__global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
+template <int DK, int NCG, typename Tout, bool SP>
+__global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ lg, const float *__restrict__ S0,
     float *__restrict__ ST, Tout *__restrict__ o, const WorkItem *__restrict__ items,
     const int *__restrict__ n_items, float *__restrict__ slots, float *__restrict__ slot_gamma,
     int T, int H, int gts, int DV, int n_pairs) {
-  using Wv = W8Wave<DK, SP>;
+  using Wv = W8Wave<DK, NCG, SP>;
   using LDS = typename Wv::LDS;
+  using Loader = W8Loader<DK, NCG, SP>;
   constexpr int C = kW8C;
   constexpr int PP = LDS::PP;
+  constexpr int SW = LDS::SW;
   constexpr int HALF = DK / 2;    // state rows per wavefront
   constexpr int NTH = DK / 32;    // 16-row state tiles per wavefront
   constexpr int NKH = DK / 64;    // 32-deep k-steps over the wavefront's half of d_k
+  constexpr bool QREM = DK % 64 != 0;  // and one 16-deep step (d_k = 96)
   __shared__ LDS s;
 
   // Block -> (pair = item * H + head, column slice); slices of a pair share an XCD.
-  const int n_slices = DV / kBfSlice;
+  const int n_slices = DV / SW;
   const int per_round = 8 * n_slices;
   const int full = (n_pairs * n_slices) / per_round * per_round;
   int pair, slice;
@@ -257,18 +283,31 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   Wv R(s, wave, lane);
-  // Row half 1 has the longer chain per chunk (wavefronts 4 and 5 also compute
-  // the two extra score tiles); let the SIMD arbiter prefer it over row half 0,
-  // which waits at the mid-chunk barrier otherwise.
-  if (wave >= 6)
-    __builtin_amdgcn_s_setprio(2);
-  else if (wave >= 4)
-    __builtin_amdgcn_s_setprio(3);
+  // Row half 1 has the longer chain per chunk (with four column groups,
+  // wavefronts 4 and 5 also compute the two extra score tiles); let the SIMD
+  // arbiter prefer it over row half 0, which waits at the mid-chunk barrier
+  // otherwise.
+  if constexpr (NCG == 4) {
+    if (wave >= 6)
+      __builtin_amdgcn_s_setprio(2);
+    else if (wave >= 4)
+      __builtin_amdgcn_s_setprio(3);
+  } else {
+    if (wave >= NCG) __builtin_amdgcn_s_setprio(2);
+  }
   const int ln = R.ln, lg4 = R.lg4;
-  const int cg = wave & 3, rh = wave >> 2;  // column group, d_k half / row half
+  int cg, rh;  // column group, d_k half / row half
+  if constexpr (NCG == 4) {
+    cg = wave & 3;
+    rh = wave >> 2;
+  } else {
+    cg = wave % NCG;
+    rh = wave / NCG;
+  }
+  const int pw = NCG == 4 ? (wave ^ 4) : (rh ? wave - NCG : wave + NCG);  // partner (cg, 1 - rh)
   const int wcol = 16 * cg;
   const int drow0 = HALF * rh;              // first state row of this wavefront
-  const int col0 = slice * kBfSlice;
+  const int col0 = slice * SW;
   const size_t dkdv = (size_t)DK * DV;
 
   // State half in accumulator layout: S_acc[t][r] = S[drow0 + 16t + 4 lg4 + r][col0 + wcol + ln].
@@ -291,7 +330,7 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
     }
   }
   if (!SP) {
-    for (int i = tid; i < C * PP / 2; i += 512) {
+    for (int i = tid; i < C * PP / 2; i += 128 * NCG) {
       reinterpret_cast<uint32_t *>(s.phi)[i] = 0u;
       reinterpret_cast<uint32_t *>(s.plo)[i] = 0u;
     }
@@ -317,7 +356,7 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
 
 
 
-  W8Loader<DK, SP> ld;
+  Loader ld;
   int t0 = w.tok_begin;
   ld.init(q, k, v, lg, t0, H, gts, h, DV, col0);
   ld.next(t0, w.tok_end, 0);
@@ -340,12 +379,18 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
 
   // key rows of this wavefront's 32 keys (js = rh) and of the partner's
   const int jo = 32 * rh, jx = 32 * (1 - rh);
-  // score tiles: tile `wave` for every wavefront, tiles 8 and 9 also for
-  // wavefronts 4 and 5 (lower triangle of 16x16 tiles, row-major)
-  const int ti1 = tile_ti(wave), tj1 = tile_tj(wave);
-  const bool two_tiles = wave == 4 || wave == 5;
+  // score tiles: tile `wave` (with four column groups every wavefront, and
+  // tiles 8 and 9 also for wavefronts 4 and 5; with six, wavefronts 0 .. 9),
+  // lower triangle of 16x16 tiles, row-major
+  const bool has_tile = NCG == 4 || wave < 10;
+  const int ti1 = tile_ti(has_tile ? wave : 0), tj1 = tile_tj(has_tile ? wave : 0);
+  const bool two_tiles = NCG == 4 && (wave == 4 || wave == 5);
   const int ti2 = 3, tj2 = wave - 2;
-  const f32x4 madd1 = R.tile_mask(ti1, tj1), madd2 = R.tile_mask(ti2, tj2);
+  f32x4 madd1, madd2;  // kept across the loop only with four column groups
+  if constexpr (NCG == 4) {
+    madd1 = R.tile_mask(ti1, tj1);
+    madd2 = R.tile_mask(ti2, tj2);
+  }
 
   for (int ci = 0; t0 < w.tok_end; t0 += C, ++ci) {
     const int n = min(C, w.tok_end - t0);
@@ -366,10 +411,10 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
     const uint16_t *sk = s.k[st];
     const uint16_t *sv = s.v[st];
     const bool has_next = t0 + C < w.tok_end;
-    if (wave < W8Loader<DK, SP>::LW) {  // only the loading wavefronts need descriptors
+    if (wave < Loader::LW) {  // only the loading wavefronts need descriptors
       ld.next(t0 + C, w.tok_end, st ^ 1);
       ld.k_part(s, wave, lane);
-      if (wave == W8Loader<DK, SP>::LW - 1) {
+      if (wave == Loader::LW - 1) {
         ld.gate_next(t0 + 2 * C, w.tok_end);
         ld.g_part(s, wave, lane, g_ld);
       }
@@ -380,8 +425,17 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
       // ---- score tile(s) and the state read over this wavefront's half of
       // d_k for all 64 rows, scheduled together:
       // part[mi][r] = sum over d in the half of S[d][wcol + 4 lg4 + r] Q[16 mi + ln][d]
+      // With six column groups the tile runs on its own before the state read
+      // (the overlapped schedule needs more registers than three wavefronts
+      // per SIMD have).
+      constexpr bool kOverlapTile = NCG == 4;
+      if (!kOverlapTile && has_tile) {
+        typename Wv::TileOps t0;
+        R.tile_read(t0, sq, sk, ti1, tj1);
+        R.tile_store(R.tile_mma(t0), t0, R.tile_mask(ti1, tj1), ti1, tj1);
+      }
       typename Wv::TileOps t1;
-      R.tile_read(t1, sq, sk, ti1, tj1);
+      if (kOverlapTile && has_tile) R.tile_read(t1, sq, sk, ti1, tj1);
       u32x4 qf[NKH][4];
 #pragma unroll
       for (int ks = 0; ks < NKH; ++ks) {
@@ -393,6 +447,14 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
           const u32x2 qb = *reinterpret_cast<const u32x2 *>(&sq[qk_off<DK>(r, d0 + 16 + 4 * lg4)]);
           qf[ks][mi] = u32x4{qa.x, qa.y, qb.x, qb.y};
         }
+      }
+      // the last 16 rows of a 48-row half: slot 4 lg4 + r <-> d = drow0 + 32 NKH + 4 lg4 + r
+      u32x2 qr[QREM ? 4 : 1];
+      if constexpr (QREM) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+          qr[mi] = *reinterpret_cast<const u32x2 *>(
+              &sq[qk_off<DK>(16 * mi + ln, drow0 + 32 * NKH + 4 * lg4)]);
       }
       __builtin_amdgcn_sched_barrier(0);
       // hi/lo bf16 of the state half (A operand), while the reads are in flight:
@@ -409,8 +471,17 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
         sh[ks] = u32x4{h[0], h[1], h[2], h[3]};
         sl[ks] = u32x4{l[0], l[1], l[2], l[3]};
       }
+      u32x2 srh, srl;
+      if constexpr (QREM) {
+        uint32_t h0, l0, h1, l1;
+        split_pk_bf16(S_acc[2 * NKH][0], S_acc[2 * NKH][1], h0, l0);
+        split_pk_bf16(S_acc[2 * NKH][2], S_acc[2 * NKH][3], h1, l1);
+        srh = u32x2{h0, h1};
+        srl = u32x2{l0, l1};
+      }
       __builtin_amdgcn_sched_barrier(0);
-      const f32x4 acc1 = R.tile_mma(t1);
+      f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};
+      if (kOverlapTile && has_tile) acc1 = R.tile_mma(t1);
       f32x4 part[4];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16(sh[0], qf[0][mi], f32x4{0.f, 0.f, 0.f, 0.f});
@@ -418,13 +489,19 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
       for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16(sl[0], qf[0][mi], part[mi]);
       __builtin_amdgcn_sched_barrier(0);
       // the tile's mask and P stores overlap the rest of the state read
-      R.tile_store(acc1, t1, madd1, ti1, tj1);
+      if (kOverlapTile && has_tile) R.tile_store(acc1, t1, madd1, ti1, tj1);
 #pragma unroll
       for (int ks = 1; ks < NKH; ++ks) {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16(sh[ks], qf[ks][mi], part[mi]);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16(sl[ks], qf[ks][mi], part[mi]);
+      }
+      if constexpr (QREM) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16k16(srh, qr[mi], part[mi]);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16k16(srl, qr[mi], part[mi]);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (two_tiles) {
@@ -456,8 +533,8 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
     auto v_frag = [&](int j0) -> u32x4 {
       const int r0 = j0 + 8 * lg4 + (ln >> 2);
       const int c = wcol + 4 * (ln & 3);
-      const u32x2 x0 = lds_tr16_nowait(&sv[v_off(r0, c)]);
-      const u32x2 x1 = lds_tr16_nowait(&sv[v_off(r0 + 4, c)]);
+      const u32x2 x0 = lds_tr16_nowait(&sv[v_off_sw<SW>(r0, c)]);
+      const u32x2 x1 = lds_tr16_nowait(&sv[v_off_sw<SW>(r0 + 4, c)]);
       return u32x4{x0.x, x0.y, x1.x, x1.y};
     };
     u32x4 vf_0 = v_frag(0);   // keys 0..31
@@ -479,33 +556,51 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
     s.kvx[wave][1][lane] = kv_l;
 
     // ---- K^T for the state update, read now and used after the barrier
-    // (A operand: slot 8 lg4 + e <-> key j0 + 8 lg4 + e, row d = drow0 + 16 t + ln)
+    // (A operand: slot 8 lg4 + e <-> key j0 + 8 lg4 + e, row d = drow0 + 16 t + ln).
+    // With six column groups the partner's keys are read after the barrier,
+    // once this wavefront's own keys are in (register budget).
+    constexpr bool kEarlyKx = NCG == 4;
     u32x4 kt_o[NTH], kt_x[NTH];
-#pragma unroll
-    for (int t = 0; t < NTH; ++t) {
+    auto kt_read = [&](int j0, int t) -> u32x4 {
       const int c = drow0 + 16 * t + 4 * (ln & 3);
-      const int ro = jo + 8 * lg4 + (ln >> 2), rx = jx + 8 * lg4 + (ln >> 2);
-      const u32x2 a0 = lds_tr16_nowait(&sk[qk_off<DK>(ro, c)]);
-      const u32x2 a1 = lds_tr16_nowait(&sk[qk_off<DK>(ro + 4, c)]);
-      const u32x2 b0 = lds_tr16_nowait(&sk[qk_off<DK>(rx, c)]);
-      const u32x2 b1 = lds_tr16_nowait(&sk[qk_off<DK>(rx + 4, c)]);
-      kt_o[t] = u32x4{a0.x, a0.y, a1.x, a1.y};
-      kt_x[t] = u32x4{b0.x, b0.y, b1.x, b1.y};
+      const int r = j0 + 8 * lg4 + (ln >> 2);
+      const u32x2 a0 = lds_tr16_nowait(&sk[qk_off<DK>(r, c)]);
+      const u32x2 a1 = lds_tr16_nowait(&sk[qk_off<DK>(r + 4, c)]);
+      return u32x4{a0.x, a0.y, a1.x, a1.y};
+    };
+    if constexpr (kEarlyKx) {
+#pragma unroll
+      for (int t = 0; t < NTH; ++t) {
+        const int c = drow0 + 16 * t + 4 * (ln & 3);
+        const int ro = jo + 8 * lg4 + (ln >> 2), rx = jx + 8 * lg4 + (ln >> 2);
+        const u32x2 a0 = lds_tr16_nowait(&sk[qk_off<DK>(ro, c)]);
+        const u32x2 a1 = lds_tr16_nowait(&sk[qk_off<DK>(ro + 4, c)]);
+        const u32x2 b0 = lds_tr16_nowait(&sk[qk_off<DK>(rx, c)]);
+        const u32x2 b1 = lds_tr16_nowait(&sk[qk_off<DK>(rx + 4, c)]);
+        kt_o[t] = u32x4{a0.x, a0.y, a1.x, a1.y};
+        kt_x[t] = u32x4{b0.x, b0.y, b1.x, b1.y};
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NTH; ++t) kt_o[t] = kt_read(jo, t);
     }
 
     ld.v_part(s, wave, lane);
     barrier_lds();  // P, the partial outputs and kappa . V are complete
-    static_assert(NTH == 4 || NTH == 2, "state tiles per wavefront");
+    static_assert(NTH == 4 || NTH == 3 || NTH == 2, "state tiles per wavefront");
     if constexpr (NTH == 4) {
       lds_after_wait(kt_o[0], kt_o[1], kt_o[2], kt_o[3]);
       lds_after_wait(kt_x[0], kt_x[1], kt_x[2], kt_x[3]);
+    } else if constexpr (NTH == 3) {  // six column groups: the partner's keys come later
+      static_assert(!kEarlyKx, "three state tiles go with six column groups");
+      lds_after_wait(kt_o[0], kt_o[1], kt_o[2]);
     } else {
       lds_after_wait(kt_o[0], kt_o[1], kt_x[0], kt_x[1]);
     }
 
     // operands of P V and of the rest of the state update
-    const u32x4 kx_h = s.kvx[wave ^ 4][0][lane];
-    const u32x4 kx_l = s.kvx[wave ^ 4][1][lane];
+    const u32x4 kx_h = s.kvx[pw][0][lane];
+    const u32x4 kx_l = s.kvx[pw][1][lane];
     // P fragments: block mi0 (rows < 32) needs keys 0..31, block mi1 (rows >= 32) all 64
     u32x4 pf_h[3], pf_l[3];
     f32x4 xp[2];
@@ -514,7 +609,7 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int mi = m ? mi1 : mi0;
-        xp[m] = s.xbuf[wave ^ 4][m][lane];
+        xp[m] = s.xbuf[pw][m][lane];
         lam[m] = s.glam[wave][16 * mi + ln];
       }
 #pragma unroll
@@ -548,6 +643,12 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
       own[1] = mfma16(vf_1, pf_l[2], own[1]);
     }
     // the partner's 32 keys
+    if constexpr (!kEarlyKx) {
+#pragma unroll
+      for (int t = 0; t < NTH; ++t) kt_x[t] = kt_read(jx, t);
+      static_assert(kEarlyKx || NTH == 3, "late partner keys: three state tiles");
+      lds_wait(kt_x[0], kt_x[1], kt_x[2]);
+    }
 #pragma unroll
     for (int t = 0; t < NTH; ++t) S_acc[t] = mfma16(kt_x[t], kx_h, S_acc[t]);
 #pragma unroll
@@ -578,34 +679,35 @@ __global__ __launch_bounds__(512) void chunk_bf16_w8_kernel(
   }
 }
 
-template <int DK, typename Tout, bool SP>
+template <int DK, int NCG, typename Tout, bool SP>
 static hipError_t launch_w8_t(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const float *g, const float *S0, float *S_T, void *o,
                               const FwdDims &d, const WorkItem *items, const int *n_items,
                               int grid_items, float *slots, float *slot_gamma,
                               hipStream_t stream) {
   const long pairs = (long)grid_items * d.H;
-  const long blocks = pairs * (d.dv / kBfSlice);
+  const long blocks = pairs * (d.dv / (16 * NCG));
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_bf16_w8_kernel<DK, Tout, SP>), dim3(blocks), dim3(512), 0, stream,
+  hipLaunchKernelGGL((chunk_bf16_w8_kernel<DK, NCG, Tout, SP>), dim3(blocks), dim3(128 * NCG), 0,
+                     stream,
                      q, k, v, g, S0, S_T, static_cast<Tout *>(o), items, n_items, slots,
                      slot_gamma, d.T, d.H, d.gts, d.dv, (int)pairs);
   return hipGetLastError();
 }
 
-template <int DK>
+template <int DK, int NCG>
 static hipError_t launch_w8_d(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const float *g, const float *S0, float *S_T, void *o, bool out_bf16,
                               const FwdDims &d, const WorkItem *items, const int *n_items,
                               int grid_items, float *slots, float *slot_gamma, bool state_pass,
                               hipStream_t stream) {
   if (state_pass)
-    return launch_w8_t<DK, float, true>(q, k, v, g, S0, S_T, o, d, items, n_items, grid_items,
+    return launch_w8_t<DK, NCG, float, true>(q, k, v, g, S0, S_T, o, d, items, n_items, grid_items,
                                         slots, slot_gamma, stream);
   if (out_bf16)
-    return launch_w8_t<DK, uint16_t, false>(q, k, v, g, S0, S_T, o, d, items, n_items,
+    return launch_w8_t<DK, NCG, uint16_t, false>(q, k, v, g, S0, S_T, o, d, items, n_items,
                                             grid_items, slots, slot_gamma, stream);
-  return launch_w8_t<DK, float, false>(q, k, v, g, S0, S_T, o, d, items, n_items, grid_items,
+  return launch_w8_t<DK, NCG, float, false>(q, k, v, g, S0, S_T, o, d, items, n_items, grid_items,
                                        slots, slot_gamma, stream);
 }
 
@@ -614,10 +716,13 @@ hipError_t launch_chunk_bf16_c64(const uint16_t *q, const uint16_t *k, const uin
                                  bool out_bf16, const FwdDims &d, const WorkItem *items,
                                  const int *n_items, int grid_items, float *slots,
                                  float *slot_gamma, bool state_pass, hipStream_t stream) {
+  if (d.dk == 96)  // 96 x 192 heads: two slices of six column groups
+    return launch_w8_d<96, 6>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
+                              slots, slot_gamma, state_pass, stream);
   if (d.dk == 128)
-    return launch_w8_d<128>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
-                            slots, slot_gamma, state_pass, stream);
-  return launch_w8_d<64>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items, slots,
+    return launch_w8_d<128, 4>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
+                               slots, slot_gamma, state_pass, stream);
+  return launch_w8_d<64, 4>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items, slots,
                          slot_gamma, state_pass, stream);
 }
 

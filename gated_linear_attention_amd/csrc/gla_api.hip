@@ -38,8 +38,12 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int round_up(long x, int m) { return (int)(((x + m - 1) / m) * m); }
 
-// State columns one workgroup of the forward owns (the column "slice").
-int slice_width(gla_dtype in_dtype) { return in_dtype == GLA_BF16 ? 64 : 32; }
+// State columns one workgroup of the forward owns (the column "slice"): 96 for
+// the twelve-wavefront bf16 kernel (d_k = 96, chunk 64), else 64 (bf16) or 32.
+int slice_width(gla_dtype in_dtype, int dk, int C) {
+  if (in_dtype != GLA_BF16) return 32;
+  return dk == 96 && C == 64 ? 96 : 64;
+}
 
 // Tokens per work item. A dense batch with enough (sequence, head, slice)
 // work units to cover every CU runs each sequence whole; otherwise sequences
@@ -47,10 +51,11 @@ int slice_width(gla_dtype in_dtype) { return in_dtype == GLA_BF16 ? 64 : 32; }
 // segments at its per-CU share of the work, so no single long sequence sets
 // the critical path. GLA_SEG_LEN overrides the choice (tuning only; the
 // result does not depend on it beyond rounding).
-int choose_seg_len(int B, int T, int H, int dv, int N, int C, bool has_cu, gla_dtype in_dtype) {
+int choose_seg_len(int B, int T, int H, int dk, int dv, int N, int C, bool has_cu,
+                   gla_dtype in_dtype) {
   long L;
   const char *env = std::getenv("GLA_SEG_LEN");
-  const int n_slices = dv / slice_width(in_dtype);
+  const int n_slices = dv / slice_width(in_dtype, dk, C);
   if (env && std::atoi(env) > 0) {
     L = std::atoi(env);
   } else if (!has_cu) {
@@ -78,7 +83,7 @@ int choose_seg_len(int B, int T, int H, int dv, int N, int C, bool has_cu, gla_d
 bool make_plan(int B, int T, int H, int dk, int dv, int N, int C, bool has_cu,
                gla_dtype in_dtype, PlanLayout &lay) {
   std::memset(&lay, 0, sizeof(lay));
-  const int L = choose_seg_len(B, T, H, dv, N, C, has_cu, in_dtype);
+  const int L = choose_seg_len(B, T, H, dk, dv, N, C, has_cu, in_dtype);
   lay.seg_len = L;
   if (!has_cu) {
     const int nseg = T > 0 ? (T + L - 1) / L : 1;
