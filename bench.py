@@ -371,8 +371,12 @@ def bench_laplace(args):
         "forward_kernel": {"c64": "chunk_bf16_w8_kernel<96,6,float,false>",
                            "c128": "chunk_bf16_kernel<128,96,float,false>"},
         "forward_algorithmic_bytes": alg_fixed,
+        "forward_traffic_c64": measured_traffic("chunk_fwd_bf16_laplace_2k_c64",
+                                                FWD_KERNELS[64][1]),
         "decode": {"N": N, "kernel_ms": round(kern_ms, 5), "gbs": round(gbs, 1),
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg_dec,
+                   "traffic": measured_traffic("decode_step_laplace_1280x16",
+                                               ["decode.hip", "gla_common.h"]),
                    "kernel": "decode_step_rows_kernel<96,192,8,bf16,float>"},
     }
 
