@@ -343,7 +343,18 @@ def bench_laplace(args):
                                                        S_T=S_T), alg_fixed)
     fwd["token_gates_c64"] = timed(
         lambda i: gla.fwd_chunked(tq, tk, tv, tlg, chunk_size=64, o=o, S_T=S_T), alg_gates)
-    del tq, tk, tv, tlg, o, S_T
+
+    # the mixer epilogue on the forward's output: fp32 o, bf16 q, k, v and gate
+    # stream in, bf16 z out (4 tiers of 4 heads)
+    gate = bf(synth.make_epilogue_inputs(B * T, H, dk, dv, seed=w.seed + 2)[4]).view(B, T, H, dv)
+    a, tier_w, tier = synth.make_epilogue_params(H, dk, dv, seed=w.seed + 3)
+    ta = torch.from_numpy(a).to(dev)
+    rms_w = gla.head_rms_weights(torch.from_numpy(tier_w).to(dev), torch.from_numpy(tier).to(dev))
+    z = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    alg_epi = tok_heads * (4 * dv + 2 * dk + 2 * dk + 2 * dv + 2 * dv + 2 * dv)
+    epi = timed(lambda i: gla.mixer_epilogue(o, tq, tk, tv, gate, ta, rms_w, 1e-6, z=z), alg_epi)
+    epi.update({"algorithmic_bytes": alg_epi, "kernel": "mixer_epilogue_kernel<96,192,float,bf16,bf16>"})
+    del tq, tk, tv, tlg, o, S_T, gate, z
 
     # decode: 1,280 sequences x 16 heads of 96 x 192 fp32 state, in place
     N, dsteps = 1280, 20
@@ -371,6 +382,7 @@ def bench_laplace(args):
         "forward_kernel": {"c64": "chunk_bf16_w8_kernel<96,6,float,false>",
                            "c128": "chunk_bf16_kernel<128,96,float,false>"},
         "forward_algorithmic_bytes": alg_fixed,
+        "epilogue": epi,
         "forward_traffic_c64": measured_traffic("chunk_fwd_bf16_laplace_2k_c64",
                                                 FWD_KERNELS[64][1]),
         "decode": {"N": N, "kernel_ms": round(kern_ms, 5), "gbs": round(gbs, 1),

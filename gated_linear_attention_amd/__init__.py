@@ -9,6 +9,7 @@ device memory and the current HIP stream.
     dq, dk, dv, dg, dS0 = bwd_chunked(q, k, v, g, dO, S0=None, cu_seqlens=None, dS_T=None)
     o = decode_step(q, k, v, g, S)          # S updated in place
     o = decode_step_slots(q, k, v, g, S_pool, slots)   # S_pool[slots] updated in place
+    z = mixer_epilogue(o, q, k, v, g_out, a, rms_w, eps)  # self-augmentation, RMSNorm, SiLU gate
 
 Shapes follow the C ABI: q, k [B, T, H, dk]; v [B, T, H, dv]; g [B, T, H]
 fp32 natural-log gates; S0 / S_T [N, H, dk, dv] fp32; cu_seqlens int32 [N+1]
@@ -19,7 +20,8 @@ from __future__ import annotations
 from . import _lib
 from ._lib import GLAError, GLA_BF16, GLA_F32
 
-__all__ = ["fwd_chunked", "fwd_chunked_fixed_decay", "bwd_chunked", "decode_step", "decode_step_slots", "workspace_size",
+__all__ = ["fwd_chunked", "fwd_chunked_fixed_decay", "bwd_chunked", "decode_step",
+           "decode_step_slots", "mixer_epilogue", "head_rms_weights", "workspace_size",
            "GLAError", "library_path"]
 
 
@@ -227,3 +229,54 @@ def decode_step_slots(q, k, v, g, S_pool, slots, out_dtype=None, o=None):
                                    _dtype_code(out_dtype), stream)
     _lib.check(st, "gla_decode_step_slots")
     return o
+
+
+def head_rms_weights(tier_weights, tier):
+    """Per-head RMSNorm weights [H, dv] from one weight row per decay tier
+    ([n_tiers, dv]) and each head's tier ([H] int): the heads of a tier share
+    their row (a gather of parameters, done once per model)."""
+    torch = _torch()
+    return tier_weights.index_select(0, tier.to(torch.long)).contiguous()
+
+
+def mixer_epilogue(o, q, k, v, g, a, rms_w, eps: float = 1e-6, out_dtype=None, z=None):
+    """Token-mixer epilogue: z = RMSNorm_h(o + sigmoid(q.(a*k)) v) * silu(g).
+
+    o, v, g [..., H, dv]; q, k [..., H, dk] (q, k, v, g one dtype); a [H, dk]
+    and rms_w [H, dv] fp32 (head_rms_weights builds rms_w from tier rows).
+    z may be o (in place) when out_dtype is o's dtype; out_dtype defaults to
+    z's dtype when z is given, else to o's. Returns z."""
+    torch = _torch()
+    lib = _lib.load()
+    H, dv = o.shape[-2], o.shape[-1]
+    dk = q.shape[-1]
+    dev = o.device
+    lead = tuple(o.shape[:-2])
+    n_tok = 1
+    for x in lead:
+        n_tok *= int(x)
+    _require(o, "o", None, dev)
+    _require(q, "q", None, dev)
+    _require(k, "k", q.dtype, dev)
+    _require(v, "v", q.dtype, dev)
+    _require(g, "g", q.dtype, dev)
+    _require(a, "a", torch.float32, dev)
+    _require(rms_w, "rms_w", torch.float32, dev)
+    if (tuple(q.shape) != lead + (H, dk) or tuple(k.shape) != lead + (H, dk)
+            or tuple(v.shape) != lead + (H, dv) or tuple(g.shape) != lead + (H, dv)
+            or tuple(a.shape) != (H, dk) or tuple(rms_w.shape) != (H, dv)):
+        raise ValueError("inconsistent o/q/k/v/g/a/rms_w shapes")
+    if out_dtype is None:
+        out_dtype = o.dtype if z is None else z.dtype
+    if z is None:
+        z = torch.empty(lead + (H, dv), dtype=out_dtype, device=dev)
+    _require(z, "z", out_dtype, dev)
+    if tuple(z.shape) != lead + (H, dv):
+        raise ValueError("z has the wrong shape")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.gla_mixer_epilogue(_ptr(o), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(a),
+                                _ptr(rms_w), float(eps), _ptr(z), n_tok, H, dk, dv,
+                                _dtype_code(o.dtype), _dtype_code(q.dtype),
+                                _dtype_code(out_dtype), stream)
+    _lib.check(st, "gla_mixer_epilogue")
+    return z

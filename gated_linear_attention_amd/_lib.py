@@ -52,6 +52,8 @@ def load():
     lib.gla_decode_step.restype = i
     lib.gla_decode_step_slots.argtypes = [vp] * 7 + [i] * 5 + [i, i, vp]
     lib.gla_decode_step_slots.restype = i
+    lib.gla_mixer_epilogue.argtypes = [vp] * 7 + [ctypes.c_float, vp] + [i] * 4 + [i, i, i, vp]
+    lib.gla_mixer_epilogue.restype = i
     _lib = lib
     return lib
 

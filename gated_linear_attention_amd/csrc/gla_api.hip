@@ -469,4 +469,34 @@ gla_status gla_decode_step_slots(const void *q, const void *k, const void *v, co
   return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
+gla_status gla_mixer_epilogue(const void *o, const void *q, const void *k, const void *v,
+                              const void *g, const float *a, const float *rms_w, float eps,
+                              void *z, int n_tokens, int H, int dk, int dv, gla_dtype o_dtype,
+                              gla_dtype in_dtype, gla_dtype out_dtype, void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (n_tokens < 0 || H < 0) return GLA_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(o_dtype) || !valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return GLA_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.f) || eps > 3.4e38f) return GLA_ERR_INVALID_ARGUMENT;  // NaN, negative, inf
+  if (!fwd_dims(dk, dv)) return GLA_ERR_UNSUPPORTED;
+  const size_t rows = (size_t)n_tokens * H;
+  if (rows == 0) return GLA_OK;
+  if (rows > (size_t)INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
+  if (!o || !q || !k || !v || !g || !a || !rms_w || !z) return GLA_ERR_INVALID_ARGUMENT;
+  const size_t es = dtype_size(in_dtype);
+  const size_t bo = rows * dv * dtype_size(o_dtype), bqk = rows * dk * es, bv = rows * dv * es;
+  const size_t ba = (size_t)H * dk * 4, bw = (size_t)H * dv * 4;
+  const size_t bz = rows * dv * dtype_size(out_dtype);
+  const bool in_place = z == o && o_dtype == out_dtype;
+  if ((!in_place && overlaps(z, bz, o, bo)) || overlaps(z, bz, q, bqk) ||
+      overlaps(z, bz, k, bqk) || overlaps(z, bz, v, bv) || overlaps(z, bz, g, bv) ||
+      overlaps(z, bz, a, ba) || overlaps(z, bz, rms_w, bw))
+    return GLA_ERR_INVALID_ARGUMENT;
+  const hipError_t err =
+      launch_mixer_epilogue(o, q, k, v, g, a, rms_w, eps, z, (long)rows, H, dk, dv,
+                            o_dtype == GLA_BF16, in_dtype == GLA_BF16, out_dtype == GLA_BF16,
+                            stream);
+  return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -113,4 +113,10 @@ hipError_t launch_dgate(const void *q, const void *k, const float *dq, const flo
                         float *dl, float *dS0, const int32_t *cu, int N, int T, int H, int DK,
                         int DV, bool in_bf16, hipStream_t stream);
 
+// Token-mixer epilogue (epilogue.hip): n_rows = tokens x heads rows.
+hipError_t launch_mixer_epilogue(const void *o, const void *q, const void *k, const void *v,
+                                 const void *g, const float *a, const float *w, float eps,
+                                 void *z, long n_rows, int H, int dk, int dv, bool o_bf16,
+                                 bool in_bf16, bool out_bf16, hipStream_t stream);
+
 }  // namespace gla

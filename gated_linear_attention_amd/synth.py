@@ -36,6 +36,8 @@ __all__ = [
     "varlen_lengths",
     "laplace_decay_schedule",
     "fixed_log_decays",
+    "make_epilogue_params",
+    "make_epilogue_inputs",
 ]
 
 
@@ -209,3 +211,31 @@ def laplace_decay_schedule(H: int = 16, t_min: float = 1.0, t_max: float = 2048.
     h = np.arange(H, dtype=np.float64)
     half_life = t_min * (t_max / t_min) ** (h / (H - 1))
     return -np.log(2.0) / half_life
+
+
+def make_epilogue_params(H: int, dk: int, dv: int, *, seed: int, n_tiers: int = 4,
+                         a_std: float = 0.1):
+    """Mixer-epilogue parameters: a [H, dk] ~ N(0, a_std^2) fp32 (0 at the
+    page's initialisation; a_std = 0 gives that), tier weights [n_tiers, dv]
+    ~ 1 + N(0, 0.1^2) fp32, and tier [H]: consecutive groups of H / n_tiers
+    heads."""
+    rng = np.random.default_rng(seed)
+    a = _normal(rng, (H, dk), a_std) if a_std > 0 else np.zeros((H, dk), np.float32)
+    tier_w = (1.0 + _normal(rng, (n_tiers, dv), 0.1)).astype(np.float32)
+    tier = (np.arange(H) * n_tiers // H).astype(np.int32)
+    return a, tier_w, tier
+
+
+def make_epilogue_inputs(n_tok: int, H: int, dk: int, dv: int, *, seed: int,
+                         dtype: str = "bf16"):
+    """(o, q, k, v, g) for an epilogue call on n_tok tokens: o [n_tok, H, dv]
+    ~ N(0, 1) fp32 (a readout); q, k, v as the forward's; g (gate stream)
+    ~ N(0, 1), in `dtype`."""
+    rng = np.random.default_rng(seed)
+    o = _normal(rng, (n_tok, H, dv))
+    q = _store(_normal(rng, (n_tok, H, dk)), dtype)
+    k = _store(_normal(rng, (n_tok, H, dk), 1.0 / math.sqrt(dk)), dtype)
+    v = _store(_normal(rng, (n_tok, H, dv)), dtype)
+    g = _store(_normal(rng, (n_tok, H, dv)), dtype)
+    return o, q, k, v, g
+

@@ -191,6 +191,36 @@ gla_status gla_decode_step_slots(const void *q, const void *k, const void *v, co
                                  int H, int dk, int dv, gla_dtype in_dtype, gla_dtype out_dtype,
                                  void *stream);
 
+/*
+ * Token-mixer epilogue around the readout (Laplace 3B on AWS Trainium2,
+ * "GLA mixer"), in one pass: per token t and head h,
+ *
+ *   o'  = o + sigmoid(sum_i q_i a[h,i] k_i) v          (self-augmentation;
+ *                                                        a = 0 adds v / 2)
+ *   z   = o' / sqrt(mean_j o'_j^2 + eps) * rms_w[h] * silu(g),
+ *   silu(x) = x * sigmoid(x)
+ *
+ * i.e. the head's RMSNorm over its d_v outputs (the heads of one decay tier
+ * pass the same weight row) and the SiLU output gate. The output projection
+ * that follows on the page is not part of this call.
+ *
+ *   o        [n_tokens, H, dv]  o_dtype (the forward's or decode's output)
+ *   q, k     [n_tokens, H, dk]  in_dtype
+ *   v, g     [n_tokens, H, dv]  in_dtype (g: the head's slice of the gate stream)
+ *   a        [H, dk]  fp32 self-augmentation scales
+ *   rms_w    [H, dv]  fp32 RMSNorm weights per head
+ *   eps      finite, >= 0
+ *   z        [n_tokens, H, dv]  out_dtype; may be o itself when out_dtype ==
+ *            o_dtype (in place), must not overlap anything else.
+ *
+ * Sizes: (dk, dv) as the forward. n_tokens = B * T for a [B, T, H, d] batch,
+ * or N for one decode step.
+ */
+gla_status gla_mixer_epilogue(const void *o, const void *q, const void *k, const void *v,
+                              const void *g, const float *a, const float *rms_w, float eps,
+                              void *z, int n_tokens, int H, int dk, int dv, gla_dtype o_dtype,
+                              gla_dtype in_dtype, gla_dtype out_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,7 @@ def test_header_declares_the_boundary():
     assert header_functions() == ["gla_bwd_chunked", "gla_bwd_chunked_workspace_size",
                                   "gla_decode_step", "gla_decode_step_slots", "gla_fwd_chunked",
                                   "gla_fwd_chunked_fixed_decay", "gla_fwd_chunked_workspace_size",
-                                  "gla_status_string"]
+                                  "gla_mixer_epilogue", "gla_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -167,3 +167,26 @@ def test_decode_slots_rejects_bad_arguments_before_launch():
     assert call(o=FAKE + 4 * G + 64) == _lib.GLA_ERR_INVALID_ARGUMENT   # o inside the pool
     assert call(slots=FAKE + 4 * G + 64) == _lib.GLA_ERR_INVALID_ARGUMENT  # slots inside the pool
     assert call(N=0) == _lib.GLA_OK
+
+
+def test_epilogue_rejects_bad_arguments_before_launch():
+    lib = _lib.load()
+    P = [FAKE + (i << 30) for i in range(7)]  # o, q, k, v, g, a, rms_w
+    Z = FAKE + (8 << 30)
+    F32, BF = _lib.GLA_F32, _lib.GLA_BF16
+    call = lambda p=P, z=Z, eps=1e-6, n=16, H=2, dk=64, dv=64, od=F32, ind=BF, outd=F32: \
+        lib.gla_mixer_epilogue(*p, eps, z, n, H, dk, dv, od, ind, outd, None)
+    assert call(n=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(od=3) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(eps=-1.0) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(eps=float("nan")) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(eps=float("inf")) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(dk=96) == _lib.GLA_ERR_UNSUPPORTED
+    assert call(dk=96, dv=192, n=0) == _lib.GLA_OK
+    assert call(p=[None] + P[1:]) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(z=None) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(z=P[1] + 64) == _lib.GLA_ERR_INVALID_ARGUMENT      # z overlaps q
+    assert call(z=P[5]) == _lib.GLA_ERR_INVALID_ARGUMENT           # z overlaps a
+    assert call(z=P[0] + 4) == _lib.GLA_ERR_INVALID_ARGUMENT       # z partly over o
+    assert call(z=P[0], outd=BF) == _lib.GLA_ERR_INVALID_ARGUMENT  # in place needs o's dtype
+    assert call(H=0) == _lib.GLA_OK
