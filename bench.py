@@ -393,6 +393,71 @@ def bench_laplace(args):
     }
 
 
+def bench_decode_layers(args, layers=24, batches=(20, 1280)):
+    """One decode step of a Laplace-shaped mixer stack (24 layers of 16 heads,
+    96 x 192; per layer the slot-indexed decode against its own state pool and
+    the mixer epilogue), run eagerly call by call and as one captured HIP
+    graph, for a replica-sized batch of 20 sequences and for 1,280."""
+    import torch
+
+    import gated_linear_attention_amd as gla
+    from gated_linear_attention_amd import synth
+
+    H, dk, dv = 16, 96, 192
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    a, tier_w, tier = synth.make_epilogue_params(H, dk, dv, seed=77)
+    ta = torch.from_numpy(a).to(dev)
+    rms_w = gla.head_rms_weights(torch.from_numpy(tier_w).to(dev), torch.from_numpy(tier).to(dev))
+    lam = torch.from_numpy(synth.fixed_log_decays(H)).to(dev)
+    out = {"layers": layers, "config": {"H": H, "dk": dk, "dv": dv, "in_dtype": "bf16",
+                                        "state": "f32 pool per layer", "z_dtype": "bf16"}}
+    for N in batches:
+        pools = [torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev).normal_(0.0, 0.02)
+                 for _ in range(layers)]
+        slots = torch.randperm(N, device=dev).to(torch.int32)
+        qkv = [(torch.randn((N, H, dk), device=dev).to(bf),
+                (torch.randn((N, H, dk), device=dev) / dk ** 0.5).to(bf),
+                torch.randn((N, H, dv), device=dev).to(bf),
+                torch.randn((N, H, dv), device=dev).to(bf)) for _ in range(layers)]
+        lg = lam.expand(N, H).contiguous()
+        o = [torch.empty((N, H, dv), dtype=torch.float32, device=dev) for _ in range(layers)]
+        z = [torch.empty((N, H, dv), dtype=bf, device=dev) for _ in range(layers)]
+
+        def step(i=0):
+            for l in range(layers):
+                q, k, v, g = qkv[l]
+                gla.decode_step_slots(q, k, v, lg, pools[l], slots, o=o[l])
+                gla.mixer_epilogue(o[l], q, k, v, g, ta, rms_w, 1e-6, z=z[l])
+
+        warm_up(step, 3, min(args.warm_seconds, 0.3))
+        steps = 20
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        eager = (time.perf_counter() - t0) / steps
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        replay = (time.perf_counter() - t0) / steps
+        state_bytes = layers * N * H * dk * dv * 4 * 2
+        out[f"N{N}"] = {"eager_ms": round(eager * 1e3, 4), "graph_ms": round(replay * 1e3, 4),
+                        "tokens_per_s_graph": round(N / replay, 1),
+                        "state_gbs_graph": round(state_bytes / replay / 1e9, 1)}
+        del pools, qkv, o, z, graph
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(host_set, target_s=10.0, min_wall=3.0):
     """Time the fp64 C oracle on a bounded sample of the headline workload:
     all 8 sequences over a subset of heads, sized to about target_s seconds."""
@@ -442,6 +507,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-laplace", action="store_true")
+    ap.add_argument("--no-decode-layers", action="store_true")
     ap.add_argument("--chunk", type=int, default=64, choices=[64, 128])
     ap.add_argument("--stream-reference", action="store_true",
                     help="only time two plain streams over the decode state's size (1.342 GB "
@@ -500,6 +566,11 @@ def main():
         log("laplace shape: building inputs")
         lap = bench_laplace(args)
         log(f"laplace: fwd {lap['forward']} decode {lap['decode']['gbs']} GB/s")
+    layers = None
+    if not args.no_decode_layers:
+        log("decode layers: building pools")
+        layers = bench_decode_layers(args)
+        log(f"decode layers: {layers}")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the fp64 oracle")
@@ -527,6 +598,7 @@ def main():
         "backward": bwd,
         "decode": dec,
         "laplace": lap,
+        "decode_layers": layers,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
