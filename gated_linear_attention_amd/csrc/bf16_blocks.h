@@ -62,7 +62,9 @@ __device__ __forceinline__ WorkItem bf_item_for(const WorkItem *items, int it, i
   w.seq = it;
   w.state_in = -1;
   w.state_out = -1;
-  w.pad0 = w.pad1 = w.pad2 = 0;
+  w.seq_begin = w.tok_begin;
+  w.seq_end = w.tok_end;
+  w.pad = 0;
   return w;
 }
 

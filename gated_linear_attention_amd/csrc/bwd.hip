@@ -9,11 +9,12 @@
 //    (dO, v, k) and initial state S0^T;
 //  * the adjoint A_u = dL/dS_u obeys A_u = g_{u+1} A_{u+1} + q_u^T dO_u from
 //    A_{end-1} = q^T dO + dS_T: a forward recurrence in reversed time whose
-//    gate at reversed position tau is l_{end-tau} (and 0 at tau = 0). With
-//    tokens reversed inside each sequence, dv_u = k_u A_u is the forward
-//    with (q, k, v) := (k, q, dO) from dS_T, and dk_u = v_u A_u^T the forward
-//    with (q, k, v) := (v, dO, q) from dS_T^T; the first of these ends in A_0,
-//    and dS0 = g_0 A_0;
+//    gate at reversed position tau is l_{end-tau} (and 0 at tau = 0). The
+//    forward kernels run it in place (their time-reversed mode reads each
+//    sequence bottom-up and writes outputs back to the original rows):
+//    dv_u = k_u A_u is that run with (q, k, v) := (k, q, dO) from dS_T, and
+//    dk_u = v_u A_u^T the run with (q, k, v) := (v, dO, q) from dS_T^T; the
+//    first of these ends in A_0, and dS0 = g_0 A_0;
 //  * with B_u the cumulative log-gate, dL/dB_u = q_u.dq_u - k_u.dk_u plus
 //    <dS_T, S_T> at a sequence's last token, and dl_t is the sum of dL/dB_u
 //    over u >= t in the same sequence.
@@ -23,53 +24,6 @@
 namespace gla {
 
 namespace {
-
-// [start, end) of the sequence holding flattened token p.
-__device__ __forceinline__ void seq_of(int p, const int32_t *cu, int N, int T, int &s, int &e) {
-  if (!cu) {
-    s = (p / T) * T;
-    e = s + T;
-    return;
-  }
-  int lo = 0, hi = N;  // largest n with cu[n] <= p
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= p) lo = mid;
-    else hi = mid;
-  }
-  s = cu[lo];
-  e = cu[lo + 1];
-}
-
-// dst[p] = src[s + e - 1 - p] row by row (one token row = row_bytes, a
-// multiple of 16): tokens reversed inside every sequence. An involution.
-__global__ __launch_bounds__(256) void reverse_rows_kernel(const char *__restrict__ src,
-                                                           char *__restrict__ dst,
-                                                           const int32_t *__restrict__ cu, int N,
-                                                           int T, int n_tok, int row_bytes) {
-  const int p = blockIdx.x;
-  if (p >= n_tok) return;
-  int s, e;
-  seq_of(p, cu, N, T, s, e);
-  const int from = s + e - 1 - p;
-  const u32x4 *a = reinterpret_cast<const u32x4 *>(src + (size_t)from * row_bytes);
-  u32x4 *b = reinterpret_cast<u32x4 *>(dst + (size_t)p * row_bytes);
-  for (int i = threadIdx.x; i < row_bytes / 16; i += 256) b[i] = a[i];
-}
-
-// Gates of the reversed-time adjoint recurrence: at reversed position tau of
-// a sequence [s, e), l_hat = 0 for tau = 0 and l[e - tau] otherwise.
-__global__ __launch_bounds__(256) void reversed_gates_kernel(const float *__restrict__ lg,
-                                                             float *__restrict__ out,
-                                                             const int32_t *__restrict__ cu, int N,
-                                                             int T, int n_tok, int H) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (long)n_tok * H) return;
-  const int p = (int)(i / H), h = (int)(i % H);
-  int s, e;
-  seq_of(p, cu, N, T, s, e);
-  out[i] = p == s ? 0.f : lg[(size_t)(s + e - p) * H + h];
-}
 
 // out[m] = in[m]^T for m = 0 .. count-1 matrices of rows x cols (fp32).
 __global__ __launch_bounds__(256) void transpose_kernel(const float *__restrict__ in,
@@ -182,24 +136,6 @@ __global__ __launch_bounds__(256) void gate_scan_kernel(
 }
 
 }  // namespace
-
-hipError_t launch_reverse_rows(const void *src, void *dst, const int32_t *cu, int N, int T,
-                               int n_tok, int row_bytes, hipStream_t stream) {
-  if (n_tok == 0) return hipSuccess;
-  hipLaunchKernelGGL(reverse_rows_kernel, dim3(n_tok), dim3(256), 0, stream,
-                     static_cast<const char *>(src), static_cast<char *>(dst), cu, N, T, n_tok,
-                     row_bytes);
-  return hipGetLastError();
-}
-
-hipError_t launch_reversed_gates(const float *lg, float *out, const int32_t *cu, int N, int T,
-                                 int n_tok, int H, hipStream_t stream) {
-  const long total = (long)n_tok * H;
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(reversed_gates_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     stream, lg, out, cu, N, T, n_tok, H);
-  return hipGetLastError();
-}
 
 hipError_t launch_transpose(const float *in, float *out, int count, int rows, int cols,
                             hipStream_t stream) {

@@ -72,7 +72,9 @@ struct BfLds {
 // three parts (K; Q; V and the gates) spread over the previous chunk's
 // compute, so the four wavefronts do not queue all their memory instructions
 // on the CU's address unit at once.
-template <int C, int DK, bool SP>
+// REV: the time-reversed run of the backward (rows read bottom-up, gates
+// shifted by one; see W8Loader in chunk_bf16_w8.hip).
+template <int C, int DK, bool SP, bool REV = false>
 struct ChunkLoader {
   static constexpr int CPR = DK / 8;                  // 16-byte chunks per Q/K row
   static constexpr int QB = C * DK * 2 / 1024;        // 1 KB blocks per Q/K tile
@@ -80,20 +82,31 @@ struct ChunkLoader {
   static constexpr int VB = C * kBfSlice * 2 / 1024;  // 1 KB blocks of the V slice (8 rows each)
   i32x4 rq, rk, rv, rg;
   uint32_t qk_row, v_row, g_row;
-  int st;
+  int st, n_ld;
   bool active;
+  static constexpr int kFar = 0x7fff0000;  // an offset past any descriptor range
 
   __device__ __forceinline__ void setup(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                         const float *lg, int t0, int tok_end, int H, int gts,
-                                        int h, int DV, int col0, int stage) {
+                                        int h, int DV, int col0, int stage, int sb = 0,
+                                        int se = 0) {
     active = t0 < tok_end;
     st = stage;
     if (!active) return;
     const int n = min(C, tok_end - t0);
-    const size_t tok0 = (size_t)t0 * H + h;
+    n_ld = n;
     qk_row = (uint32_t)H * DK * 2;
     v_row = (uint32_t)H * DV * 2;
     g_row = (uint32_t)gts * 4;
+    if constexpr (REV) {  // lowest memory row sb + se - t0 - n; gates one row later
+      const size_t lo = (size_t)(sb + se - t0 - n), tok0 = lo * H + h;
+      rk = make_rsrc(k + tok0 * DK, (n - 1) * qk_row + DK * 2);
+      if (!SP) rq = make_rsrc(q + tok0 * DK, (n - 1) * qk_row + DK * 2);
+      rv = make_rsrc(v + tok0 * DV + col0, (n - 1) * v_row + kBfSlice * 2);
+      rg = make_rsrc(lg + (lo + 1) * gts + h, (n - 1) * g_row + (t0 == sb ? 0 : 4));
+      return;
+    }
+    const size_t tok0 = (size_t)t0 * H + h;
     rk = make_rsrc(k + tok0 * DK, (n - 1) * qk_row + DK * 2);
     if (!SP) rq = make_rsrc(q + tok0 * DK, (n - 1) * qk_row + DK * 2);
     rv = make_rsrc(v + tok0 * DV + col0, (n - 1) * v_row + kBfSlice * 2);
@@ -109,7 +122,9 @@ struct ChunkLoader {
       const int e = blk * 64 + lane;
       const int row = e / CPR;
       const int c = (e % CPR) ^ qk_swz<DK>(row);
-      buffer_load_to_lds(r, (lds_u32 *)&dst[st][blk * 512], 16, row * qk_row + c * 16, 0, 0, 0);
+      int vo = row * qk_row + c * 16;
+      if constexpr (REV) vo = row < n_ld ? (n_ld - 1 - row) * qk_row + c * 16 : kFar;
+      buffer_load_to_lds(r, (lds_u32 *)&dst[st][blk * 512], 16, vo, 0, 0, 0);
     }
   }
   __device__ __forceinline__ void k_part(BfLds<C, DK, SP> &s, int wave, int lane) {
@@ -125,12 +140,18 @@ struct ChunkLoader {
       const int blk = wave * (VB / 4) + i;
       const int r = blk * 8 + lane / 8;
       const int c = (lane % 8) ^ (r & 7);
-      buffer_load_to_lds(rv, (lds_u32 *)&s.v[st][blk * 512], 16, r * v_row + c * 16, 0, 0, 0);
+      int vo = r * v_row + c * 16;
+      if constexpr (REV) vo = r < n_ld ? (n_ld - 1 - r) * v_row + c * 16 : kFar;
+      buffer_load_to_lds(rv, (lds_u32 *)&s.v[st][blk * 512], 16, vo, 0, 0, 0);
     }
     if (wave == 0) {
 #pragma unroll
-      for (int i = 0; i < C / 64; ++i)
-        buffer_load_to_lds(rg, (lds_u32 *)&s.lg[st][64 * i], 4, (64 * i + lane) * g_row, 0, 0, 0);
+      for (int i = 0; i < C / 64; ++i) {
+        const int j = 64 * i + lane;
+        int vo = j * g_row;
+        if constexpr (REV) vo = j < n_ld ? (n_ld - 1 - j) * g_row : kFar;
+        buffer_load_to_lds(rg, (lds_u32 *)&s.lg[st][64 * i], 4, vo, 0, 0, 0);
+      }
     }
   }
   __device__ __forceinline__ void all(BfLds<C, DK, SP> &s, int wave, int lane) {
@@ -240,7 +261,7 @@ struct BfRun {
   }
 };
 
-template <int C, int DK, typename Tout, bool SP>
+template <int C, int DK, typename Tout, bool SP, bool REV = false>
 __global__ __launch_bounds__(256) void chunk_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ lg, const float *__restrict__ S0,
@@ -315,6 +336,15 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
   // O[16 mi + ln][wcol + 4 lg4 + r]: one 16-byte piece of a row.
   auto store_prev = [&]() {
     if (SP || t_prev < 0) return;
+    if constexpr (REV) {  // logical row t is memory row sb + se - 1 - t
+      const int r0 = w.seq_begin + w.seq_end - 1 - t_prev - ln;
+      Tout *ob = o + (size_t)h * DV + col0 + wcol + 4 * lg4;
+#pragma unroll
+      for (int mi = 0; mi < NM; ++mi)
+        if (16 * mi + ln < n_prev)
+          store4_from_f32(ob + (size_t)(r0 - 16 * mi) * H * DV, O_prev[mi]);
+      return;
+    }
     Tout *ob = o + ((size_t)(t_prev + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
     const size_t rs16 = (size_t)16 * H * DV;  // 16 rows
 #pragma unroll
@@ -322,9 +352,9 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
       if (16 * mi + ln < n_prev) store4_from_f32(ob + mi * rs16, O_prev[mi]);
   };
 
-  ChunkLoader<C, DK, SP> ld;
+  ChunkLoader<C, DK, SP, REV> ld;
   int t0 = w.tok_begin;
-  ld.setup(q, k, v, lg, t0, w.tok_end, H, gts, h, DV, col0, 0);
+  ld.setup(q, k, v, lg, t0, w.tok_end, H, gts, h, DV, col0, 0, w.seq_begin, w.seq_end);
   ld.all(s, wave, lane);
 
   for (int ci = 0; t0 < w.tok_end; t0 += C, ++ci) {
@@ -336,7 +366,8 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
     const uint16_t *sq = s.q[SP ? 0 : st];
     const uint16_t *sk = s.k[st];
     const uint16_t *sv = s.v[st];
-    if (NST == 2) ld.setup(q, k, v, lg, t1, w.tok_end, H, gts, h, DV, col0, st ^ 1);
+    if (NST == 2)
+      ld.setup(q, k, v, lg, t1, w.tok_end, H, gts, h, DV, col0, st ^ 1, w.seq_begin, w.seq_end);
     if (NST == 2) ld.k_part(s, wave, lane);
 
     const float gam = R.gates(st, n, lsum);
@@ -447,7 +478,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
     }
     if (NST == 1 && t1 < w.tok_end) {
       barrier_lds();  // every wavefront is done with the single stage
-      ld.setup(q, k, v, lg, t1, w.tok_end, H, gts, h, DV, col0, 0);
+      ld.setup(q, k, v, lg, t1, w.tok_end, H, gts, h, DV, col0, 0, w.seq_begin, w.seq_end);
       ld.all(s, wave, lane);
     }
   }
@@ -470,7 +501,7 @@ __global__ __launch_bounds__(256) void chunk_bf16_kernel(
   }
 }
 
-template <int C, int DK, typename Tout, bool SP>
+template <int C, int DK, typename Tout, bool SP, bool REV = false>
 static hipError_t launch_bf_t(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const float *g, const float *S0, float *S_T, void *o,
                               const FwdDims &d, const WorkItem *items, const int *n_items,
@@ -479,7 +510,7 @@ static hipError_t launch_bf_t(const uint16_t *q, const uint16_t *k, const uint16
   const long pairs = (long)grid_items * d.H;
   const long blocks = pairs * (d.dv / kBfSlice);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_bf16_kernel<C, DK, Tout, SP>), dim3(blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL((chunk_bf16_kernel<C, DK, Tout, SP, REV>), dim3(blocks), dim3(256), 0, stream,
                      q, k, v, g, S0, S_T, static_cast<Tout *>(o), items, n_items, slots,
                      slot_gamma, d.T, d.H, d.gts, d.dv, (int)pairs);
   return hipGetLastError();
@@ -491,6 +522,18 @@ static hipError_t launch_bf_c(const uint16_t *q, const uint16_t *k, const uint16
                               const FwdDims &d, const WorkItem *items, const int *n_items,
                               int grid_items, float *slots, float *slot_gamma, bool state_pass,
                               hipStream_t stream) {
+  if (d.rev) {  // time-reversed runs of the backward: fp32 outputs, d_k in {64, 128}
+    if constexpr (DK == 96) {
+      return hipErrorInvalidValue;
+    } else {
+      if (state_pass)
+        return launch_bf_t<C, DK, float, true, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
+                                                     grid_items, slots, slot_gamma, stream);
+      if (out_bf16) return hipErrorInvalidValue;
+      return launch_bf_t<C, DK, float, false, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
+                                                    grid_items, slots, slot_gamma, stream);
+    }
+  }
   if (state_pass)
     return launch_bf_t<C, DK, float, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
                                            grid_items, slots, slot_gamma, stream);

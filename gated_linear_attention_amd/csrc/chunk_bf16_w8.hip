@@ -59,11 +59,18 @@ struct W8Lds {
 };
 
 // HBM -> LDS copy of one chunk into stage st, done by the wavefronts of row
-// half 0 (the others, whose chain per chunk is longer, only store outputs). Tiles are swizzled as in ChunkLoader (chunk_bf16.hip). The row
-// pointers advance by one chunk per next() call, so a chunk costs a few scalar
-// adds and one clamp of the descriptor ranges. The log-gates go to a
-// three-slot ring two chunks ahead of their use.
-template <int DK, int NCG, bool SP>
+// half 0 (the others, whose chain per chunk is longer, only store outputs).
+// Tiles are swizzled as in ChunkLoader (chunk_bf16.hip). The row pointers
+// advance by one chunk per next() call, so a chunk costs a few scalar adds and
+// one clamp of the descriptor ranges. The log-gates go to a three-slot ring
+// two chunks ahead of their use.
+//
+// REV (time-reversed run, used by the backward): logical token t of a
+// sequence [sb, se) is memory row sb + se - 1 - t, so a chunk's rows are read
+// bottom-up into the same LDS layout, and the gate at logical position
+// u = t - sb is the log-gate of memory row se - u (u >= 1; 0 at u = 0). Rows
+// past a chunk's end get an offset beyond the descriptor range (zeros).
+template <int DK, int NCG, bool SP, bool REV = false>
 struct W8Loader {
   using LDS = W8Lds<DK, NCG, SP>;
   static constexpr int C = kW8C;
@@ -81,10 +88,23 @@ struct W8Loader {
   uint32_t qk_row, v_row, g_row;   // bytes per token
   int st;
   bool active, g_active;
+  // REV: head / slice bases, sb + se, the sequence start, and the current chunk's row count
+  const uint16_t *qh, *kh, *vh;
+  const float *gh;
+  int se_sum, seq_b, n_ld, n_g;
+  static constexpr int kFar = 0x7fff0000;  // an offset past any descriptor range
 
   __device__ __forceinline__ void init(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                        const float *lg, int t0, int H, int gts, int h, int DV,
-                                       int col0) {
+                                       int col0, int sb = 0, int se = 0) {
+    if constexpr (REV) {
+      qh = q + (size_t)h * DK;
+      kh = k + (size_t)h * DK;
+      vh = v + (size_t)h * DV + col0;
+      gh = lg + h;
+      se_sum = sb + se;
+      seq_b = sb;
+    }
     const size_t tok0 = (size_t)t0 * H + h;
     qp = q + tok0 * DK;
     kp = k + tok0 * DK;
@@ -104,6 +124,13 @@ struct W8Loader {
     st = stage;
     if (!active) return;
     const uint32_t last = (uint32_t)(min(C, tok_end - t0) - 1);
+    if constexpr (REV) {  // lowest memory row of the chunk: sb + se - t0 - n
+      n_ld = (int)last + 1;
+      const size_t lo = (size_t)(se_sum - t0 - n_ld);
+      qp = qh + lo * (qk_row / 2);
+      kp = kh + lo * (qk_row / 2);
+      vp = vh + lo * (v_row / 2);
+    }
     rk = make_rsrc(kp, last * qk_row + DK * 2);
     if (!SP) rq = make_rsrc(qp, last * qk_row + DK * 2);
     rv = make_rsrc(vp, last * v_row + SW * 2);
@@ -118,6 +145,12 @@ struct W8Loader {
     g_active = t0 < tok_end;
     if (!g_active) return;
     const uint32_t last = (uint32_t)(min(C, tok_end - t0) - 1);
+    if constexpr (REV) {  // rows se - u for u = t0 - sb + n - 1 .. t0 - sb; u = 0 is out of range
+      n_g = (int)last + 1;
+      rg = make_rsrc(gh + (size_t)(se_sum - t0 - n_g + 1) * (g_row / 4),
+                     last * g_row + (t0 == seq_b ? 0 : 4));
+      return;
+    }
     rg = make_rsrc(gp, last * g_row + 4);
     gp += g_step;
   }
@@ -136,7 +169,9 @@ struct W8Loader {
         row = blk * RPB + lane / CPR;
         c = (lane % CPR) ^ (row & (CPR - 1));
       }
-      buffer_load_to_lds(r, (lds_u32 *)&dst[st][blk * 512], 16, row * qk_row + c * 16, 0, 0, 0);
+      int vo = row * qk_row + c * 16;
+      if constexpr (REV) vo = row < n_ld ? (n_ld - 1 - row) * qk_row + c * 16 : kFar;
+      buffer_load_to_lds(r, (lds_u32 *)&dst[st][blk * 512], 16, vo, 0, 0, 0);
     }
   }
   __device__ __forceinline__ void k_part(LDS &s, int wave, int lane) {
@@ -159,12 +194,17 @@ struct W8Loader {
         r = e / 12;
         c = (e % 12) ^ qk_swz<96>(r);
       }
-      buffer_load_to_lds(rv, (lds_u32 *)&s.v[st][blk * 512], 16, r * v_row + c * 16, 0, 0, 0);
+      int vo = r * v_row + c * 16;
+      if constexpr (REV) vo = r < n_ld ? (n_ld - 1 - r) * v_row + c * 16 : kFar;
+      buffer_load_to_lds(rv, (lds_u32 *)&s.v[st][blk * 512], 16, vo, 0, 0, 0);
     }
   }
   __device__ __forceinline__ void g_part(LDS &s, int wave, int lane, int slot) {
-    if (g_active && wave == LW - 1)
-      buffer_load_to_lds(rg, (lds_u32 *)&s.lgb[slot][0], 4, lane * g_row, 0, 0, 0);
+    if (g_active && wave == LW - 1) {
+      int vo = lane * g_row;
+      if constexpr (REV) vo = lane < n_g ? (n_g - 1 - lane) * g_row : kFar;
+      buffer_load_to_lds(rg, (lds_u32 *)&s.lgb[slot][0], 4, vo, 0, 0, 0);
+    }
   }
 };
 
@@ -243,7 +283,7 @@ struct W8Wave {
 
 }  // namespace
 
-template <int DK, int NCG, typename Tout, bool SP>
+template <int DK, int NCG, typename Tout, bool SP, bool REV = false>
 __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ lg, const float *__restrict__ S0,
@@ -252,7 +292,7 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
     int T, int H, int gts, int DV, int n_pairs) {
   using Wv = W8Wave<DK, NCG, SP>;
   using LDS = typename Wv::LDS;
-  using Loader = W8Loader<DK, NCG, SP>;
+  using Loader = W8Loader<DK, NCG, SP, REV>;
   constexpr int C = kW8C;
   constexpr int PP = LDS::PP;
   constexpr int SW = LDS::SW;
@@ -349,16 +389,23 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
   const size_t rs16 = (size_t)16 * H * DV;
   auto store_out = [&](int tc, int nc, const f32x4 (&own)[2]) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    Tout *ob = o + ((size_t)(tc + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
-    if (16 * mi0 + ln < nc) store4_from_f32(ob + mi0 * rs16, own[0]);
-    if (16 * mi1 + ln < nc) store4_from_f32(ob + mi1 * rs16, own[1]);
+    if constexpr (REV) {  // logical row t is memory row sb + se - 1 - t
+      const int se1 = w.seq_begin + w.seq_end - 1 - tc - ln;
+      Tout *ob = o + ((size_t)h) * DV + col0 + wcol + 4 * lg4;
+      if (16 * mi0 + ln < nc) store4_from_f32(ob + (size_t)(se1 - 16 * mi0) * H * DV, own[0]);
+      if (16 * mi1 + ln < nc) store4_from_f32(ob + (size_t)(se1 - 16 * mi1) * H * DV, own[1]);
+    } else {
+      Tout *ob = o + ((size_t)(tc + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
+      if (16 * mi0 + ln < nc) store4_from_f32(ob + mi0 * rs16, own[0]);
+      if (16 * mi1 + ln < nc) store4_from_f32(ob + mi1 * rs16, own[1]);
+    }
   };
 
 
 
   Loader ld;
   int t0 = w.tok_begin;
-  ld.init(q, k, v, lg, t0, H, gts, h, DV, col0);
+  ld.init(q, k, v, lg, t0, H, gts, h, DV, col0, w.seq_begin, w.seq_end);
   ld.next(t0, w.tok_end, 0);
   ld.k_part(s, wave, lane);
   ld.q_part(s, wave, lane);
@@ -679,7 +726,7 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
   }
 }
 
-template <int DK, int NCG, typename Tout, bool SP>
+template <int DK, int NCG, typename Tout, bool SP, bool REV = false>
 static hipError_t launch_w8_t(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const float *g, const float *S0, float *S_T, void *o,
                               const FwdDims &d, const WorkItem *items, const int *n_items,
@@ -688,7 +735,7 @@ static hipError_t launch_w8_t(const uint16_t *q, const uint16_t *k, const uint16
   const long pairs = (long)grid_items * d.H;
   const long blocks = pairs * (d.dv / (16 * NCG));
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_bf16_w8_kernel<DK, NCG, Tout, SP>), dim3(blocks), dim3(128 * NCG), 0,
+  hipLaunchKernelGGL((chunk_bf16_w8_kernel<DK, NCG, Tout, SP, REV>), dim3(blocks), dim3(128 * NCG), 0,
                      stream,
                      q, k, v, g, S0, S_T, static_cast<Tout *>(o), items, n_items, slots,
                      slot_gamma, d.T, d.H, d.gts, d.dv, (int)pairs);
@@ -701,6 +748,18 @@ static hipError_t launch_w8_d(const uint16_t *q, const uint16_t *k, const uint16
                               const FwdDims &d, const WorkItem *items, const int *n_items,
                               int grid_items, float *slots, float *slot_gamma, bool state_pass,
                               hipStream_t stream) {
+  if constexpr (NCG == 4) {  // time-reversed runs of the backward: fp32 outputs
+    if (d.rev) {
+      if (state_pass)
+        return launch_w8_t<DK, NCG, float, true, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
+                                                       grid_items, slots, slot_gamma, stream);
+      if (out_bf16) return hipErrorInvalidValue;
+      return launch_w8_t<DK, NCG, float, false, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
+                                                      grid_items, slots, slot_gamma, stream);
+    }
+  } else {
+    if (d.rev) return hipErrorInvalidValue;
+  }
   if (state_pass)
     return launch_w8_t<DK, NCG, float, true>(q, k, v, g, S0, S_T, o, d, items, n_items, grid_items,
                                         slots, slot_gamma, stream);

@@ -33,11 +33,16 @@ __device__ __forceinline__ WorkItem item_for(const WorkItem *items, int it, int 
   w.seq = it;
   w.state_in = -1;
   w.state_out = -1;
-  w.pad0 = w.pad1 = w.pad2 = 0;
+  w.seq_begin = w.tok_begin;
+  w.seq_end = w.tok_end;
+  w.pad = 0;
   return w;
 }
 
-template <int C, int DK, typename Tout, bool STATE_PASS>
+// REV: the time-reversed run of the backward: logical token t of a sequence
+// [sb, se) reads and writes memory row sb + se - 1 - t, and its gate is the
+// log-gate of row se - (t - sb) (0 for t = sb).
+template <int C, int DK, typename Tout, bool STATE_PASS, bool REV = false>
 __global__ __launch_bounds__(256) void chunk_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ lg, const float *__restrict__ S0, float *__restrict__ ST,
@@ -66,6 +71,8 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
   const int c0 = slice * DVS;
   const int tid = threadIdx.x;
   const size_t dkdv = (size_t)DK * DV;
+  const int sb = w.seq_begin, se = w.seq_end;
+  auto mrow = [&](int t) -> size_t { return (size_t)(REV ? sb + se - 1 - t : t); };
 
   // initial state slice
   const float *sin = nullptr;
@@ -83,10 +90,21 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
     const int n = min(C, w.tok_end - t0);
     __syncthreads();
     // gates: inclusive scan of the chunk's log-gates (padding rows add 0)
-    if (tid < C) bcum[tid] = (tid < n) ? lg[(size_t)(t0 + tid) * gts + h] : 0.f;
+    if (tid < C) {
+      float x = 0.f;
+      if (tid < n) {
+        if (REV) {
+          const int u = t0 + tid - sb;
+          x = u == 0 ? 0.f : lg[(size_t)(se - u) * gts + h];
+        } else {
+          x = lg[(size_t)(t0 + tid) * gts + h];
+        }
+      }
+      bcum[tid] = x;
+    }
     for (int e = tid; e < C * DVS; e += 256) {
       const int j = e / DVS, c = e % DVS;
-      Vs[j][c] = (j < n) ? v[((size_t)(t0 + j) * H + h) * DV + c0 + c] : 0.f;
+      Vs[j][c] = (j < n) ? v[(mrow(t0 + j) * H + h) * DV + c0 + c] : 0.f;
     }
     for (int off = 1; off < C; off *= 2) {
       __syncthreads();
@@ -116,8 +134,8 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
         for (int e = tid; e < C * KB; e += 256) {
           const int i = e / KB, dd = e % KB;
           const bool ok = i < n;
-          Qb[i][dd] = ok ? q[((size_t)(t0 + i) * H + h) * DK + db + dd] : 0.f;
-          Kb[i][dd] = ok ? k[((size_t)(t0 + i) * H + h) * DK + db + dd] : 0.f;
+          Qb[i][dd] = ok ? q[(mrow(t0 + i) * H + h) * DK + db + dd] : 0.f;
+          Kb[i][dd] = ok ? k[(mrow(t0 + i) * H + h) * DK + db + dd] : 0.f;
         }
         __syncthreads();
 #pragma unroll
@@ -153,7 +171,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
         float a = 0.f;
         for (int j = 0; j <= i; ++j) a += P[i][j] * Vs[j][c];
         const float r = lam[i] * oacc[m] + a;
-        if (i < n) store_from_f32(o, ((size_t)(t0 + i) * H + h) * DV + c0 + c, r);
+        if (i < n) store_from_f32(o, (mrow(t0 + i) * H + h) * DV + c0 + c, r);
       }
     }
     // state advance: S <- gamma S + (kappa K)^T V, one key block at a time
@@ -161,7 +179,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
       __syncthreads();
       for (int e = tid; e < C * KB; e += 256) {
         const int j = e / KB, dd = e % KB;
-        Kb[j][dd] = (j < n) ? k[((size_t)(t0 + j) * H + h) * DK + db + dd] * kap[j] : 0.f;
+        Kb[j][dd] = (j < n) ? k[(mrow(t0 + j) * H + h) * DK + db + dd] * kap[j] : 0.f;
       }
       __syncthreads();
       const float gam = gam_s;
@@ -191,14 +209,14 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
   }
 }
 
-template <int C, int DK, typename Tout, bool SP>
+template <int C, int DK, typename Tout, bool SP, bool REV = false>
 static hipError_t launch_f32_t(const float *q, const float *k, const float *v, const float *g,
                                const float *S0, float *S_T, void *o, const FwdDims &d,
                                const WorkItem *items, const int *n_items, int grid_items,
                                float *slots, float *slot_gamma, hipStream_t stream) {
   const long blocks = (long)grid_items * d.H * (d.dv / kF32Slice);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_f32_kernel<C, DK, Tout, SP>), dim3(blocks), dim3(256), 0, stream, q,
+  hipLaunchKernelGGL((chunk_f32_kernel<C, DK, Tout, SP, REV>), dim3(blocks), dim3(256), 0, stream, q,
                      k, v, g, S0, S_T, static_cast<Tout *>(o), items, n_items, slots, slot_gamma,
                      d.T, d.H, d.gts, d.dv);
   return hipGetLastError();
@@ -210,6 +228,18 @@ static hipError_t launch_f32_c(const float *q, const float *k, const float *v, c
                                const FwdDims &d, const WorkItem *items, const int *n_items,
                                int grid_items, float *slots, float *slot_gamma, bool state_pass,
                                hipStream_t stream) {
+  if (d.rev) {  // time-reversed runs of the backward: fp32 outputs, d_k in {64, 128}
+    if constexpr (DK == 96) {
+      return hipErrorInvalidValue;
+    } else {
+      if (state_pass)
+        return launch_f32_t<C, DK, float, true, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
+                                                      grid_items, slots, slot_gamma, stream);
+      if (out_bf16) return hipErrorInvalidValue;
+      return launch_f32_t<C, DK, float, false, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
+                                                     grid_items, slots, slot_gamma, stream);
+    }
+  }
   if (state_pass)
     return launch_f32_t<C, DK, float, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
                                             grid_items, slots, slot_gamma, stream);

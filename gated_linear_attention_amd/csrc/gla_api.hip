@@ -136,7 +136,7 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
                     const int32_t *cu_seqlens, void *o, float *S_T, int B, int T, int H, int dk,
                     int dv, int N, int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
                     void *workspace, size_t workspace_bytes, hipStream_t stream,
-                    bool fixed_decay) {
+                    bool fixed_decay, bool rev) {
   const bool has_cu = cu_seqlens != nullptr;
   FwdDims d;
   d.B = B;
@@ -147,6 +147,7 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
   d.N = N;
   d.C = chunk_size;
   d.gts = fixed_decay ? 0 : H;
+  d.rev = rev;
   PlanLayout lay;
   const bool planned = make_plan(B, T, H, dk, dv, N, chunk_size, has_cu, in_dtype, lay);
   if (planned && (!workspace || workspace_bytes < lay.total_bytes)) return GLA_ERR_WORKSPACE;
@@ -286,7 +287,7 @@ namespace {
 
 // Workspace layout of the backward (all offsets 256-byte aligned).
 struct BwdLayout {
-  size_t rq, rk, rv, rdo, lhat, s0t, dstt, stt, a0, rdv, rdk, fws, total, fws_bytes;
+  size_t s0t, dstt, stt, a0, fws, total, fws_bytes;
 };
 
 BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int N, int C, bool has_cu,
@@ -300,17 +301,12 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int N, int C, bool has
     off = align256(off + bytes);
     return at;
   };
-  L.rq = take(ntok * dk * es);
-  L.rk = take(ntok * dk * es);
-  L.rv = take(ntok * dv * es);
-  L.rdo = take(ntok * dv * es);
-  L.lhat = take(ntok * 4);
+  (void)ntok;
+  (void)es;
   L.s0t = take(mat);
   L.dstt = take(mat);
   L.stt = take(mat);
   L.a0 = take(mat);
-  L.rdv = take(ntok * dv * 4);
-  L.rdk = take(ntok * dk * 4);
   const size_t f1 = fwd_workspace(B, T, H, dv, dk, N, C, has_cu, in_dtype);
   const size_t f2 = fwd_workspace(B, T, H, dk, dv, N, C, has_cu, in_dtype);
   L.fws_bytes = f1 > f2 ? f1 : f2;
@@ -373,30 +369,14 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   if (!workspace || workspace_bytes < L.total) return GLA_ERR_WORKSPACE;
 
   char *ws = static_cast<char *>(workspace);
-  void *rq = ws + L.rq, *rk = ws + L.rk, *rv = ws + L.rv, *rdo = ws + L.rdo;
-  float *lhat = reinterpret_cast<float *>(ws + L.lhat);
   float *s0t = S0 ? reinterpret_cast<float *>(ws + L.s0t) : nullptr;
   float *dstt = dS_T ? reinterpret_cast<float *>(ws + L.dstt) : nullptr;
   float *stt = reinterpret_cast<float *>(ws + L.stt);
   float *a0 = reinterpret_cast<float *>(ws + L.a0);
-  float *rdv = reinterpret_cast<float *>(ws + L.rdv);
-  float *rdk = reinterpret_cast<float *>(ws + L.rdk);
   void *fws = L.fws_bytes ? ws + L.fws : nullptr;
-  const int ntk = B * T;
-  const int row_qk = H * DK * (int)es, row_v = H * DV * (int)es;
-  hipError_t err = hipSuccess;
-  auto hip_ok = [&](hipError_t e) {
-    err = e;
-    return e == hipSuccess;
-  };
-  // inputs of the reversed-time passes; transposed initial states
-  if (!hip_ok(launch_reverse_rows(q, rq, cu_seqlens, N, T, ntk, row_qk, stream)) ||
-      !hip_ok(launch_reverse_rows(k, rk, cu_seqlens, N, T, ntk, row_qk, stream)) ||
-      !hip_ok(launch_reverse_rows(v, rv, cu_seqlens, N, T, ntk, row_v, stream)) ||
-      !hip_ok(launch_reverse_rows(dO, rdo, cu_seqlens, N, T, ntk, row_v, stream)) ||
-      !hip_ok(launch_reversed_gates(g, lhat, cu_seqlens, N, T, ntk, H, stream)) ||
-      (S0 && !hip_ok(launch_transpose(S0, s0t, N * H, DK, DV, stream))) ||
-      (dS_T && !hip_ok(launch_transpose(dS_T, dstt, N * H, DK, DV, stream))))
+  // transposed initial states
+  if ((S0 && launch_transpose(S0, s0t, N * H, DK, DV, stream) != hipSuccess) ||
+      (dS_T && launch_transpose(dS_T, dstt, N * H, DK, DV, stream) != hipSuccess))
     return GLA_ERR_HIP;
   gla_status st;
   // dq: forward with (q, k, v) = (dO, v, k) on the transposed state; its final
@@ -404,20 +384,17 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   st = fwd_core(dO, v, k, g, s0t, cu_seqlens, dq, stt, B, T, H, DV, DK, N, chunk_size, in_dtype,
                 GLA_F32, fws, L.fws_bytes, stream);
   if (st != GLA_OK) return st;
-  // dv (reversed): (q, k, v) = (k, q, dO) reversed, from dS_T; ends in A_0
-  st = fwd_core(rk, rq, rdo, lhat, dS_T, cu_seqlens, rdv, a0, B, T, H, DK, DV, N, chunk_size,
-                in_dtype, GLA_F32, fws, L.fws_bytes, stream);
+  // dv: the reversed-time run with (q, k, v) = (k, q, dO) from dS_T; ends in A_0
+  st = fwd_core(k, q, dO, g, dS_T, cu_seqlens, dv, a0, B, T, H, DK, DV, N, chunk_size, in_dtype,
+                GLA_F32, fws, L.fws_bytes, stream, false, true);
   if (st != GLA_OK) return st;
-  // dk (reversed): (q, k, v) = (v, dO, q) reversed, from dS_T^T
-  st = fwd_core(rv, rdo, rq, lhat, dstt, cu_seqlens, rdk, nullptr, B, T, H, DV, DK, N, chunk_size,
-                in_dtype, GLA_F32, fws, L.fws_bytes, stream);
+  // dk: the reversed-time run with (q, k, v) = (v, dO, q) from dS_T^T
+  st = fwd_core(v, dO, q, g, dstt, cu_seqlens, dk, nullptr, B, T, H, DV, DK, N, chunk_size,
+                in_dtype, GLA_F32, fws, L.fws_bytes, stream, false, true);
   if (st != GLA_OK) return st;
-  if (!hip_ok(launch_reverse_rows(rdv, dv, cu_seqlens, N, T, ntk, H * DV * 4, stream)) ||
-      !hip_ok(launch_reverse_rows(rdk, dk, cu_seqlens, N, T, ntk, H * DK * 4, stream)) ||
-      !hip_ok(launch_dgate(q, k, dq, dk, g, stt, dstt, a0, dg, dS0, cu_seqlens, N, T, H, DK, DV,
-                           in_dtype == GLA_BF16, stream)))
+  if (launch_dgate(q, k, dq, dk, g, stt, dstt, a0, dg, dS0, cu_seqlens, N, T, H, DK, DV,
+                   in_dtype == GLA_BF16, stream) != hipSuccess)
     return GLA_ERR_HIP;
-  (void)err;
   return GLA_OK;
 }
 

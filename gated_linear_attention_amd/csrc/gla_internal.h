@@ -22,7 +22,8 @@ struct WorkItem {
   int seq;
   int state_in;
   int state_out;
-  int pad0, pad1, pad2;
+  int seq_begin, seq_end;  // the whole sequence's tokens (time-reversed runs map through them)
+  int pad;
 };
 constexpr int kNoStateOut = -2;
 
@@ -57,6 +58,10 @@ struct PlanLayout {
 struct FwdDims {
   int B, T, H, dk, dv, N, C;
   int gts;  // gate token stride in floats: H (log_g [.., T, H]) or 0 (one fixed log-decay per head)
+  // time-reversed run: logical token t of sequence [sb, se) is memory row
+  // sb + se - 1 - t for q, k, v and o, and its gate is log_g[se - (t - sb)]
+  // (0 at t = sb): the adjoint recurrence of the backward
+  bool rev;
 };
 
 // slots == nullptr: state of pair (n, h) is S[n, h]; otherwise S[slots[n], h]
@@ -93,19 +98,17 @@ hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_
                              hipStream_t stream);
 
 // The chunked forward after argument checks (gla_api.hip), and its workspace.
-// g is log_g [.., T, H], or with fixed_decay one log-decay per head [H].
+// g is log_g [.., T, H], or with fixed_decay one log-decay per head [H]. rev
+// runs every sequence in reversed time (FwdDims::rev): o is written in the
+// inputs' order, S0 / S_T are the reversed run's initial and final states.
 gla_status fwd_core(const void *q, const void *k, const void *v, const float *g, const float *S0,
                     const int32_t *cu_seqlens, void *o, float *S_T, int B, int T, int H, int dk,
                     int dv, int N, int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
                     void *workspace, size_t workspace_bytes, hipStream_t stream,
-                    bool fixed_decay = false);
+                    bool fixed_decay = false, bool rev = false);
 size_t fwd_workspace(int B, int T, int H, int dk, int dv, int N, int chunk_size, bool has_cu,
                      gla_dtype in_dtype);
 // Backward helpers (bwd.hip).
-hipError_t launch_reverse_rows(const void *src, void *dst, const int32_t *cu, int N, int T,
-                               int n_tok, int row_bytes, hipStream_t stream);
-hipError_t launch_reversed_gates(const float *lg, float *out, const int32_t *cu, int N, int T,
-                                 int n_tok, int H, hipStream_t stream);
 hipError_t launch_transpose(const float *in, float *out, int count, int rows, int cols,
                             hipStream_t stream);
 hipError_t launch_dgate(const void *q, const void *k, const float *dq, const float *dk,

@@ -142,7 +142,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
         it.seq = n;
         it.state_in = split ? slot_base + s : -1;
         it.state_out = (s == nseg - 1) ? -1 : kNoStateOut;
-        it.pad0 = it.pad1 = it.pad2 = 0;
+        it.seq_begin = start;
+        it.seq_end = start + len;
+        it.pad = 0;
         items[pos] = it;
         if (split && s < nseg - 1) {
           WorkItem si = it;
