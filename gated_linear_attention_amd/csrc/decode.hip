@@ -105,11 +105,16 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const Tin *__restrict_
   }
 }
 
-// The same step for row widths whose 4-column groups do not divide a
-// wavefront (d_v = 192 in Laplace 3B's 96 x 192 heads, "GLA mixer"): RP rows
-// per pass of TPR = d_v / 4 threads each, and the d_k reduction of o through
-// LDS (each thread's partial sum, then one thread per column group adds RP).
-template <int DK, int DV, int RP, typename Tin, typename Tout>
+// The same step with the columns of a (sequence, head) split over
+// workgroups of CW columns each (CW = d_v: one workgroup per pair). Each
+// output column depends only on its own state column, so slices need no
+// reduction between them: RP rows per pass of TPR = CW / 4 threads, and the
+// d_k reduction of o through LDS (each thread's partial sum, then one thread
+// per column group adds RP). Serves row widths whose 4-column groups do not
+// divide a wavefront (d_v = 192 in Laplace 3B's 96 x 192 heads, "GLA mixer")
+// and small batches, whose few (sequence, head) pairs would leave CUs idle or
+// unevenly loaded.
+template <int DK, int DV, int CW, int RP, typename Tin, typename Tout>
 __global__ __launch_bounds__(512) void decode_step_rows_kernel(const Tin *__restrict__ q,
                                                                const Tin *__restrict__ k,
                                                                const Tin *__restrict__ v,
@@ -118,12 +123,14 @@ __global__ __launch_bounds__(512) void decode_step_rows_kernel(const Tin *__rest
                                                                Tout *__restrict__ o,
                                                                const int32_t *__restrict__ slots,
                                                                int P, int H) {
-  constexpr int TPR = DV / 4;
+  constexpr int TPR = CW / 4;
+  constexpr int NS = DV / CW;  // column slices per pair
   constexpr int NP = DK / RP;
-  static_assert(DK % RP == 0 && DV % 4 == 0, "row tiling");
+  static_assert(DK % RP == 0 && DV % CW == 0 && CW % 4 == 0, "row tiling");
   __shared__ f32x4 red[RP][TPR];
 
-  const size_t p = blockIdx.x;
+  const size_t p = blockIdx.x / NS;
+  const int col0 = (int)(blockIdx.x % NS) * CW;
   const int t = threadIdx.x;
   const int c4 = t % TPR;
   const int r0 = t / TPR;
@@ -132,7 +139,7 @@ __global__ __launch_bounds__(512) void decode_step_rows_kernel(const Tin *__rest
     const int slot = slots[p / H];
     if (slot < 0 || slot >= P) {
       if (t < TPR) {
-        Tout *op = o + p * DV + 4 * t;
+        Tout *op = o + p * DV + col0 + 4 * t;
 #pragma unroll
         for (int j = 0; j < 4; ++j) store_from_f32(op, j, 0.f);
       }
@@ -140,24 +147,26 @@ __global__ __launch_bounds__(512) void decode_step_rows_kernel(const Tin *__rest
     }
     sp = (size_t)slot * H + p % H;
   }
-  f32x4 *Sp = reinterpret_cast<f32x4 *>(S + sp * (size_t)(DK * DV));
+  f32x4 *Sp = reinterpret_cast<f32x4 *>(S + sp * (size_t)(DK * DV) + col0);
 
   f32x4 s[NP];
 #pragma unroll
-  for (int i = 0; i < NP; ++i) s[i] = __builtin_nontemporal_load(Sp + (r0 + i * RP) * TPR + c4);
+  for (int i = 0; i < NP; ++i)
+    s[i] = __builtin_nontemporal_load(Sp + (r0 + i * RP) * (DV / 4) + c4);
   const float gate = expf(g[p]);
+  const size_t vc = p * DV + col0 + 4 * c4;
   f32x4 vv;
-  vv.x = load_as_f32(v, p * DV + 4 * c4 + 0);
-  vv.y = load_as_f32(v, p * DV + 4 * c4 + 1);
-  vv.z = load_as_f32(v, p * DV + 4 * c4 + 2);
-  vv.w = load_as_f32(v, p * DV + 4 * c4 + 3);
+  vv.x = load_as_f32(v, vc + 0);
+  vv.y = load_as_f32(v, vc + 1);
+  vv.z = load_as_f32(v, vc + 2);
+  vv.w = load_as_f32(v, vc + 3);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const float kk = load_as_f32(k, p * DK + r0 + i * RP);
     const float qq = load_as_f32(q, p * DK + r0 + i * RP);
     const f32x4 x = gate * s[i] + kk * vv;
-    __builtin_nontemporal_store(x, Sp + (r0 + i * RP) * TPR + c4);
+    __builtin_nontemporal_store(x, Sp + (r0 + i * RP) * (DV / 4) + c4);
     acc += qq * x;
   }
   red[r0][c4] = acc;
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(512) void decode_step_rows_kernel(const Tin *__rest
     f32x4 r = red[0][t];
 #pragma unroll
     for (int i = 1; i < RP; ++i) r += red[i][t];
-    Tout *op = o + p * DV + 4 * t;
+    Tout *op = o + p * DV + col0 + 4 * t;
     store_from_f32(op, 0, r.x);
     store_from_f32(op, 1, r.y);
     store_from_f32(op, 2, r.z);
@@ -183,6 +192,9 @@ struct DecodeArgs {
   int P, H, pairs;
 };
 
+// pairs below this many per CU run as column slices
+constexpr int kSplitPairsPerCu = 2;
+
 template <int DK, int DV, typename Tin, typename Tout>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_step_kernel<DK, DV, Tin, Tout>), dim3(a.pairs), dim3(256), 0, stream,
@@ -192,24 +204,25 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int DK, int DV, int RP, typename Tin, typename Tout>
+template <int DK, int DV, int CW, int RP, typename Tin, typename Tout>
 static hipError_t launch_decode_rows_t(const DecodeArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_step_rows_kernel<DK, DV, RP, Tin, Tout>), dim3(a.pairs),
-                     dim3(RP * DV / 4), 0, stream, static_cast<const Tin *>(a.q),
+  hipLaunchKernelGGL((decode_step_rows_kernel<DK, DV, CW, RP, Tin, Tout>),
+                     dim3((unsigned)a.pairs * (DV / CW)), dim3(RP * CW / 4), 0, stream,
+                     static_cast<const Tin *>(a.q),
                      static_cast<const Tin *>(a.k), static_cast<const Tin *>(a.v), a.g, a.S,
                      static_cast<Tout *>(a.o), a.slots, a.P, a.H);
   return hipGetLastError();
 }
 
-template <int DK, int DV, int RP>
+template <int DK, int DV, int CW, int RP>
 static hipError_t launch_decode_rows_d(const DecodeArgs &a, bool in_bf16, bool out_bf16,
                                        hipStream_t stream) {
   if (in_bf16) {
-    return out_bf16 ? launch_decode_rows_t<DK, DV, RP, uint16_t, uint16_t>(a, stream)
-                    : launch_decode_rows_t<DK, DV, RP, uint16_t, float>(a, stream);
+    return out_bf16 ? launch_decode_rows_t<DK, DV, CW, RP, uint16_t, uint16_t>(a, stream)
+                    : launch_decode_rows_t<DK, DV, CW, RP, uint16_t, float>(a, stream);
   }
-  return out_bf16 ? launch_decode_rows_t<DK, DV, RP, float, uint16_t>(a, stream)
-                  : launch_decode_rows_t<DK, DV, RP, float, float>(a, stream);
+  return out_bf16 ? launch_decode_rows_t<DK, DV, CW, RP, float, uint16_t>(a, stream)
+                  : launch_decode_rows_t<DK, DV, CW, RP, float, float>(a, stream);
 }
 
 template <int DK, int DV>
@@ -225,14 +238,26 @@ static hipError_t launch_decode_d(const DecodeArgs &a, bool in_bf16, bool out_bf
 
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g, float *S,
                          void *o, int N, int H, int dk, int dv, bool in_bf16, bool out_bf16,
-                         const int32_t *slots, int P, hipStream_t stream) {
+                         const int32_t *slots, int P, int n_cu, hipStream_t stream) {
   const long pairs = (long)N * H;
   if (pairs == 0) return hipSuccess;
   const DecodeArgs a{q, k, v, g, S, o, slots, P, H, (int)pairs};
+  if (pairs < (long)kSplitPairsPerCu * n_cu) {  // few pairs: 64- or 32-column slices
+    if (dk == 128 && dv == 128)
+      return launch_decode_rows_d<128, 128, 32, 32>(a, in_bf16, out_bf16, stream);
+    if (dk == 128 && dv == 64)
+      return launch_decode_rows_d<128, 64, 32, 32>(a, in_bf16, out_bf16, stream);
+    if (dk == 64 && dv == 128)
+      return launch_decode_rows_d<64, 128, 32, 32>(a, in_bf16, out_bf16, stream);
+    if (dk == 96 && dv == 192)
+      return launch_decode_rows_d<96, 192, 64, 16>(a, in_bf16, out_bf16, stream);
+    return launch_decode_rows_d<64, 64, 32, 32>(a, in_bf16, out_bf16, stream);
+  }
   if (dk == 128 && dv == 128) return launch_decode_d<128, 128>(a, in_bf16, out_bf16, stream);
   if (dk == 128 && dv == 64) return launch_decode_d<128, 64>(a, in_bf16, out_bf16, stream);
   if (dk == 64 && dv == 128) return launch_decode_d<64, 128>(a, in_bf16, out_bf16, stream);
-  if (dk == 96 && dv == 192) return launch_decode_rows_d<96, 192, 8>(a, in_bf16, out_bf16, stream);
+  if (dk == 96 && dv == 192)
+    return launch_decode_rows_d<96, 192, 192, 8>(a, in_bf16, out_bf16, stream);
   return launch_decode_d<64, 64>(a, in_bf16, out_bf16, stream);
 }
 

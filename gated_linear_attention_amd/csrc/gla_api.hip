@@ -417,7 +417,7 @@ gla_status gla_decode_step(const void *q, const void *k, const void *v, const fl
       overlaps(S, bS, k, bq) || overlaps(S, bS, v, bv) || overlaps(S, bS, g, bg))
     return GLA_ERR_INVALID_ARGUMENT;
   const hipError_t err = launch_decode(q, k, v, g, S, o, N, H, dk, dv, in_dtype == GLA_BF16,
-                                       out_dtype == GLA_BF16, nullptr, 0, stream);
+                                       out_dtype == GLA_BF16, nullptr, 0, cu_count(), stream);
   return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
@@ -442,7 +442,7 @@ gla_status gla_decode_step_slots(const void *q, const void *k, const void *v, co
       overlaps(S_pool, bS, g, bg) || overlaps(S_pool, bS, slots, bs))
     return GLA_ERR_INVALID_ARGUMENT;
   const hipError_t err = launch_decode(q, k, v, g, S_pool, o, N, H, dk, dv, in_dtype == GLA_BF16,
-                                       out_dtype == GLA_BF16, slots, P, stream);
+                                       out_dtype == GLA_BF16, slots, P, cu_count(), stream);
   return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 

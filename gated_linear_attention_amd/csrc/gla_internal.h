@@ -66,9 +66,11 @@ struct FwdDims {
 
 // slots == nullptr: state of pair (n, h) is S[n, h]; otherwise S[slots[n], h]
 // for slots[n] in [0, P), and a padded lane (no state touched, o = 0) else.
+// Batches with fewer than two (sequence, head) pairs per CU (n_cu CUs) split
+// each pair's columns over several workgroups.
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g, float *S,
                          void *o, int N, int H, int dk, int dv, bool in_bf16, bool out_bf16,
-                         const int32_t *slots, int P, hipStream_t stream);
+                         const int32_t *slots, int P, int n_cu, hipStream_t stream);
 
 hipError_t launch_plan(const int32_t *cu_seqlens, const FwdDims &d, const PlanLayout &lay,
                        void *workspace, hipStream_t stream);

@@ -39,10 +39,13 @@ def _run_chain(N, H, dk, dv, steps, dtype, out_dtype, seed=7, sample=None):
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128), (96, 192)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_decode_small(dk, dv, dtype):
+@pytest.mark.parametrize("N", [37, 200])
+def test_decode_small(dk, dv, dtype, N):
+    """37 x 3 pairs run as column slices (fewer than two pairs per CU), 200 x 3
+    with one workgroup per pair."""
     import torch
-    gu.say(f"decode small dk={dk} dv={dv} {dtype}")
-    eo, eS = _run_chain(N=37, H=3, dk=dk, dv=dv, steps=4, dtype=dtype, out_dtype=torch.float32)
+    gu.say(f"decode dk={dk} dv={dv} {dtype} N={N}")
+    eo, eS = _run_chain(N=N, H=3, dk=dk, dv=dv, steps=4, dtype=dtype, out_dtype=torch.float32)
     tol = gu.TOL_BF16 if dtype == "bf16" else gu.TOL_F32
     assert eo <= tol and eS <= tol, (eo, eS)
     assert eo <= 1e-5 and eS <= 1e-6  # fp32 arithmetic on exact inputs

@@ -60,6 +60,19 @@ def test_slots_match_dense_on_gathered_states(dk, dv, dtype):
     assert eo <= 1e-5 and eS <= 1e-6
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (96, 192)])
+def test_slots_many_requests(dk, dv):
+    """200 requests x 3 heads (one workgroup per pair) on a 300-entry pool,
+    every fifth lane padded."""
+    gu.say(f"decode slots, 200 requests dk={dk} dv={dv}")
+    rng = np.random.default_rng(9)
+    slots = [int(x) for x in rng.permutation(300)[:200]]
+    slots = [-1 if n % 5 == 4 else s for n, s in enumerate(slots)]
+    eo, eS = run_slots(P=300, H=3, dk=dk, dv=dv, slots=slots, dtype="bf16")
+    gu.say(f"   o err {eo:.2e}  S err {eS:.2e}")
+    assert eo <= 1e-5 and eS <= 1e-6
+
+
 def test_slots_out_of_range_are_padding():
     gu.say("decode slots out of range")
     eo, eS = run_slots(P=6, H=2, dk=128, dv=128, slots=[6, -5, 2, 1000, 5], dtype="bf16")
