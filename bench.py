@@ -77,7 +77,15 @@ def time_launches(fn, steps, stream):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in ev]
+    time_launches.last = sorted(per)
     return wall, sum(per) / len(per)
+
+
+def percentiles_ms(per):
+    """median, p10, p90 of per-launch times (ms), as bench.py reports them."""
+    n = len(per)
+    pick = lambda f: per[min(n - 1, int(f * (n - 1) + 0.5))]
+    return {"median": round(pick(0.5), 5), "p10": round(pick(0.1), 5), "p90": round(pick(0.9), 5)}
 
 
 def warm_up(fn, steps, seconds):
@@ -137,6 +145,7 @@ def bench_forward(args):
     step = step_at(C)
     n_warm = warm_up(step, args.warmup, args.warm_seconds)
     wall, kern_ms = time_launches(step, args.steps, stream)
+    kern_pct = percentiles_ms(time_launches.last)
     ms_per_step = 1e3 * wall / args.steps
     tokens = B * T
     tok_heads = B * T * H
@@ -167,6 +176,7 @@ def bench_forward(args):
         "tokens": tokens,
         "ms_per_step": ms_per_step,
         "kernel_ms": kern_ms,
+        "kernel_ms_pct": kern_pct,
         "value": tokens / (ms_per_step * 1e-3),
         "config": {"workload": "train_2k chunked forward", "B": B, "T": T, "H": H, "dk": dk,
                    "dv": dv, "chunk": C, "in_dtype": "bf16", "out_dtype": "f32", "S0": "zeros",
@@ -300,6 +310,127 @@ def bench_decode(args):
                        "gbs": round(gbs_s, 1), "frac": round(gbs_s / HBM_PEAK_GBS, 4),
                        "entry": "gla_decode_step_slots"},
     }
+
+
+def _device_inputs(B, T, H, dk, dv, gate_bias, seed, dev):
+    """Seeded device-side draws with the synthetic workloads' distributions
+    (q, v ~ N(0, 1), k ~ N(0, 1/d_k), bf16; log-gates logsigmoid(N(0, 1) +
+    gate_bias)), for shapes too large to draw on the host quickly."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(seed)
+    q = torch.randn((B, T, H, dk), device=dev, generator=g).to(torch.bfloat16)
+    k = (torch.randn((B, T, H, dk), device=dev, generator=g) / dk ** 0.5).to(torch.bfloat16)
+    v = torch.randn((B, T, H, dv), device=dev, generator=g).to(torch.bfloat16)
+    lg = torch.nn.functional.logsigmoid(torch.randn((B, T, H), device=dev, generator=g) + gate_bias)
+    return q, k, v, lg
+
+
+def bench_prefill(args):
+    """The 65,536-token prefill: B=1, H=32, d=128, bf16, S0 ~ N(0, 0.02^2), at
+    both chunk sizes; the forward splits the sequence over the CUs (state
+    pass, combine, output pass)."""
+    import torch
+
+    import gated_linear_attention_amd as gla
+    from gated_linear_attention_amd import synth
+
+    w = synth.WORKLOADS["prefill_64k"]
+    dev = torch.device("cuda:0")
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    q, k, v, lg = _device_inputs(B, T, H, dk, dv, w.gate_bias, w.seed, dev)
+    S0 = torch.empty((B, H, dk, dv), device=dev).normal_(0.0, w.s0_std)
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    S_T = torch.empty_like(S0)
+    stream = torch.cuda.current_stream(dev)
+    tok_heads = B * T * H
+    alg = tok_heads * (2 * dk + 2 * dk + 2 * dv + 4 + 4 * dv) + 2 * B * H * dk * dv * 4
+    out = {"config": {"workload": "prefill_64k", "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
+                      "S0": "N(0, 0.02^2)"}, "algorithmic_bytes": alg}
+    for C in (64, 128):
+        ws = torch.empty(max(1, gla.workspace_size(B, T, H, dk, dv, B, C)), dtype=torch.uint8,
+                         device=dev)
+        fn = lambda i, C=C, ws=ws: gla.fwd_chunked(q, k, v, lg, S0, chunk_size=C, o=o, S_T=S_T,
+                                                   workspace=ws)
+        warm_up(fn, 3, min(args.warm_seconds, 0.3))
+        steps = max(5, args.steps // 5)
+        wall, call_ms = time_launches(fn, steps, stream)
+        gbs = alg / (call_ms * 1e-3) / 1e9
+        # the forward's segment rule: ceil(CUs / units) segments for a dense
+        # batch with fewer (sequence, head, slice) units than CUs
+        units = B * H * dv // 64
+        n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+        segs = 1 if units >= n_cu else -(-n_cu // units)
+        out[f"c{C}"] = {"call_ms": round(call_ms, 4), "tokens_per_s": round(B * T / (wall / steps), 1),
+                        "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "segments_per_sequence": segs, **percentiles_ms(time_launches.last)}
+    return out
+
+
+def bench_varlen(args):
+    """The packed 64-sequence batch (lengths i.i.d. uniform on [128, 8192],
+    H=16, d=128, bf16, per-sequence S0), at both chunk sizes, against a dense
+    batch of about the same token count; with the critical path in chunks."""
+    import numpy as np
+    import torch
+
+    import gated_linear_attention_amd as gla
+    from gated_linear_attention_amd import synth
+
+    w = synth.WORKLOADS["varlen_64"]
+    dev = torch.device("cuda:0")
+    H, dk, dv = w.H, w.dk, w.dv
+    lengths = synth.varlen_lengths(np.random.default_rng(w.seed), w.num_seqs, w.len_lo, w.len_hi)
+    cu_h = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu_h[1:] = np.cumsum(lengths)
+    total = int(cu_h[-1])
+    cu = torch.from_numpy(cu_h).to(dev)
+    q, k, v, lg = _device_inputs(1, total, H, dk, dv, w.gate_bias, w.seed, dev)
+    N = len(lengths)
+    S0 = torch.empty((N, H, dk, dv), device=dev).normal_(0.0, w.s0_std)
+    S_T = torch.empty_like(S0)
+    o = torch.empty((1, total, H, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    steps = max(5, args.steps // 5)
+    tok_heads = total * H
+    alg = tok_heads * (2 * dk + 2 * dk + 2 * dv + 4 + 4 * dv) + 2 * N * H * dk * dv * 4
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = {"config": {"workload": "varlen_64", "sequences": N, "tokens": total, "H": H,
+                      "dk": dk, "dv": dv, "longest": int(lengths.max()),
+                      "shortest": int(lengths.min())}, "algorithmic_bytes": alg}
+    # dense comparison: T = 2048, B = tokens / 2048 rounded
+    Bd = max(1, round(total / 2048))
+    qd, kd, vd, lgd = (x[:, :Bd * 2048].reshape((Bd, 2048) + tuple(x.shape[2:])) for x in (q, k, v, lg))
+    od = torch.empty((Bd, 2048, H, dv), dtype=torch.float32, device=dev)
+    STd = torch.empty((Bd, H, dk, dv), device=dev)
+    for C in (64, 128):
+        ws = torch.empty(max(1, gla.workspace_size(1, total, H, dk, dv, N, C, True)),
+                         dtype=torch.uint8, device=dev)
+        fn = lambda i, C=C, ws=ws: gla.fwd_chunked(q, k, v, lg, S0, cu, chunk_size=C, o=o,
+                                                   S_T=S_T, workspace=ws)
+        warm_up(fn, 3, min(args.warm_seconds, 0.3))
+        wall, call_ms = time_launches(fn, steps, stream)
+        pct = percentiles_ms(time_launches.last)
+        fd = lambda i, C=C: gla.fwd_chunked(qd, kd, vd, lgd, None, chunk_size=C, o=od, S_T=STd)
+        warm_up(fd, 3, min(args.warm_seconds, 0.3))
+        wall_d, _ = time_launches(fd, steps, stream)
+        tps = total / (wall / steps)
+        tps_d = Bd * 2048 / (wall_d / steps)
+        gbs = alg / (call_ms * 1e-3) / 1e9
+        # critical path: the longest work item in chunks (the forward splits a
+        # packed batch's sequences at its per-CU share of the work) against
+        # the chunk steps per CU of a perfectly balanced schedule
+        slices = dv // 64
+        share = max(C, -(-(total * H * slices // n_cu) // C) * C)
+        seg = min(share, 65536)
+        crit = int(-(-min(int(lengths.max()), seg) // C))
+        balanced = sum(-(-int(L) // C) for L in lengths) * H * slices / n_cu
+        out[f"c{C}"] = {"call_ms": round(call_ms, 4), "tokens_per_s": round(tps, 1),
+                        "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "dense_same_tokens_tokens_per_s": round(tps_d, 1),
+                        "efficiency_vs_dense": round(tps / tps_d, 4),
+                        "critical_path_chunks": crit,
+                        "balanced_chunks_per_cu": round(balanced, 1), **pct}
+    return out
 
 
 def bench_laplace(args):
@@ -468,11 +599,16 @@ def cpu_baseline(host_set, target_s=10.0, min_wall=3.0):
     q, k, v, lg = host_set
     B, T, H, dk = q.shape
     pick = lambda a, hs: np.ascontiguousarray(a[:, :, hs])
-    # calibrate on one head of one sequence, single-threaded
-    t0 = time.perf_counter()
-    c_oracle.fwd(pick(q[:1], [0]), pick(k[:1], [0]), pick(v[:1], [0]), pick(lg[:1], [0]),
-                 nthreads=1)
-    t1 = time.perf_counter() - t0
+    # one core: one head of one sequence on one thread, repeated to about 1 s
+    # (also the calibration of the all-core sample)
+    one = (pick(q[:1], [0]), pick(k[:1], [0]), pick(v[:1], [0]), pick(lg[:1], [0]))
+    n1, t_one = 0, 0.0
+    while n1 == 0 or (t_one < 1.0 and n1 < 200):
+        t0 = time.perf_counter()
+        c_oracle.fwd(*one, nthreads=1)
+        t_one += time.perf_counter() - t0
+        n1 += 1
+    t1 = t_one / n1
     _, _, cores = c_oracle.fwd(pick(q[:1], [0]), pick(k[:1], [0]), pick(v[:1], [0]),
                                pick(lg[:1], [0]), nthreads=0)
     n_heads = int(max(1, min(H, round(target_s * cores / max(t1, 1e-6) / B))))
@@ -492,7 +628,10 @@ def cpu_baseline(host_set, target_s=10.0, min_wall=3.0):
             "sample": f"train_2k: all {B} sequences x {n_heads} of {H} heads x {T} tokens "
                       f"({tok_heads} token-heads) x {reps} runs, {el:.1f} s; value scaled to "
                       f"tokens/s of a {H}-head layer",
-            "seconds": round(el, 2)}
+            "seconds": round(el, 2),
+            "one_core_value": round(T / t1 / H, 1),
+            "one_core_sample": f"one sequence x one head x {T} tokens on one thread, "
+                               f"{n1} runs, {t_one:.2f} s"}
 
 
 def main():
@@ -508,6 +647,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-laplace", action="store_true")
     ap.add_argument("--no-decode-layers", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 65,536-token prefill and the packed varlen batch")
     ap.add_argument("--chunk", type=int, default=64, choices=[64, 128])
     ap.add_argument("--stream-reference", action="store_true",
                     help="only time two plain streams over the decode state's size (1.342 GB "
@@ -566,6 +707,14 @@ def main():
         log("laplace shape: building inputs")
         lap = bench_laplace(args)
         log(f"laplace: fwd {lap['forward']} decode {lap['decode']['gbs']} GB/s")
+    pre = var = None
+    if not args.no_long:
+        log("prefill_64k: building inputs")
+        pre = bench_prefill(args)
+        log(f"prefill_64k: {pre}")
+        log("varlen_64: building inputs")
+        var = bench_varlen(args)
+        log(f"varlen_64: {var}")
     layers = None
     if not args.no_decode_layers:
         log("decode layers: building pools")
@@ -575,6 +724,7 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the fp64 oracle")
         cpu = cpu_baseline(host_set)
+        cpu["gpu_over_cpu"] = round(fwd["value"] / cpu["value"], 1)
         log(f"cpu baseline: {cpu['value']} tokens/s on {cpu['cores']} threads")
 
     line = {
@@ -592,11 +742,14 @@ def main():
         "data": "synthetic",
         "config": fwd["config"],
         "kernel_ms": round(fwd["kernel_ms"], 5),
+        "kernel_ms_pct": fwd["kernel_ms_pct"],
         "roofline": fwd["roofline"],
         "mfma": fwd["mfma"],
         "other_chunk": fwd["other_chunk"],
         "backward": bwd,
         "decode": dec,
+        "prefill_64k": pre,
+        "varlen_64": var,
         "laplace": lap,
         "decode_layers": layers,
         "cpu_baseline": cpu,
