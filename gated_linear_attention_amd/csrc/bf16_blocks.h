@@ -135,6 +135,11 @@ __device__ __forceinline__ void lds_after_wait(u32x4 &a, u32x4 &b, u32x4 &c) {
 __device__ __forceinline__ void counters_drained() { __builtin_amdgcn_s_waitcnt(0); }
 // gfx9 s_waitcnt immediate: vmcnt(2) expcnt(7) lgkmcnt(0).
 __device__ __forceinline__ void counters_drained_but_2() { __builtin_amdgcn_s_waitcnt(0x0072); }
+// The same with four stores allowed in flight (vmcnt(4)).
+__device__ __forceinline__ void barrier_all_but_4() {
+  asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void counters_drained_but_4() { __builtin_amdgcn_s_waitcnt(0x0074); }
 
 // Inclusive prefix sum across the 64 lanes of a wavefront with DPP row shifts
 // and row broadcasts (no LDS round trips).

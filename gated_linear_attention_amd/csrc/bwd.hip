@@ -67,6 +67,26 @@ __global__ __launch_bounds__(256) void gate_dot_kernel(const Tin *__restrict__ q
   if (row < rows && l == 0) dB[row] = acc;
 }
 
+// dB[token * H + h] = sum over p of dq_part[p][h][token] - dk_part[p][h][token]:
+// the per-token dot products q.dq - k.dk from the partial sums the chunk-64
+// forward runs wrote (one per 16-column group p). Thread i reads element i of
+// every [h][token] plane (coalesced) and writes its (token, h) entry.
+__global__ __launch_bounds__(256) void gate_parts_kernel(const float *__restrict__ dq_part,
+                                                         const float *__restrict__ dk_part,
+                                                         int n_part, long n_tok, int H,
+                                                         float *__restrict__ dB) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;  // h * n_tok + token
+  const long rows = n_tok * H;
+  if (i >= rows) return;
+  float a = 0.f, b = 0.f;
+  for (int p = 0; p < n_part; ++p) {
+    a += dq_part[(size_t)p * rows + i];
+    b += dk_part[(size_t)p * rows + i];
+  }
+  const long h = i / n_tok, t = i % n_tok;
+  dB[t * H + h] = a - b;
+}
+
 // One workgroup per (sequence, head): dl = reverse cumulative sum of dB over
 // the sequence (plus <dS_T, S_T> at its last token), in tiles of 2048 tokens
 // from the end; and dS0 = g_0 A_0. ST_t and dST_t are S_T^T and dS_T^T
@@ -137,6 +157,15 @@ __global__ __launch_bounds__(256) void gate_scan_kernel(
 
 }  // namespace
 
+hipError_t launch_gate_parts(const float *dq_part, const float *dk_part, int n_part,
+                             long n_tok, int H, float *dB, hipStream_t stream) {
+  const long rows = n_tok * H;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(gate_parts_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
+                     dq_part, dk_part, n_part, n_tok, H, dB);
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose(const float *in, float *out, int count, int rows, int cols,
                             hipStream_t stream) {
   const size_t mat = (size_t)rows * cols;
@@ -153,9 +182,9 @@ hipError_t launch_transpose(const float *in, float *out, int count, int rows, in
 hipError_t launch_dgate(const void *q, const void *k, const float *dq, const float *dk,
                         const float *lg, const float *ST_t, const float *dST_t, const float *A0,
                         float *dl, float *dS0, const int32_t *cu, int N, int T, int H, int DK,
-                        int DV, bool in_bf16, hipStream_t stream) {
+                        int DV, bool in_bf16, bool have_dB, hipStream_t stream) {
   const long rows = (long)(cu ? T : (long)N * T) * H;  // token rows of the batch
-  if (rows > 0) {
+  if (rows > 0 && !have_dB) {
     const dim3 grid((unsigned)((rows + 7) / 8)), block(256);
     if (in_bf16)
       hipLaunchKernelGGL(gate_dot_kernel<uint16_t>, grid, block, 0, stream,

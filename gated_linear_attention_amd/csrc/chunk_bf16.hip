@@ -555,6 +555,7 @@ hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_
   if (d.C == 64)
     return launch_chunk_bf16_c64(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
                                  slots, slot_gamma, state_pass, stream);
+  if (d.dot_x) return hipErrorInvalidValue;  // row dots: chunk-64 kernel only
   if (d.dk == 96)
     return launch_bf_c<128, 96>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
                                 slots, slot_gamma, state_pass, stream);

@@ -283,13 +283,18 @@ struct W8Wave {
 
 }  // namespace
 
-template <int DK, int NCG, typename Tout, bool SP, bool REV = false>
+// DOT: also the row dot products of the outputs with x (a bf16 tensor of the
+// outputs' shape): each wavefront sums o * x over its 16 columns per row and
+// writes part[((slice * NCG + column group) * H + h) * part_stride + token]
+// (part_stride = tokens; a wavefront's 16 rows are 64 contiguous bytes).
+template <int DK, int NCG, typename Tout, bool SP, bool REV = false, bool DOT = false>
 __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ lg, const float *__restrict__ S0,
     float *__restrict__ ST, Tout *__restrict__ o, const WorkItem *__restrict__ items,
     const int *__restrict__ n_items, float *__restrict__ slots, float *__restrict__ slot_gamma,
-    int T, int H, int gts, int DV, int n_pairs) {
+    int T, int H, int gts, int DV, int n_pairs, const uint16_t *__restrict__ xd,
+    float *__restrict__ dpart, long part_stride) {
   using Wv = W8Wave<DK, NCG, SP>;
   using LDS = typename Wv::LDS;
   using Loader = W8Loader<DK, NCG, SP, REV>;
@@ -387,8 +392,28 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
   // long before, they have landed); the barrier that opens the next chunk then
   // lets just these stores stay in flight.
   const size_t rs16 = (size_t)16 * H * DV;
-  auto store_out = [&](int tc, int nc, const f32x4 (&own)[2]) {
+  auto mem_row = [&](int t) -> size_t {
+    return (size_t)(REV ? w.seq_begin + w.seq_end - 1 - t : t);
+  };
+  auto store_out = [&](int tc, int nc, const f32x4 (&own)[2], const u32x2 (&xv)[2]) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (DOT) {  // partial row dot products: 16 columns, reduced over lg4
+      float dsum[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const float x0 = __uint_as_float(xv[m].x << 16), x1 = __uint_as_float(xv[m].x & 0xffff0000u);
+        const float x2 = __uint_as_float(xv[m].y << 16), x3 = __uint_as_float(xv[m].y & 0xffff0000u);
+        float d = own[m][0] * x0 + own[m][1] * x1 + own[m][2] * x2 + own[m][3] * x3;
+        d += __shfl_xor(d, 16);
+        d += __shfl_xor(d, 32);
+        dsum[m] = d;
+      }
+      float *pp = dpart + ((size_t)(slice * NCG + cg) * H + h) * part_stride;
+      if (lg4 == 0) {
+        if (16 * mi0 + ln < nc) pp[mem_row(tc + 16 * mi0 + ln)] = dsum[0];
+        if (16 * mi1 + ln < nc) pp[mem_row(tc + 16 * mi1 + ln)] = dsum[1];
+      }
+    }
     if constexpr (REV) {  // logical row t is memory row sb + se - 1 - t
       const int se1 = w.seq_begin + w.seq_end - 1 - tc - ln;
       Tout *ob = o + ((size_t)h) * DV + col0 + wcol + 4 * lg4;
@@ -415,6 +440,10 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
   ld.gate_next(t0 + C, w.tok_end);
   ld.g_part(s, wave, lane, 1);
   barrier_all();
+  // With the x loads inside the chunk loop, the initial-state loads must be
+  // known drained here, or the compiler's wait insertion would wait for every
+  // later load (the x loads included) before their first use in the loop.
+  if constexpr (DOT) counters_drained();
   // gates of the first chunk; each later chunk's are prepared at the end of
   // the chunk before it, from the ring slot loaded two chunks ahead
   float gam = 1.f;
@@ -449,6 +478,9 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
     if (SP) {
       barrier_all();
       counters_drained();
+    } else if (DOT) {  // two output and two dot-product stores
+      barrier_all_but_4();
+      counters_drained_but_4();
     } else {
       barrier_all_but_2();
       counters_drained_but_2();
@@ -464,6 +496,19 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
       if (wave == Loader::LW - 1) {
         ld.gate_next(t0 + 2 * C, w.tok_end);
         ld.g_part(s, wave, lane, g_ld);
+      }
+    }
+
+    // x row pieces matching this chunk's outputs (DOT); they land long before
+    // the chunk-end stores, which wait for every load anyway
+    u32x2 xv[2] = {u32x2{0u, 0u}, u32x2{0u, 0u}};
+    if constexpr (DOT) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int r = 16 * (m ? mi1 : mi0) + ln;
+        if (r < n)
+          xv[m] = *reinterpret_cast<const u32x2 *>(
+              xd + (mem_row(t0 + r) * H + h) * DV + col0 + wcol + 4 * lg4);
       }
     }
 
@@ -705,7 +750,7 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
       const float x = s.lgb[g_rd][lane];
       gam = R.gates(lane < w.tok_end - t0 - C ? x : 0.f, lsum);
     }
-    if (!SP) store_out(t0, n, own);
+    if (!SP) store_out(t0, n, own, xv);
     g_rd = g_rd == 2 ? 0 : g_rd + 1;
     g_ld = g_ld == 2 ? 0 : g_ld + 1;
   }
@@ -726,7 +771,7 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
   }
 }
 
-template <int DK, int NCG, typename Tout, bool SP, bool REV = false>
+template <int DK, int NCG, typename Tout, bool SP, bool REV = false, bool DOT = false>
 static hipError_t launch_w8_t(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const float *g, const float *S0, float *S_T, void *o,
                               const FwdDims &d, const WorkItem *items, const int *n_items,
@@ -735,10 +780,10 @@ static hipError_t launch_w8_t(const uint16_t *q, const uint16_t *k, const uint16
   const long pairs = (long)grid_items * d.H;
   const long blocks = pairs * (d.dv / (16 * NCG));
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_bf16_w8_kernel<DK, NCG, Tout, SP, REV>), dim3(blocks), dim3(128 * NCG), 0,
-                     stream,
-                     q, k, v, g, S0, S_T, static_cast<Tout *>(o), items, n_items, slots,
-                     slot_gamma, d.T, d.H, d.gts, d.dv, (int)pairs);
+  hipLaunchKernelGGL((chunk_bf16_w8_kernel<DK, NCG, Tout, SP, REV, DOT>), dim3(blocks),
+                     dim3(128 * NCG), 0, stream, q, k, v, g, S0, S_T, static_cast<Tout *>(o),
+                     items, n_items, slots, slot_gamma, d.T, d.H, d.gts, d.dv, (int)pairs,
+                     d.dot_x, d.dot_part, d.dot_stride);
   return hipGetLastError();
 }
 
@@ -748,17 +793,30 @@ static hipError_t launch_w8_d(const uint16_t *q, const uint16_t *k, const uint16
                               const FwdDims &d, const WorkItem *items, const int *n_items,
                               int grid_items, float *slots, float *slot_gamma, bool state_pass,
                               hipStream_t stream) {
-  if constexpr (NCG == 4) {  // time-reversed runs of the backward: fp32 outputs
-    if (d.rev) {
-      if (state_pass)
-        return launch_w8_t<DK, NCG, float, true, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
-                                                       grid_items, slots, slot_gamma, stream);
-      if (out_bf16) return hipErrorInvalidValue;
-      return launch_w8_t<DK, NCG, float, false, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
-                                                      grid_items, slots, slot_gamma, stream);
+  if constexpr (NCG == 4) {  // the backward's runs: fp32 outputs, optionally reversed / dots
+    if (d.rev || d.dot_x) {
+      if (state_pass) {
+        if (d.rev)
+          return launch_w8_t<DK, NCG, float, true, true>(q, k, v, g, S0, S_T, o, d, items,
+                                                         n_items, grid_items, slots, slot_gamma,
+                                                         stream);
+      } else {
+        if (out_bf16) return hipErrorInvalidValue;
+        if (d.rev && d.dot_x)
+          return launch_w8_t<DK, NCG, float, false, true, true>(q, k, v, g, S0, S_T, o, d, items,
+                                                                n_items, grid_items, slots,
+                                                                slot_gamma, stream);
+        if (d.rev)
+          return launch_w8_t<DK, NCG, float, false, true>(q, k, v, g, S0, S_T, o, d, items,
+                                                          n_items, grid_items, slots, slot_gamma,
+                                                          stream);
+        return launch_w8_t<DK, NCG, float, false, false, true>(q, k, v, g, S0, S_T, o, d, items,
+                                                               n_items, grid_items, slots,
+                                                               slot_gamma, stream);
+      }
     }
   } else {
-    if (d.rev) return hipErrorInvalidValue;
+    if (d.rev || d.dot_x) return hipErrorInvalidValue;
   }
   if (state_pass)
     return launch_w8_t<DK, NCG, float, true>(q, k, v, g, S0, S_T, o, d, items, n_items, grid_items,

@@ -255,6 +255,7 @@ hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, cons
                             const FwdDims &d, const WorkItem *items, const int *n_items,
                             int grid_items, float *slots, float *slot_gamma, bool state_pass,
                             hipStream_t stream) {
+  if (d.dot_x) return hipErrorInvalidValue;  // row dots: bf16 chunk-64 kernel only
   if (d.dk == 96) {
     if (d.C == 64)
       return launch_f32_c<64, 96>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,

@@ -136,7 +136,7 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
                     const int32_t *cu_seqlens, void *o, float *S_T, int B, int T, int H, int dk,
                     int dv, int N, int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
                     void *workspace, size_t workspace_bytes, hipStream_t stream,
-                    bool fixed_decay, bool rev) {
+                    bool fixed_decay, bool rev, const DotOut *dot) {
   const bool has_cu = cu_seqlens != nullptr;
   FwdDims d;
   d.B = B;
@@ -148,6 +148,9 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
   d.C = chunk_size;
   d.gts = fixed_decay ? 0 : H;
   d.rev = rev;
+  d.dot_x = dot ? static_cast<const uint16_t *>(dot->x) : nullptr;
+  d.dot_part = dot ? dot->part : nullptr;
+  d.dot_stride = dot ? dot->stride : 0;
   PlanLayout lay;
   const bool planned = make_plan(B, T, H, dk, dv, N, chunk_size, has_cu, in_dtype, lay);
   if (planned && (!workspace || workspace_bytes < lay.total_bytes)) return GLA_ERR_WORKSPACE;
@@ -287,7 +290,8 @@ namespace {
 
 // Workspace layout of the backward (all offsets 256-byte aligned).
 struct BwdLayout {
-  size_t s0t, dstt, stt, a0, fws, total, fws_bytes;
+  size_t s0t, dstt, stt, a0, dqp, dkp, fws, total, fws_bytes;
+  bool fused_dots;  // dq and dk passes write partial q.dq, k.dk (bf16, chunk 64)
 };
 
 BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int N, int C, bool has_cu,
@@ -301,12 +305,15 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int N, int C, bool has
     off = align256(off + bytes);
     return at;
   };
-  (void)ntok;
   (void)es;
   L.s0t = take(mat);
   L.dstt = take(mat);
   L.stt = take(mat);
   L.a0 = take(mat);
+  L.fused_dots = in_dtype == GLA_BF16 && C == 64;
+  const size_t parts = L.fused_dots ? (size_t)(dk / 16) * ntok * 4 : 0;
+  L.dqp = take(parts);
+  L.dkp = take(parts);
   const size_t f1 = fwd_workspace(B, T, H, dv, dk, N, C, has_cu, in_dtype);
   const size_t f2 = fwd_workspace(B, T, H, dk, dv, N, C, has_cu, in_dtype);
   L.fws_bytes = f1 > f2 ? f1 : f2;
@@ -374,6 +381,11 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   float *stt = reinterpret_cast<float *>(ws + L.stt);
   float *a0 = reinterpret_cast<float *>(ws + L.a0);
   void *fws = L.fws_bytes ? ws + L.fws : nullptr;
+  // with the chunk-64 bf16 kernels the dq and dk runs also write the partial
+  // sums of q.dq and k.dk (one per 16-column group) for the gate gradient
+  const DotOut dq_dot{q, reinterpret_cast<float *>(ws + L.dqp), (long)B * T};
+  const DotOut dk_dot{k, reinterpret_cast<float *>(ws + L.dkp), (long)B * T};
+  const bool fuse = L.fused_dots;
   // transposed initial states
   if ((S0 && launch_transpose(S0, s0t, N * H, DK, DV, stream) != hipSuccess) ||
       (dS_T && launch_transpose(dS_T, dstt, N * H, DK, DV, stream) != hipSuccess))
@@ -382,7 +394,7 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   // dq: forward with (q, k, v) = (dO, v, k) on the transposed state; its final
   // state is S_T^T
   st = fwd_core(dO, v, k, g, s0t, cu_seqlens, dq, stt, B, T, H, DV, DK, N, chunk_size, in_dtype,
-                GLA_F32, fws, L.fws_bytes, stream);
+                GLA_F32, fws, L.fws_bytes, stream, false, false, fuse ? &dq_dot : nullptr);
   if (st != GLA_OK) return st;
   // dv: the reversed-time run with (q, k, v) = (k, q, dO) from dS_T; ends in A_0
   st = fwd_core(k, q, dO, g, dS_T, cu_seqlens, dv, a0, B, T, H, DK, DV, N, chunk_size, in_dtype,
@@ -390,10 +402,13 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   if (st != GLA_OK) return st;
   // dk: the reversed-time run with (q, k, v) = (v, dO, q) from dS_T^T
   st = fwd_core(v, dO, q, g, dstt, cu_seqlens, dk, nullptr, B, T, H, DV, DK, N, chunk_size,
-                in_dtype, GLA_F32, fws, L.fws_bytes, stream, false, true);
+                in_dtype, GLA_F32, fws, L.fws_bytes, stream, false, true,
+                fuse ? &dk_dot : nullptr);
   if (st != GLA_OK) return st;
-  if (launch_dgate(q, k, dq, dk, g, stt, dstt, a0, dg, dS0, cu_seqlens, N, T, H, DK, DV,
-                   in_dtype == GLA_BF16, stream) != hipSuccess)
+  if ((fuse && launch_gate_parts(dq_dot.part, dk_dot.part, DK / 16, (long)B * T, H, dg,
+                                 stream) != hipSuccess) ||
+      launch_dgate(q, k, dq, dk, g, stt, dstt, a0, dg, dS0, cu_seqlens, N, T, H, DK, DV,
+                   in_dtype == GLA_BF16, fuse, stream) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;
 }

@@ -62,6 +62,20 @@ struct FwdDims {
   // sb + se - 1 - t for q, k, v and o, and its gate is log_g[se - (t - sb)]
   // (0 at t = sb): the adjoint recurrence of the backward
   bool rev;
+  // optional row dot products of the outputs with x ([.., T, H, dv] bf16):
+  // part[(p * H + h) * stride + token] = sum over the columns of column group
+  // p of o * x (stride = tokens; the backward's q . dq and k . dk); chunk 64,
+  // bf16 only
+  const uint16_t *dot_x;
+  float *dot_part;
+  long dot_stride;
+};
+
+// Row dot products requested from a forward run (see FwdDims::dot_x).
+struct DotOut {
+  const void *x;
+  float *part;
+  long stride;
 };
 
 // slots == nullptr: state of pair (n, h) is S[n, h]; otherwise S[slots[n], h]
@@ -107,16 +121,21 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
                     const int32_t *cu_seqlens, void *o, float *S_T, int B, int T, int H, int dk,
                     int dv, int N, int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
                     void *workspace, size_t workspace_bytes, hipStream_t stream,
-                    bool fixed_decay = false, bool rev = false);
+                    bool fixed_decay = false, bool rev = false, const DotOut *dot = nullptr);
 size_t fwd_workspace(int B, int T, int H, int dk, int dv, int N, int chunk_size, bool has_cu,
                      gla_dtype in_dtype);
 // Backward helpers (bwd.hip).
+// dB[token * H + h] = sum_p dq_part[p][h][token] - sum_p dk_part[p][h][token]
+// (the gate gradient's per-token dot products from the forward runs' partial
+// sums).
+hipError_t launch_gate_parts(const float *dq_part, const float *dk_part, int n_part,
+                             long n_tok, int H, float *dB, hipStream_t stream);
 hipError_t launch_transpose(const float *in, float *out, int count, int rows, int cols,
                             hipStream_t stream);
 hipError_t launch_dgate(const void *q, const void *k, const float *dq, const float *dk,
                         const float *lg, const float *ST_t, const float *dST_t, const float *A0,
                         float *dl, float *dS0, const int32_t *cu, int N, int T, int H, int DK,
-                        int DV, bool in_bf16, hipStream_t stream);
+                        int DV, bool in_bf16, bool have_dB, hipStream_t stream);
 
 // Token-mixer epilogue (epilogue.hip): n_rows = tokens x heads rows.
 hipError_t launch_mixer_epilogue(const void *o, const void *q, const void *k, const void *v,
