@@ -106,9 +106,9 @@ def warm_up(fn, steps, seconds):
 # kernel that runs the headline forward at each chunk size, and the sources
 # whose hash keys its committed counter record
 FWD_KERNELS = {
-    64: ("chunk_bf16_w8_kernel<128,4,float,false>",
+    64: ("chunk_bf16_w8_kernel<128,4,float,false,false,false>",
          ["chunk_bf16_w8.hip", "bf16_blocks.h", "gla_common.h"]),
-    128: ("chunk_bf16_kernel<128,128,float,false>",
+    128: ("chunk_bf16_kernel<128,128,float,false,false>",
           ["chunk_bf16.hip", "bf16_blocks.h", "gla_common.h"]),
 }
 
@@ -484,7 +484,8 @@ def bench_laplace(args):
     z = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     alg_epi = tok_heads * (4 * dv + 2 * dk + 2 * dk + 2 * dv + 2 * dv + 2 * dv)
     epi = timed(lambda i: gla.mixer_epilogue(o, tq, tk, tv, gate, ta, rms_w, 1e-6, z=z), alg_epi)
-    epi.update({"algorithmic_bytes": alg_epi, "kernel": "mixer_epilogue_kernel<96,192,float,bf16,bf16>"})
+    epi.update({"algorithmic_bytes": alg_epi, "kernel": "mixer_epilogue_kernel<96,192,float,bf16,bf16>",
+                "traffic": measured_traffic("mixer_epilogue_laplace_2k", ["epilogue.hip", "gla_common.h"])})
     del tq, tk, tv, tlg, o, S_T, gate, z
 
     # decode: 1,280 sequences x 16 heads of 96 x 192 fp32 state, in place
@@ -510,8 +511,8 @@ def bench_laplace(args):
                    "H": H, "dk": dk, "dv": dv, "in_dtype": "bf16", "out_dtype": "f32",
                    "decays": "fixed geometric schedule, half-lives 1 .. 2048 tokens"},
         "forward": fwd,
-        "forward_kernel": {"c64": "chunk_bf16_w8_kernel<96,6,float,false>",
-                           "c128": "chunk_bf16_kernel<128,96,float,false>"},
+        "forward_kernel": {"c64": "chunk_bf16_w8_kernel<96,6,float,false,false,false>",
+                           "c128": "chunk_bf16_kernel<128,96,float,false,false>"},
         "forward_algorithmic_bytes": alg_fixed,
         "epilogue": epi,
         "forward_traffic_c64": measured_traffic("chunk_fwd_bf16_laplace_2k_c64",
@@ -520,7 +521,7 @@ def bench_laplace(args):
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg_dec,
                    "traffic": measured_traffic("decode_step_laplace_1280x16",
                                                ["decode.hip", "gla_common.h"]),
-                   "kernel": "decode_step_rows_kernel<96,192,8,bf16,float>"},
+                   "kernel": "decode_step_rows_kernel<96,192,192,8,bf16,float>"},
     }
 
 
