@@ -1,4 +1,5 @@
 // C ABI of libgla.so: argument validation, work planning and kernel launches.
+#include <algorithm>
 #include <climits>
 #include <cstdlib>
 #include <cstring>
@@ -85,19 +86,39 @@ bool make_plan(int B, int T, int H, int dk, int dv, int N, int C, bool has_cu,
   std::memset(&lay, 0, sizeof(lay));
   const int L = choose_seg_len(B, T, H, dk, dv, N, C, has_cu, in_dtype);
   lay.seg_len = L;
+  long seg_items;  // (a bound on) the non-last segments, each one state-pass run
   if (!has_cu) {
     const int nseg = T > 0 ? (T + L - 1) / L : 1;
     if (nseg <= 1) return false;
-    lay.max_items = B * nseg;
-    lay.max_state_items = B * (nseg - 1);
-    lay.max_multi = B;
-    lay.max_slots = B * nseg;
+    seg_items = (long)B * (nseg - 1);
   } else {
-    const int full = T / L;  // segments that can be full length
-    lay.max_items = N + full;
-    lay.max_state_items = full;
-    lay.max_multi = full;
-    lay.max_slots = 2 * full;
+    seg_items = T / L;  // segments that can be full length
+  }
+  // The state pass runs each non-last segment in n_sub pieces so that it has
+  // at least about four workgroups per CU (pieces of at least 8 chunks); the
+  // combine then chains the pieces. GLA_STATE_SUB overrides n_sub (tuning and
+  // tests; results do not depend on it beyond rounding).
+  int want = 1;
+  if (seg_items > 0) {
+    const long units = seg_items * H * (dv / slice_width(in_dtype, dk, C));
+    want = (int)((4L * cu_count() + units - 1) / units);
+    want = std::min(want, std::max(1, L / (8 * C)));
+  }
+  const char *env = std::getenv("GLA_STATE_SUB");
+  if (env && std::atoi(env) > 0) want = std::atoi(env);
+  want = std::max(1, std::min(want, L / C));
+  lay.sub_len = round_up((L + want - 1) / want, C);
+  lay.n_sub = (L + lay.sub_len - 1) / lay.sub_len;
+  if (!has_cu) {
+    lay.max_items = (int)(seg_items + B);
+    lay.max_state_items = (int)(seg_items * lay.n_sub);
+    lay.max_multi = B;
+    lay.max_slots = (int)(seg_items * lay.n_sub + B);
+  } else {
+    lay.max_items = (int)(N + seg_items);
+    lay.max_state_items = (int)(seg_items * lay.n_sub);
+    lay.max_multi = (int)seg_items;
+    lay.max_slots = (int)(seg_items * (lay.n_sub + 1));
   }
   size_t off = 0;
   lay.off_header = off;

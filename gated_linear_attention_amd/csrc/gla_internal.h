@@ -27,12 +27,14 @@ struct WorkItem {
 };
 constexpr int kNoStateOut = -2;
 
-// A sequence split into `nseg` > 1 segments whose start states live in slots
-// slot_base .. slot_base + nseg - 1 (slot s holds the start state of segment s).
+// A sequence split into segments: its chain of `nslot` state slots starts at
+// slot_base (slot_base holds S0; slot_base + b the state after b state items,
+// each a sub-segment of sub_len tokens of a non-last segment; segment s starts
+// from slot_base + s * (sub-segments per segment)).
 struct MultiSeq {
   int seq;
   int slot_base;
-  int nseg;
+  int nslot;
   int pad;
 };
 
@@ -46,6 +48,8 @@ struct PlanHeader {
 // Workspace layout of a planned forward (all offsets 256-byte aligned).
 struct PlanLayout {
   int seg_len;          // tokens per segment (multiple of the chunk size)
+  int sub_len;          // tokens per state-pass item (divides the segment into n_sub pieces)
+  int n_sub;            // state-pass items per non-last segment
   int max_items;        // bound on output-pass items
   int max_state_items;  // bound on state-pass items
   int max_multi;        // bound on split sequences

@@ -5,9 +5,11 @@
 // sequence. Items are ordered longest first (a counting sort on their chunk
 // count) so the workgroup dispatcher's greedy placement balances sequences
 // of very different lengths. A sequence longer than seg_len is split into
-// segments: a state pass computes each non-last segment's local state and
-// total log-decay, the combine kernel chains them into every segment's start
-// state, and the output pass then runs all segments in parallel. The chain
+// segments: a state pass computes the local state and total log-decay of
+// every non-last segment, in n_sub pieces of sub_len tokens (so that the pass
+// has enough workgroups to fill the GPU), the combine kernel chains them into
+// every segment's start state, and the output pass then runs all segments in
+// parallel. The chain
 // uses that the per-token update is affine in S, so whole segments compose:
 // the state after a segment is exp(sum of its log-gates) times the state
 // before it plus the segment's own contribution from a zero state (Laplace 3B
@@ -46,7 +48,8 @@ __device__ int block_exclusive_scan_1024(int x, int *scratch /* >= 16 ints */, i
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ cu, int N, int T,
-                                                    int L, int C, int max_items,
+                                                    int L, int C, int Ls, int n_sub,
+                                                    int max_items,
                                                     int max_state_items, int max_multi,
                                                     int max_slots, PlanHeader *__restrict__ hdr,
                                                     WorkItem *__restrict__ items,
@@ -87,9 +90,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
     atomicAdd(&hist[(last + C - 1) / C], 1);
     atomicAdd(&totals[0], nseg);
     if (nseg > 1) {
-      atomicAdd(&totals[1], nseg - 1);
+      atomicAdd(&totals[1], (nseg - 1) * n_sub);
       atomicAdd(&totals[2], 1);
-      atomicAdd(&totals[3], nseg);
+      atomicAdd(&totals[3], (nseg - 1) * n_sub + 1);
     }
   }
   __syncthreads();
@@ -125,8 +128,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
     const int nseg = valid ? max(1, (len + L - 1) / L) : 0;
     const bool split = nseg > 1;
     int ts, tsi, tm;
-    const int e_slot = block_exclusive_scan_1024(split ? nseg : 0, scratch, ts);
-    const int e_sitem = block_exclusive_scan_1024(split ? nseg - 1 : 0, scratch, tsi);
+    const int e_slot = block_exclusive_scan_1024(split ? (nseg - 1) * n_sub + 1 : 0, scratch, ts);
+    const int e_sitem = block_exclusive_scan_1024(split ? (nseg - 1) * n_sub : 0, scratch, tsi);
     const int e_multi = block_exclusive_scan_1024(split ? 1 : 0, scratch, tm);
     if (valid) {
       const int start = seq_start(n);
@@ -140,24 +143,28 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
         it.tok_begin = tb;
         it.tok_end = te;
         it.seq = n;
-        it.state_in = split ? slot_base + s : -1;
+        it.state_in = split ? slot_base + s * n_sub : -1;
         it.state_out = (s == nseg - 1) ? -1 : kNoStateOut;
         it.seq_begin = start;
         it.seq_end = start + len;
         it.pad = 0;
         items[pos] = it;
-        if (split && s < nseg - 1) {
-          WorkItem si = it;
-          si.state_in = -1;
-          si.state_out = slot_base + s + 1;
-          sitems[carry_sitem + e_sitem + s] = si;
+        if (split && s < nseg - 1) {  // non-last segments are full: L tokens
+          for (int j = 0; j < n_sub; ++j) {
+            WorkItem si = it;
+            si.tok_begin = tb + j * Ls;
+            si.tok_end = min(tb + (j + 1) * Ls, te);
+            si.state_in = -1;
+            si.state_out = slot_base + s * n_sub + j + 1;
+            sitems[carry_sitem + e_sitem + s * n_sub + j] = si;
+          }
         }
       }
       if (split) {
         MultiSeq m;
         m.seq = n;
         m.slot_base = slot_base;
-        m.nseg = nseg;
+        m.nslot = (nseg - 1) * n_sub + 1;
         m.pad = 0;
         multi[carry_multi + e_multi] = m;
       }
@@ -172,10 +179,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
   }
 }
 
-// Chain segment states: slot[base] = S0 (or 0); for s >= 1
-//   slot[base+s] = exp(gamma[base+s]) * slot[base+s-1] + slot[base+s]
-// where the state pass left segment s-1's local state and total log-decay in
-// slot base+s. One thread per four consecutive state elements.
+// Chain the state pieces: slot[base] = S0 (or 0); for b >= 1
+//   slot[base+b] = exp(gamma[base+b]) * slot[base+b-1] + slot[base+b]
+// where the state pass left piece b-1's local state and total log-decay in
+// slot base+b. One thread per four consecutive state elements.
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ S0,
                                                       const PlanHeader *__restrict__ hdr,
                                                       const MultiSeq *__restrict__ multi,
@@ -192,7 +199,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   if (S0) cur = *reinterpret_cast<const f32x4 *>(S0 + ((size_t)ms.seq * H + h) * dkdv + e);
   f32x4 *slot0 = reinterpret_cast<f32x4 *>(slots + ((size_t)ms.slot_base * H + h) * dkdv + e);
   *slot0 = cur;
-  for (int s = 1; s < ms.nseg; ++s) {
+  for (int s = 1; s < ms.nslot; ++s) {
     const int sl = ms.slot_base + s;
     f32x4 *p = reinterpret_cast<f32x4 *>(slots + ((size_t)sl * H + h) * dkdv + e);
     const float decay = expf(slot_gamma[(size_t)sl * H + h]);
@@ -207,7 +214,8 @@ hipError_t launch_plan(const int32_t *cu_seqlens, const FwdDims &d, const PlanLa
   const int nb = lay.seg_len / d.C + 1;
   const size_t lds = sizeof(int) * (3 * nb + 32);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), lds, stream, cu_seqlens, d.N, d.T,
-                     lay.seg_len, d.C, lay.max_items, lay.max_state_items, lay.max_multi,
+                     lay.seg_len, d.C, lay.sub_len, lay.n_sub, lay.max_items,
+                     lay.max_state_items, lay.max_multi,
                      lay.max_slots, reinterpret_cast<PlanHeader *>(ws + lay.off_header),
                      reinterpret_cast<WorkItem *>(ws + lay.off_items),
                      reinterpret_cast<WorkItem *>(ws + lay.off_state_items),

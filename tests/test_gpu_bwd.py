@@ -105,12 +105,13 @@ def test_bwd_near_reset_and_unit_gates():
     check_bwd(q, k, v, lg, S0, cu, dO, dS_T, "bf16", tight=1e-4)
 
 
-@pytest.mark.parametrize("seg", [64, 192])
-def test_bwd_forced_segment_split(seg, monkeypatch):
+@pytest.mark.parametrize("seg,sub", [(64, 1), (192, 1), (256, 4)])
+def test_bwd_forced_segment_split(seg, sub, monkeypatch):
     """Long sequences split into segments inside the forward runs (state pass,
-    combine, output pass) give the same gradients."""
-    gu.say(f"bwd forced split seg={seg}")
+    in `sub` pieces per segment, combine, output pass) give the same gradients."""
+    gu.say(f"bwd forced split seg={seg} pieces={sub}")
     monkeypatch.setenv("GLA_SEG_LEN", str(seg))
+    monkeypatch.setenv("GLA_STATE_SUB", str(sub))
     w = dataclasses.replace(W["varlen_64"], H=2)
     check_bwd(*_inputs(w, 650, lengths=[500, 3, 257, 0, 64]), "bf16", tight=1e-4)
 

@@ -131,6 +131,29 @@ def test_forced_segment_split(seg, C, varlen, monkeypatch):
     check(*synth.make_forward_inputs(w, lengths=lengths), "bf16", C=C)
 
 
+@pytest.mark.parametrize("seg,sub,C", [(256, 4, 64), (320, 3, 64), (384, 2, 128)])
+@pytest.mark.parametrize("varlen", [False, True])
+def test_forced_state_pieces(seg, sub, C, varlen, monkeypatch):
+    """Segments whose states the state pass computes in several pieces, which
+    the combine chains (including a shorter last piece: 320 = 3 x 128 - 64)."""
+    gu.say(f"state pieces seg_len={seg} n_sub={sub} C={C} varlen={varlen}")
+    monkeypatch.setenv("GLA_SEG_LEN", str(seg))
+    monkeypatch.setenv("GLA_STATE_SUB", str(sub))
+    w = synth.Workload("t", B=2, T=1000, H=2, dk=128, dv=128, dtype="bf16", gate_bias=3.0,
+                       s0_std=0.03, chunk=C, seed=27)
+    lengths = [1000, 0, 37, 700, 129, 333] if varlen else None
+    check(*synth.make_forward_inputs(w, lengths=lengths), "bf16", C=C, tight=2e-5)
+
+
+def test_forced_state_pieces_f32(monkeypatch):
+    gu.say("state pieces fp32")
+    monkeypatch.setenv("GLA_SEG_LEN", "256")
+    monkeypatch.setenv("GLA_STATE_SUB", "4")
+    w = synth.Workload("t", B=1, T=900, H=2, dk=64, dv=64, dtype="f32", gate_bias=3.0,
+                       s0_std=0.03, chunk=64, seed=28)
+    check(*synth.make_forward_inputs(w), "f32")
+
+
 def test_forced_segment_split_f32(monkeypatch):
     gu.say("segment split fp32")
     monkeypatch.setenv("GLA_SEG_LEN", "128")
