@@ -529,7 +529,8 @@ def bench_decode_layers(args, layers=24, batches=(20, 1280)):
     """One decode step of a Laplace-shaped mixer stack (24 layers of 16 heads,
     96 x 192; per layer the slot-indexed decode against its own state pool and
     the mixer epilogue), run eagerly call by call and as one captured HIP
-    graph, for a replica-sized batch of 20 sequences and for 1,280."""
+    graph, for a replica-sized batch of 20 sequences and for 1,280; then the
+    same with the decode and the epilogue fused into one kernel per layer."""
     import torch
 
     import gated_linear_attention_amd as gla
@@ -581,11 +582,39 @@ def bench_decode_layers(args, layers=24, batches=(20, 1280)):
             graph.replay()
         torch.cuda.synchronize()
         replay = (time.perf_counter() - t0) / steps
+        # the same step with the fused decode + epilogue: one kernel per layer
+        def step_fused(i=0):
+            for l in range(layers):
+                q, k, v, g = qkv[l]
+                gla.decode_mixer(q, k, v, lg, pools[l], g, ta, rms_w, 1e-6, slots=slots, z=z[l])
+
+        warm_up(step_fused, 3, min(args.warm_seconds, 0.3))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step_fused(i)
+        torch.cuda.synchronize()
+        eager_f = (time.perf_counter() - t0) / steps
+        graph_f = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph_f):
+            step_fused()
+        for _ in range(3):
+            graph_f.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graph_f.replay()
+        torch.cuda.synchronize()
+        replay_f = (time.perf_counter() - t0) / steps
         state_bytes = layers * N * H * dk * dv * 4 * 2
         out[f"N{N}"] = {"eager_ms": round(eager * 1e3, 4), "graph_ms": round(replay * 1e3, 4),
                         "tokens_per_s_graph": round(N / replay, 1),
-                        "state_gbs_graph": round(state_bytes / replay / 1e9, 1)}
-        del pools, qkv, o, z, graph
+                        "state_gbs_graph": round(state_bytes / replay / 1e9, 1),
+                        "fused_eager_ms": round(eager_f * 1e3, 4),
+                        "fused_graph_ms": round(replay_f * 1e3, 4),
+                        "fused_tokens_per_s_graph": round(N / replay_f, 1),
+                        "fused_state_gbs_graph": round(state_bytes / replay_f / 1e9, 1)}
+        del pools, qkv, o, z, graph, graph_f
         torch.cuda.empty_cache()
     return out
 

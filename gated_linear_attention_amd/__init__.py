@@ -10,6 +10,7 @@ device memory and the current HIP stream.
     o = decode_step(q, k, v, g, S)          # S updated in place
     o = decode_step_slots(q, k, v, g, S_pool, slots)   # S_pool[slots] updated in place
     z = mixer_epilogue(o, q, k, v, g_out, a, rms_w, eps)  # self-augmentation, RMSNorm, SiLU gate
+    z = decode_mixer(q, k, v, g, S, g_out, a, rms_w, eps, slots=None)  # decode + epilogue, fused
 
 Shapes follow the C ABI: q, k [B, T, H, dk]; v [B, T, H, dv]; g [B, T, H]
 fp32 natural-log gates; S0 / S_T [N, H, dk, dv] fp32; cu_seqlens int32 [N+1]
@@ -21,7 +22,8 @@ from . import _lib
 from ._lib import GLAError, GLA_BF16, GLA_F32
 
 __all__ = ["fwd_chunked", "fwd_chunked_fixed_decay", "bwd_chunked", "decode_step",
-           "decode_step_slots", "mixer_epilogue", "head_rms_weights", "workspace_size",
+           "decode_step_slots", "mixer_epilogue", "decode_mixer", "head_rms_weights",
+           "workspace_size",
            "GLAError", "library_path"]
 
 
@@ -280,3 +282,40 @@ def mixer_epilogue(o, q, k, v, g, a, rms_w, eps: float = 1e-6, out_dtype=None, z
                                 _dtype_code(out_dtype), stream)
     _lib.check(st, "gla_mixer_epilogue")
     return z
+
+
+def decode_mixer(q, k, v, g, S, g_out, a, rms_w, eps: float = 1e-6, slots=None,
+                 out_dtype=None, z=None):
+    """One decode step with the mixer epilogue fused: S (dense [N, H, dk, dv],
+    or a pool [P, H, dk, dv] addressed by int32 slots [N]) is updated in place
+    and z = epilogue(o) is returned; o itself is not materialised."""
+    torch = _torch()
+    lib = _lib.load()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or g.dim() != 2 or S.dim() != 4:
+        raise ValueError("expected q, k [N, H, dk], v [N, H, dv], g [N, H], S [., H, dk, dv]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    for x, name, dt in ((q, "q", None), (k, "k", q.dtype), (v, "v", q.dtype),
+                        (g, "g", torch.float32), (S, "S", torch.float32),
+                        (g_out, "g_out", q.dtype), (a, "a", torch.float32),
+                        (rms_w, "rms_w", torch.float32)):
+        _require(x, name, dt, dev)
+    _require(slots, "slots", torch.int32, dev)
+    if (tuple(S.shape[1:]) != (H, dk, dv) or tuple(g.shape) != (N, H)
+            or tuple(g_out.shape) != (N, H, dv) or tuple(a.shape) != (H, dk)
+            or tuple(rms_w.shape) != (H, dv) or (slots is None and S.shape[0] != N)
+            or (slots is not None and slots.numel() != N)):
+        raise ValueError("inconsistent decode_mixer shapes")
+    if out_dtype is None:
+        out_dtype = torch.float32 if z is None else z.dtype
+    if z is None:
+        z = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    _require(z, "z", out_dtype, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = lib.gla_decode_mixer(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S), _ptr(slots),
+                              S.shape[0], _ptr(g_out), _ptr(a), _ptr(rms_w), float(eps), _ptr(z),
+                              N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype), stream)
+    _lib.check(st, "gla_decode_mixer")
+    return z
+

@@ -54,6 +54,9 @@ def load():
     lib.gla_decode_step_slots.restype = i
     lib.gla_mixer_epilogue.argtypes = [vp] * 7 + [ctypes.c_float, vp] + [i] * 4 + [i, i, i, vp]
     lib.gla_mixer_epilogue.restype = i
+    lib.gla_decode_mixer.argtypes = ([vp] * 6 + [i] + [vp] * 3 + [ctypes.c_float, vp] + [i] * 4
+                                     + [i, i, vp])
+    lib.gla_decode_mixer.restype = i
     _lib = lib
     return lib
 

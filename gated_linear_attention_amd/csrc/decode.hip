@@ -183,6 +183,101 @@ __global__ __launch_bounds__(512) void decode_step_rows_kernel(const Tin *__rest
   }
 }
 
+// One decode step followed by the token-mixer epilogue in the same workgroup
+// (Laplace 3B on AWS Trainium2, "GLA mixer": the readout o of a head gets a
+// gated copy of v, o' = o + sigmoid(q . (a * k)) v, then the head's RMSNorm
+// and the SiLU output gate, z = o' / sqrt(mean(o'^2) + eps) * w * silu(g_out)).
+// The workgroup owns the whole row of its (sequence, head), so o never leaves
+// registers: the state is streamed as in decode_step_rows_kernel, the logit
+// is a block sum over d_k (shuffles, then one LDS value per wavefront), and
+// wavefront 0 finishes the row (its d_v / 4 <= 64 column groups) with a
+// wavefront sum for the RMS.
+template <int DK, int DV, int RP, typename Tin, typename Tout>
+__global__ __launch_bounds__(512) void decode_mixer_kernel(
+    const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
+    const float *__restrict__ g, float *__restrict__ S, const Tin *__restrict__ gout,
+    const float *__restrict__ a, const float *__restrict__ w, float eps, Tout *__restrict__ z,
+    const int32_t *__restrict__ slots, int P, int H) {
+  constexpr int TPR = DV / 4;
+  constexpr int NP = DK / RP;
+  constexpr int NW = RP * TPR / 64;  // wavefronts
+  static_assert(DK % RP == 0 && DV % 4 == 0 && TPR <= 64 && (RP * TPR) % 64 == 0, "row tiling");
+  __shared__ f32x4 red[RP][TPR];
+  __shared__ float lred[NW];
+
+  const size_t p = blockIdx.x;
+  const int t = threadIdx.x;
+  const int c4 = t % TPR;
+  const int r0 = t / TPR;
+  const int h = (int)(p % H);
+  size_t sp = p;
+  if (slots) {
+    const int slot = slots[p / H];
+    if (slot < 0 || slot >= P) {  // padded lane: no state touched, z = 0
+      if (t < TPR) {
+        Tout *zp = z + p * DV + 4 * t;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) store_from_f32(zp, j, 0.f);
+      }
+      return;
+    }
+    sp = (size_t)slot * H + h;
+  }
+  f32x4 *Sp = reinterpret_cast<f32x4 *>(S + sp * (size_t)(DK * DV));
+
+  f32x4 s[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) s[i] = __builtin_nontemporal_load(Sp + (r0 + i * RP) * TPR + c4);
+  const float gate = expf(g[p]);
+  const size_t vc = p * DV + 4 * c4;
+  f32x4 vv;
+  vv.x = load_as_f32(v, vc + 0);
+  vv.y = load_as_f32(v, vc + 1);
+  vv.z = load_as_f32(v, vc + 2);
+  vv.w = load_as_f32(v, vc + 3);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const float kk = load_as_f32(k, p * DK + r0 + i * RP);
+    const float qq = load_as_f32(q, p * DK + r0 + i * RP);
+    const f32x4 x = gate * s[i] + kk * vv;
+    __builtin_nontemporal_store(x, Sp + (r0 + i * RP) * TPR + c4);
+    acc += qq * x;
+  }
+  red[r0][c4] = acc;
+  // the logit q . (a * k): one key channel per thread, summed over the block
+  float lp = 0.f;
+  if (t < DK) lp = load_as_f32(q, p * DK + t) * a[(size_t)h * DK + t] * load_as_f32(k, p * DK + t);
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) lp += __shfl_xor(lp, m);
+  if (t % 64 == 0) lred[t / 64] = lp;
+  __syncthreads();
+  if (t < 64) {
+    float logit = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) logit += lred[i];
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    if (t < TPR) {
+#pragma unroll
+      for (int i = 0; i < RP; ++i) o += red[i][t];
+    }
+    const float sg = 1.f / (1.f + expf(-logit));
+    const f32x4 x = o + sg * vv;  // thread t < TPR owns columns 4t .. 4t+3 (c4 = t)
+    float ss = t < TPR ? x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3] : 0.f;
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) ss += __shfl_xor(ss, m);
+    const float inv = 1.f / sqrtf(ss * (1.f / DV) + eps);
+    if (t < TPR) {
+      Tout *zp = z + p * DV + 4 * t;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gg = load_as_f32(gout, p * DV + 4 * t + j);
+        store_from_f32(zp, j, x[j] * inv * w[(size_t)h * DV + 4 * t + j] * (gg / (1.f + expf(-gg))));
+      }
+    }
+  }
+}
+
 struct DecodeArgs {
   const void *q, *k, *v;
   const float *g;
@@ -259,6 +354,38 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const floa
   if (dk == 96 && dv == 192)
     return launch_decode_rows_d<96, 192, 192, 8>(a, in_bf16, out_bf16, stream);
   return launch_decode_d<64, 64>(a, in_bf16, out_bf16, stream);
+}
+
+template <int DK, int DV, int RP, typename Tin, typename Tout>
+static hipError_t launch_mixer_t(const MixerArgs &m, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_mixer_kernel<DK, DV, RP, Tin, Tout>), dim3((unsigned)m.pairs),
+                     dim3(RP * DV / 4), 0, stream, static_cast<const Tin *>(m.q),
+                     static_cast<const Tin *>(m.k), static_cast<const Tin *>(m.v), m.g, m.S,
+                     static_cast<const Tin *>(m.gout), m.a, m.w, m.eps, static_cast<Tout *>(m.z),
+                     m.slots, m.P, m.H);
+  return hipGetLastError();
+}
+
+template <int DK, int DV, int RP>
+static hipError_t launch_mixer_d(const MixerArgs &m, bool in_bf16, bool out_bf16,
+                                 hipStream_t stream) {
+  if (in_bf16) {
+    return out_bf16 ? launch_mixer_t<DK, DV, RP, uint16_t, uint16_t>(m, stream)
+                    : launch_mixer_t<DK, DV, RP, uint16_t, float>(m, stream);
+  }
+  return out_bf16 ? launch_mixer_t<DK, DV, RP, float, uint16_t>(m, stream)
+                  : launch_mixer_t<DK, DV, RP, float, float>(m, stream);
+}
+
+hipError_t launch_decode_mixer(const MixerArgs &m, int dk, int dv, bool in_bf16, bool out_bf16,
+                               hipStream_t stream) {
+  if (m.pairs == 0) return hipSuccess;
+  if (dk == 128 && dv == 128) return launch_mixer_d<128, 128, 8>(m, in_bf16, out_bf16, stream);
+  if (dk == 128 && dv == 64) return launch_mixer_d<128, 64, 16>(m, in_bf16, out_bf16, stream);
+  if (dk == 64 && dv == 128) return launch_mixer_d<64, 128, 8>(m, in_bf16, out_bf16, stream);
+  if (dk == 96 && dv == 192) return launch_mixer_d<96, 192, 8>(m, in_bf16, out_bf16, stream);
+  if (dk == 64 && dv == 64) return launch_mixer_d<64, 64, 16>(m, in_bf16, out_bf16, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gla

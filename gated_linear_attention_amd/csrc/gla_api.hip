@@ -512,4 +512,36 @@ gla_status gla_mixer_epilogue(const void *o, const void *q, const void *k, const
   return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
+gla_status gla_decode_mixer(const void *q, const void *k, const void *v, const float *g,
+                            float *S, const int32_t *slots, int P, const void *g_out,
+                            const float *a, const float *rms_w, float eps, void *z, int N, int H,
+                            int dk, int dv, gla_dtype in_dtype, gla_dtype out_dtype,
+                            void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (N < 0 || H < 0 || (slots && P < 0)) return GLA_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.f) || eps > 3.4e38f) return GLA_ERR_INVALID_ARGUMENT;
+  if (!fwd_dims(dk, dv)) return GLA_ERR_UNSUPPORTED;
+  const size_t pairs = (size_t)N * H;
+  if (pairs == 0) return GLA_OK;
+  const size_t n_states = slots ? (size_t)P * H : pairs;
+  if (pairs > (size_t)INT_MAX || n_states > (size_t)INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
+  if (!q || !k || !v || !g || !g_out || !a || !rms_w || !z || (n_states > 0 && !S))
+    return GLA_ERR_INVALID_ARGUMENT;
+  const size_t es = dtype_size(in_dtype);
+  const size_t bq = pairs * dk * es, bv = pairs * dv * es, bg = pairs * 4;
+  const size_t bS = n_states * dk * dv * 4, bz = pairs * dv * dtype_size(out_dtype);
+  const size_t ba = (size_t)H * dk * 4, bw = (size_t)H * dv * 4, bs = slots ? (size_t)N * 4 : 0;
+  const void *ins[] = {q, k, v, g, g_out, a, rms_w, slots};
+  const size_t nins[] = {bq, bq, bv, bg, bv, ba, bw, bs};
+  for (int i = 0; i < 8; ++i)
+    if (overlaps(z, bz, ins[i], nins[i]) || overlaps(S, bS, ins[i], nins[i]))
+      return GLA_ERR_INVALID_ARGUMENT;
+  if (overlaps(z, bz, S, bS)) return GLA_ERR_INVALID_ARGUMENT;
+  MixerArgs m{q, k, v, g, S, g_out, a, rms_w, eps, z, slots, slots ? P : 0, H, (long)pairs};
+  const hipError_t err =
+      launch_decode_mixer(m, dk, dv, in_dtype == GLA_BF16, out_dtype == GLA_BF16, stream);
+  return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -141,6 +141,23 @@ hipError_t launch_dgate(const void *q, const void *k, const float *dq, const flo
                         float *dl, float *dS0, const int32_t *cu, int N, int T, int H, int DK,
                         int DV, bool in_bf16, bool have_dB, hipStream_t stream);
 
+// One decode step with the mixer epilogue fused (decode.hip): S (or the pool
+// entries slots[n], as launch_decode) updated in place, z written; o is not.
+struct MixerArgs {
+  const void *q, *k, *v;
+  const float *g;
+  float *S;
+  const void *gout;
+  const float *a, *w;
+  float eps;
+  void *z;
+  const int32_t *slots;
+  int P, H;
+  long pairs;
+};
+hipError_t launch_decode_mixer(const MixerArgs &m, int dk, int dv, bool in_bf16, bool out_bf16,
+                               hipStream_t stream);
+
 // Token-mixer epilogue (epilogue.hip): n_rows = tokens x heads rows.
 hipError_t launch_mixer_epilogue(const void *o, const void *q, const void *k, const void *v,
                                  const void *g, const float *a, const float *w, float eps,

@@ -221,6 +221,28 @@ gla_status gla_mixer_epilogue(const void *o, const void *q, const void *k, const
                               void *z, int n_tokens, int H, int dk, int dv, gla_dtype o_dtype,
                               gla_dtype in_dtype, gla_dtype out_dtype, void *stream);
 
+/*
+ * One decode step with the token-mixer epilogue fused (Laplace 3B on AWS
+ * Trainium2, "GLA mixer" and "Inference optimization"): the state update of
+ * gla_decode_step (slots == NULL: S is [N, H, dk, dv]) or of
+ * gla_decode_step_slots (slots != NULL: S is the pool [P, H, dk, dv]), then
+ * gla_mixer_epilogue's arithmetic on the readout, in one kernel; the readout
+ * o itself is not written.
+ *
+ *   q, k [N, H, dk], v [N, H, dv], g [N, H] fp32: as gla_decode_step
+ *   g_out [N, H, dv] in_dtype   the gate stream of the epilogue
+ *   a [H, dk], rms_w [H, dv]    fp32, eps finite >= 0: as gla_mixer_epilogue
+ *   z [N, H, dv] out_dtype      the epilogue's output (padded lanes: 0)
+ *
+ * Sizes and dtypes as gla_decode_step. z must not overlap anything; S must not
+ * overlap the inputs.
+ */
+gla_status gla_decode_mixer(const void *q, const void *k, const void *v, const float *g,
+                            float *S, const int32_t *slots, int P, const void *g_out,
+                            const float *a, const float *rms_w, float eps, void *z, int N, int H,
+                            int dk, int dv, gla_dtype in_dtype, gla_dtype out_dtype,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

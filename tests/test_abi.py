@@ -19,9 +19,11 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     assert header_functions() == ["gla_bwd_chunked", "gla_bwd_chunked_workspace_size",
-                                  "gla_decode_step", "gla_decode_step_slots", "gla_fwd_chunked",
-                                  "gla_fwd_chunked_fixed_decay", "gla_fwd_chunked_workspace_size",
-                                  "gla_mixer_epilogue", "gla_status_string"]
+                                  "gla_decode_mixer", "gla_decode_step", "gla_decode_step_slots",
+                                  "gla_fwd_chunked",
+                                  "gla_fwd_chunked_fixed_decay",
+                                  "gla_fwd_chunked_workspace_size", "gla_mixer_epilogue",
+                                  "gla_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -190,3 +192,26 @@ def test_epilogue_rejects_bad_arguments_before_launch():
     assert call(z=P[0] + 4) == _lib.GLA_ERR_INVALID_ARGUMENT       # z partly over o
     assert call(z=P[0], outd=BF) == _lib.GLA_ERR_INVALID_ARGUMENT  # in place needs o's dtype
     assert call(H=0) == _lib.GLA_OK
+
+
+def test_decode_mixer_rejects_bad_arguments_before_launch():
+    lib = _lib.load()
+    F32, BF = _lib.GLA_F32, _lib.GLA_BF16
+    q, k, v, g, S, go, a, w, z = (FAKE + (i << 30) for i in range(9))
+
+    def call(N=4, H=2, dk=64, dv=64, eps=1e-6, slots=None, P=0, zz=None, ind=BF, ptrs=None):
+        p = ptrs or (q, k, v, g, S)
+        return lib.gla_decode_mixer(*p, slots, P, go, a, w, eps, zz or z, N, H, dk, dv, ind,
+                                    F32, None)
+    assert call(N=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(eps=-1.0) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(ind=9) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(dk=96) == _lib.GLA_ERR_UNSUPPORTED
+    assert call(dk=96, dv=192, N=0) == _lib.GLA_OK
+    assert call(slots=FAKE + (10 << 30), P=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(ptrs=(None, k, v, g, S)) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(zz=S + 64) == _lib.GLA_ERR_INVALID_ARGUMENT       # z inside the state
+    assert call(zz=go) == _lib.GLA_ERR_INVALID_ARGUMENT           # z over the gate stream
+    assert call(ptrs=(q, k, v, g, q + 16)) == _lib.GLA_ERR_INVALID_ARGUMENT  # S over q
+    assert call(H=0) == _lib.GLA_OK
+
