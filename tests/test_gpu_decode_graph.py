@@ -96,3 +96,55 @@ def test_graph_replays_match_eager_and_oracle():
         assert np.all(gu.host(o[0])[[n for n in range(N) if n not in valid]] == 0.0)
     eS = orc.normwise_error(gu.host(pools[0]), ref[0])
     assert eS <= 1e-6, eS
+
+
+def test_graph_of_fused_decode_mixer_matches_eager():
+    """The fused decode + epilogue (one kernel per layer) captured the same way:
+    replays with fresh inputs equal eager runs on copies of the pools, bit for bit."""
+    import torch
+    import gated_linear_attention_amd as gla
+    gu.say("decode graph: fused decode + epilogue, 3 layers")
+    L, P, H, dk, dv = 3, 10, 16, 96, 192
+    slots_h = [4, 9, -1, 0]
+    N = len(slots_h)
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    slots = gu.dev(np.asarray(slots_h, np.int32))
+    pools = [gu.dev(synth.make_decode_state(P, H, dk, dv, seed=160 + l)) for l in range(L)]
+    pools_e = [p.clone() for p in pools]
+    params = [synth.make_epilogue_params(H, dk, dv, seed=170 + l) for l in range(L)]
+    a = [gu.dev(p[0]) for p in params]
+    w = [gla.head_rms_weights(gu.dev(p[1]), gu.dev(p[2])) for p in params]
+    q = [torch.zeros((N, H, dk), dtype=bf, device=dev) for _ in range(L)]
+    k = [torch.zeros_like(x) for x in q]
+    v = [torch.zeros((N, H, dv), dtype=bf, device=dev) for _ in range(L)]
+    gate = [torch.zeros_like(x) for x in v]
+    lg = [torch.zeros((N, H), dtype=torch.float32, device=dev) for _ in range(L)]
+    z = [torch.empty((N, H, dv), dtype=bf, device=dev) for _ in range(L)]
+    z_e = [torch.empty_like(x) for x in z]
+
+    def step(pl, zz):
+        for l in range(L):
+            gla.decode_mixer(q[l], k[l], v[l], lg[l], pl[l], gate[l], a[l], w[l], 1e-6,
+                             slots=slots, z=zz[l])
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(pools, z)
+    torch.cuda.synchronize()
+    for r in range(3):
+        for l in range(L):
+            qq, kk, vv, gg = synth.make_decode_step_inputs(N, H, dk, dv, seed=1800 + 10 * r + l)
+            q[l].copy_(gu.dev(qq, bf))
+            k[l].copy_(gu.dev(kk, bf))
+            v[l].copy_(gu.dev(vv, bf))
+            lg[l].copy_(gu.dev(gg))
+            gate[l].copy_(gu.dev(synth.make_epilogue_inputs(N, H, dk, dv, seed=1900 + 10 * r + l)[4], bf))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(pools_e, z_e)
+        torch.cuda.synchronize()
+        for l in range(L):
+            assert torch.equal(z[l], z_e[l]) and torch.equal(pools[l], pools_e[l]), (r, l)
+        assert torch.count_nonzero(z[0][2]) == 0  # the padded lane
