@@ -325,6 +325,29 @@ def _device_inputs(B, T, H, dk, dv, gate_bias, seed, dev):
     return q, k, v, lg
 
 
+def bench_tiny(args):
+    """The tiny fp32 workload (B=1, H=2, T=256, d=64, fp32 inputs and
+    arithmetic, chunk 64): launch-latency bound, reported for information."""
+    import torch
+
+    import gated_linear_attention_amd as gla
+    from gated_linear_attention_amd import synth
+
+    w = synth.WORKLOADS["tiny_f32"]
+    dev = torch.device("cuda:0")
+    q, k, v, lg, _, _ = synth.make_forward_inputs(w)
+    tq, tk, tv, tl = (torch.from_numpy(a).to(dev) for a in (q, k, v, lg))
+    o = torch.empty((w.B, w.T, w.H, w.dv), device=dev)
+    S_T = torch.empty((w.B, w.H, w.dk, w.dv), device=dev)
+    fn = lambda i: gla.fwd_chunked(tq, tk, tv, tl, chunk_size=64, o=o, S_T=S_T)
+    warm_up(fn, 20, min(args.warm_seconds, 0.2))
+    steps = 200
+    wall, kern_ms = time_launches(fn, steps, torch.cuda.current_stream(dev))
+    return {"workload": "tiny_f32", "B": w.B, "T": w.T, "H": w.H, "d": w.dk,
+            "call_us": round(1e6 * wall / steps, 2), "event_us": round(1e3 * kern_ms, 2),
+            **{f"{k}_us": round(1e3 * v, 2) for k, v in percentiles_ms(time_launches.last).items()}}
+
+
 def bench_prefill(args):
     """The 65,536-token prefill: B=1, H=32, d=128, bf16, S0 ~ N(0, 0.02^2), at
     both chunk sizes; the forward splits the sequence over the CUs (state
@@ -737,6 +760,8 @@ def main():
         log("laplace shape: building inputs")
         lap = bench_laplace(args)
         log(f"laplace: fwd {lap['forward']} decode {lap['decode']['gbs']} GB/s")
+    tiny = bench_tiny(args)
+    log(f"tiny_f32: {tiny}")
     pre = var = None
     if not args.no_long:
         log("prefill_64k: building inputs")
@@ -778,6 +803,7 @@ def main():
         "other_chunk": fwd["other_chunk"],
         "backward": bwd,
         "decode": dec,
+        "tiny_f32": tiny,
         "prefill_64k": pre,
         "varlen_64": var,
         "laplace": lap,
