@@ -183,6 +183,21 @@ __global__ __launch_bounds__(512) void decode_step_rows_kernel(const Tin *__rest
   }
 }
 
+// Sum over the 64 lanes of a wavefront (every lane active), returned as a
+// wave-uniform value: pairs and quads by quad permutes, rows of 16 by row
+// rotations, then the row broadcasts carry rows 0-1 into row 3, whose last
+// lane ends with the total.
+__device__ __forceinline__ float dpp_add(float x, int v) { return x + __int_as_float(v); }
+__device__ __forceinline__ float wave_total(float x) {
+  x = dpp_add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+  x = dpp_add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));
+  x = dpp_add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+  x = dpp_add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+  x = dpp_add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false));
+  x = dpp_add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 // One decode step followed by the token-mixer epilogue in the same workgroup
 // (Laplace 3B on AWS Trainium2, "GLA mixer": the readout o of a head gets a
 // gated copy of v, o' = o + sigmoid(q . (a * k)) v, then the head's RMSNorm
@@ -214,17 +229,27 @@ __global__ __launch_bounds__(512) void decode_mixer_kernel(
   if (slots) {
     const int slot = slots[p / H];
     if (slot < 0 || slot >= P) {  // padded lane: no state touched, z = 0
-      if (t < TPR) {
-        Tout *zp = z + p * DV + 4 * t;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) store_from_f32(zp, j, 0.f);
-      }
+      if (t < TPR) store4_from_f32(z + p * DV + 4 * t, f32x4{0.f, 0.f, 0.f, 0.f});
       return;
     }
     sp = (size_t)slot * H + h;
   }
   f32x4 *Sp = reinterpret_cast<f32x4 *>(S + sp * (size_t)(DK * DV));
 
+  // The epilogue's own operands go out before the state stream: loads and
+  // stores share one counter, so a load issued after the state stores would
+  // make its first use wait for all of them.
+  // Branch-free (clamped indices, unused values dropped later), so that they
+  // share a basic block with the state loads and nothing waits for them early.
+  const int tk = t < DK ? t : 0, tc = t < TPR ? t : 0;
+  const float lq = load_as_f32(q, p * DK + tk), la = a[(size_t)h * DK + tk],
+              lk = load_as_f32(k, p * DK + tk);  // the logit q . (a * k): one key channel per thread
+  float go[4], wr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    go[j] = load_as_f32(gout, p * DV + 4 * tc + j);
+    wr[j] = w[(size_t)h * DV + 4 * tc + j];
+  }
   f32x4 s[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) s[i] = __builtin_nontemporal_load(Sp + (r0 + i * RP) * TPR + c4);
@@ -245,11 +270,8 @@ __global__ __launch_bounds__(512) void decode_mixer_kernel(
     acc += qq * x;
   }
   red[r0][c4] = acc;
-  // the logit q . (a * k): one key channel per thread, summed over the block
-  float lp = 0.f;
-  if (t < DK) lp = load_as_f32(q, p * DK + t) * a[(size_t)h * DK + t] * load_as_f32(k, p * DK + t);
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) lp += __shfl_xor(lp, m);
+  // the logit, summed over the block
+  const float lp = wave_total(t < DK ? lq * la * lk : 0.f);
   if (t % 64 == 0) lred[t / 64] = lp;
   __syncthreads();
   if (t < 64) {
@@ -263,17 +285,14 @@ __global__ __launch_bounds__(512) void decode_mixer_kernel(
     }
     const float sg = 1.f / (1.f + expf(-logit));
     const f32x4 x = o + sg * vv;  // thread t < TPR owns columns 4t .. 4t+3 (c4 = t)
-    float ss = t < TPR ? x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3] : 0.f;
-#pragma unroll
-    for (int m = 32; m > 0; m >>= 1) ss += __shfl_xor(ss, m);
+    const float ss = wave_total(t < TPR ? x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3] : 0.f);
     const float inv = 1.f / sqrtf(ss * (1.f / DV) + eps);
     if (t < TPR) {
       Tout *zp = z + p * DV + 4 * t;
+      f32x4 zz;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float gg = load_as_f32(gout, p * DV + 4 * t + j);
-        store_from_f32(zp, j, x[j] * inv * w[(size_t)h * DV + 4 * t + j] * (gg / (1.f + expf(-gg))));
-      }
+      for (int j = 0; j < 4; ++j) zz[j] = x[j] * inv * wr[j] * (go[j] / (1.f + expf(-go[j])));
+      store4_from_f32(zp, zz);
     }
   }
 }
