@@ -49,11 +49,18 @@ def _ptr(x):
     return None if x is None else x.data_ptr()
 
 
-def _require(x, name, dtype=None, device=None):
+def _require(x, name, dtype=None, device=None, align=16):
+    """Contiguous, of the given dtype and device, and starting on an `align`-byte
+    boundary (16 for tensors; 4 for the log-gate streams and int32 arrays)."""
     if x is None:
         return
+    if x.device.type != "cuda":
+        raise ValueError(f"{name} must be in GPU memory, got a {x.device.type} tensor")
     if not x.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if x.data_ptr() % align:
+        raise ValueError(f"{name} must start on a {align}-byte boundary (a view with a storage "
+                         f"offset may not); pass a copy")
     if dtype is not None and x.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {x.dtype}")
     if device is not None and x.device != device:
@@ -97,9 +104,9 @@ def _fwd(q, k, v, g, S0, cu_seqlens, chunk_size, out_dtype, output_final_state, 
     _require(q, "q", None, dev)
     _require(k, "k", q.dtype, dev)
     _require(v, "v", q.dtype, dev)
-    _require(g, "g", torch.float32, dev)
+    _require(g, "g", torch.float32, dev, align=4)
     _require(S0, "S0", torch.float32, dev)
-    _require(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, dev, align=4)
     g_shape = (H,) if fixed_decay else (B, T, H)
     if tuple(k.shape) != (B, T, H, dk) or tuple(v.shape[:3]) != (B, T, H) or tuple(g.shape) != g_shape:
         raise ValueError("inconsistent q/k/v/g shapes")
@@ -143,10 +150,10 @@ def bwd_chunked(q, k, v, g, dO, S0=None, cu_seqlens=None, dS_T=None, chunk_size:
     _require(k, "k", q.dtype, dev)
     _require(v, "v", q.dtype, dev)
     _require(dO, "dO", q.dtype, dev)
-    _require(g, "g", torch.float32, dev)
+    _require(g, "g", torch.float32, dev, align=4)
     _require(S0, "S0", torch.float32, dev)
     _require(dS_T, "dS_T", torch.float32, dev)
-    _require(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, dev, align=4)
     if (tuple(k.shape) != (B, T, H, dk) or tuple(v.shape[:3]) != (B, T, H)
             or tuple(g.shape) != (B, T, H) or tuple(dO.shape) != tuple(v.shape)):
         raise ValueError("inconsistent q/k/v/g/dO shapes")
@@ -186,7 +193,7 @@ def decode_step(q, k, v, g, S, out_dtype=None, o=None):
     _require(q, "q", None, dev)
     _require(k, "k", q.dtype, dev)
     _require(v, "v", q.dtype, dev)
-    _require(g, "g", torch.float32, dev)
+    _require(g, "g", torch.float32, dev, align=4)
     _require(S, "S", torch.float32, dev)
     if tuple(S.shape) != (N, H, dk, dv) or tuple(g.shape) != (N, H):
         raise ValueError("inconsistent decode shapes")
@@ -216,9 +223,9 @@ def decode_step_slots(q, k, v, g, S_pool, slots, out_dtype=None, o=None):
     _require(q, "q", None, dev)
     _require(k, "k", q.dtype, dev)
     _require(v, "v", q.dtype, dev)
-    _require(g, "g", torch.float32, dev)
+    _require(g, "g", torch.float32, dev, align=4)
     _require(S_pool, "S_pool", torch.float32, dev)
-    _require(slots, "slots", torch.int32, dev)
+    _require(slots, "slots", torch.int32, dev, align=4)
     if tuple(S_pool.shape[1:]) != (H, dk, dv) or tuple(g.shape) != (N, H) or slots.numel() != N:
         raise ValueError("inconsistent decode shapes")
     out_dtype = torch.float32 if out_dtype is None else out_dtype
@@ -297,11 +304,11 @@ def decode_mixer(q, k, v, g, S, g_out, a, rms_w, eps: float = 1e-6, slots=None,
     dv = v.shape[-1]
     dev = q.device
     for x, name, dt in ((q, "q", None), (k, "k", q.dtype), (v, "v", q.dtype),
-                        (g, "g", torch.float32), (S, "S", torch.float32),
-                        (g_out, "g_out", q.dtype), (a, "a", torch.float32),
-                        (rms_w, "rms_w", torch.float32)):
+                        (S, "S", torch.float32), (g_out, "g_out", q.dtype),
+                        (a, "a", torch.float32), (rms_w, "rms_w", torch.float32)):
         _require(x, name, dt, dev)
-    _require(slots, "slots", torch.int32, dev)
+    _require(g, "g", torch.float32, dev, align=4)
+    _require(slots, "slots", torch.int32, dev, align=4)
     if (tuple(S.shape[1:]) != (H, dk, dv) or tuple(g.shape) != (N, H)
             or tuple(g_out.shape) != (N, H, dv) or tuple(a.shape) != (H, dk)
             or tuple(rms_w.shape) != (H, dv) or (slots is None and S.shape[0] != N)

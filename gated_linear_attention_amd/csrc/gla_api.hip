@@ -3,6 +3,7 @@
 #include <climits>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 
 #include "gla.h"
 #include "gla_internal.h"
@@ -145,6 +146,21 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 size_t dtype_size(gla_dtype t) { return t == GLA_BF16 ? 2 : 4; }
 
+// Tensors that the kernels read or write in 8- or 16-byte pieces, or copy
+// straight into LDS, must start on a 16-byte boundary; the per-token scalar
+// streams (log-gates, their gradient, sequence offsets, slots) on their
+// element size. NULL passes both.
+bool all_al16(std::initializer_list<const void *> ps) {
+  for (const void *p : ps)
+    if ((uintptr_t)p & 15) return false;
+  return true;
+}
+bool all_al4(std::initializer_list<const void *> ps) {
+  for (const void *p : ps)
+    if ((uintptr_t)p & 3) return false;
+  return true;
+}
+
 bool valid_dtype(int t) { return t == GLA_F32 || t == GLA_BF16; }
 
 }  // namespace
@@ -259,6 +275,8 @@ gla_status fwd_checked(const void *q, const void *k, const void *v, const float 
   if ((long)B * T > INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
   if (!fwd_dims(dk, dv)) return GLA_ERR_UNSUPPORTED;
   if (chunk_size != 64 && chunk_size != 128) return GLA_ERR_UNSUPPORTED;
+  if (!all_al16({q, k, v, o, S0, S_T, workspace}) || !all_al4({g, cu_seqlens}))
+    return GLA_ERR_INVALID_ARGUMENT;
   const int N = num_seqs;
   if (H == 0 || N == 0) return GLA_OK;
   const size_t ntok = (size_t)B * T * H;
@@ -371,6 +389,9 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   if ((long)B * T > INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
   if (!supported_head_dim(DK) || !supported_head_dim(DV)) return GLA_ERR_UNSUPPORTED;
   if (chunk_size != 64 && chunk_size != 128) return GLA_ERR_UNSUPPORTED;
+  if (!all_al16({q, k, v, dO, S0, dS_T, dq, dk, dv, dS0, workspace}) ||
+      !all_al4({g, dg, cu_seqlens}))
+    return GLA_ERR_INVALID_ARGUMENT;
   const int N = num_seqs;
   if (H == 0 || N == 0) return GLA_OK;
   const size_t ntok = (size_t)B * T * H;
@@ -441,6 +462,7 @@ gla_status gla_decode_step(const void *q, const void *k, const void *v, const fl
   if (N < 0 || H < 0) return GLA_ERR_INVALID_ARGUMENT;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
   if (!fwd_dims(dk, dv)) return GLA_ERR_UNSUPPORTED;
+  if (!all_al16({q, k, v, S, o}) || !all_al4({g})) return GLA_ERR_INVALID_ARGUMENT;
   const size_t pairs = (size_t)N * H;
   if (pairs == 0) return GLA_OK;
   if (pairs > (size_t)INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
@@ -465,6 +487,7 @@ gla_status gla_decode_step_slots(const void *q, const void *k, const void *v, co
   if (N < 0 || P < 0 || H < 0) return GLA_ERR_INVALID_ARGUMENT;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
   if (!fwd_dims(dk, dv)) return GLA_ERR_UNSUPPORTED;
+  if (!all_al16({q, k, v, S_pool, o}) || !all_al4({g, slots})) return GLA_ERR_INVALID_ARGUMENT;
   const size_t pairs = (size_t)N * H;
   if (pairs == 0) return GLA_OK;
   if (pairs > (size_t)INT_MAX || (size_t)P * H > (size_t)INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
@@ -492,6 +515,7 @@ gla_status gla_mixer_epilogue(const void *o, const void *q, const void *k, const
     return GLA_ERR_INVALID_ARGUMENT;
   if (!(eps >= 0.f) || eps > 3.4e38f) return GLA_ERR_INVALID_ARGUMENT;  // NaN, negative, inf
   if (!fwd_dims(dk, dv)) return GLA_ERR_UNSUPPORTED;
+  if (!all_al16({o, q, k, v, g, a, rms_w, z})) return GLA_ERR_INVALID_ARGUMENT;
   const size_t rows = (size_t)n_tokens * H;
   if (rows == 0) return GLA_OK;
   if (rows > (size_t)INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
@@ -522,6 +546,8 @@ gla_status gla_decode_mixer(const void *q, const void *k, const void *v, const f
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
   if (!(eps >= 0.f) || eps > 3.4e38f) return GLA_ERR_INVALID_ARGUMENT;
   if (!fwd_dims(dk, dv)) return GLA_ERR_UNSUPPORTED;
+  if (!all_al16({q, k, v, S, g_out, a, rms_w, z}) || !all_al4({g, slots}))
+    return GLA_ERR_INVALID_ARGUMENT;
   const size_t pairs = (size_t)N * H;
   if (pairs == 0) return GLA_OK;
   const size_t n_states = slots ? (size_t)P * H : pairs;

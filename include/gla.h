@@ -20,6 +20,12 @@
  *    caller. The library allocates no device memory and keeps no state
  *    between calls; it is re-entrant, and calls on different streams do not
  *    interact. Calls on the same buffers from two streams race.
+ *  - Alignment: every tensor and workspace pointer must be 16-byte aligned,
+ *    except the fp32 log-gate streams (g, log_lambda, dlog_g) and the int32
+ *    arrays (cu_seqlens, slots), which need 4-byte alignment. (Fresh
+ *    allocations of HIP and of PyTorch's caching allocator are 256-byte
+ *    aligned; a view with a storage offset may not be.) A misaligned pointer
+ *    returns GLA_ERR_INVALID_ARGUMENT.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued on it and the call returns without synchronising.
  *  - Argument errors are detected on the host before anything is enqueued and
@@ -45,7 +51,8 @@ extern "C" {
 
 typedef enum {
   GLA_OK = 0,
-  GLA_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad dtype, o aliasing an input */
+  GLA_ERR_INVALID_ARGUMENT = 1, /* null or misaligned pointer, negative size, bad dtype,
+                                   o aliasing an input */
   GLA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (head dims, chunk size) */
   GLA_ERR_WORKSPACE = 3,        /* workspace NULL or smaller than the size query returns */
   GLA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */

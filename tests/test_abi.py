@@ -74,13 +74,13 @@ def test_fwd_rejects_bad_arguments_before_launch():
 
 def test_fixed_decay_fwd_rejects_bad_arguments_before_launch():
     P = dict(q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30),
-             o=FAKE + (4 << 30), H=4)
+             o=FAKE + (4 << 30), H=8)
     assert _fwd(True, B=-1, **P) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert _fwd(True, dk=96, **P) == _lib.GLA_ERR_UNSUPPORTED
     assert _fwd(True, C=256, **P) == _lib.GLA_ERR_UNSUPPORTED
     assert _fwd(True, **{**P, "g": None}) == _lib.GLA_ERR_INVALID_ARGUMENT
-    # log_lambda holds H = 4 floats: an o that starts at its last one overlaps it
-    assert _fwd(True, **{**P, "o": P["g"] + 12}) == _lib.GLA_ERR_INVALID_ARGUMENT
+    # log_lambda holds H = 8 floats: an o that starts at its fifth overlaps it
+    assert _fwd(True, **{**P, "o": P["g"] + 16}) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert _fwd(True, H=0, **{k: v for k, v in P.items() if k != "H"}) == _lib.GLA_OK
 
 
@@ -114,7 +114,7 @@ def test_decode_rejects_bad_arguments_before_launch():
     assert call(base, ind=5) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call([None] + base[1:]) == _lib.GLA_ERR_INVALID_ARGUMENT
     bad = list(base)
-    bad[5] = base[4] + 8  # o inside S
+    bad[5] = base[4] + 16  # o inside S
     assert call(bad) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call(base, N=0) == _lib.GLA_OK
 
@@ -189,7 +189,7 @@ def test_epilogue_rejects_bad_arguments_before_launch():
     assert call(z=None) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call(z=P[1] + 64) == _lib.GLA_ERR_INVALID_ARGUMENT      # z overlaps q
     assert call(z=P[5]) == _lib.GLA_ERR_INVALID_ARGUMENT           # z overlaps a
-    assert call(z=P[0] + 4) == _lib.GLA_ERR_INVALID_ARGUMENT       # z partly over o
+    assert call(z=P[0] + 16) == _lib.GLA_ERR_INVALID_ARGUMENT      # z partly over o
     assert call(z=P[0], outd=BF) == _lib.GLA_ERR_INVALID_ARGUMENT  # in place needs o's dtype
     assert call(H=0) == _lib.GLA_OK
 
@@ -215,3 +215,70 @@ def test_decode_mixer_rejects_bad_arguments_before_launch():
     assert call(ptrs=(q, k, v, g, q + 16)) == _lib.GLA_ERR_INVALID_ARGUMENT  # S over q
     assert call(H=0) == _lib.GLA_OK
 
+
+
+def test_misaligned_pointers_rejected_before_launch():
+    """Tensors need 16-byte alignment (4 bytes for the log-gate streams and the
+    int32 arrays); each entry point refuses an offset pointer, and accepts the
+    scalar streams at 4-byte offsets."""
+    lib = _lib.load()
+    G = 1 << 30
+    BAD = _lib.GLA_ERR_INVALID_ARGUMENT
+    F32, BF = _lib.GLA_F32, _lib.GLA_BF16
+    P = dict(q=FAKE, k=FAKE + G, v=FAKE + 2 * G, g=FAKE + 3 * G, o=FAKE + 4 * G, H=0)
+    # H = 0 returns before launching anything, but after the pointer checks
+    assert _fwd(**P) == _lib.GLA_OK
+    for name, off in [("q", 2), ("k", 8), ("v", 4), ("o", 8), ("S0", 4), ("ST", 12)]:
+        base = P.get(name, FAKE + 5 * G)
+        kw = {**P, name: base + off}
+        assert _fwd(**kw) == BAD, name
+        assert _fwd(True, **kw) == BAD, name
+    assert _fwd(**{**P, "g": P["g"] + 4}) == _lib.GLA_OK      # gates: 4-byte alignment
+    assert _fwd(**{**P, "g": P["g"] + 2}) == BAD
+    assert _fwd(**{**P, "cu": FAKE + 6 * G + 4, "B": 1, "N": 1}) == _lib.GLA_OK
+    assert _fwd(**{**P, "cu": FAKE + 6 * G + 2, "B": 1, "N": 1}) == BAD
+    assert _fwd(**{**P, "ws": FAKE + 7 * G + 8, "wsb": 1 << 20}) == BAD
+
+    B = dict(q=FAKE, k=FAKE + G, v=FAKE + 2 * G, g=FAKE + 3 * G, dO=FAKE + 4 * G,
+             dq=FAKE + 5 * G, dk=FAKE + 6 * G, dv=FAKE + 7 * G, dg=FAKE + 8 * G, H=0)
+    assert _bwd(**B) == _lib.GLA_OK
+    for name in ["q", "k", "v", "dO", "dq", "dk", "dv"]:
+        assert _bwd(**{**B, name: B[name] + 8}) == BAD, name
+    assert _bwd(**{**B, "dS0": FAKE + 9 * G + 4}) == BAD
+    assert _bwd(**{**B, "dg": B["dg"] + 4}) == _lib.GLA_OK
+    assert _bwd(**{**B, "dg": B["dg"] + 1}) == BAD
+
+    ptr = [FAKE + i * G for i in range(6)]  # q, k, v, g, S, o
+    dec = lambda p: lib.gla_decode_step(*p, 4, 2, 64, 64, BF, F32, None)
+    for i in [0, 1, 2, 4, 5]:
+        assert dec([x + 8 * (j == i) for j, x in enumerate(ptr)]) == BAD, i
+    slots = FAKE + 40 * G
+    dsl = lambda p, s: lib.gla_decode_step_slots(*p[:5], s, p[5], 4, 8, 2, 64, 64, BF, F32, None)
+    assert dsl(ptr, slots + 2) == BAD
+    assert dsl([x + 8 * (j == 4) for j, x in enumerate(ptr)], slots) == BAD  # the pool
+
+    E = [FAKE + (i << 30) for i in range(7)]  # o, q, k, v, g, a, rms_w
+    epi = lambda p, z: lib.gla_mixer_epilogue(*p, 1e-6, z, 16, 2, 64, 64, F32, BF, F32, None)
+    for i in range(7):
+        assert epi([x + 8 * (j == i) for j, x in enumerate(E)], FAKE + (8 << 30)) == BAD, i
+    assert epi(E, FAKE + (8 << 30) + 4) == BAD
+
+    q, k, v, g, S, go, a, w, z = (FAKE + (i << 30) for i in range(9))
+    mix = lambda q=q, S=S, go=go, z=z, g=g: lib.gla_decode_mixer(
+        q, k, v, g, S, None, 0, go, a, w, 1e-6, z, 4, 2, 64, 64, BF, F32, None)
+    assert mix(q=q + 8) == BAD and mix(S=S + 4) == BAD and mix(go=go + 2) == BAD
+    assert mix(z=z + 8) == BAD and mix(g=g + 2) == BAD
+
+
+def test_binding_refuses_host_tensors():
+    """The binding hands only device memory to the library: host tensors are
+    refused before any call into it."""
+    import torch
+    import gated_linear_attention_amd as gla
+    q = torch.zeros((1, 64, 1, 64), dtype=torch.bfloat16)
+    g = torch.zeros((1, 64, 1), dtype=torch.float32)
+    for call in (lambda: gla.fwd_chunked(q, q, q, g),
+                 lambda: gla.decode_step(q[0], q[0], q[0], g[0], torch.zeros((64, 1, 64, 64))),
+                 lambda: gla.bwd_chunked(q, q, q, g, q)):
+        with pytest.raises(ValueError, match="GPU memory"):
+            call()

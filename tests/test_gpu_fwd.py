@@ -195,3 +195,23 @@ def test_varlen_64_full_size_sampled_heads(C):
     """64 packed sequences, lengths uniform in [128, 8192], H=16, d=128, bf16."""
     gu.say(f"varlen_64 full size C={C}")
     check(*synth.make_forward_inputs(W["varlen_64"]), "bf16", C=C, heads=[1, 12], tight=1e-4)
+
+
+def test_binding_refuses_misaligned_views():
+    """A contiguous view that starts 4 bytes into its storage is refused by the
+    binding (before any launch) with a message; its copy runs."""
+    import torch
+    import gated_linear_attention_amd as gla
+    gu.say("misaligned views refused")
+    dev = torch.device("cuda:0")
+    n = 64 * 64
+    buf = torch.randn(n + 8, device=dev).to(torch.bfloat16)
+    q = buf[2:2 + n].view(1, 64, 1, 64)  # 4 bytes past a 16-byte boundary
+    assert q.is_contiguous() and q.data_ptr() % 16 == 4
+    k = torch.randn((1, 64, 1, 64), device=dev).to(torch.bfloat16)
+    g = torch.full((1, 64, 1), -0.1, device=dev)
+    with pytest.raises(ValueError, match="16-byte boundary"):
+        gla.fwd_chunked(q, k, k, g)
+    o, _ = gla.fwd_chunked(q.clone(), k, k, g)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
