@@ -637,6 +637,12 @@ def bench_decode_layers(args, layers=24, batches=(20, 1280)):
                         "fused_graph_ms": round(replay_f * 1e3, 4),
                         "fused_tokens_per_s_graph": round(N / replay_f, 1),
                         "fused_state_gbs_graph": round(state_bytes / replay_f / 1e9, 1)}
+        if N == 1280:  # HBM bytes per fused launch from the committed counter runs
+            out[f"N{N}"]["fused_kernel"] = "decode_mixer_kernel<96,192,8,bf16,bf16>"
+            out[f"N{N}"]["fused_algorithmic_bytes_per_layer"] = N * H * (
+                2 * dk * dv * 4 + 2 * dk * 2 + 3 * dv * 2 + 4)
+            out[f"N{N}"]["fused_traffic_per_layer"] = measured_traffic(
+                "decode_mixer_laplace_1280x16", ["decode.hip", "gla_common.h"])
         del pools, qkv, o, z, graph, graph_f
         torch.cuda.empty_cache()
     return out
