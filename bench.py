@@ -507,7 +507,7 @@ def bench_laplace(args):
     z = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
     alg_epi = tok_heads * (4 * dv + 2 * dk + 2 * dk + 2 * dv + 2 * dv + 2 * dv)
     epi = timed(lambda i: gla.mixer_epilogue(o, tq, tk, tv, gate, ta, rms_w, 1e-6, z=z), alg_epi)
-    epi.update({"algorithmic_bytes": alg_epi, "kernel": "mixer_epilogue_kernel<96,192,float,bf16,bf16>",
+    epi.update({"algorithmic_bytes": alg_epi, "kernel": "mixer_epilogue_r16_kernel<96,192,float,bf16,bf16>",
                 "traffic": measured_traffic("mixer_epilogue_laplace_2k", ["epilogue.hip", "gla_common.h"])})
     del tq, tk, tv, tlg, o, S_T, gate, z
 

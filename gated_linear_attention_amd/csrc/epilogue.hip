@@ -156,6 +156,11 @@ __device__ __forceinline__ f32x2 ld2(const uint16_t *p) {
   return f32x2{__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
 }
 
+// Rows per 16-lane group in the kernel below: one (with their loads, a lane
+// already has 12 value and 6 key channels in flight; two, three and four rows
+// measured 3%, 6% and 8% slower).
+constexpr int kR16Rows = 1;
+
 // 192-channel rows (the Laplace heads), where d_v / 4 = 48 lanes per row would
 // leave 16 of 64 idle: a (token, head) row is one DPP row of 16 lanes, four
 // rows per wavefront (11% faster on laplace_2k; slower for 64- and
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(256) void mixer_epilogue_r16_kernel(
   // writes the same elements of z.
   constexpr int CV = DV / 64;  // 4-channel value pieces per lane
   constexpr int CK = DK / 32;  // 2-channel key pieces per lane
-  constexpr int U = kEpiUnroll;
+  constexpr int U = kR16Rows;
   static_assert(DV % 64 == 0 && DK % 32 == 0, "row layout");
   const int lane = threadIdx.x % 64;
   const int li = lane % 16;
@@ -238,7 +243,7 @@ hipError_t launch_epi_t(const void *o, const void *q, const void *k, const void 
                         const void *g, const float *a, const float *w, float eps, void *z,
                         long n_rows, int H, hipStream_t stream) {
   if constexpr (DV == 192) {
-    const long per_block = 16L * kEpiUnroll;  // four wavefronts of four rows, U rows each
+    const long per_block = 16L * kR16Rows;  // four wavefronts of four row groups
     const long blocks = (n_rows + per_block - 1) / per_block;
     hipLaunchKernelGGL((mixer_epilogue_r16_kernel<DK, DV, To, Tin, Tout>),
                        dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<const To *>(o),
