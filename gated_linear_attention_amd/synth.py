@@ -206,10 +206,12 @@ def laplace_decay_schedule(H: int = 16, t_min: float = 1.0, t_max: float = 2048.
     (lambda_0 = 0.5) and head 15 half-life 2048 (lambda_15 ~ 0.9997). The
     equations themselves are lost from the page; the reading taken here is a
     geometric spread of half-lives, half_life_h = T_min (T_max/T_min)^(h/(H-1)),
-    with lambda_h = 2^(-1/half_life_h). Returns ln(lambda_h), shape [H], fp64.
+    with lambda_h = 2^(-1/half_life_h); a single head (H = 1) takes T_min.
+    Returns ln(lambda_h), shape [H], fp64.
     """
     h = np.arange(H, dtype=np.float64)
-    half_life = t_min * (t_max / t_min) ** (h / (H - 1))
+    frac = h / (H - 1) if H > 1 else np.zeros(H)
+    half_life = t_min * (t_max / t_min) ** frac
     return -np.log(2.0) / half_life
 
 
