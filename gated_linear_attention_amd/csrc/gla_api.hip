@@ -1,6 +1,7 @@
 // C ABI of libgla.so: argument validation, work planning and kernel launches.
 #include <algorithm>
 #include <climits>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <initializer_list>
@@ -68,6 +69,22 @@ int choose_seg_len(int B, int T, int H, int dk, int dv, int N, int C, bool has_c
     } else {
       const long nseg = (ncu + units - 1) / units;
       L = (T + nseg - 1) / nseg;
+    }
+    if (in_dtype == GLA_BF16) {
+      // A split adds three launches (plan, state pass, combine) and a combine
+      // chain that is sequential in the segments of a sequence, so on the
+      // matrix-core kernels short segments do not pay: a sequence of at most
+      // 8 chunks (chunk 64) or 2 (chunk 128) runs whole, and at chunk 64
+      // segments keep about sqrt(chunks) / 1.7 chunks (measured on MI355X for
+      // 256 - 4,096 tokens and 1 - 64 work units; the fp32 kernel, several
+      // times slower per chunk, always gains from the split).
+      const long chunks = ((long)T + C - 1) / C;
+      if (chunks <= (C == 64 ? 8 : 2)) {
+        L = T;
+      } else if (C == 64) {
+        const long seg_chunks = std::max(1L, std::lround(std::sqrt((double)chunks) / 1.7));
+        L = std::max(L, seg_chunks * C);
+      }
     }
   } else {
     const long work = (long)T * H * n_slices;
