@@ -89,7 +89,13 @@ int choose_seg_len(int B, int T, int H, int dk, int dv, int N, int C, bool has_c
   } else {
     const long work = (long)T * H * n_slices;
     L = work / cu_count();
-    (void)N;
+    if (in_dtype == GLA_BF16 && C == 64 && N > 0) {
+      // the segment floor of dense batches, from the mean sequence length
+      // (the lengths themselves stay on the device)
+      const double mean_chunks = (double)T / N / C;
+      const long seg_chunks = std::max(1L, std::lround(std::sqrt(mean_chunks) / 1.7));
+      L = std::max(L, seg_chunks * C);
+    }
   }
   L = round_up(L < C ? C : L, C);
   const long cap = round_up(T < C ? C : T, C);
