@@ -172,6 +172,17 @@ def bench_forward(args):
     C2 = 128 if C == 64 else 64
     warm_up(step_at(C2), 10, 0.2)
     wall2, kern_ms2 = time_launches(step_at(C2), args.steps, stream)
+    # the same forward writing o in bf16 (as a bf16 training stack would take it)
+    o16 = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+
+    def step_bf16_out(i):
+        q, k, v, lg = sets[i % 3]
+        gla.fwd_chunked(q, k, v, lg, None, None, chunk_size=C, o=o16, S_T=S_T,
+                        out_dtype=torch.bfloat16)
+
+    warm_up(step_bf16_out, 10, 0.2)
+    wall3, kern_ms3 = time_launches(step_bf16_out, args.steps, stream)
+    alg_bytes16 = alg_bytes - tok_heads * dv * 2
     res = {
         "tokens": tokens,
         "ms_per_step": ms_per_step,
@@ -189,6 +200,10 @@ def bench_forward(args):
                         "kernel_ms": round(kern_ms2, 5),
                         "tokens_per_s": round(tokens / (wall2 / args.steps), 1),
                         "hbm_frac": round(alg_bytes / (kern_ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "bf16_out": {"kernel_ms": round(kern_ms3, 5),
+                     "tokens_per_s": round(tokens / (wall3 / args.steps), 1),
+                     "algorithmic_bytes": alg_bytes16,
+                     "hbm_frac": round(alg_bytes16 / (kern_ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "mfma": {"algorithmic_tflops": round(alg_flops / (kern_ms * 1e-3) / 1e12, 1),
                  "algorithmic_util": round(alg_flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  "issued_tflops": round(issued_flops / (kern_ms * 1e-3) / 1e12, 1),
@@ -807,6 +822,7 @@ def main():
         "roofline": fwd["roofline"],
         "mfma": fwd["mfma"],
         "other_chunk": fwd["other_chunk"],
+        "bf16_out": fwd["bf16_out"],
         "backward": bwd,
         "decode": dec,
         "tiny_f32": tiny,
