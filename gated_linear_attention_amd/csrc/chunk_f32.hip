@@ -12,11 +12,14 @@
 // D is evaluated per element as the exponential of a difference (never as a
 // product e^{b_i} e^{-b_j}, which overflows for strong decay).
 //
-// This path serves fp32 callers that need fp32 accuracy; the bf16 path runs
-// the same algebra on the matrix cores. One 256-thread workgroup owns one
-// work item (a run of tokens of one sequence) for one head and a slice of
-// DVS = 32 state columns; the state slice lives in LDS, Q and K are staged
-// 32 key-dimensions at a time.
+// This path serves fp32 callers that need fp32 accuracy. One 256-thread
+// workgroup owns one work item (a run of tokens of one sequence) for one head
+// and a slice of DVS = 32 state columns; the state slice lives in LDS, Q and K
+// are staged 32 key-dimensions at a time. The four contractions (scores Q K^T,
+// the state read Q S, P V and the state update K^T V) run on the fp32 matrix
+// cores (v_mfma_f32_16x16x4_f32: fp32 operands, fp32 accumulation), each
+// wavefront owning whole 16 x 16 output tiles.
+#include "bf16_blocks.h"
 #include "gla_common.h"
 #include "gla_internal.h"
 
@@ -24,6 +27,12 @@ namespace gla {
 
 constexpr int kF32Slice = 32;  // state columns per workgroup
 constexpr int kF32DkBlk = 32;  // key dimensions staged at a time
+
+// D += A B for a 16 x 4 A and a 4 x 16 B, fp32. Lane l supplies A[l % 16][l / 16]
+// and B[l / 16][l % 16]; it holds D[4 (l / 16) + r][l % 16] in element r.
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ WorkItem item_for(const WorkItem *items, int it, int T) {
   if (items) return items[it];
@@ -49,16 +58,19 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
     Tout *__restrict__ o, const WorkItem *__restrict__ items, const int *__restrict__ n_items,
     float *__restrict__ slots, float *__restrict__ slot_gamma, int T, int H, int gts, int DV) {
   constexpr int DVS = kF32Slice, KB = kF32DkBlk;
-  constexpr int NPE = C * C / 256;    // score entries per thread
-  constexpr int NOE = C * DVS / 256;  // output entries per thread
-  constexpr int NSE = KB * DVS / 256; // state entries per thread per key block
-  static_assert(NPE >= 1 && NOE >= 1 && NSE >= 1, "tile too small");
+  constexpr int NT = C / 16;               // 16-row tiles of a chunk
+  constexpr int NST = NT * (NT + 1) / 2;   // lower-triangular score tiles
+  constexpr int SPW = (NST + 3) / 4;       // score tiles per wavefront (at most)
+  constexpr int NCT = DVS / 16;            // 16-column tiles of the slice
+  constexpr int OPW = NT * NCT / 4;        // output tiles per wavefront
+  constexpr int UPW = (KB / 16) * NCT / 4; // state tiles per wavefront per key block
+  static_assert(NT * NCT % 4 == 0 && (KB / 16) * NCT % 4 == 0 && KB % 16 == 0, "tiling");
 
   __shared__ float Qb[C][KB + 1];
   __shared__ float Kb[C][KB + 1];
   __shared__ float Vs[C][DVS + 1];
   __shared__ float P[C][C + 1];
-  __shared__ float Ss[DK][DVS];
+  __shared__ float Ss[DK][DVS + 1];
   __shared__ float bcum[C], lam[C], kap[C];
   __shared__ float gam_s, gsum_s;
 
@@ -70,6 +82,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
   const WorkItem w = item_for(items, it, T);
   const int c0 = slice * DVS;
   const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), ln = tid % 16, l4 = (tid / 16) % 4;
   const size_t dkdv = (size_t)DK * DV;
   const int sb = w.seq_begin, se = w.seq_end;
   auto mrow = [&](int t) -> size_t { return (size_t)(REV ? sb + se - 1 - t : t); };
@@ -121,14 +134,14 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
     if (tid == 0) gam_s = expf(blast);
     gsum += blast;
 
-    float oacc[NOE];
     if (!STATE_PASS) {
-      float pacc[NPE];
+      // score tiles t = wave, wave + 4, ... (lower triangle, row-major) and the
+      // output tiles u -> (row tile, column tile), accumulated over key blocks
+      f32x4 sacc[SPW], oacc[OPW];
 #pragma unroll
-      for (int m = 0; m < NPE; ++m) pacc[m] = 0.f;
+      for (int s = 0; s < SPW; ++s) sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < NOE; ++m) oacc[m] = 0.f;
-      // scores Q K^T and the state read Q S, one key block at a time
+      for (int u = 0; u < OPW; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int db = 0; db < DK; db += KB) {
         __syncthreads();
         for (int e = tid; e < C * KB; e += 256) {
@@ -138,43 +151,57 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
           Kb[i][dd] = ok ? k[(mrow(t0 + i) * H + h) * DK + db + dd] : 0.f;
         }
         __syncthreads();
+        // scores Q K^T: A = Q rows, B = K^T
 #pragma unroll
-        for (int m = 0; m < NPE; ++m) {
-          const int e = tid + 256 * m, i = e / C, j = e % C;
-          float a = 0.f;
-          if (j <= i) {
-#pragma unroll 8
-            for (int dd = 0; dd < KB; ++dd) a += Qb[i][dd] * Kb[j][dd];
+        for (int s = 0; s < SPW; ++s) {
+          const int t = wave + 4 * s;
+          if (t < NST) {
+            const int ti = tile_ti(t), tj = tile_tj(t);
+#pragma unroll
+            for (int ks = 0; ks < KB / 4; ++ks)
+              sacc[s] = mfma_f32(Qb[16 * ti + ln][4 * ks + l4], Kb[16 * tj + ln][4 * ks + l4], sacc[s]);
           }
-          pacc[m] += a;
         }
+        // state read Q S over this key block
 #pragma unroll
-        for (int m = 0; m < NOE; ++m) {
-          const int e = tid + 256 * m, i = e / DVS, c = e % DVS;
-          float a = 0.f;
-#pragma unroll 8
-          for (int dd = 0; dd < KB; ++dd) a += Qb[i][dd] * Ss[db + dd][c];
-          oacc[m] += a;
+        for (int u = 0; u < OPW; ++u) {
+          const int ot = wave + 4 * u, ti = ot / NCT, tc = ot % NCT;
+#pragma unroll
+          for (int ks = 0; ks < KB / 4; ++ks)
+            oacc[u] = mfma_f32(Qb[16 * ti + ln][4 * ks + l4], Ss[db + 4 * ks + l4][16 * tc + ln], oacc[u]);
         }
       }
-      // decay mask
+      // decay mask: P[i][j] = score * e^{b_i - b_j} for j <= i, else 0
 #pragma unroll
-      for (int m = 0; m < NPE; ++m) {
-        const int e = tid + 256 * m, i = e / C, j = e % C;
-        P[i][j] = (j <= i) ? pacc[m] * expf(bcum[i] - bcum[j]) : 0.f;
+      for (int s = 0; s < SPW; ++s) {
+        const int t = wave + 4 * s;
+        if (t < NST) {
+          const int ti = tile_ti(t), tj = tile_tj(t), j = 16 * tj + ln;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * ti + 4 * l4 + r;
+            P[i][j] = (j <= i) ? sacc[s][r] * expf(bcum[i] - bcum[j]) : 0.f;
+          }
+        }
       }
       __syncthreads();
-      // intra-chunk attention and the decayed state read
+      // o = e^{b_i} (Q S) + P V, keys up to the end of the row tile
 #pragma unroll
-      for (int m = 0; m < NOE; ++m) {
-        const int e = tid + 256 * m, i = e / DVS, c = e % DVS;
-        float a = 0.f;
-        for (int j = 0; j <= i; ++j) a += P[i][j] * Vs[j][c];
-        const float r = lam[i] * oacc[m] + a;
-        if (i < n) store_from_f32(o, (mrow(t0 + i) * H + h) * DV + c0 + c, r);
+      for (int u = 0; u < OPW; ++u) {
+        const int ot = wave + 4 * u, ti = ot / NCT, tc = ot % NCT;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[u][r] *= lam[16 * ti + 4 * l4 + r];
+        for (int ks = 0; ks < 4 * (ti + 1); ++ks)
+          oacc[u] = mfma_f32(P[16 * ti + ln][4 * ks + l4], Vs[4 * ks + l4][16 * tc + ln], oacc[u]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ti + 4 * l4 + r;
+          if (i < n) store_from_f32(o, (mrow(t0 + i) * H + h) * DV + c0 + 16 * tc + ln, oacc[u][r]);
+        }
       }
     }
-    // state advance: S <- gamma S + (kappa K)^T V, one key block at a time
+    // state advance: S <- gamma S + (kappa K)^T V, one key block at a time;
+    // each wavefront owns whole 16 x 16 tiles of the block's state rows
     for (int db = 0; db < DK; db += KB) {
       __syncthreads();
       for (int e = tid; e < C * KB; e += 256) {
@@ -184,11 +211,16 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
       __syncthreads();
       const float gam = gam_s;
 #pragma unroll
-      for (int m = 0; m < NSE; ++m) {
-        const int e = tid + 256 * m, dd = e / DVS, c = e % DVS;
-        float a = 0.f;
-        for (int j = 0; j < C; ++j) a += Kb[j][dd] * Vs[j][c];
-        Ss[db + dd][c] = gam * Ss[db + dd][c] + a;
+      for (int u = 0; u < UPW; ++u) {
+        const int ut = wave + 4 * u, td = ut / NCT, tc = ut % NCT;
+        f32x4 acc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = gam * Ss[db + 16 * td + 4 * l4 + r][16 * tc + ln];
+#pragma unroll
+        for (int ks = 0; ks < C / 4; ++ks)
+          acc = mfma_f32(Kb[4 * ks + l4][16 * td + ln], Vs[4 * ks + l4][16 * tc + ln], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ss[db + 16 * td + 4 * l4 + r][16 * tc + ln] = acc[r];
       }
     }
   }

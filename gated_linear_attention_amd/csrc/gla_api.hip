@@ -63,11 +63,13 @@ int choose_seg_len(int B, int T, int H, int dk, int dv, int N, int C, bool has_c
     L = std::atoi(env);
   } else if (!has_cu) {
     const long units = (long)B * H * n_slices;
-    const int ncu = cu_count();
-    if (units >= ncu) {
+    // workgroups to aim for: one per CU on the bf16 kernels, four on the
+    // fp32 one (two fit per CU, and it is bound by latency, not bandwidth)
+    const long target = (long)cu_count() * (in_dtype == GLA_BF16 ? 1 : 4);
+    if (units >= target) {
       L = T;
     } else {
-      const long nseg = (ncu + units - 1) / units;
+      const long nseg = (target + units - 1) / units;
       L = (T + nseg - 1) / nseg;
     }
     if (in_dtype == GLA_BF16) {
@@ -88,7 +90,7 @@ int choose_seg_len(int B, int T, int H, int dk, int dv, int N, int C, bool has_c
     }
   } else {
     const long work = (long)T * H * n_slices;
-    L = work / cu_count();
+    L = work / ((long)cu_count() * (in_dtype == GLA_BF16 ? 1 : 4));
     if (in_dtype == GLA_BF16 && C == 64 && N > 0) {
       // the segment floor of dense batches, from the mean sequence length
       // (the lengths themselves stay on the device)
