@@ -65,6 +65,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
   constexpr int OPW = NT * NCT / 4;        // output tiles per wavefront
   constexpr int UPW = (KB / 16) * NCT / 4; // state tiles per wavefront per key block
   static_assert(NT * NCT % 4 == 0 && (KB / 16) * NCT % 4 == 0 && KB % 16 == 0, "tiling");
+  static_assert(C == 64 || C == 128, "the gate scan covers one or two wavefronts");
 
   __shared__ float Qb[C][KB + 1];
   __shared__ float Kb[C][KB + 1];
@@ -102,7 +103,8 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
   for (int t0 = w.tok_begin; t0 < w.tok_end; t0 += C) {
     const int n = min(C, w.tok_end - t0);
     __syncthreads();
-    // gates: inclusive scan of the chunk's log-gates (padding rows add 0)
+    // gates: inclusive scan of the chunk's log-gates (padding rows add 0), one
+    // wavefront scan per 64 tokens; a second 64 adds the first one's total
     if (tid < C) {
       float x = 0.f;
       if (tid < n) {
@@ -113,19 +115,19 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
           x = lg[(size_t)(t0 + tid) * gts + h];
         }
       }
-      bcum[tid] = x;
+      bcum[tid] = wave_inclusive_scan(x);
     }
     for (int e = tid; e < C * DVS; e += 256) {
       const int j = e / DVS, c = e % DVS;
       Vs[j][c] = (j < n) ? v[(mrow(t0 + j) * H + h) * DV + c0 + c] : 0.f;
     }
-    for (int off = 1; off < C; off *= 2) {
-      __syncthreads();
-      float y = (tid < C && tid >= off) ? bcum[tid - off] : 0.f;
-      __syncthreads();
-      if (tid < C) bcum[tid] += y;
-    }
     __syncthreads();
+    if constexpr (C == 128) {
+      const float first = bcum[63];
+      __syncthreads();
+      if (tid >= 64 && tid < 128) bcum[tid] += first;
+      __syncthreads();
+    }
     const float blast = bcum[n - 1];
     if (tid < C) {
       lam[tid] = expf(bcum[tid]);
