@@ -87,6 +87,24 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
   const size_t dkdv = (size_t)DK * DV;
   const int sb = w.seq_begin, se = w.seq_end;
   auto mrow = [&](int t) -> size_t { return (size_t)(REV ? sb + se - 1 - t : t); };
+  // Key blocks of a chunk go through registers: the block after the one being
+  // computed is loaded while the matrix cores work on LDS (thread tid moves
+  // elements tid + 256 e, e < EPT, of the block's C x KB tile).
+  constexpr int EPT = C * KB / 256;
+  auto load_blk = [&](const float *src, int t0, int n, int db, float (&x)[EPT]) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int i = (tid + 256 * e) / KB, dd = (tid + 256 * e) % KB;
+      x[e] = i < n ? src[(mrow(t0 + i) * H + h) * DK + db + dd] : 0.f;
+    }
+  };
+  auto store_blk = [&](float (&dst)[C][KB + 1], const float (&x)[EPT], const float *scale) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int i = (tid + 256 * e) / KB, dd = (tid + 256 * e) % KB;
+      dst[i][dd] = scale ? x[e] * scale[i] : x[e];
+    }
+  };
 
   // initial state slice
   const float *sin = nullptr;
@@ -144,15 +162,18 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
       for (int s = 0; s < SPW; ++s) sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < OPW; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float qx[EPT], kx[EPT];
+      load_blk(q, t0, n, 0, qx);
+      load_blk(k, t0, n, 0, kx);
       for (int db = 0; db < DK; db += KB) {
         __syncthreads();
-        for (int e = tid; e < C * KB; e += 256) {
-          const int i = e / KB, dd = e % KB;
-          const bool ok = i < n;
-          Qb[i][dd] = ok ? q[(mrow(t0 + i) * H + h) * DK + db + dd] : 0.f;
-          Kb[i][dd] = ok ? k[(mrow(t0 + i) * H + h) * DK + db + dd] : 0.f;
-        }
+        store_blk(Qb, qx, nullptr);
+        store_blk(Kb, kx, nullptr);
         __syncthreads();
+        if (db + KB < DK) {
+          load_blk(q, t0, n, db + KB, qx);
+          load_blk(k, t0, n, db + KB, kx);
+        }
         // scores Q K^T: A = Q rows, B = K^T
 #pragma unroll
         for (int s = 0; s < SPW; ++s) {
@@ -204,13 +225,13 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
     }
     // state advance: S <- gamma S + (kappa K)^T V, one key block at a time;
     // each wavefront owns whole 16 x 16 tiles of the block's state rows
+    float kx[EPT];
+    load_blk(k, t0, n, 0, kx);
     for (int db = 0; db < DK; db += KB) {
       __syncthreads();
-      for (int e = tid; e < C * KB; e += 256) {
-        const int j = e / KB, dd = e % KB;
-        Kb[j][dd] = (j < n) ? k[(mrow(t0 + j) * H + h) * DK + db + dd] * kap[j] : 0.f;
-      }
+      store_blk(Kb, kx, kap);
       __syncthreads();
+      if (db + KB < DK) load_blk(k, t0, n, db + KB, kx);
       const float gam = gam_s;
 #pragma unroll
       for (int u = 0; u < UPW; ++u) {
