@@ -98,6 +98,24 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
       x[e] = i < n ? src[(mrow(t0 + i) * H + h) * DK + db + dd] : 0.f;
     }
   };
+  // the chunk's log-gate (thread tid < C holds token tid) and V slice elements
+  // (tid + 256 e, e < VPT, of the C x DVS tile), also loaded a chunk ahead
+  constexpr int VPT = C * DVS / 256;
+  auto load_gate = [&](int t0, int n) -> float {
+    if (tid >= n) return 0.f;
+    if (REV) {
+      const int u = t0 + tid - sb;
+      return u == 0 ? 0.f : lg[(size_t)(se - u) * gts + h];
+    }
+    return lg[(size_t)(t0 + tid) * gts + h];
+  };
+  auto load_v = [&](int t0, int n, float (&x)[VPT]) {
+#pragma unroll
+    for (int e = 0; e < VPT; ++e) {
+      const int j = (tid + 256 * e) / DVS, c = (tid + 256 * e) % DVS;
+      x[e] = j < n ? v[(mrow(t0 + j) * H + h) * DV + c0 + c] : 0.f;
+    }
+  };
   auto store_blk = [&](float (&dst)[C][KB + 1], const float (&x)[EPT], const float *scale) {
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
@@ -118,27 +136,34 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
   }
   float gsum = 0.f;  // total log-decay of the run (state pass)
 
+  // registers of the next loads: gate and V of the chunk, Q and K blocks of the
+  // scores, K blocks of the state update. At chunk 64 a chunk's first loads are
+  // issued during the previous chunk's last state-update block; at chunk 128
+  // (twice the registers per load) at the chunk's start.
+  constexpr bool kAhead = C == 64;
+  float gx = 0.f, vx[VPT], qx[EPT], kx[EPT], ka[EPT];
+  auto first_loads = [&](int t1) {
+    const int n1 = min(C, w.tok_end - t1);
+    gx = load_gate(t1, n1);
+    load_v(t1, n1, vx);
+    if (STATE_PASS) {
+      load_blk(k, t1, n1, 0, ka);
+    } else {
+      load_blk(q, t1, n1, 0, qx);
+      load_blk(k, t1, n1, 0, kx);
+    }
+  };
+  if (kAhead && w.tok_begin < w.tok_end) first_loads(w.tok_begin);
+
   for (int t0 = w.tok_begin; t0 < w.tok_end; t0 += C) {
     const int n = min(C, w.tok_end - t0);
+    if (!kAhead) first_loads(t0);
     __syncthreads();
     // gates: inclusive scan of the chunk's log-gates (padding rows add 0), one
     // wavefront scan per 64 tokens; a second 64 adds the first one's total
-    if (tid < C) {
-      float x = 0.f;
-      if (tid < n) {
-        if (REV) {
-          const int u = t0 + tid - sb;
-          x = u == 0 ? 0.f : lg[(size_t)(se - u) * gts + h];
-        } else {
-          x = lg[(size_t)(t0 + tid) * gts + h];
-        }
-      }
-      bcum[tid] = wave_inclusive_scan(x);
-    }
-    for (int e = tid; e < C * DVS; e += 256) {
-      const int j = e / DVS, c = e % DVS;
-      Vs[j][c] = (j < n) ? v[(mrow(t0 + j) * H + h) * DV + c0 + c] : 0.f;
-    }
+    if (tid < C) bcum[tid] = wave_inclusive_scan(gx);
+#pragma unroll
+    for (int e = 0; e < VPT; ++e) Vs[(tid + 256 * e) / DVS][(tid + 256 * e) % DVS] = vx[e];
     __syncthreads();
     if constexpr (C == 128) {
       const float first = bcum[63];
@@ -162,9 +187,6 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
       for (int s = 0; s < SPW; ++s) sacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < OPW; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      float qx[EPT], kx[EPT];
-      load_blk(q, t0, n, 0, qx);
-      load_blk(k, t0, n, 0, kx);
       for (int db = 0; db < DK; db += KB) {
         __syncthreads();
         store_blk(Qb, qx, nullptr);
@@ -173,6 +195,8 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
         if (db + KB < DK) {
           load_blk(q, t0, n, db + KB, qx);
           load_blk(k, t0, n, db + KB, kx);
+        } else if (kAhead) {  // the state update's first block, in flight through P V
+          load_blk(k, t0, n, 0, ka);
         }
         // scores Q K^T: A = Q rows, B = K^T
 #pragma unroll
@@ -225,13 +249,16 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
     }
     // state advance: S <- gamma S + (kappa K)^T V, one key block at a time;
     // each wavefront owns whole 16 x 16 tiles of the block's state rows
-    float kx[EPT];
-    load_blk(k, t0, n, 0, kx);
+    if (!kAhead && !STATE_PASS) load_blk(k, t0, n, 0, ka);
     for (int db = 0; db < DK; db += KB) {
       __syncthreads();
-      store_blk(Kb, kx, kap);
+      store_blk(Kb, ka, kap);
       __syncthreads();
-      if (db + KB < DK) load_blk(k, t0, n, db + KB, kx);
+      if (db + KB < DK) {
+        load_blk(k, t0, n, db + KB, ka);
+      } else if (kAhead && t0 + C < w.tok_end) {  // the next chunk's first loads
+        first_loads(t0 + C);
+      }
       const float gam = gam_s;
 #pragma unroll
       for (int u = 0; u < UPW; ++u) {
