@@ -154,6 +154,8 @@ def bench_forward(args):
     # algorithmic flops of the chunked form at chunk C: causal intra-chunk scores
     # and P V, the state read Q S and the state update K^T V
     alg_flops = tok_heads * ((C + 1) * (dk + dv) + 4 * dk * dv)
+    # the same with whole diagonal tiles (the dense-tile count)
+    dense_tile_flops = tok_heads * (2 * C * (dk + dv) + 4 * dk * dv)
     # flops the matrix cores issue (whole 16x16 tiles, bf16 hi/lo splits, the
     # score tiles recomputed by each 64-column slice)
     n_chunks = B * H * (T // C)
@@ -209,6 +211,8 @@ def bench_forward(args):
                  "issued_tflops": round(issued_flops / (kern_ms * 1e-3) / 1e12, 1),
                  "issued_util": round(issued_flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  "algorithmic_flops": alg_flops, "issued_flops": issued_flops,
+                 "dense_tile_flops": dense_tile_flops, "chunk": C,
+                 "dense_tile_util": round(dense_tile_flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  "peak_tflops": BF16_PEAK_TFLOPS},
     }
     return res, host_set0
