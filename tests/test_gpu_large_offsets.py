@@ -1,8 +1,8 @@
 """Tensors past 2^31 elements: no 32-bit offset anywhere on the path.
 
-A chunked forward whose q, k, v each hold more than 2^31 elements (B=1,
-T=1,049,576, H=32, d=64; the fp32 output is 8.6 GB) and a decode step whose
-state holds 4.3e9 fp32 elements (17 GB) at its highest addresses. The forward's
+A chunked forward and a backward whose inputs each hold more than 2^31
+elements (B=1, T=1,049,576, H=32, d=64; an fp32 output is 8.6 GB) and a decode
+step whose state holds 4.3e9 fp32 elements (17 GB) at its highest addresses. The forward's
 last head is compared bit for bit with the same head run alone (small tensors,
 the same segment plan forced by GLA_SEG_LEN / GLA_STATE_SUB, so the same
 arithmetic), and with the fp64 oracle on its last tokens and final state; the
@@ -106,4 +106,46 @@ def test_decode_beyond_4g_state_elements(pooled):
         gu.say(f"   request {n} (entry {e}): o err {eo:.2e}, S err {eS:.2e}")
         assert eo <= 1e-5 and eS <= 1e-6, (n, eo, eS)
     del S, q, k, v, g, o
+    torch.cuda.empty_cache()
+
+
+def test_backward_beyond_2g_elements(monkeypatch):
+    """The backward (three forward runs, two reversed, the fused gate dots,
+    the gate kernels) at 2.15e9 elements per input: the highest-addressed
+    head equals the same head's backward run alone, bit for bit, under the
+    same forced segment plan (the head-alone path is checked against the
+    oracle by the backward tests at small sizes)."""
+    import torch
+    import gated_linear_attention_amd as gla
+    B, T, H, d = 1, (1 << 20) + 1000, 32, 64
+    gu.say(f"large backward: B={B} T={T} H={H} d={d} bf16")
+    monkeypatch.setenv("GLA_SEG_LEN", "65536")
+    monkeypatch.setenv("GLA_STATE_SUB", "4")
+    gen = torch.Generator(device="cuda").manual_seed(4444)
+    bf = torch.bfloat16
+    q = _draw(gen, (B, T, H, d), dtype=bf)
+    k = _draw(gen, (B, T, H, d), d ** -0.5, bf)
+    v = _draw(gen, (B, T, H, d), dtype=bf)
+    dO = _draw(gen, (B, T, H, d), dtype=bf)
+    g = torch.nn.functional.logsigmoid(_draw(gen, (B, T, H)) + 3.0)
+    S0 = _draw(gen, (B, H, d, d), 0.02)
+    dS_T = _draw(gen, (B, H, d, d), 0.02)
+    got = gla.bwd_chunked(q, k, v, g, dO, S0=S0, dS_T=dS_T)
+    torch.cuda.synchronize()
+    gu.say("   full batch done")
+    hh = H - 1
+    last = [x[:, :, hh].clone() if x.dim() >= 3 and x.shape[1] == T else x[:, hh].clone()
+            for x in got]
+    one = lambda x: x[:, :, hh:hh + 1].contiguous()
+    ins = (one(q), one(k), one(v), one(g), one(dO))
+    S01, dST1 = S0[:, hh:hh + 1].contiguous(), dS_T[:, hh:hh + 1].contiguous()
+    del got, q, k, v, dO, g
+    torch.cuda.empty_cache()
+    alone = gla.bwd_chunked(*ins, S0=S01, dS_T=dST1)
+    torch.cuda.synchronize()
+    for name, a, b in zip(["dq", "dk", "dv", "dlog_g", "dS0"], last, alone):
+        b = b[:, :, 0] if b.dim() >= 3 and b.shape[1] == T else b[:, 0]
+        assert torch.equal(a, b), name
+    gu.say("   last head bit-identical to the head run alone (dq, dk, dv, dlog_g, dS0)")
+    del last, alone, ins
     torch.cuda.empty_cache()
