@@ -2,7 +2,8 @@
 
 A chunked forward and a backward whose inputs each hold more than 2^31
 elements (B=1, T=1,049,576, H=32, d=64; an fp32 output is 8.6 GB) and a decode
-step whose state holds 4.3e9 fp32 elements (17 GB) at its highest addresses. The forward's
+step whose state holds 4.3e9 fp32 elements (17 GB) at its highest addresses,
+and the mixer epilogue over 2.15e9-element rows. The forward's
 last head is compared bit for bit with the same head run alone (small tensors,
 the same segment plan forced by GLA_SEG_LEN / GLA_STATE_SUB, so the same
 arithmetic), and with the fp64 oracle on its last tokens and final state; the
@@ -148,4 +149,35 @@ def test_backward_beyond_2g_elements(monkeypatch):
         assert torch.equal(a, b), name
     gu.say("   last head bit-identical to the head run alone (dq, dk, dv, dlog_g, dS0)")
     del last, alone, ins
+    torch.cuda.empty_cache()
+
+
+def test_epilogue_beyond_2g_elements():
+    """The mixer epilogue over 11.2M rows of 192 channels (2.15e9 elements in
+    o, v, g and z): the last rows against the fp64 epilogue oracle."""
+    import torch
+    import gated_linear_attention_amd as gla
+    from gated_linear_attention_amd import synth
+    from oracle import epilogue_oracle as eo
+    n_tok, H, dk, dv = 700_000, 16, 96, 192
+    assert n_tok * H * dv > (1 << 31)
+    gu.say(f"large epilogue: {n_tok} tokens x {H} heads, {dk}x{dv}")
+    gen = torch.Generator(device="cuda").manual_seed(4545)
+    bf = torch.bfloat16
+    o = _draw(gen, (n_tok, H, dv))
+    q = _draw(gen, (n_tok, H, dk), dtype=bf)
+    k = _draw(gen, (n_tok, H, dk), dk ** -0.5, bf)
+    v = _draw(gen, (n_tok, H, dv), dtype=bf)
+    gt = _draw(gen, (n_tok, H, dv), dtype=bf)
+    a, tw, tier = synth.make_epilogue_params(H, dk, dv, seed=46)
+    w = gla.head_rms_weights(gu.dev(tw), gu.dev(tier))
+    z = gla.mixer_epilogue(o, q, k, v, gt, gu.dev(a), w, 1e-6, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    tail = slice(n_tok - 3, n_tok)
+    host = lambda x: x[tail].float().cpu().numpy()
+    ref = eo.mixer_epilogue(host(o), host(q), host(k), host(v), host(gt), a, tw, tier, 1e-6)
+    e = orc.normwise_error(gu.host(z[tail]), ref)
+    gu.say(f"   last 3 tokens (48 rows) err {e:.2e}")
+    assert e <= 1e-5, e
+    del o, q, k, v, gt, z
     torch.cuda.empty_cache()
