@@ -110,6 +110,18 @@ def test_gate_extremes(gate):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("C", [64, 128])
+def test_growing_state(dtype, C):
+    """l > 0 (a growing state) is computed as given: l = +0.03 per token over
+    150 tokens, about 90x growth, with S0."""
+    gu.say(f"growing state {dtype} C={C}")
+    w = synth.Workload("t", B=2, T=150, H=2, dk=64, dv=64, dtype=dtype, gate_bias=3.0,
+                       s0_std=0.02, chunk=C, seed=29)
+    q, k, v, lg, S0, cu = synth.make_forward_inputs(w)
+    check(q, k, v, np.full_like(lg, 0.03), S0, cu, dtype, C=C)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_varlen_with_edge_lengths(dtype):
     """Packed batch with empty, length-1, sub-chunk and multi-chunk sequences."""
     gu.say(f"varlen edge lengths {dtype}")
