@@ -404,9 +404,15 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
         const float x0 = __uint_as_float(xv[m].x << 16), x1 = __uint_as_float(xv[m].x & 0xffff0000u);
         const float x2 = __uint_as_float(xv[m].y << 16), x3 = __uint_as_float(xv[m].y & 0xffff0000u);
         float d = own[m][0] * x0 + own[m][1] * x1 + own[m][2] * x2 + own[m][3] * x3;
-        d += __shfl_xor(d, 16);
-        d += __shfl_xor(d, 32);
-        dsum[m] = d;
+        // the sum over the four lane groups of the row, in registers: swapping a
+        // value with itself across 16-lane rows (then 32-lane halves) and adding
+        // the two results gives d[l] + d[l ^ 16] (then + d[l ^ 32]) in every lane
+        const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d), __float_as_uint(d),
+                                                          false, false);
+        d = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+        const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(d), __float_as_uint(d),
+                                                          false, false);
+        dsum[m] = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
       }
       float *pp = dpart + ((size_t)(slice * NCG + cg) * H + h) * part_stride;
       if (lg4 == 0) {
