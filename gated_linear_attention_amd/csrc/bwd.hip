@@ -67,33 +67,18 @@ __global__ __launch_bounds__(256) void gate_dot_kernel(const Tin *__restrict__ q
   if (row < rows && l == 0) dB[row] = acc;
 }
 
-// dB[token * H + h] = sum over p of dq_part[p][h][token] - dk_part[p][h][token]:
-// the per-token dot products q.dq - k.dk from the partial sums the chunk-64
-// forward runs wrote (one per 16-column group p). Thread i reads element i of
-// every [h][token] plane (coalesced) and writes its (token, h) entry.
-__global__ __launch_bounds__(256) void gate_parts_kernel(const float *__restrict__ dq_part,
-                                                         const float *__restrict__ dk_part,
-                                                         int n_part, long n_tok, int H,
-                                                         float *__restrict__ dB) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;  // h * n_tok + token
-  const long rows = n_tok * H;
-  if (i >= rows) return;
-  float a = 0.f, b = 0.f;
-  for (int p = 0; p < n_part; ++p) {
-    a += dq_part[(size_t)p * rows + i];
-    b += dk_part[(size_t)p * rows + i];
-  }
-  const long h = i / n_tok, t = i % n_tok;
-  dB[t * H + h] = a - b;
-}
-
 // One workgroup per (sequence, head): dl = reverse cumulative sum of dB over
 // the sequence (plus <dS_T, S_T> at its last token), in tiles of 2048 tokens
-// from the end; and dS0 = g_0 A_0. ST_t and dST_t are S_T^T and dS_T^T
-// ([dv][dk]; dST_t null for dS_T = 0); A0 is the adjoint after the first
-// token ([dk][dv]). dB and dl may be the same array.
+// from the end; and dS0 = g_0 A_0. With NP > 0 the per-token dB = q.dq -
+// k.dk is formed here from the partial sums the chunk-64 forward runs wrote
+// (dq_part / dk_part [NP][H][n_tok], one plane per 16-column group, read
+// along the tokens); otherwise it is read from dB [token][H]. ST_t and dST_t
+// are S_T^T and dS_T^T ([dv][dk]; dST_t null for dS_T = 0); A0 is the adjoint
+// after the first token ([dk][dv]). dB and dl may be the same array.
+template <int NP>
 __global__ __launch_bounds__(256) void gate_scan_kernel(
-    const float *dB, const float *__restrict__ lg, const float *__restrict__ ST_t,
+    const float *dB, const float *__restrict__ dq_part, const float *__restrict__ dk_part,
+    long n_tok, const float *__restrict__ lg, const float *__restrict__ ST_t,
     const float *__restrict__ dST_t, const float *__restrict__ A0, float *dl,
     float *__restrict__ dS0, const int32_t *__restrict__ cu, int T, int H, int DK, int DV) {
   const int n = blockIdx.x / H, h = blockIdx.x % H;
@@ -101,6 +86,7 @@ __global__ __launch_bounds__(256) void gate_scan_kernel(
   const int s = cu ? cu[n] : n * T, e = cu ? cu[n + 1] : (n + 1) * T;
   const size_t mat = (size_t)DK * DV, base = ((size_t)n * H + h) * mat;
   __shared__ float red[256];
+  __shared__ float xs[2048];
 
   // <dS_T, S_T>
   float fro = 0.f;
@@ -123,14 +109,37 @@ __global__ __launch_bounds__(256) void gate_scan_kernel(
 
   // tiles of 8 tokens per thread, last tile first; carry = sum over later tiles
   float carry = fro;
+  const size_t plane = (size_t)n_tok * H;
   for (int hi = e; hi > s; hi -= 2048) {
     const int lo = hi - 2048 > s ? hi - 2048 : s;
-    const int t0 = lo + 8 * tid;
+    // the tile's dB into LDS (the partial planes are read along the tokens,
+    // every load of the tile issued before the first sum; addresses clamped
+    // into the tile)
+    const int cnt = hi - lo;
+    float d[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const size_t t = (size_t)lo + min(tid + 256 * j, cnt - 1);
+      if constexpr (NP > 0) {
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          a += dq_part[p * plane + h * (size_t)n_tok + t];
+          b += dk_part[p * plane + h * (size_t)n_tok + t];
+        }
+        d[j] = a - b;
+      } else {
+        d[j] = dB[t * H + h];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (tid + 256 * j < cnt) xs[tid + 256 * j] = d[j];
+    __syncthreads();
     float x[8], tot = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int t = t0 + j;
-      x[j] = t < hi ? dB[(size_t)t * H + h] : 0.f;
+      x[j] = lo + 8 * tid + j < hi ? xs[8 * tid + j] : 0.f;
       tot += x[j];
     }
     // inclusive suffix sums of the per-thread totals
@@ -147,7 +156,7 @@ __global__ __launch_bounds__(256) void gate_scan_kernel(
     __syncthreads();
 #pragma unroll
     for (int j = 7; j >= 0; --j) {
-      const int t = t0 + j;
+      const int t = lo + 8 * tid + j;
       run += x[j];
       if (t < hi) dl[(size_t)t * H + h] = run;
     }
@@ -156,15 +165,6 @@ __global__ __launch_bounds__(256) void gate_scan_kernel(
 }
 
 }  // namespace
-
-hipError_t launch_gate_parts(const float *dq_part, const float *dk_part, int n_part,
-                             long n_tok, int H, float *dB, hipStream_t stream) {
-  const long rows = n_tok * H;
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(gate_parts_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
-                     dq_part, dk_part, n_part, n_tok, H, dB);
-  return hipGetLastError();
-}
 
 hipError_t launch_transpose(const float *in, float *out, int count, int rows, int cols,
                             hipStream_t stream) {
@@ -182,9 +182,10 @@ hipError_t launch_transpose(const float *in, float *out, int count, int rows, in
 hipError_t launch_dgate(const void *q, const void *k, const float *dq, const float *dk,
                         const float *lg, const float *ST_t, const float *dST_t, const float *A0,
                         float *dl, float *dS0, const int32_t *cu, int N, int T, int H, int DK,
-                        int DV, bool in_bf16, bool have_dB, hipStream_t stream) {
+                        int DV, bool in_bf16, const float *dq_part, const float *dk_part,
+                        int n_part, hipStream_t stream) {
   const long rows = (long)(cu ? T : (long)N * T) * H;  // token rows of the batch
-  if (rows > 0 && !have_dB) {
+  if (rows > 0 && n_part == 0) {
     const dim3 grid((unsigned)((rows + 7) / 8)), block(256);
     if (in_bf16)
       hipLaunchKernelGGL(gate_dot_kernel<uint16_t>, grid, block, 0, stream,
@@ -198,8 +199,11 @@ hipError_t launch_dgate(const void *q, const void *k, const float *dq, const flo
     if (e != hipSuccess) return e;
   }
   if ((long)N * H == 0) return hipSuccess;
-  hipLaunchKernelGGL(gate_scan_kernel, dim3((unsigned)(N * H)), dim3(256), 0, stream, dl, lg,
-                     ST_t, dST_t, A0, dl, dS0, cu, T, H, DK, DV);
+  auto kern = n_part == 8 ? gate_scan_kernel<8> : n_part == 4 ? gate_scan_kernel<4>
+                                                                : gate_scan_kernel<0>;
+  if (n_part != 0 && n_part != 4 && n_part != 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(N * H)), dim3(256), 0, stream, dl, dq_part, dk_part,
+                     cu ? (long)T : (long)N * T, lg, ST_t, dST_t, A0, dl, dS0, cu, T, H, DK, DV);
   return hipGetLastError();
 }
 

@@ -472,10 +472,9 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
                 in_dtype, GLA_F32, fws, L.fws_bytes, stream, false, true,
                 fuse ? &dk_dot : nullptr);
   if (st != GLA_OK) return st;
-  if ((fuse && launch_gate_parts(dq_dot.part, dk_dot.part, DK / 16, (long)B * T, H, dg,
-                                 stream) != hipSuccess) ||
-      launch_dgate(q, k, dq, dk, g, stt, dstt, a0, dg, dS0, cu_seqlens, N, T, H, DK, DV,
-                   in_dtype == GLA_BF16, fuse, stream) != hipSuccess)
+  if (launch_dgate(q, k, dq, dk, g, stt, dstt, a0, dg, dS0, cu_seqlens, N, T, H, DK, DV,
+                   in_dtype == GLA_BF16, fuse ? dq_dot.part : nullptr,
+                   fuse ? dk_dot.part : nullptr, fuse ? DK / 16 : 0, stream) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;
 }

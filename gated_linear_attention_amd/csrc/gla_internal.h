@@ -129,17 +129,16 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
 size_t fwd_workspace(int B, int T, int H, int dk, int dv, int N, int chunk_size, bool has_cu,
                      gla_dtype in_dtype);
 // Backward helpers (bwd.hip).
-// dB[token * H + h] = sum_p dq_part[p][h][token] - sum_p dk_part[p][h][token]
-// (the gate gradient's per-token dot products from the forward runs' partial
-// sums).
-hipError_t launch_gate_parts(const float *dq_part, const float *dk_part, int n_part,
-                             long n_tok, int H, float *dB, hipStream_t stream);
 hipError_t launch_transpose(const float *in, float *out, int count, int rows, int cols,
                             hipStream_t stream);
+// The gate gradient dl (reverse cumulative sums of q.dq - k.dk per sequence)
+// and dS0. With n_part > 0 the dots come from the forward runs' partial sums
+// dq_part / dk_part; otherwise they are formed from q, dq, k, dk first.
 hipError_t launch_dgate(const void *q, const void *k, const float *dq, const float *dk,
                         const float *lg, const float *ST_t, const float *dST_t, const float *A0,
                         float *dl, float *dS0, const int32_t *cu, int N, int T, int H, int DK,
-                        int DV, bool in_bf16, bool have_dB, hipStream_t stream);
+                        int DV, bool in_bf16, const float *dq_part, const float *dk_part,
+                        int n_part, hipStream_t stream);
 
 // One decode step with the mixer epilogue fused (decode.hip): S (or the pool
 // entries slots[n], as launch_decode) updated in place, z written; o is not.
