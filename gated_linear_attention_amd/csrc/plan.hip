@@ -108,15 +108,17 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
     return;
   }
 
-  // 2. bucket offsets, longest items first
-  if (tid == 0) {
-    int run = 0;
-    for (int key = nb - 1; key >= 0; --key) {
-      off[key] = run;
-      run += hist[key];
-    }
-    hdr->n_items = run;
+  // 2. bucket offsets, longest items first: an exclusive scan of the
+  // histogram from the highest key down, 1024 keys at a time
+  int run = 0;
+  for (int r0 = 0; r0 < nb; r0 += 1024) {
+    const int r = r0 + tid, key = nb - 1 - r;
+    int tot;
+    const int ex = block_exclusive_scan_1024(r < nb ? hist[key] : 0, scratch, tot);
+    if (r < nb) off[key] = run + ex;
+    run += tot;
   }
+  if (tid == 0) hdr->n_items = run;
   __syncthreads();
 
   // 3. emit items, 1024 sequences at a time
