@@ -145,7 +145,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
         it.tok_begin = tb;
         it.tok_end = te;
         it.seq = n;
-        it.state_in = split ? slot_base + s * n_sub : -1;
+        it.state_in = split && s > 0 ? slot_base + s * n_sub : -1;  // segment 0: S0 itself
         it.state_out = (s == nseg - 1) ? -1 : kNoStateOut;
         it.seq_begin = start;
         it.seq_end = start + len;
@@ -181,16 +181,19 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
   }
 }
 
-// Chain the state pieces: slot[base] = S0 (or 0); for b >= 1
+// Chain the state pieces: from S0 (or 0) as the state before piece 0, for b >= 1
 //   slot[base+b] = exp(gamma[base+b]) * slot[base+b-1] + slot[base+b]
 // where the state pass left piece b-1's local state and total log-decay in
-// slot base+b. One thread per four consecutive state elements.
+// slot base+b. Only the starts of segments after the first (b a positive
+// multiple of n_sub) are read afterwards, so only they are written back; the
+// first segment starts from S0 itself. One thread per four
+// consecutive state elements.
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ S0,
                                                       const PlanHeader *__restrict__ hdr,
                                                       const MultiSeq *__restrict__ multi,
                                                       float *__restrict__ slots,
                                                       const float *__restrict__ slot_gamma,
-                                                      int H, int dkdv) {
+                                                      int H, int dkdv, int n_sub) {
   const int bph = dkdv / 1024;  // blocks per (sequence, head)
   const int m = blockIdx.x / (H * bph);
   if (m >= hdr->n_multi) return;
@@ -199,14 +202,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   const MultiSeq ms = multi[m];
   f32x4 cur = {0.f, 0.f, 0.f, 0.f};
   if (S0) cur = *reinterpret_cast<const f32x4 *>(S0 + ((size_t)ms.seq * H + h) * dkdv + e);
-  f32x4 *slot0 = reinterpret_cast<f32x4 *>(slots + ((size_t)ms.slot_base * H + h) * dkdv + e);
-  *slot0 = cur;
-  for (int s = 1; s < ms.nslot; ++s) {
-    const int sl = ms.slot_base + s;
-    f32x4 *p = reinterpret_cast<f32x4 *>(slots + ((size_t)sl * H + h) * dkdv + e);
-    const float decay = expf(slot_gamma[(size_t)sl * H + h]);
-    cur = decay * cur + *p;
-    *p = cur;
+  // eight pieces at a time: their loads all issued before the chain's stores
+  // (which the compiler would otherwise wait for before each next load);
+  // indexes past the last piece are clamped to it and their values unused
+  for (int s0 = 1; s0 < ms.nslot; s0 += 8) {
+    f32x4 val[8];
+    float lgam[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sl = ms.slot_base + min(s0 + j, ms.nslot - 1);
+      val[j] = *reinterpret_cast<const f32x4 *>(slots + ((size_t)sl * H + h) * dkdv + e);
+      lgam[j] = slot_gamma[(size_t)sl * H + h];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j < ms.nslot) {
+        const int sl = ms.slot_base + s0 + j;
+        cur = expf(lgam[j]) * cur + val[j];
+        if ((s0 + j) % n_sub == 0)
+          *reinterpret_cast<f32x4 *>(slots + ((size_t)sl * H + h) * dkdv + e) = cur;
+      }
+    }
   }
 }
 
@@ -235,7 +251,8 @@ hipError_t launch_combine(const float *S0, const FwdDims &d, const PlanLayout &l
                      reinterpret_cast<const PlanHeader *>(ws + lay.off_header),
                      reinterpret_cast<const MultiSeq *>(ws + lay.off_multi),
                      reinterpret_cast<float *>(ws + lay.off_slots),
-                     reinterpret_cast<const float *>(ws + lay.off_slot_gamma), d.H, dkdv);
+                     reinterpret_cast<const float *>(ws + lay.off_slot_gamma), d.H, dkdv,
+                     lay.n_sub);
   return hipGetLastError();
 }
 
