@@ -517,6 +517,23 @@ def bench_laplace(args):
     fwd["token_gates_c64"] = timed(
         lambda i: gla.fwd_chunked(tq, tk, tv, tlg, chunk_size=64, o=o, S_T=S_T), alg_gates)
 
+    # the backward on the same inputs (the decays as a per-token gate stream, dO
+    # drawn like v, dS_T = 0); its dq and dk runs have 192-dim keys and run, with
+    # the dv run, on the fp32-arithmetic kernel
+    gen = torch.Generator(device=dev).manual_seed(w.seed + 4)
+    tdo = torch.randn((B, T, H, dv), generator=gen, device=dev).to(torch.bfloat16)
+    bws = torch.empty(gla._lib.load().gla_bwd_chunked_workspace_size(B, T, H, dk, dv, B, 64, 0,
+                                                                     gla._lib.GLA_BF16),
+                      dtype=torch.uint8, device=dev)
+    alg_bwd = tok_heads * (2 * dk + 2 * dk + 2 * dv + 2 * dv + 4 + 4 * dk + 4 * dk + 4 * dv + 4)
+    bwd = timed(lambda i: gla.bwd_chunked(tq, tk, tv, tlg, tdo, chunk_size=64, need_dS0=False,
+                                          workspace=bws), alg_bwd)
+    bwd.update({"algorithmic_bytes": alg_bwd, "chunk": 64,
+                "kernels": "chunk_f32_kernel<64,192,float,false,false,bf16> (dq), "
+                           "chunk_f32_kernel<64,96,float,false,true,bf16> (dv), "
+                           "chunk_f32_kernel<64,192,float,false,true,bf16> (dk), gate kernels"})
+    del tdo, bws
+
     # the mixer epilogue on the forward's output: fp32 o, bf16 q, k, v and gate
     # stream in, bf16 z out (4 tiers of 4 heads)
     gate = bf(synth.make_epilogue_inputs(B * T, H, dk, dv, seed=w.seed + 2)[4]).view(B, T, H, dv)
@@ -556,6 +573,7 @@ def bench_laplace(args):
         "forward_kernel": {"c64": "chunk_bf16_w8_kernel<96,6,float,false,false,false>",
                            "c128": "chunk_bf16_kernel<128,96,float,false,false>"},
         "forward_algorithmic_bytes": alg_fixed,
+        "backward": bwd,
         "epilogue": epi,
         "forward_traffic_c64": measured_traffic("chunk_fwd_bf16_laplace_2k_c64",
                                                 FWD_KERNELS[64][1]),

@@ -51,9 +51,9 @@ __device__ __forceinline__ WorkItem item_for(const WorkItem *items, int it, int 
 // REV: the time-reversed run of the backward: logical token t of a sequence
 // [sb, se) reads and writes memory row sb + se - 1 - t, and its gate is the
 // log-gate of row se - (t - sb) (0 for t = sb).
-template <int C, int DK, typename Tout, bool STATE_PASS, bool REV = false>
+template <int C, int DK, typename Tout, bool STATE_PASS, bool REV = false, typename Tin = float>
 __global__ __launch_bounds__(256) void chunk_f32_kernel(
-    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ lg, const float *__restrict__ S0, float *__restrict__ ST,
     Tout *__restrict__ o, const WorkItem *__restrict__ items, const int *__restrict__ n_items,
     float *__restrict__ slots, float *__restrict__ slot_gamma, int T, int H, int gts, int DV) {
@@ -91,11 +91,11 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
   // computed is loaded while the matrix cores work on LDS (thread tid moves
   // elements tid + 256 e, e < EPT, of the block's C x KB tile).
   constexpr int EPT = C * KB / 256;
-  auto load_blk = [&](const float *src, int t0, int n, int db, float (&x)[EPT]) {
+  auto load_blk = [&](const Tin *src, int t0, int n, int db, float (&x)[EPT]) {
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const int i = (tid + 256 * e) / KB, dd = (tid + 256 * e) % KB;
-      x[e] = i < n ? src[(mrow(t0 + i) * H + h) * DK + db + dd] : 0.f;
+      x[e] = i < n ? load_as_f32(src, (mrow(t0 + i) * H + h) * DK + db + dd) : 0.f;
     }
   };
   // the chunk's log-gate (thread tid < C holds token tid) and V slice elements
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
 #pragma unroll
     for (int e = 0; e < VPT; ++e) {
       const int j = (tid + 256 * e) / DVS, c = (tid + 256 * e) % DVS;
-      x[e] = j < n ? v[(mrow(t0 + j) * H + h) * DV + c0 + c] : 0.f;
+      x[e] = j < n ? load_as_f32(v, (mrow(t0 + j) * H + h) * DV + c0 + c) : 0.f;
     }
   };
   auto store_blk = [&](float (&dst)[C][KB + 1], const float (&x)[EPT], const float *scale) {
@@ -291,72 +291,119 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
   }
 }
 
-template <int C, int DK, typename Tout, bool SP, bool REV = false>
-static hipError_t launch_f32_t(const float *q, const float *k, const float *v, const float *g,
+template <int C, int DK, typename Tin, typename Tout, bool SP, bool REV = false>
+static hipError_t launch_f32_t(const Tin *q, const Tin *k, const Tin *v, const float *g,
                                const float *S0, float *S_T, void *o, const FwdDims &d,
                                const WorkItem *items, const int *n_items, int grid_items,
                                float *slots, float *slot_gamma, hipStream_t stream) {
   const long blocks = (long)grid_items * d.H * (d.dv / kF32Slice);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((chunk_f32_kernel<C, DK, Tout, SP, REV>), dim3(blocks), dim3(256), 0, stream, q,
-                     k, v, g, S0, S_T, static_cast<Tout *>(o), items, n_items, slots, slot_gamma,
-                     d.T, d.H, d.gts, d.dv);
+  hipLaunchKernelGGL((chunk_f32_kernel<C, DK, Tout, SP, REV, Tin>), dim3(blocks), dim3(256), 0,
+                     stream, q, k, v, g, S0, S_T, static_cast<Tout *>(o), items, n_items, slots,
+                     slot_gamma, d.T, d.H, d.gts, d.dv);
   return hipGetLastError();
 }
 
+// fp32 inputs: the fp32 forward (d_k in {64, 96, 128}, bf16 or fp32 o) and the
+// backward's runs (fp32 o; time-reversed or not; d_k 192 for the 96 x 192
+// heads' dq and dk runs).
 template <int C, int DK>
 static hipError_t launch_f32_c(const float *q, const float *k, const float *v, const float *g,
                                const float *S0, float *S_T, void *o, bool out_bf16,
                                const FwdDims &d, const WorkItem *items, const int *n_items,
                                int grid_items, float *slots, float *slot_gamma, bool state_pass,
                                hipStream_t stream) {
-  if (d.rev) {  // time-reversed runs of the backward: fp32 outputs, d_k in {64, 128}
-    if constexpr (DK == 96) {
-      return hipErrorInvalidValue;
-    } else {
-      if (state_pass)
-        return launch_f32_t<C, DK, float, true, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
-                                                      grid_items, slots, slot_gamma, stream);
-      if (out_bf16) return hipErrorInvalidValue;
-      return launch_f32_t<C, DK, float, false, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
-                                                     grid_items, slots, slot_gamma, stream);
-    }
+  if (d.rev) {  // time-reversed runs of the backward: fp32 outputs
+    if (out_bf16) return hipErrorInvalidValue;
+    if (state_pass)
+      return launch_f32_t<C, DK, float, float, true, true>(q, k, v, g, S0, S_T, o, d, items,
+                                                           n_items, grid_items, slots, slot_gamma,
+                                                           stream);
+    return launch_f32_t<C, DK, float, float, false, true>(q, k, v, g, S0, S_T, o, d, items,
+                                                          n_items, grid_items, slots, slot_gamma,
+                                                          stream);
   }
   if (state_pass)
-    return launch_f32_t<C, DK, float, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
-                                            grid_items, slots, slot_gamma, stream);
-  if (out_bf16)
-    return launch_f32_t<C, DK, uint16_t, false>(q, k, v, g, S0, S_T, o, d, items, n_items,
-                                                grid_items, slots, slot_gamma, stream);
-  return launch_f32_t<C, DK, float, false>(q, k, v, g, S0, S_T, o, d, items, n_items,
-                                           grid_items, slots, slot_gamma, stream);
+    return launch_f32_t<C, DK, float, float, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
+                                                   grid_items, slots, slot_gamma, stream);
+  if constexpr (DK != 192) {
+    if (out_bf16)
+      return launch_f32_t<C, DK, float, uint16_t, false>(q, k, v, g, S0, S_T, o, d, items,
+                                                         n_items, grid_items, slots, slot_gamma,
+                                                         stream);
+  } else {
+    if (out_bf16) return hipErrorInvalidValue;
+  }
+  return launch_f32_t<C, DK, float, float, false>(q, k, v, g, S0, S_T, o, d, items, n_items,
+                                                  grid_items, slots, slot_gamma, stream);
 }
 
-hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, const float *g,
-                            const float *S0, float *S_T, void *o, bool out_bf16,
+// bf16 inputs through the fp32 kernel: the backward's runs for the 96 x 192
+// heads (d_k 96 or 192, fp32 o), which the bf16 kernels do not cover.
+template <int C, int DK>
+static hipError_t launch_f32_bf16in(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                    const float *g, const float *S0, float *S_T, void *o,
+                                    bool out_bf16, const FwdDims &d, const WorkItem *items,
+                                    const int *n_items, int grid_items, float *slots,
+                                    float *slot_gamma, bool state_pass, hipStream_t stream) {
+  if (out_bf16) return hipErrorInvalidValue;
+  if (d.rev) {
+    if (state_pass)
+      return launch_f32_t<C, DK, uint16_t, float, true, true>(q, k, v, g, S0, S_T, o, d, items,
+                                                              n_items, grid_items, slots,
+                                                              slot_gamma, stream);
+    return launch_f32_t<C, DK, uint16_t, float, false, true>(q, k, v, g, S0, S_T, o, d, items,
+                                                             n_items, grid_items, slots,
+                                                             slot_gamma, stream);
+  }
+  if (state_pass)
+    return launch_f32_t<C, DK, uint16_t, float, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
+                                                      grid_items, slots, slot_gamma, stream);
+  return launch_f32_t<C, DK, uint16_t, float, false>(q, k, v, g, S0, S_T, o, d, items, n_items,
+                                                     grid_items, slots, slot_gamma, stream);
+}
+
+hipError_t launch_chunk_f32(const void *q, const void *k, const void *v, const float *g,
+                            const float *S0, float *S_T, void *o, bool in_bf16, bool out_bf16,
                             const FwdDims &d, const WorkItem *items, const int *n_items,
                             int grid_items, float *slots, float *slot_gamma, bool state_pass,
                             hipStream_t stream) {
   if (d.dot_x) return hipErrorInvalidValue;  // row dots: bf16 chunk-64 kernel only
-  if (d.dk == 96) {
-    if (d.C == 64)
-      return launch_f32_c<64, 96>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
-                                  slots, slot_gamma, state_pass, stream);
-    return launch_f32_c<128, 96>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
-                                 slots, slot_gamma, state_pass, stream);
+  if (in_bf16) {
+    const auto *qb = static_cast<const uint16_t *>(q), *kb = static_cast<const uint16_t *>(k),
+               *vb = static_cast<const uint16_t *>(v);
+    if (d.dk == 96)
+      return d.C == 64 ? launch_f32_bf16in<64, 96>(qb, kb, vb, g, S0, S_T, o, out_bf16, d, items,
+                                                   n_items, grid_items, slots, slot_gamma,
+                                                   state_pass, stream)
+                       : launch_f32_bf16in<128, 96>(qb, kb, vb, g, S0, S_T, o, out_bf16, d,
+                                                    items, n_items, grid_items, slots,
+                                                    slot_gamma, state_pass, stream);
+    if (d.dk == 192)
+      return d.C == 64 ? launch_f32_bf16in<64, 192>(qb, kb, vb, g, S0, S_T, o, out_bf16, d,
+                                                    items, n_items, grid_items, slots,
+                                                    slot_gamma, state_pass, stream)
+                       : launch_f32_bf16in<128, 192>(qb, kb, vb, g, S0, S_T, o, out_bf16, d,
+                                                     items, n_items, grid_items, slots,
+                                                     slot_gamma, state_pass, stream);
+    return hipErrorInvalidValue;
   }
-  if (d.C == 64) {
-    if (d.dk == 128)
-      return launch_f32_c<64, 128>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items,
-                                   grid_items, slots, slot_gamma, state_pass, stream);
-    return launch_f32_c<64, 64>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
-                                slots, slot_gamma, state_pass, stream);
-  }
-  if (d.dk == 128)
-    return launch_f32_c<128, 128>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items,
-                                  grid_items, slots, slot_gamma, state_pass, stream);
-  return launch_f32_c<128, 64>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
-                               slots, slot_gamma, state_pass, stream);
+  const auto *qf = static_cast<const float *>(q), *kf = static_cast<const float *>(k),
+             *vf = static_cast<const float *>(v);
+#define GLA_F32_CASE(CC, DD)                                                                   \
+  if (d.C == CC && d.dk == DD)                                                                \
+    return launch_f32_c<CC, DD>(qf, kf, vf, g, S0, S_T, o, out_bf16, d, items, n_items,       \
+                                grid_items, slots, slot_gamma, state_pass, stream);
+  GLA_F32_CASE(64, 64)
+  GLA_F32_CASE(64, 96)
+  GLA_F32_CASE(64, 128)
+  GLA_F32_CASE(64, 192)
+  GLA_F32_CASE(128, 64)
+  GLA_F32_CASE(128, 96)
+  GLA_F32_CASE(128, 128)
+  GLA_F32_CASE(128, 192)
+#undef GLA_F32_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace gla

@@ -198,7 +198,7 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
                     const int32_t *cu_seqlens, void *o, float *S_T, int B, int T, int H, int dk,
                     int dv, int N, int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
                     void *workspace, size_t workspace_bytes, hipStream_t stream,
-                    bool fixed_decay, bool rev, const DotOut *dot) {
+                    bool fixed_decay, bool rev, const DotOut *dot, bool f32_kernel) {
   const bool has_cu = cu_seqlens != nullptr;
   FwdDims d;
   d.B = B;
@@ -214,19 +214,19 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
   d.dot_part = dot ? dot->part : nullptr;
   d.dot_stride = dot ? dot->stride : 0;
   PlanLayout lay;
-  const bool planned = make_plan(B, T, H, dk, dv, N, chunk_size, has_cu, in_dtype, lay);
+  const bool planned = make_plan(B, T, H, dk, dv, N, chunk_size, has_cu,
+                                 f32_kernel ? GLA_F32 : in_dtype, lay);
   if (planned && (!workspace || workspace_bytes < lay.total_bytes)) return GLA_ERR_WORKSPACE;
 
   const bool bf = in_dtype == GLA_BF16, out_bf = out_dtype == GLA_BF16;
   auto run_chunks = [&](const WorkItem *items, const int *n_items, int grid_items, float *slots,
                         float *slot_gamma, bool state_pass) -> hipError_t {
-    if (bf)
+    if (bf && !f32_kernel)
       return launch_chunk_bf16(static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
                                static_cast<const uint16_t *>(v), g, S0, S_T, o, out_bf, d, items,
                                n_items, grid_items, slots, slot_gamma, state_pass, stream);
-    return launch_chunk_f32(static_cast<const float *>(q), static_cast<const float *>(k),
-                            static_cast<const float *>(v), g, S0, S_T, o, out_bf, d, items,
-                            n_items, grid_items, slots, slot_gamma, state_pass, stream);
+    return launch_chunk_f32(q, k, v, g, S0, S_T, o, bf, out_bf, d, items, n_items, grid_items,
+                            slots, slot_gamma, state_pass, stream);
   };
 
   hipError_t err;
@@ -253,9 +253,10 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
 
 // Workspace of fwd_core for these sizes (0 when it runs without a plan).
 size_t fwd_workspace(int B, int T, int H, int dk, int dv, int N, int chunk_size, bool has_cu,
-                     gla_dtype in_dtype) {
+                     gla_dtype in_dtype, bool f32_kernel) {
   PlanLayout lay;
-  if (!make_plan(B, T, H, dk, dv, N, chunk_size, has_cu, in_dtype, lay)) return 0;
+  if (!make_plan(B, T, H, dk, dv, N, chunk_size, has_cu, f32_kernel ? GLA_F32 : in_dtype, lay))
+    return 0;
   return lay.total_bytes;
 }
 
@@ -352,6 +353,15 @@ gla_status gla_fwd_chunked_fixed_decay(const void *q, const void *k, const void 
 
 namespace {
 
+// Head shapes of the backward: (d_k, d_v) in {64, 128}^2 on the forward
+// kernels of the input type, and the Laplace 96 x 192 heads, whose dq and dk
+// runs are forwards with 192-dim keys: those run on the fp32 kernel (which
+// reads bf16 inputs too), the dv run with them.
+bool bwd_dims(int dk, int dv) {
+  return (supported_head_dim(dk) && supported_head_dim(dv)) || (dk == 96 && dv == 192);
+}
+bool bwd_f32_kernel(int dk, int dv) { return dk == 96 && dv == 192; }
+
 // Workspace layout of the backward (all offsets 256-byte aligned).
 struct BwdLayout {
   size_t s0t, dstt, stt, a0, dqp, dkp, fws, total, fws_bytes;
@@ -374,12 +384,13 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int N, int C, bool has
   L.dstt = take(mat);
   L.stt = take(mat);
   L.a0 = take(mat);
-  L.fused_dots = in_dtype == GLA_BF16 && C == 64;
+  const bool f32k = bwd_f32_kernel(dk, dv);
+  L.fused_dots = in_dtype == GLA_BF16 && C == 64 && !f32k;
   const size_t parts = L.fused_dots ? (size_t)(dk / 16) * ntok * 4 : 0;
   L.dqp = take(parts);
   L.dkp = take(parts);
-  const size_t f1 = fwd_workspace(B, T, H, dv, dk, N, C, has_cu, in_dtype);
-  const size_t f2 = fwd_workspace(B, T, H, dk, dv, N, C, has_cu, in_dtype);
+  const size_t f1 = fwd_workspace(B, T, H, dv, dk, N, C, has_cu, in_dtype, f32k);
+  const size_t f2 = fwd_workspace(B, T, H, dk, dv, N, C, has_cu, in_dtype, f32k);
   L.fws_bytes = f1 > f2 ? f1 : f2;
   L.fws = take(L.fws_bytes);
   L.total = off;
@@ -392,9 +403,8 @@ extern "C" {
 
 size_t gla_bwd_chunked_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
                                       int chunk_size, int has_cu_seqlens, gla_dtype in_dtype) {
-  if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !supported_head_dim(dk) ||
-      !supported_head_dim(dv) || (chunk_size != 64 && chunk_size != 128) ||
-      !valid_dtype(in_dtype))
+  if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !bwd_dims(dk, dv) ||
+      (chunk_size != 64 && chunk_size != 128) || !valid_dtype(in_dtype))
     return 0;
   return bwd_layout(B, T, H, dk, dv, num_seqs, chunk_size, has_cu_seqlens != 0, in_dtype).total;
 }
@@ -412,7 +422,7 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   const bool has_cu = cu_seqlens != nullptr;
   if (has_cu ? (B != 1) : (num_seqs != B)) return GLA_ERR_INVALID_ARGUMENT;
   if ((long)B * T > INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
-  if (!supported_head_dim(DK) || !supported_head_dim(DV)) return GLA_ERR_UNSUPPORTED;
+  if (!bwd_dims(DK, DV)) return GLA_ERR_UNSUPPORTED;
   if (chunk_size != 64 && chunk_size != 128) return GLA_ERR_UNSUPPORTED;
   if (!all_al16({q, k, v, dO, S0, dS_T, dq, dk, dv, dS0, workspace}) ||
       !all_al4({g, dg, cu_seqlens}))
@@ -453,6 +463,7 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   const DotOut dq_dot{q, reinterpret_cast<float *>(ws + L.dqp), (long)B * T};
   const DotOut dk_dot{k, reinterpret_cast<float *>(ws + L.dkp), (long)B * T};
   const bool fuse = L.fused_dots;
+  const bool f32k = bwd_f32_kernel(DK, DV);
   // transposed initial states
   if ((S0 && launch_transpose(S0, s0t, N * H, DK, DV, stream) != hipSuccess) ||
       (dS_T && launch_transpose(dS_T, dstt, N * H, DK, DV, stream) != hipSuccess))
@@ -461,16 +472,16 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   // dq: forward with (q, k, v) = (dO, v, k) on the transposed state; its final
   // state is S_T^T
   st = fwd_core(dO, v, k, g, s0t, cu_seqlens, dq, stt, B, T, H, DV, DK, N, chunk_size, in_dtype,
-                GLA_F32, fws, L.fws_bytes, stream, false, false, fuse ? &dq_dot : nullptr);
+                GLA_F32, fws, L.fws_bytes, stream, false, false, fuse ? &dq_dot : nullptr, f32k);
   if (st != GLA_OK) return st;
   // dv: the reversed-time run with (q, k, v) = (k, q, dO) from dS_T; ends in A_0
   st = fwd_core(k, q, dO, g, dS_T, cu_seqlens, dv, a0, B, T, H, DK, DV, N, chunk_size, in_dtype,
-                GLA_F32, fws, L.fws_bytes, stream, false, true);
+                GLA_F32, fws, L.fws_bytes, stream, false, true, nullptr, f32k);
   if (st != GLA_OK) return st;
   // dk: the reversed-time run with (q, k, v) = (v, dO, q) from dS_T^T
   st = fwd_core(v, dO, q, g, dstt, cu_seqlens, dk, nullptr, B, T, H, DV, DK, N, chunk_size,
                 in_dtype, GLA_F32, fws, L.fws_bytes, stream, false, true,
-                fuse ? &dk_dot : nullptr);
+                fuse ? &dk_dot : nullptr, f32k);
   if (st != GLA_OK) return st;
   if (launch_dgate(q, k, dq, dk, g, stt, dstt, a0, dg, dS0, cu_seqlens, N, T, H, DK, DV,
                    in_dtype == GLA_BF16, fuse ? dq_dot.part : nullptr,

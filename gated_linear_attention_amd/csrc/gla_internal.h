@@ -96,9 +96,11 @@ hipError_t launch_plan(const int32_t *cu_seqlens, const FwdDims &d, const PlanLa
 hipError_t launch_combine(const float *S0, const FwdDims &d, const PlanLayout &lay,
                           void *workspace, hipStream_t stream);
 
-// fp32 inputs, fp32 arithmetic. state_pass: compute segment-local states only.
-hipError_t launch_chunk_f32(const float *q, const float *k, const float *v, const float *g,
-                            const float *S0, float *S_T, void *o, bool out_bf16,
+// fp32 arithmetic on fp32 inputs, or on bf16 inputs (in_bf16; d_k 96 or 192,
+// fp32 o: the backward's runs for the 96 x 192 heads). state_pass: compute
+// segment-local states only.
+hipError_t launch_chunk_f32(const void *q, const void *k, const void *v, const float *g,
+                            const float *S0, float *S_T, void *o, bool in_bf16, bool out_bf16,
                             const FwdDims &d, const WorkItem *items, const int *n_items,
                             int grid_items, float *slots, float *slot_gamma, bool state_pass,
                             hipStream_t stream);
@@ -125,9 +127,11 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
                     const int32_t *cu_seqlens, void *o, float *S_T, int B, int T, int H, int dk,
                     int dv, int N, int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
                     void *workspace, size_t workspace_bytes, hipStream_t stream,
-                    bool fixed_decay = false, bool rev = false, const DotOut *dot = nullptr);
+                    bool fixed_decay = false, bool rev = false, const DotOut *dot = nullptr,
+                    bool f32_kernel = false);
+// f32_kernel: run the fp32 kernel whatever in_dtype is (its workspace plan differs).
 size_t fwd_workspace(int B, int T, int H, int dk, int dv, int N, int chunk_size, bool has_cu,
-                     gla_dtype in_dtype);
+                     gla_dtype in_dtype, bool f32_kernel = false);
 // Backward helpers (bwd.hip).
 hipError_t launch_transpose(const float *in, float *out, int count, int rows, int cols,
                             hipStream_t stream);

@@ -146,10 +146,15 @@ gla_status gla_fwd_chunked_fixed_decay(const void *q, const void *k, const void 
  * in time (the adjoint dL/dS_t obeys the same recurrence backwards, with the
  * gates shifted by one token); dg follows from dL/dB_t = q_t.dq_t - k_t.dk_t
  * (B the cumulative log-gate, plus <dS_T, S_T> at a sequence's last token)
- * summed over later tokens of the sequence. Outputs must not overlap the
- * inputs or each other. The workspace (gla_bwd_chunked_workspace_size bytes,
- * never 0 for a non-empty batch) holds the reversed inputs and intermediate
- * results; its contents on entry do not matter. Errors as gla_fwd_chunked.
+ * summed over later tokens of the sequence. Head shapes: (dk, dv) in
+ * {64, 128} x {64, 128}, and 96 x 192 (Laplace 3B's heads; its dq and dk runs
+ * have 192-dim keys and run, with the dv run, on the fp32-arithmetic kernel,
+ * which reads bf16 inputs as they are); others give GLA_ERR_UNSUPPORTED.
+ * Outputs must not overlap the inputs or each other. The workspace
+ * (gla_bwd_chunked_workspace_size bytes, never 0 for a non-empty batch) holds
+ * transposed states, the adjoint after the first token, per-token partial
+ * sums and the forward runs' plans; its contents on entry do not matter.
+ * Errors as gla_fwd_chunked.
  */
 size_t gla_bwd_chunked_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
                                       int chunk_size, int has_cu_seqlens, gla_dtype in_dtype);

@@ -136,7 +136,7 @@ def test_bwd_rejects_bad_arguments_before_launch():
              dq=FAKE + 5 * G, dk=FAKE + 6 * G, dv=FAKE + 7 * G, dg=FAKE + 8 * G)
     lib = _lib.load()
     n = lib.gla_bwd_chunked_workspace_size(1, 64, 1, 64, 64, 1, 64, 0, _lib.GLA_BF16)
-    assert n > 0  # the reversed inputs live in the workspace
+    assert n > 0  # transposed states and per-token partial sums live in the workspace
     W = dict(ws=FAKE + 9 * G, wsb=n)
     assert _bwd(B=-1, **P, **W) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert _bwd(ind=5, **P, **W) == _lib.GLA_ERR_INVALID_ARGUMENT
@@ -151,6 +151,10 @@ def test_bwd_rejects_bad_arguments_before_launch():
     assert _bwd(**P, ws=FAKE + 9 * G, wsb=n - 1) == _lib.GLA_ERR_WORKSPACE
     assert _bwd(H=0, **P) == _lib.GLA_OK
     assert lib.gla_bwd_chunked_workspace_size(1, 64, 1, 96, 64, 1, 64, 0, _lib.GLA_BF16) == 0
+    # Laplace 3B's 96 x 192 heads are supported; their transpose 192 x 96 is not
+    assert lib.gla_bwd_chunked_workspace_size(1, 64, 1, 96, 192, 1, 64, 0, _lib.GLA_BF16) > 0
+    assert lib.gla_bwd_chunked_workspace_size(1, 64, 1, 192, 96, 1, 64, 0, _lib.GLA_BF16) == 0
+    assert _bwd(dkd=192, dvd=96, **P, **W) == _lib.GLA_ERR_UNSUPPORTED
 
 
 def test_decode_slots_rejects_bad_arguments_before_launch():

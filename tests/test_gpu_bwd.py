@@ -2,7 +2,9 @@
 oracle's backward (the reverse-mode adjoint of the token-by-token recurrence
 of Laplace 3B on AWS Trainium2, "GLA mixer"; training differentiates through
 the chunked state updates, "Challenge 1"). Tolerances as for the forward:
-max relative error (normwise per tensor) 2e-3 for bf16 inputs, 1e-5 for fp32.
+max relative error (normwise per tensor) 2e-3 for bf16 inputs, 1e-5 for fp32;
+for the log-gate gradient, a difference of two dot products, those bars times
+how much the two cancel (gpu_util.dg_tolerance).
 """
 import dataclasses
 import os
@@ -39,11 +41,15 @@ def check_bwd(q, k, v, lg, S0, cu, dO, dS_T, dtype, C=64, heads=None, tight=None
     ref = orc.recurrent_backward(q, k, v, lg, dO, dS_T, S0, cu, heads=heads)
     tol = gu.TOL_BF16 if dtype == "bf16" else gu.TOL_F32
     errs = [orc.normwise_error(g, r) for g, r in zip(got, ref)]
-    gu.say("   " + "  ".join(f"{n} {e:.2e}" for n, e in zip(NAMES, errs)) + f"  (tol {tol:.0e})")
+    qh, kh = (q, k) if heads is None else (q[:, :, heads], k[:, :, heads])
+    cancel = gu.dg_tolerance(1.0, qh, kh, ref[0], ref[1])  # the gate gradient's bars scale by it
+    gu.say("   " + "  ".join(f"{n} {e:.2e}" for n, e in zip(NAMES, errs))
+           + f"  (tol {tol:.0e}; dg x{cancel:.1f})")
     for n, e in zip(NAMES, errs):
-        assert e <= tol, (n, e)
+        scale = cancel if n == "dg" else 1.0
+        assert e <= tol * scale, (n, e)
         if tight is not None:
-            assert e <= tight, (n, e)
+            assert e <= tight * scale, (n, e)
 
 
 def _inputs(w, seed, B=None, T=None, H=None, lengths=None, final_state=True):
@@ -123,3 +129,40 @@ def test_bwd_full_train_2k_sampled_heads():
     q, k, v, lg, S0, cu = synth.make_forward_inputs(w)
     dO, dS_T = synth.make_backward_grads(w, w.B, w.T, w.H, w.B, seed=w.seed + 7)
     check_bwd(q, k, v, lg, S0, cu, dO, dS_T, "bf16", heads=[0, 11], tight=1e-4)
+
+
+# Laplace 3B's 96 x 192 heads (Laplace 3B on AWS Trainium2, "GLA mixer": d_k = 96,
+# d_v = 192; "Challenge 1": training differentiates through the state updates).
+# Their dq and dk runs have 192-dim keys and run on the fp32-arithmetic kernel,
+# bf16 inputs included, so bf16 inputs are held to a tighter bar as well.
+
+def _laplace(s0=0.02, H=2):
+    return dataclasses.replace(W["laplace_2k"], H=H, s0_std=s0, fixed_decay=False, gate_bias=3.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("C", [64, 128])
+@pytest.mark.parametrize("T", [1, 300])
+def test_bwd_laplace_heads(dtype, C, T):
+    """96 x 192 heads: one token, and several chunks with a ragged tail; S0 and dS_T."""
+    gu.say(f"bwd laplace 96x192 {dtype} C={C} T={T}")
+    check_bwd(*_inputs(_laplace(), 700 + T + C, B=2, T=T, H=2), dtype, C=C,
+              tight=1e-4 if dtype == "bf16" else None)
+
+
+def test_bwd_laplace_fixed_decays_varlen():
+    """The geometric decay schedule as the gate stream (16 heads, half-lives 1 ..
+    2048 tokens), a packed batch with empty and short sequences, no dS_T."""
+    gu.say("bwd laplace fixed decays, varlen")
+    w = dataclasses.replace(W["laplace_2k"], s0_std=0.02)
+    lengths = [0, 1, 65, 200, 0, 130]
+    check_bwd(*_inputs(w, 720, lengths=lengths, final_state=False), "bf16", tight=1e-4)
+
+
+@pytest.mark.parametrize("seg,sub", [(64, 1), (128, 3)])
+def test_bwd_laplace_forced_segment_split(seg, sub, monkeypatch):
+    gu.say(f"bwd laplace forced split seg={seg} pieces={sub}")
+    monkeypatch.setenv("GLA_SEG_LEN", str(seg))
+    monkeypatch.setenv("GLA_STATE_SUB", str(sub))
+    w = dataclasses.replace(_laplace(), H=1)
+    check_bwd(*_inputs(w, 730, lengths=[400, 3, 0, 129]), "bf16", tight=1e-4)
