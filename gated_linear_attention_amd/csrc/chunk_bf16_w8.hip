@@ -821,8 +821,16 @@ static hipError_t launch_w8_d(const uint16_t *q, const uint16_t *k, const uint16
                                                                slot_gamma, stream);
       }
     }
-  } else {
-    if (d.rev || d.dot_x) return hipErrorInvalidValue;
+  } else {  // 96 x 192 heads: the backward's dv run (reversed, fp32 output, no dots)
+    if (d.dot_x) return hipErrorInvalidValue;
+    if (d.rev) {
+      if (state_pass)
+        return launch_w8_t<DK, NCG, float, true, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
+                                                       grid_items, slots, slot_gamma, stream);
+      if (out_bf16) return hipErrorInvalidValue;
+      return launch_w8_t<DK, NCG, float, false, true>(q, k, v, g, S0, S_T, o, d, items, n_items,
+                                                      grid_items, slots, slot_gamma, stream);
+    }
   }
   if (state_pass)
     return launch_w8_t<DK, NCG, float, true>(q, k, v, g, S0, S_T, o, d, items, n_items, grid_items,

@@ -361,6 +361,11 @@ bool bwd_dims(int dk, int dv) {
   return (supported_head_dim(dk) && supported_head_dim(dv)) || (dk == 96 && dv == 192);
 }
 bool bwd_f32_kernel(int dk, int dv) { return dk == 96 && dv == 192; }
+// The dv run of those heads is a 96 x 192 forward: on the twelve-wavefront
+// bf16 kernel for bf16 inputs at chunk 64, otherwise with the dq and dk runs.
+bool bwd_dv_f32_kernel(int dk, int dv, int C, gla_dtype in_dtype) {
+  return bwd_f32_kernel(dk, dv) && !(in_dtype == GLA_BF16 && C == 64);
+}
 
 // Workspace layout of the backward (all offsets 256-byte aligned).
 struct BwdLayout {
@@ -390,7 +395,8 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int N, int C, bool has
   L.dqp = take(parts);
   L.dkp = take(parts);
   const size_t f1 = fwd_workspace(B, T, H, dv, dk, N, C, has_cu, in_dtype, f32k);
-  const size_t f2 = fwd_workspace(B, T, H, dk, dv, N, C, has_cu, in_dtype, f32k);
+  const size_t f2 = fwd_workspace(B, T, H, dk, dv, N, C, has_cu, in_dtype,
+                                  bwd_dv_f32_kernel(dk, dv, C, in_dtype));
   L.fws_bytes = f1 > f2 ? f1 : f2;
   L.fws = take(L.fws_bytes);
   L.total = off;
@@ -476,7 +482,8 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   if (st != GLA_OK) return st;
   // dv: the reversed-time run with (q, k, v) = (k, q, dO) from dS_T; ends in A_0
   st = fwd_core(k, q, dO, g, dS_T, cu_seqlens, dv, a0, B, T, H, DK, DV, N, chunk_size, in_dtype,
-                GLA_F32, fws, L.fws_bytes, stream, false, true, nullptr, f32k);
+                GLA_F32, fws, L.fws_bytes, stream, false, true, nullptr,
+                bwd_dv_f32_kernel(DK, DV, chunk_size, in_dtype));
   if (st != GLA_OK) return st;
   // dk: the reversed-time run with (q, k, v) = (v, dO, q) from dS_T^T
   st = fwd_core(v, dO, q, g, dstt, cu_seqlens, dk, nullptr, B, T, H, DV, DK, N, chunk_size,

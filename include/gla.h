@@ -148,8 +148,8 @@ gla_status gla_fwd_chunked_fixed_decay(const void *q, const void *k, const void 
  * (B the cumulative log-gate, plus <dS_T, S_T> at a sequence's last token)
  * summed over later tokens of the sequence. Head shapes: (dk, dv) in
  * {64, 128} x {64, 128}, and 96 x 192 (Laplace 3B's heads; its dq and dk runs
- * have 192-dim keys and run, with the dv run, on the fp32-arithmetic kernel,
- * which reads bf16 inputs as they are); others give GLA_ERR_UNSUPPORTED.
+ * have 192-dim keys and run on the fp32-arithmetic kernel, which reads bf16
+ * inputs as they are); others give GLA_ERR_UNSUPPORTED.
  * Outputs must not overlap the inputs or each other. The workspace
  * (gla_bwd_chunked_workspace_size bytes, never 0 for a non-empty batch) holds
  * transposed states, the adjoint after the first token, per-token partial
