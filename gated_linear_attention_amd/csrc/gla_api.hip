@@ -64,8 +64,11 @@ int choose_seg_len(int B, int T, int H, int dk, int dv, int N, int C, bool has_c
   } else if (!has_cu) {
     const long units = (long)B * H * n_slices;
     // workgroups to aim for: one per CU on the bf16 kernels, four on the
-    // fp32 one (two fit per CU, and it is bound by latency, not bandwidth)
-    const long target = (long)cu_count() * (in_dtype == GLA_BF16 ? 1 : 4);
+    // fp32 one (two fit per CU, and it is bound by latency, not bandwidth),
+    // except with 192-dim keys (the 96 x 192 backward's dq and dk runs), whose
+    // chunks carry enough work that a split costs more than it hides
+    // (laplace_2k backward: 3.82 ms whole against 4.04 ms in three segments)
+    const long target = (long)cu_count() * (in_dtype == GLA_BF16 || dk == 192 ? 1 : 4);
     if (units >= target) {
       L = T;
     } else {
