@@ -160,6 +160,17 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
   return __int_as_float(v);
 }
 
+// Last set bit of `mask` at or below bit `lane` (-1 if none): with bit p set
+// where gate position p of a wavefront is a reset, the last reset at or
+// before position `lane`.
+__device__ __forceinline__ int last_set_upto(uint64_t mask, int lane) {
+  const uint64_t upto = mask & ((2ull << lane) - 1ull);  // lane 63: every bit
+  return upto ? 63 - __builtin_clzll(upto) : -1;
+}
+__device__ __forceinline__ int last_set(uint64_t mask) {
+  return mask ? 63 - __builtin_clzll(mask) : -1;
+}
+
 // Score tile index -> (row tile ti, column tile tj), tj <= ti, row-major over
 // the lower triangle (t = ti (ti + 1) / 2 + tj). Branch-free so that it folds
 // to constants once the tile loop is unrolled.

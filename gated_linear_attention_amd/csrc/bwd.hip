@@ -2,7 +2,8 @@
 //
 // The backward of the recurrence S_t = g_t S_{t-1} + k_t^T v_t, o_t = q_t S_t
 // (Laplace 3B on AWS Trainium2, automationscribe.com/?p=7116, "GLA mixer";
-// training differentiates through the chunked state updates, "Challenge 1")
+// training differentiates through every sequential state update, "Challenge 3:
+// Backward-pass unrolling for a sequential recurrence")
 // is computed from three runs of the chunked forward and the kernels below:
 //  * dq_t = dO_t S_t^T is the forward output for the transposed state
 //    S'_t = g_t S'_{t-1} + v_t^T k_t, i.e. the forward with (q, k, v) :=
@@ -75,6 +76,14 @@ __global__ __launch_bounds__(256) void gate_dot_kernel(const Tin *__restrict__ q
 // along the tokens); otherwise it is read from dB [token][H]. ST_t and dST_t
 // are S_T^T and dS_T^T ([dv][dk]; dST_t null for dS_T = 0); A0 is the adjoint
 // after the first token ([dk][dv]). dB and dl may be the same array.
+//
+// A reset gate at token r (g_r = 0) makes the loss independent of every
+// earlier token's log-gate through tokens u >= r, and of l_r itself
+// (dL/dl_r = g_r <A_r, S_{r-1}> = 0): the sum restarts at r, dl_r = 0, and
+// earlier tokens sum dB over [t, r) only (the terms from r on sum to zero in
+// exact arithmetic; dropping them drops their rounding). Each thread's eight
+// tokens act on the running sum as run -> a run + b (a = 0 if they hold a
+// reset), and the tile composes these maps from the right.
 template <int NP>
 __global__ __launch_bounds__(256) void gate_scan_kernel(
     const float *dB, const float *__restrict__ dq_part, const float *__restrict__ dk_part,
@@ -83,10 +92,20 @@ __global__ __launch_bounds__(256) void gate_scan_kernel(
     float *__restrict__ dS0, const int32_t *__restrict__ cu, int T, int H, int DK, int DV) {
   const int n = blockIdx.x / H, h = blockIdx.x % H;
   const int tid = threadIdx.x;
-  const int s = cu ? cu[n] : n * T, e = cu ? cu[n + 1] : (n + 1) * T;
+  // sequence bounds; packed offsets are clamped to [0, T] with e >= s (as the
+  // forward's planner does), so malformed offsets stay inside the arrays
+  int s, e;
+  if (cu) {
+    s = min(max(cu[n], 0), T);
+    e = max(min(max(cu[n + 1], 0), T), s);
+  } else {
+    s = n * T;
+    e = (n + 1) * T;
+  }
   const size_t mat = (size_t)DK * DV, base = ((size_t)n * H + h) * mat;
-  __shared__ float red[256];
+  __shared__ float red[256], reda[256];
   __shared__ float xs[2048];
+  __shared__ unsigned char fs[2048];
 
   // <dS_T, S_T>
   float fro = 0.f;
@@ -103,20 +122,25 @@ __global__ __launch_bounds__(256) void gate_scan_kernel(
 
   // dS0 = g_0 A_0 (an empty sequence passes dS_T through: A_0 = dS_T)
   if (dS0) {
-    const float g0 = e > s ? fast_exp2(lg[(size_t)s * H + h] * kLog2e) : 1.f;
+    float g0 = 1.f;
+    if (e > s) {
+      const float l0 = lg[(size_t)s * H + h];
+      g0 = is_reset(l0) ? 0.f : fast_exp2(l0 * kLog2e);
+    }
     for (size_t i = tid; i < mat; i += 256) dS0[base + i] = g0 * A0[base + i];
   }
 
-  // tiles of 8 tokens per thread, last tile first; carry = sum over later tiles
+  // tiles of 8 tokens per thread, last tile first; carry = the running sum
+  // entering the tile from the right
   float carry = fro;
   const size_t plane = (size_t)n_tok * H;
   for (int hi = e; hi > s; hi -= 2048) {
     const int lo = hi - 2048 > s ? hi - 2048 : s;
-    // the tile's dB into LDS (the partial planes are read along the tokens,
-    // every load of the tile issued before the first sum; addresses clamped
-    // into the tile)
+    // the tile's dB and reset flags into LDS (the partial planes are read
+    // along the tokens, every load of the tile issued before the first sum;
+    // addresses clamped into the tile)
     const int cnt = hi - lo;
-    float d[8];
+    float d[8], l[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const size_t t = (size_t)lo + min(tid + 256 * j, cnt - 1);
@@ -131,36 +155,57 @@ __global__ __launch_bounds__(256) void gate_scan_kernel(
       } else {
         d[j] = dB[t * H + h];
       }
+      l[j] = lg[t * H + h];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (tid + 256 * j < cnt) xs[tid + 256 * j] = d[j];
+      if (tid + 256 * j < cnt) {
+        xs[tid + 256 * j] = d[j];
+        fs[tid + 256 * j] = is_reset(l[j]);
+      }
     __syncthreads();
-    float x[8], tot = 0.f;
+    // this thread's map run -> ta run + tb
+    float x[8], tb = 0.f, ta = 1.f;
+    bool f[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      x[j] = lo + 8 * tid + j < hi ? xs[8 * tid + j] : 0.f;
-      tot += x[j];
+      const bool in = lo + 8 * tid + j < hi;
+      x[j] = in ? xs[8 * tid + j] : 0.f;
+      f[j] = in && fs[8 * tid + j];
     }
-    // inclusive suffix sums of the per-thread totals
-    red[tid] = tot;
+#pragma unroll
+    for (int j = 7; j >= 0; --j) {
+      if (f[j]) {
+        tb = 0.f;
+        ta = 0.f;
+      } else {
+        tb += x[j];
+      }
+    }
+    // inclusive compositions from the right: (A, B)[tid] = map tid after maps tid+1, ...
+    red[tid] = tb;
+    reda[tid] = ta;
     __syncthreads();
     for (int w = 1; w < 256; w <<= 1) {
-      const float y = tid + w < 256 ? red[tid + w] : 0.f;
+      const float yb = tid + w < 256 ? red[tid + w] : 0.f;
+      const float ya = tid + w < 256 ? reda[tid + w] : 1.f;
       __syncthreads();
-      red[tid] += y;
+      red[tid] = reda[tid] * yb + red[tid];
+      reda[tid] *= ya;
       __syncthreads();
     }
-    float run = carry + red[tid] - tot;
-    const float tile_total = red[0];
+    // the sum entering this thread from the right, and the tile's carry out
+    float run = tid < 255 ? reda[tid + 1] * carry + red[tid + 1] : carry;
+    const float out = reda[0] * carry + red[0];
     __syncthreads();
 #pragma unroll
     for (int j = 7; j >= 0; --j) {
       const int t = lo + 8 * tid + j;
-      run += x[j];
+      if (f[j]) run = 0.f;
+      else run += x[j];
       if (t < hi) dl[(size_t)t * H + h] = run;
     }
-    carry += tile_total;
+    carry = out;
   }
 }
 

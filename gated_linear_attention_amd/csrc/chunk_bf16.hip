@@ -63,8 +63,9 @@ struct BfLds {
   uint16_t phi[QR * PP];
   uint16_t plo[QR * PP];
   float gb2[4][C];   // per wavefront: in-chunk prefix sums of the log-gates, log2 units
-  float glam[4][C];  // 2^(b2_i)
-  float gkap[4][C];  // 2^(b2_last - b2_j)
+  float glam[4][C];  // 2^(b2_i), 0 from the chunk's first reset on
+  float gkap[4][C];  // 2^(b2_last - b2_j), 0 before the chunk's last reset
+  int grs[4][C];     // last reset at or before position i (-1: none)
 };
 
 // HBM -> LDS copies of one chunk (rows [t0, t0 + n) of the run) into stage
@@ -181,30 +182,47 @@ struct BfRun {
   // Gates of the chunk in stage st (n tokens): in-chunk prefix sums (log2
   // units) and the decay factors, into this wavefront's LDS arrays. Positions
   // past the end add 0 (a fixed decay loads its value into every position).
+  // A reset gate adds 0 and cuts every product of gates that spans it (the
+  // chunk decay, e^{b_i} from the first reset on, kappa_j before the last
+  // one, score keys before the query's last reset).
   // Returns the chunk decay; adds the chunk's natural-log gate sum to lsum.
   __device__ __forceinline__ float gates(int st, int n, float &lsum) {
+    static_assert(E == 1 || E == 2, "gate positions per lane");
     float part[E];
+    bool rst[E];
     float run = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const float x = s.lg[st][lane * E + e];
-      run += lane * E + e < n ? x : 0.f;
+      const float x = lane * E + e < n ? s.lg[st][lane * E + e] : 0.f;
+      rst[e] = is_reset(x);
+      run += rst[e] ? 0.f : x;
       part[e] = run;
     }
+    // last reset at or before each position: in this lane, else in the last
+    // lane before it that holds one (position j = lane E + e)
+    const uint64_t m_any = __builtin_amdgcn_ballot_w64(rst[0] || rst[E - 1]);
+    const uint64_t m_hi = __builtin_amdgcn_ballot_w64(rst[E - 1]);
+    const int lp = last_set_upto(m_any, lane - 1 < 0 ? 0 : lane - 1);
+    const int before = lane == 0 || lp < 0 ? -1 : lp * E + (E == 2 && ((m_hi >> lp) & 1));
+    const int la = last_set(m_any);
+    const int rl = la < 0 ? -1 : la * E + (E == 2 && ((m_hi >> la) & 1));
     const float incl = wave_inclusive_scan(run);
     const float excl = incl - run;
     const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
     const float b2last = total * kLog2e;
+    int ri = before;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = lane * E + e;
+      if (rst[e]) ri = j;
       const float b2 = (excl + part[e]) * kLog2e;
       s.gb2[wave][j] = b2;
-      s.glam[wave][j] = fast_exp2(b2);
-      s.gkap[wave][j] = fast_exp2(b2last - b2);
+      s.grs[wave][j] = ri;
+      s.glam[wave][j] = ri < 0 ? fast_exp2(b2) : 0.f;
+      s.gkap[wave][j] = j < rl ? 0.f : fast_exp2(b2last - b2);
     }
-    lsum += total;
-    return fast_exp2(b2last);
+    lsum += rl < 0 ? total : -__builtin_huge_valf();
+    return rl < 0 ? fast_exp2(b2last) : 0.f;
   }
 
   // Score tiles W, W+4, ... of A^T = K Q^T (compile-time list, so the tiles'
@@ -236,12 +254,13 @@ struct BfRun {
       // acc[m][r] = A^T[j][i] with j = 16 tj + 4 lg4 + r, i = 16 ti + ln
       const int i = 16 * ti + ln;
       const float b2i = s.gb2[wave][i];
+      const int ri = s.grs[wave][i];  // keys before the query's last reset are cut off
       float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * tj + 4 * lg4 + r;
         const float d = fast_exp2(b2i - s.gb2[wave][j]);
-        p[r] = (ti > tj || j <= i) ? acc[m][r] * d : 0.f;
+        p[r] = (ti > tj || j <= i) && j >= ri ? acc[m][r] * d : 0.f;
       }
       uint32_t h0, l0, h1, l1;
       split_pk_bf16(p[0], p[1], h0, l0);

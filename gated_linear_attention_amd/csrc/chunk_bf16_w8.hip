@@ -54,8 +54,9 @@ struct W8Lds {
   u32x4 kvx[NW][2][64];            // kappa . V (hi, lo) for the partner's 32 keys
   float lgb[3][C];                 // log-gates, loaded two chunks ahead
   float gb2[NW][C];   // per wavefront: in-chunk prefix sums of the log-gates, log2 units
-  float glam[NW][C];  // 2^(b2_i)
-  float gkap[NW][C];  // 2^(b2_last - b2_j)
+  float glam[NW][C];  // 2^(b2_i), 0 from the chunk's first reset on
+  float gkap[NW][C];  // 2^(b2_last - b2_j), 0 before the chunk's last reset
+  int grs[NW][C];     // last reset at or before position i (-1: none)
 };
 
 // HBM -> LDS copy of one chunk into stage st, done by the wavefronts of row
@@ -220,17 +221,26 @@ struct W8Wave {
   __device__ __forceinline__ W8Wave(LDS &s_, int w, int l)
       : s(s_), wave(w), lane(l), ln(l % 16), lg4(l / 16) {}
 
-  // x = this lane's log-gate (0 past the end of the run); returns the chunk decay.
+  // x = this lane's log-gate (0 past the end of the run); returns the chunk
+  // decay. A reset gate enters the prefix sums as 0 and cuts every product of
+  // gates that spans it: the chunk decay and e^{b_i} are 0 from the chunk's
+  // first reset on, kappa_j = 0 for keys before its last reset, and the score
+  // mask drops keys before the query's last reset (grs, -1 without one).
+  // Without resets the values are those of the plain scan.
   __device__ __forceinline__ float gates(float x, float &lsum) {
-    const float incl = wave_inclusive_scan(x);
+    const bool rst = is_reset(x);
+    const uint64_t rm = __builtin_amdgcn_ballot_w64(rst);
+    const float incl = wave_inclusive_scan(rst ? 0.f : x);
     const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
     const float b2last = total * kLog2e;
     const float b2 = incl * kLog2e;
+    const int ri = last_set_upto(rm, lane), rl = last_set(rm);
     s.gb2[wave][lane] = b2;
-    s.glam[wave][lane] = fast_exp2(b2);
-    s.gkap[wave][lane] = fast_exp2(b2last - b2);
-    lsum += total;
-    return fast_exp2(b2last);
+    s.grs[wave][lane] = ri;
+    s.glam[wave][lane] = ri < 0 ? fast_exp2(b2) : 0.f;
+    s.gkap[wave][lane] = lane < rl ? 0.f : fast_exp2(b2last - b2);
+    lsum += rl < 0 ? total : -__builtin_huge_valf();
+    return rl < 0 ? fast_exp2(b2last) : 0.f;
   }
 
   // One 16x16 score tile of A^T = K Q^T (rows: keys 16 tj.., columns: queries
@@ -239,6 +249,7 @@ struct W8Wave {
   struct TileOps {
     u32x4 a[NKS], b[NKS];
     float b2i;
+    int rq;  // the query's last reset in the chunk (-1: none)
     f32x4 g4;
   };
   __device__ __forceinline__ void tile_read(TileOps &t, const uint16_t *sq, const uint16_t *sk,
@@ -249,6 +260,7 @@ struct W8Wave {
       t.b[ks] = *reinterpret_cast<const u32x4 *>(&sq[qk_off<DK>(16 * ti + ln, 32 * ks + 8 * lg4)]);
     }
     t.b2i = s.gb2[wave][16 * ti + ln];
+    t.rq = s.grs[wave][16 * ti + ln];
     t.g4 = *reinterpret_cast<const f32x4 *>(&s.gb2[wave][16 * tj + 4 * lg4]);
   }
   __device__ __forceinline__ f32x4 tile_mma(const TileOps &t) {
@@ -257,13 +269,16 @@ struct W8Wave {
     for (int ks = 0; ks < NKS; ++ks) acc = mfma16(t.a[ks], t.b[ks], acc);
     return acc;
   }
-  // madd[r] = 0 where key 16 tj + 4 lg4 + r may attend (j <= i), -inf where masked;
-  // the decay factor is 2^(b2_i - b2_j + madd).
-  __device__ __forceinline__ f32x4 tile_mask(int ti, int tj) const {
+  // madd[r] = 0 where key j = 16 tj + 4 lg4 + r may attend query i = 16 ti + ln
+  // (j <= i, and j at or after the query's last reset rq; rq = -1 without
+  // one), -inf where masked; the decay factor is 2^(b2_i - b2_j + madd).
+  __device__ __forceinline__ f32x4 tile_mask(int ti, int tj, int rq = -1) const {
     f32x4 m;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      m[r] = (ti > tj || 16 * tj + 4 * lg4 + r <= 16 * ti + ln) ? 0.f : -__builtin_huge_valf();
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * tj + 4 * lg4 + r;
+      m[r] = (ti > tj || j <= 16 * ti + ln) && j >= rq ? 0.f : -__builtin_huge_valf();
+    }
     return m;
   }
   __device__ __forceinline__ void tile_store(const f32x4 &acc, const TileOps &t, const f32x4 &madd,
@@ -468,11 +483,6 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
   const int ti1 = tile_ti(has_tile ? wave : 0), tj1 = tile_tj(has_tile ? wave : 0);
   const bool two_tiles = NCG == 4 && (wave == 4 || wave == 5);
   const int ti2 = 3, tj2 = wave - 2;
-  f32x4 madd1, madd2;  // kept across the loop only with four column groups
-  if constexpr (NCG == 4) {
-    madd1 = R.tile_mask(ti1, tj1);
-    madd2 = R.tile_mask(ti2, tj2);
-  }
 
   for (int ci = 0; t0 < w.tok_end; t0 += C, ++ci) {
     const int n = min(C, w.tok_end - t0);
@@ -530,7 +540,7 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
       if (!kOverlapTile && has_tile) {
         typename Wv::TileOps t0;
         R.tile_read(t0, sq, sk, ti1, tj1);
-        R.tile_store(R.tile_mma(t0), t0, R.tile_mask(ti1, tj1), ti1, tj1);
+        R.tile_store(R.tile_mma(t0), t0, R.tile_mask(ti1, tj1, t0.rq), ti1, tj1);
       }
       typename Wv::TileOps t1;
       if (kOverlapTile && has_tile) R.tile_read(t1, sq, sk, ti1, tj1);
@@ -587,7 +597,7 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
       for (int mi = 0; mi < 4; ++mi) part[mi] = mfma16(sl[0], qf[0][mi], part[mi]);
       __builtin_amdgcn_sched_barrier(0);
       // the tile's mask and P stores overlap the rest of the state read
-      if (kOverlapTile && has_tile) R.tile_store(acc1, t1, madd1, ti1, tj1);
+      if (kOverlapTile && has_tile) R.tile_store(acc1, t1, R.tile_mask(ti1, tj1, t1.rq), ti1, tj1);
 #pragma unroll
       for (int ks = 1; ks < NKH; ++ks) {
 #pragma unroll
@@ -605,7 +615,7 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
       if (two_tiles) {
         typename Wv::TileOps t2;
         R.tile_read(t2, sq, sk, ti2, tj2);
-        R.tile_store(R.tile_mma(t2), t2, madd2, ti2, tj2);
+        R.tile_store(R.tile_mma(t2), t2, R.tile_mask(ti2, tj2, t2.rq), ti2, tj2);
       }
       ld.q_part(s, wave, lane);
       // rows of the partner's blocks go through LDS (rh is wave-uniform: no

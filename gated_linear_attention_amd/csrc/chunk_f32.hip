@@ -73,6 +73,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
   __shared__ float P[C][C + 1];
   __shared__ float Ss[DK][DVS + 1];
   __shared__ float bcum[C], lam[C], kap[C];
+  __shared__ int rpos[C];  // last reset at or before position i (-1: none)
   __shared__ float gam_s, gsum_s;
 
   const int n_slices = DV / DVS;
@@ -160,24 +161,37 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
     if (!kAhead) first_loads(t0);
     __syncthreads();
     // gates: inclusive scan of the chunk's log-gates (padding rows add 0), one
-    // wavefront scan per 64 tokens; a second 64 adds the first one's total
-    if (tid < C) bcum[tid] = wave_inclusive_scan(gx);
+    // wavefront scan per 64 tokens; a second 64 adds the first one's total.
+    // A reset gate adds 0 and cuts every product of gates that spans it: the
+    // chunk decay, e^{b_i} from the chunk's first reset on, kappa_j before its
+    // last reset, and score keys before the query's last reset.
+    if (tid < C) {
+      const bool rst = is_reset(gx);
+      const int ri = last_set_upto(__builtin_amdgcn_ballot_w64(rst), tid % 64);
+      bcum[tid] = wave_inclusive_scan(rst ? 0.f : gx);
+      rpos[tid] = ri < 0 ? -1 : (tid & ~63) + ri;
+    }
 #pragma unroll
     for (int e = 0; e < VPT; ++e) Vs[(tid + 256 * e) / DVS][(tid + 256 * e) % DVS] = vx[e];
     __syncthreads();
     if constexpr (C == 128) {
       const float first = bcum[63];
+      const int r_first = rpos[63];
       __syncthreads();
-      if (tid >= 64 && tid < 128) bcum[tid] += first;
+      if (tid >= 64 && tid < 128) {
+        bcum[tid] += first;
+        if (rpos[tid] < 0) rpos[tid] = r_first;
+      }
       __syncthreads();
     }
     const float blast = bcum[n - 1];
+    const int rlast = rpos[n - 1];
     if (tid < C) {
-      lam[tid] = expf(bcum[tid]);
-      kap[tid] = expf(blast - bcum[tid]);
+      lam[tid] = rpos[tid] < 0 ? expf(bcum[tid]) : 0.f;
+      kap[tid] = tid < rlast ? 0.f : expf(blast - bcum[tid]);
     }
-    if (tid == 0) gam_s = expf(blast);
-    gsum += blast;
+    if (tid == 0) gam_s = rlast < 0 ? expf(blast) : 0.f;
+    gsum += rlast < 0 ? blast : -__builtin_huge_valf();
 
     if (!STATE_PASS) {
       // score tiles t = wave, wave + 4, ... (lower triangle, row-major) and the
@@ -218,7 +232,8 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
             oacc[u] = mfma_f32(Qb[16 * ti + ln][4 * ks + l4], Ss[db + 4 * ks + l4][16 * tc + ln], oacc[u]);
         }
       }
-      // decay mask: P[i][j] = score * e^{b_i - b_j} for j <= i, else 0
+      // decay mask: P[i][j] = score * e^{b_i - b_j} for j <= i with no reset in
+    // (j, i], else 0
 #pragma unroll
       for (int s = 0; s < SPW; ++s) {
         const int t = wave + 4 * s;
@@ -227,7 +242,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 16 * ti + 4 * l4 + r;
-            P[i][j] = (j <= i) ? sacc[s][r] * expf(bcum[i] - bcum[j]) : 0.f;
+            P[i][j] = (j <= i && j >= rpos[i]) ? sacc[s][r] * expf(bcum[i] - bcum[j]) : 0.f;
           }
         }
       }

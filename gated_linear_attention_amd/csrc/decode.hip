@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const Tin *__restrict_
 #pragma unroll
   for (int i = 0; i < NP; ++i) s[i] = __builtin_nontemporal_load(Sp + (r0 + i * RP) * TPR + c4);
 
-  const float gate = expf(g[p]);
+  const float gate = gate_exp(g[p]);
   f32x4 vv;
   vv.x = load_as_f32(v, p * DV + 4 * c4 + 0);
   vv.y = load_as_f32(v, p * DV + 4 * c4 + 1);
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(512) void decode_step_rows_kernel(const Tin *__rest
 #pragma unroll
   for (int i = 0; i < NP; ++i)
     s[i] = __builtin_nontemporal_load(Sp + (r0 + i * RP) * (DV / 4) + c4);
-  const float gate = expf(g[p]);
+  const float gate = gate_exp(g[p]);
   const size_t vc = p * DV + col0 + 4 * c4;
   f32x4 vv;
   vv.x = load_as_f32(v, vc + 0);
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(512) void decode_mixer_kernel(
   f32x4 s[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) s[i] = __builtin_nontemporal_load(Sp + (r0 + i * RP) * TPR + c4);
-  const float gate = expf(g[p]);
+  const float gate = gate_exp(g[p]);
   const size_t vc = p * DV + 4 * c4;
   f32x4 vv;
   vv.x = load_as_f32(v, vc + 0);

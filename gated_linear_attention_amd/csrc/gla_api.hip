@@ -1,5 +1,6 @@
 // C ABI of libgla.so: argument validation, work planning and kernel launches.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdlib>
@@ -14,19 +15,21 @@ using namespace gla;
 namespace {
 
 constexpr int kMaxDevices = 64;
-int g_cu_count[kMaxDevices];  // cache of each device's CU count (a device constant)
+// cache of each device's CU count (a device constant): threads that race on
+// an entry all store the same value, through atomics
+std::atomic<int> g_cu_count[kMaxDevices];
 
 int cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  if (g_cu_count[dev] == 0) {
-    int n = 0;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    g_cu_count[dev] = n;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
   }
-  return g_cu_count[dev];
+  return n;
 }
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
@@ -92,8 +95,9 @@ int choose_seg_len(int B, int T, int H, int dk, int dv, int N, int C, bool has_c
       }
     }
   } else {
+    // the dense rule's per-CU target, 192-dim keys included
     const long work = (long)T * H * n_slices;
-    L = work / ((long)cu_count() * (in_dtype == GLA_BF16 ? 1 : 4));
+    L = work / ((long)cu_count() * (in_dtype == GLA_BF16 || dk == 192 ? 1 : 4));
     if (in_dtype == GLA_BF16 && C == 64 && N > 0) {
       // the segment floor of dense batches, from the mean sequence length
       // (the lengths themselves stay on the device)
@@ -243,12 +247,18 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
   const WorkItem *sitems = reinterpret_cast<const WorkItem *>(ws + lay.off_state_items);
   float *slots = reinterpret_cast<float *>(ws + lay.off_slots);
   float *slot_gamma = reinterpret_cast<float *>(ws + lay.off_slot_gamma);
-  if ((err = launch_plan(cu_seqlens, d, lay, workspace, stream)) != hipSuccess) return GLA_ERR_HIP;
+  // S_T over S0 (the one overlap the header allows): the last segment of a
+  // split sequence writes S_T[seq] while its first segment, another
+  // workgroup, reads S0[seq], so that one reads a copy made by the combine
+  const bool s0_copy = S0 && S_T == S0;
+  if ((err = launch_plan(cu_seqlens, d, lay, s0_copy, workspace, stream)) != hipSuccess)
+    return GLA_ERR_HIP;
   if (lay.max_state_items > 0) {
     if ((err = run_chunks(sitems, &hdr->n_state_items, lay.max_state_items, slots, slot_gamma,
                           true)) != hipSuccess)
       return GLA_ERR_HIP;
-    if ((err = launch_combine(S0, d, lay, workspace, stream)) != hipSuccess) return GLA_ERR_HIP;
+    if ((err = launch_combine(S0, d, lay, s0_copy, workspace, stream)) != hipSuccess)
+      return GLA_ERR_HIP;
   }
   err = run_chunks(items, &hdr->n_items, lay.max_items, slots, slot_gamma, false);
   return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;

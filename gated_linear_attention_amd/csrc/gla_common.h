@@ -8,6 +8,16 @@ namespace gla {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// A log-gate at or below -128 ln 2 (a multiplier g <= 2^-128, under the
+// smallest normal fp32) is taken as g = 0 exactly: the gate resets the state
+// (the previous state is multiplied by zero). -inf is the canonical reset.
+// Exponentials of sums that contain such a gate are never formed: the scans
+// treat it as 0 and cut every decay product that spans it.
+constexpr float kResetLn = -88.72283906f;
+__device__ __forceinline__ bool is_reset(float l) { return l <= kResetLn; }
+// exp(l), with every reset gate exactly 0.
+__device__ __forceinline__ float gate_exp(float l) { return is_reset(l) ? 0.f : expf(l); }
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

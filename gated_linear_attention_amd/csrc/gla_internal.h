@@ -90,11 +90,14 @@ hipError_t launch_decode(const void *q, const void *k, const void *v, const floa
                          void *o, int N, int H, int dk, int dv, bool in_bf16, bool out_bf16,
                          const int32_t *slots, int P, int n_cu, hipStream_t stream);
 
+// s0_copy: the output pass writes S_T over S0, so the first segment of a
+// split sequence reads a copy of S0 that the combine leaves in the chain's
+// first slot (another workgroup writes S_T[seq]).
 hipError_t launch_plan(const int32_t *cu_seqlens, const FwdDims &d, const PlanLayout &lay,
-                       void *workspace, hipStream_t stream);
+                       bool s0_copy, void *workspace, hipStream_t stream);
 
 hipError_t launch_combine(const float *S0, const FwdDims &d, const PlanLayout &lay,
-                          void *workspace, hipStream_t stream);
+                          bool s0_copy, void *workspace, hipStream_t stream);
 
 // fp32 arithmetic on fp32 inputs, or on bf16 inputs (in_bf16; d_k 96 or 192,
 // fp32 o: the backward's runs for the 96 x 192 heads). state_pass: compute

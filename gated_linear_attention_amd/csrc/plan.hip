@@ -51,7 +51,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
                                                     int L, int C, int Ls, int n_sub,
                                                     int max_items,
                                                     int max_state_items, int max_multi,
-                                                    int max_slots, PlanHeader *__restrict__ hdr,
+                                                    int max_slots, int s0_copy,
+                                                    PlanHeader *__restrict__ hdr,
                                                     WorkItem *__restrict__ items,
                                                     WorkItem *__restrict__ sitems,
                                                     MultiSeq *__restrict__ multi) {
@@ -145,7 +146,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
         it.tok_begin = tb;
         it.tok_end = te;
         it.seq = n;
-        it.state_in = split && s > 0 ? slot_base + s * n_sub : -1;  // segment 0: S0 itself
+        // segment 0 reads S0 itself, or its copy in the chain's first slot
+        // when S_T is S0 (the last segment, another workgroup, overwrites it)
+        it.state_in = split && (s > 0 || s0_copy) ? slot_base + s * n_sub : -1;
         it.state_out = (s == nseg - 1) ? -1 : kNoStateOut;
         it.seq_begin = start;
         it.seq_end = start + len;
@@ -186,14 +189,15 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
 // where the state pass left piece b-1's local state and total log-decay in
 // slot base+b. Only the starts of segments after the first (b a positive
 // multiple of n_sub) are read afterwards, so only they are written back; the
-// first segment starts from S0 itself. One thread per four
+// first segment starts from S0 itself, or (s0_copy, when the output pass
+// writes S_T over S0) from a copy of it in slot base. One thread per four
 // consecutive state elements.
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ S0,
                                                       const PlanHeader *__restrict__ hdr,
                                                       const MultiSeq *__restrict__ multi,
                                                       float *__restrict__ slots,
                                                       const float *__restrict__ slot_gamma,
-                                                      int H, int dkdv, int n_sub) {
+                                                      int H, int dkdv, int n_sub, int s0_copy) {
   const int bph = dkdv / 1024;  // blocks per (sequence, head)
   const int m = blockIdx.x / (H * bph);
   if (m >= hdr->n_multi) return;
@@ -202,6 +206,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   const MultiSeq ms = multi[m];
   f32x4 cur = {0.f, 0.f, 0.f, 0.f};
   if (S0) cur = *reinterpret_cast<const f32x4 *>(S0 + ((size_t)ms.seq * H + h) * dkdv + e);
+  if (s0_copy)
+    *reinterpret_cast<f32x4 *>(slots + ((size_t)ms.slot_base * H + h) * dkdv + e) = cur;
   // eight pieces at a time: their loads all issued before the chain's stores
   // (which the compiler would otherwise wait for before each next load);
   // indexes past the last piece are clamped to it and their values unused
@@ -227,14 +233,15 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 }
 
 hipError_t launch_plan(const int32_t *cu_seqlens, const FwdDims &d, const PlanLayout &lay,
-                       void *workspace, hipStream_t stream) {
+                       bool s0_copy, void *workspace, hipStream_t stream) {
   char *ws = static_cast<char *>(workspace);
   const int nb = lay.seg_len / d.C + 1;
   const size_t lds = sizeof(int) * (3 * nb + 32);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), lds, stream, cu_seqlens, d.N, d.T,
                      lay.seg_len, d.C, lay.sub_len, lay.n_sub, lay.max_items,
                      lay.max_state_items, lay.max_multi,
-                     lay.max_slots, reinterpret_cast<PlanHeader *>(ws + lay.off_header),
+                     lay.max_slots, (int)s0_copy,
+                     reinterpret_cast<PlanHeader *>(ws + lay.off_header),
                      reinterpret_cast<WorkItem *>(ws + lay.off_items),
                      reinterpret_cast<WorkItem *>(ws + lay.off_state_items),
                      reinterpret_cast<MultiSeq *>(ws + lay.off_multi));
@@ -242,7 +249,7 @@ hipError_t launch_plan(const int32_t *cu_seqlens, const FwdDims &d, const PlanLa
 }
 
 hipError_t launch_combine(const float *S0, const FwdDims &d, const PlanLayout &lay,
-                          void *workspace, hipStream_t stream) {
+                          bool s0_copy, void *workspace, hipStream_t stream) {
   if (lay.max_multi == 0) return hipSuccess;
   char *ws = static_cast<char *>(workspace);
   const int dkdv = d.dk * d.dv;
@@ -252,7 +259,7 @@ hipError_t launch_combine(const float *S0, const FwdDims &d, const PlanLayout &l
                      reinterpret_cast<const MultiSeq *>(ws + lay.off_multi),
                      reinterpret_cast<float *>(ws + lay.off_slots),
                      reinterpret_cast<const float *>(ws + lay.off_slot_gamma), d.H, dkdv,
-                     lay.n_sub);
+                     lay.n_sub, (int)s0_copy);
   return hipGetLastError();
 }
 

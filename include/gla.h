@@ -34,9 +34,15 @@
  *    caller's next synchronisation, as with any HIP library.
  *  - Tensor values are not validated: NaN/Inf propagate, and l_t > 0 (a
  *    growing state) is computed as given.
+ *  - Reset gates: l_t = -inf (g_t = 0) is allowed and resets the state,
+ *    S_t = k_t^T v_t, exactly, in every entry point. Any l_t <= -128 ln 2
+ *    (about -88.72, i.e. g_t <= 2^-128, below the smallest normal fp32) is
+ *    treated the same way: g_t = 0 exactly. No decay product that spans a
+ *    reset is formed, so a reset never turns into NaN; the backward returns
+ *    dlog_g = 0 at a reset and no gradient crosses it.
  *  - Supported sizes: d_k, d_v in {64, 128}; chunk_size in {64, 128}. The
- *    forward and the decode steps also take (d_k, d_v) = (96, 192), the head
- *    shape of Laplace 3B ("GLA mixer"); the backward does not. Anything else
+ *    forward, the backward and the decode steps also take (d_k, d_v) =
+ *    (96, 192), the head shape of Laplace 3B ("GLA mixer"). Anything else
  *    returns GLA_ERR_UNSUPPORTED.
  */
 #ifndef GLA_H_
@@ -130,8 +136,8 @@ gla_status gla_fwd_chunked_fixed_decay(const void *q, const void *k, const void 
 
 /*
  * Backward of gla_fwd_chunked (training; Laplace 3B on AWS Trainium2,
- * "Challenge 1": the training step differentiates through the chunk-by-chunk
- * state updates). For upstream gradients dO of o and dS_T of S_T it returns
+ * "Challenge 3: Backward-pass unrolling for a sequential recurrence": the
+ * training step differentiates through the chunk-by-chunk state updates). For upstream gradients dO of o and dS_T of S_T it returns
  * the gradients of L = sum <dO, o> + sum <dS_T, S_T>:
  *
  *   dq, dk [B, T, H, dk] fp32;  dv [B, T, H, dv] fp32

@@ -1,10 +1,13 @@
 """GPU parity of the chunked backward (gla_bwd_chunked) against the fp64
 oracle's backward (the reverse-mode adjoint of the token-by-token recurrence
 of Laplace 3B on AWS Trainium2, "GLA mixer"; training differentiates through
-the chunked state updates, "Challenge 1"). Tolerances as for the forward:
-max relative error (normwise per tensor) 2e-3 for bf16 inputs, 1e-5 for fp32;
-for the log-gate gradient, a difference of two dot products, those bars times
-how much the two cancel (gpu_util.dg_tolerance).
+every sequential state update, "Challenge 3: Backward-pass unrolling for a
+sequential recurrence"). Tolerances as for the forward: max relative error,
+normwise per (sequence, head) pair, 2e-3 for bf16 inputs, 1e-5 for fp32. The
+log-gate gradient, a difference of two dot products, is taken normwise over
+the whole tensor (gpu_util.grad_errors; its per-pair error is printed), at
+the plain bars, and on the 96 x 192 heads at those bars times how much the
+two cancel (capped at gpu_util.DG_CANCEL_CAP).
 """
 import dataclasses
 import os
@@ -33,18 +36,24 @@ def run_bwd(q, k, v, lg, S0, cu, dO, dS_T, dtype, C):
     return [gu.host(x) for x in res]
 
 
-def check_bwd(q, k, v, lg, S0, cu, dO, dS_T, dtype, C=64, heads=None, tight=None):
+def check_bwd(q, k, v, lg, S0, cu, dO, dS_T, dtype, C=64, heads=None, tight=None,
+              scaled_dg=False):
+    """Every gradient against the oracle's backward (gpu_util.grad_errors).
+    The log-gate gradient is held to the plain bar, or with scaled_dg (the
+    96 x 192 cases) to the bar times its cancellation factor, which must stay
+    at or below gpu_util.DG_CANCEL_CAP."""
     got = run_bwd(q, k, v, lg, S0, cu, dO, dS_T, dtype, C)
     if heads is not None:
         got = [g[:, :, heads] if g.ndim >= 3 and g.shape[0] == q.shape[0] and n != "dS0"
                else g[:, heads] for g, n in zip(got, NAMES)]
     ref = orc.recurrent_backward(q, k, v, lg, dO, dS_T, S0, cu, heads=heads)
     tol = gu.TOL_BF16 if dtype == "bf16" else gu.TOL_F32
-    errs = [orc.normwise_error(g, r) for g, r in zip(got, ref)]
+    *errs, dg_pair = gu.grad_errors(got, ref, cu)
     qh, kh = (q, k) if heads is None else (q[:, :, heads], k[:, :, heads])
-    cancel = gu.dg_tolerance(1.0, qh, kh, ref[0], ref[1])  # the gate gradient's bars scale by it
+    cancel = gu.dg_cancellation(qh, kh, ref[0], ref[1]) if scaled_dg else 1.0
     gu.say("   " + "  ".join(f"{n} {e:.2e}" for n, e in zip(NAMES, errs))
-           + f"  (tol {tol:.0e}; dg x{cancel:.1f})")
+           + f"  (dg per pair {dg_pair:.1e}; tol {tol:.0e}"
+           + (f"; dg x{cancel:.1f})" if scaled_dg else ")"))
     for n, e in zip(NAMES, errs):
         scale = cancel if n == "dg" else 1.0
         assert e <= tol * scale, (n, e)
@@ -122,17 +131,41 @@ def test_bwd_forced_segment_split(seg, sub, monkeypatch):
     check_bwd(*_inputs(w, 650, lengths=[500, 3, 257, 0, 64]), "bf16", tight=1e-4)
 
 
-def test_bwd_full_train_2k_sampled_heads():
-    """B=8, T=2048, H=16, d=128 bf16 (the training shape), heads 0 and 11 checked."""
-    gu.say("bwd train_2k full size, heads 0 and 11")
-    w = W["train_2k"]
+def check_bwd_full(w, scaled_dg, tight):
+    """A full-size backward against the C oracle's backward on every
+    (sequence, head) pair."""
+    from oracle import c_oracle
     q, k, v, lg, S0, cu = synth.make_forward_inputs(w)
     dO, dS_T = synth.make_backward_grads(w, w.B, w.T, w.H, w.B, seed=w.seed + 7)
-    check_bwd(q, k, v, lg, S0, cu, dO, dS_T, "bf16", heads=[0, 11], tight=1e-4)
+    got = run_bwd(q, k, v, lg, S0, cu, dO, dS_T, w.dtype, 64)
+    *ref, used = c_oracle.bwd(q, k, v, lg, dO, dS_T, S0, cu, nthreads=16)
+    tol = gu.TOL_BF16 if w.dtype == "bf16" else gu.TOL_F32
+    *errs, dg_pair = gu.grad_errors(got, ref, cu)
+    cancel = gu.dg_cancellation(q, k, ref[0], ref[1]) if scaled_dg else 1.0
+    gu.say("   " + "  ".join(f"{n} {e:.2e}" for n, e in zip(NAMES, errs))
+           + f"  (dg per pair {dg_pair:.1e}; oracle {used} threads"
+           + (f"; dg x{cancel:.1f})" if scaled_dg else ")"))
+    for n, e in zip(NAMES, errs):
+        scale = cancel if n == "dg" else 1.0
+        assert e <= tol * scale and e <= tight * scale, (n, e)
+
+
+def test_bwd_full_train_2k():
+    """B=8, T=2048, H=16, d=128 bf16 (the training shape), with dS_T: every
+    head of every sequence."""
+    gu.say("bwd train_2k full size")
+    check_bwd_full(W["train_2k"], scaled_dg=False, tight=1e-4)
+
+
+def test_bwd_full_laplace_2k():
+    """laplace_2k (8 x 2,048 tokens, 16 heads of 96 x 192, the fixed decays as
+    a gate stream): every head of every sequence."""
+    gu.say("bwd laplace_2k full size")
+    check_bwd_full(W["laplace_2k"], scaled_dg=True, tight=1e-4)
 
 
 # Laplace 3B's 96 x 192 heads (Laplace 3B on AWS Trainium2, "GLA mixer": d_k = 96,
-# d_v = 192; "Challenge 1": training differentiates through the state updates).
+# d_v = 192; "Challenge 3": training differentiates through the state updates).
 # Their dq and dk runs have 192-dim keys and run on the fp32-arithmetic kernel,
 # bf16 inputs included, so bf16 inputs are held to a tighter bar as well.
 
@@ -147,7 +180,7 @@ def test_bwd_laplace_heads(dtype, C, T):
     """96 x 192 heads: one token, and several chunks with a ragged tail; S0 and dS_T."""
     gu.say(f"bwd laplace 96x192 {dtype} C={C} T={T}")
     check_bwd(*_inputs(_laplace(), 700 + T + C, B=2, T=T, H=2), dtype, C=C,
-              tight=1e-4 if dtype == "bf16" else None)
+              tight=1e-4 if dtype == "bf16" else None, scaled_dg=True)
 
 
 def test_bwd_laplace_fixed_decays_varlen():
@@ -156,7 +189,8 @@ def test_bwd_laplace_fixed_decays_varlen():
     gu.say("bwd laplace fixed decays, varlen")
     w = dataclasses.replace(W["laplace_2k"], s0_std=0.02)
     lengths = [0, 1, 65, 200, 0, 130]
-    check_bwd(*_inputs(w, 720, lengths=lengths, final_state=False), "bf16", tight=1e-4)
+    check_bwd(*_inputs(w, 720, lengths=lengths, final_state=False), "bf16", tight=1e-4,
+              scaled_dg=True)
 
 
 @pytest.mark.parametrize("seg,sub", [(64, 1), (128, 3)])
@@ -165,4 +199,4 @@ def test_bwd_laplace_forced_segment_split(seg, sub, monkeypatch):
     monkeypatch.setenv("GLA_SEG_LEN", str(seg))
     monkeypatch.setenv("GLA_STATE_SUB", str(sub))
     w = dataclasses.replace(_laplace(), H=1)
-    check_bwd(*_inputs(w, 730, lengths=[400, 3, 0, 129]), "bf16", tight=1e-4)
+    check_bwd(*_inputs(w, 730, lengths=[400, 3, 0, 129]), "bf16", tight=1e-4, scaled_dg=True)

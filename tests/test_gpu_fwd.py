@@ -32,6 +32,8 @@ def run_gpu(q, k, v, lg, S0, cu, dtype, C=64, out_dtype=None, alias=False):
 
 def check(q, k, v, lg, S0, cu, dtype, C=64, heads=None, tol=None, out_dtype=None, alias=False,
           tight=None):
+    """GPU forward against the C oracle: the largest normwise error over
+    (sequence, head) pairs, for o and for S_T."""
     o, ST = run_gpu(q, k, v, lg, S0, cu, dtype, C, out_dtype, alias)
     if heads is not None:
         sl = lambda a: None if a is None else np.ascontiguousarray(a[:, :, heads] if a.ndim >= 3 else a)
@@ -43,13 +45,30 @@ def check(q, k, v, lg, S0, cu, dtype, C=64, heads=None, tol=None, out_dtype=None
         o_ref, S_ref, _ = c_oracle.fwd(q, k, v, lg, S0, cu, nthreads=16)
     if out_dtype is not None:
         o_ref = synth.round_bf16(o_ref.astype(np.float32))
-    eo, eS = orc.normwise_error(o, o_ref), orc.normwise_error(ST, S_ref)
+    eo, eS = gu.tok_error(o, o_ref, cu), gu.state_error(ST, S_ref)
     tol = tol if tol is not None else (gu.TOL_BF16 if dtype == "bf16" else gu.TOL_F32)
     gu.say(f"   o err {eo:.3e}  S_T err {eS:.3e}  (tol {tol:.1e})")
     assert eo <= tol and eS <= tol, (eo, eS)
     if tight is not None:
         assert eo <= tight and eS <= tight, (eo, eS)
     return eo, eS
+
+
+def check_full_size(name, tight):
+    """A full-size workload at both chunk sizes, in the launch configuration
+    the benchmark times, against one oracle run over every sequence and head."""
+    w = W[name]
+    q, k, v, lg, S0, cu = synth.make_forward_inputs(w)
+    o_ref, S_ref, used = c_oracle.fwd(q, k, v, lg, S0, cu, nthreads=16)
+    gu.say(f"   oracle: {used} threads")
+    for C in (64, 128):
+        o, ST = run_gpu(q, k, v, lg, S0, cu, w.dtype, C)
+        eo, eS = gu.tok_error(o, o_ref, cu), gu.state_error(ST, S_ref)
+        gu.say(f"   C={C}: o err {eo:.3e}  S_T err {eS:.3e} (max over {o_ref.shape[2]} heads "
+               f"x {len(S_ref)} sequences)")
+        assert eo <= gu.TOL_BF16 and eS <= gu.TOL_BF16, (C, eo, eS)
+        assert eo <= tight and eS <= tight, (C, eo, eS)
+        del o, ST
 
 
 W = synth.WORKLOADS
@@ -96,6 +115,21 @@ def test_state_aliasing_S0_S_T():
     w = synth.Workload("t", B=2, T=190, H=2, dk=128, dv=128, dtype="bf16", gate_bias=3.0,
                        s0_std=0.05, chunk=64, seed=14)
     check(*synth.make_forward_inputs(w), "bf16", alias=True)
+
+
+@pytest.mark.parametrize("dtype,C", [("bf16", 64), ("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("varlen", [False, True])
+def test_state_aliasing_with_split(dtype, C, varlen, monkeypatch):
+    """S_T written over S0 while sequences run as several segments: the first
+    segment reads S0 while the last one, another workgroup, writes S_T; the
+    first reads a copy of S0 made by the combine."""
+    gu.say(f"S_T aliases S0 with a split: {dtype} C={C} varlen={varlen}")
+    monkeypatch.setenv("GLA_SEG_LEN", "128" if C == 64 else "256")
+    monkeypatch.setenv("GLA_STATE_SUB", "2")
+    w = synth.Workload("t", B=2, T=600, H=3, dk=64, dv=64, dtype=dtype, gate_bias=3.0,
+                       s0_std=0.05, chunk=C, seed=30)
+    lengths = [600, 0, 100, 513] if varlen else None
+    check(*synth.make_forward_inputs(w, lengths=lengths), dtype, C=C, alias=True)
 
 
 @pytest.mark.parametrize("gate", ["zero", "strong"])
@@ -186,27 +220,24 @@ def test_chunk_size_independence_f32():
 
 
 # ----------------------------------------------------------- full-size workloads
-@pytest.mark.parametrize("C", [64, 128])
-def test_train_2k_full_size_sampled_heads(C):
-    """B=8, H=16, T=2048, d=128, bf16, S0 = 0: all heads run on the GPU; the
-    oracle checks 3 heads of every sequence."""
-    gu.say(f"train_2k full size C={C}")
-    check(*synth.make_forward_inputs(W["train_2k"]), "bf16", C=C, heads=[0, 7, 15], tight=1e-4)
+def test_train_2k_full_size():
+    """B=8, H=16, T=2048, d=128, bf16, S0 = 0: every head of every sequence."""
+    gu.say("train_2k full size")
+    check_full_size("train_2k", tight=1e-4)
 
 
-@pytest.mark.parametrize("C", [64, 128])
-def test_prefill_64k_full_size_sampled_heads(C):
-    """B=1, H=32, T=65536, d=128, bf16, nonzero S0, split into segments; the
-    oracle checks 2 heads over the whole sequence."""
-    gu.say(f"prefill_64k full size C={C}")
-    check(*synth.make_forward_inputs(W["prefill_64k"]), "bf16", C=C, heads=[3, 30], tight=1e-4)
+def test_prefill_64k_full_size():
+    """B=1, H=32, T=65536, d=128, bf16, nonzero S0, split into segments: all 32
+    heads over the whole sequence."""
+    gu.say("prefill_64k full size")
+    check_full_size("prefill_64k", tight=1e-4)
 
 
-@pytest.mark.parametrize("C", [64, 128])
-def test_varlen_64_full_size_sampled_heads(C):
-    """64 packed sequences, lengths uniform in [128, 8192], H=16, d=128, bf16."""
-    gu.say(f"varlen_64 full size C={C}")
-    check(*synth.make_forward_inputs(W["varlen_64"]), "bf16", C=C, heads=[1, 12], tight=1e-4)
+def test_varlen_64_full_size():
+    """64 packed sequences, lengths uniform in [128, 8192], H=16, d=128, bf16:
+    every (sequence, head) pair."""
+    gu.say("varlen_64 full size")
+    check_full_size("varlen_64", tight=1e-4)
 
 
 def test_binding_refuses_misaligned_views():

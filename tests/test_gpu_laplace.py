@@ -88,7 +88,7 @@ def test_fixed_decay_equals_broadcast_gates(dk, dv, dtype, C):
     o_f, S_f = run_fixed(q, k, v, lam, S0, cu, dtype, C)
     o_g, S_g = run_gpu(q, k, v, lg, S0, cu, dtype, C)
     assert np.array_equal(o_f, o_g) and np.array_equal(S_f, S_g)
-    check(q, k, v, lg, S0, cu, dtype, C=C, heads=[0, 5, 15])
+    check(q, k, v, lg, S0, cu, dtype, C=C)
 
 
 @pytest.mark.parametrize("C", [64, 128])
@@ -104,7 +104,7 @@ def test_fixed_decay_varlen_split(C, monkeypatch):
     o_f, S_f = run_fixed(q, k, v, lam, S0, cu, "bf16", C)
     o_g, S_g = run_gpu(q, k, v, lg, S0, cu, "bf16", C)
     assert np.array_equal(o_f, o_g) and np.array_equal(S_f, S_g)
-    check(q, k, v, lg, S0, cu, "bf16", C=C, heads=[0, 9, 15])
+    check(q, k, v, lg, S0, cu, "bf16", C=C)
 
 
 def test_fixed_decay_rejects_bad_shapes():
@@ -118,46 +118,41 @@ def test_fixed_decay_rejects_bad_shapes():
 
 
 # ------------------------------------------------------------ full size
-@pytest.mark.parametrize("C", [64, 128])
-def test_laplace_2k_full_size_sampled_heads(C):
-    """B=8, H=16, T=2048, 96 x 192, bf16, fixed decays: every head runs on the
-    GPU through the fixed-decay entry point; the oracle checks heads 0 (half-
-    life 1 token), 8 and 15 (half-life 2,048 tokens) of every sequence."""
-    gu.say(f"laplace_2k full size C={C}")
+def test_laplace_2k_full_size():
+    """B=8, H=16, T=2048, 96 x 192, bf16, fixed decays through the fixed-decay
+    entry point at both chunk sizes: every (sequence, head) pair, each held to
+    its own normwise bar (the heads' magnitudes differ by more than 10x:
+    half-lives of 1 to 2,048 tokens)."""
+    gu.say("laplace_2k full size")
     w = W["laplace_2k"]
     q, k, v, lg, S0, cu = synth.make_forward_inputs(w)
-    o, ST = run_fixed(q, k, v, synth.fixed_log_decays(w.H), S0, cu, "bf16", C)
-    heads = [0, 8, 15]
-    sl = lambda a: np.ascontiguousarray(a[:, :, heads])
-    o_ref, S_ref, _ = c_oracle.fwd(sl(q), sl(k), sl(v), sl(lg), None, None, nthreads=16)
-    eo = orc.normwise_error(o[:, :, heads], o_ref)
-    eS = orc.normwise_error(ST[:, heads], S_ref)
-    gu.say(f"   o err {eo:.3e}  S_T err {eS:.3e}")
-    assert eo <= 1e-4 and eS <= 1e-4, (eo, eS)
+    o_ref, S_ref, _ = c_oracle.fwd(q, k, v, lg, None, None, nthreads=16)
+    for C in (64, 128):
+        o, ST = run_fixed(q, k, v, synth.fixed_log_decays(w.H), S0, cu, "bf16", C)
+        eo, eS = gu.tok_error(o, o_ref), gu.state_error(ST, S_ref)
+        gu.say(f"   C={C}: o err {eo:.3e}  S_T err {eS:.3e}")
+        assert eo <= 1e-4 and eS <= 1e-4, (C, eo, eS)
 
 
 # ------------------------------------------------------------ decode
-def test_laplace_decode_chain_sampled():
+def test_laplace_decode_chain():
     """256 sequences x 16 heads of 96 x 192 fp32 state, 20 chained steps with
-    the fixed decays; the oracle follows 48 sampled (sequence, head) pairs."""
+    the fixed decays; every (sequence, head) pair at every step."""
     import torch
     import gated_linear_attention_amd as gla
     gu.say("laplace decode chain")
     N, H, dk, dv = 256, 16, 96, 192
     S_np = synth.make_decode_state(N, H, dk, dv, seed=37)
     S = gu.dev(S_np)
-    rng = np.random.default_rng(38)
-    pick_n, pick_h = rng.integers(0, N, 48), rng.integers(0, H, 48)
-    pick = lambda a: np.ascontiguousarray(a[pick_n, pick_h][:, None])
-    S_ref = pick(S_np.astype(np.float64)).copy()
+    S_ref = S_np.astype(np.float64)
     lg = np.ascontiguousarray(np.broadcast_to(synth.fixed_log_decays(H), (N, H)))
     worst = 0.0
     for s in range(20):
         q, k, v, _ = synth.make_decode_step_inputs(N, H, dk, dv, seed=5000 + s)
         o = gla.decode_step(gu.dev(q, torch.bfloat16), gu.dev(k, torch.bfloat16),
                             gu.dev(v, torch.bfloat16), gu.dev(lg), S)
-        o_ref, _ = c_oracle.decode(pick(q), pick(k), pick(v), pick(lg), S_ref, nthreads=8)
-        worst = max(worst, orc.normwise_error(pick(gu.host(o)), o_ref))
-    eS = orc.normwise_error(pick(gu.host(S)), S_ref)
+        o_ref, _ = c_oracle.decode(q, k, v, lg, S_ref, nthreads=16)
+        worst = max(worst, gu.state_error(gu.host(o), o_ref))
+    eS = gu.state_error(gu.host(S), S_ref)
     gu.say(f"   o err {worst:.2e}  S err {eS:.2e}")
     assert worst <= 1e-5 and eS <= 1e-6, (worst, eS)

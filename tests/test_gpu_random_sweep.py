@@ -7,8 +7,9 @@ sizes (including zero tokens), gate strength (from near-reset to near-unit
 gates), initial state or none, fixed per-head decays, and forced segment
 splits with state pieces. The reference is the token-by-token recurrence of
 Laplace 3B on AWS Trainium2 (automationscribe.com/?p=7116), "GLA mixer", in
-fp64; tolerances as everywhere: 2e-3 normwise for bf16 inputs, 1e-5 for fp32,
-for the log-gate gradient times how much its two dot products cancel.
+fp64; tolerances as everywhere: 2e-3 normwise per (sequence, head) pair for
+bf16 inputs, 1e-5 for fp32, and on the 96 x 192 heads the log-gate gradient's
+bar times how much its two dot products cancel (capped).
 Sizes stay small so the oracle answers in well under a second per case.
 """
 import dataclasses
@@ -98,23 +99,23 @@ def test_forward_sweep(seed, monkeypatch):
         assert o.size == 0 and np.array_equal(ST, S_ref), "empty batch"
         return
     tol = gu.TOL_BF16 if c["dtype"] == "bf16" else gu.TOL_F32
-    eo_, eS = orc.normwise_error(o, o_ref), orc.normwise_error(ST, S_ref)
+    eo_, eS = gu.tok_error(o, o_ref, cu), gu.state_error(ST, S_ref)
     gu.say(f"   o err {eo_:.2e}  S_T err {eS:.2e}  (tol {tol:.0e})")
     assert eo_ <= tol and eS <= tol, (eo_, eS)
 
 
 @pytest.mark.parametrize("seed", range(7100, 7112))
 def test_backward_sweep(seed, monkeypatch):
-    _backward_case(seed, monkeypatch, BWD_DIMS)
+    _backward_case(seed, monkeypatch, BWD_DIMS, scaled_dg=False)
 
 
 @pytest.mark.parametrize("seed", range(7150, 7156))
 def test_backward_sweep_laplace(seed, monkeypatch):
     """The same draws on Laplace 3B's 96 x 192 heads."""
-    _backward_case(seed, monkeypatch, [(96, 192)])
+    _backward_case(seed, monkeypatch, [(96, 192)], scaled_dg=True)
 
 
-def _backward_case(seed, monkeypatch, dims):
+def _backward_case(seed, monkeypatch, dims, scaled_dg):
     import torch
     import gated_linear_attention_amd as gla
     c = _draw_fwd(seed, dims, allow_fixed=False)
@@ -140,10 +141,11 @@ def _backward_case(seed, monkeypatch, dims):
             assert g.size == r.size and np.array_equal(g, r), n
         return
     tol = gu.TOL_BF16 if c["dtype"] == "bf16" else gu.TOL_F32
-    errs = [orc.normwise_error(g, r) for g, r in zip(got, ref)]
-    tol_dg = gu.dg_tolerance(tol, q, k, ref[0], ref[1])
+    *errs, dg_pair = gu.grad_errors(got, ref, cu)
+    # the 96 x 192 draws hold dlog_g to the bar times its (capped) cancellation
+    tol_dg = gu.dg_tolerance(tol, q, k, ref[0], ref[1]) if scaled_dg else tol
     gu.say("   " + "  ".join(f"{n} {e:.2e}" for n, e in zip(names, errs))
-           + f"  (tol {tol:.0e}, dlog_g {tol_dg:.1e})")
+           + f"  (dlog_g per pair {dg_pair:.1e}; tol {tol:.0e}, dlog_g {tol_dg:.1e})")
     for n, e in zip(names, errs):
         assert e <= (tol_dg if n == "dlog_g" else tol), (n, e)
 
@@ -206,8 +208,8 @@ def test_decode_sweep(seed):
     if out_bf16:
         ref = synth.round_bf16(ref.astype(np.float32))
     tol = (gu.TOL_BF16_OUT if out_bf16 else 1e-5)
-    e = orc.normwise_error(got, ref)
-    eS = orc.normwise_error(gu.host(S)[idx], S_ref[idx]) if idx else 0.0
+    e = gu.state_error(got, ref)  # per (sequence, head): [N, H, dv]
+    eS = gu.state_error(gu.host(S)[idx], S_ref[idx]) if idx else 0.0
     gu.say(f"   out err {e:.2e}  S err {eS:.2e}")
     assert e <= tol and eS <= 1e-6, (e, eS)
     untouched = sorted(set(range(P)) - set(idx))

@@ -196,3 +196,28 @@ def test_backward_mutants_fail_the_pin(mutation):
     fds = _finite_differences(q, k, v, lg, S0, dO, dS_T, None)
     worst = max(np.abs(g - fd).max() / np.abs(fd).max() for g, fd in zip(bad, fds))
     assert worst > 1e-3, mutation
+
+
+@pytest.mark.parametrize("cu,reset_at,s0,dst", [
+    (None, None, True, True),
+    (None, 4, False, True),
+    (np.array([0, 0, 9, 10, 23], dtype=np.int64), 11, True, False),
+])
+def test_c_backward_matches_numpy(cu, reset_at, s0, dst):
+    """The C oracle's backward (oracle/gla_oracle.c, used at full sizes) is a
+    second, independent transcription of the adjoint walk: it must give the
+    numpy backward's gradients, which the finite-difference and autograd pins
+    above hold to the definition, to fp64 rounding (dense and packed batches,
+    an empty sequence, a reset gate, with and without S0 and dS_T)."""
+    from oracle import c_oracle
+    B = 2 if cu is None else 1
+    T = 23
+    q, k, v, lg, S0, dO, dS_T = _inputs(31, B, T, 3, 8, 6, cu=cu, s0=s0, dst=dst,
+                                        reset_at=reset_at)
+    f32 = lambda a: None if a is None else a.astype(np.float32)
+    q, k, v, lg, S0, dO, dS_T = (f32(x) for x in (q, k, v, lg, S0, dO, dS_T))
+    ref = G.recurrent_backward(q, k, v, lg, dO, dS_T, S0, cu)
+    got = c_oracle.bwd(q, k, v, lg, dO, dS_T, S0, cu, nthreads=3)[:5]
+    for g, r in zip(got, ref):
+        assert g.shape == r.shape
+        assert np.abs(g - r).max() <= 1e-12 * max(1.0, np.abs(r).max())
