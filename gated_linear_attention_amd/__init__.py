@@ -6,6 +6,7 @@ device memory and the current HIP stream.
 
     o, S_T = fwd_chunked(q, k, v, g, S0=None, cu_seqlens=None, chunk_size=64)
     o, S_T = fwd_chunked_fixed_decay(q, k, v, log_lambda, S0=None, cu_seqlens=None)
+    o, S_T = fwd_chunked_noalloc(q, k, v, g, S0=None, cu_seqlens=None)  # no workspace
     dq, dk, dv, dg, dS0 = bwd_chunked(q, k, v, g, dO, S0=None, cu_seqlens=None, dS_T=None)
     o = decode_step(q, k, v, g, S)          # S updated in place
     o = decode_step_slots(q, k, v, g, S_pool, slots)   # S_pool[slots] updated in place
@@ -21,7 +22,8 @@ from __future__ import annotations
 from . import _lib
 from ._lib import GLAError, GLA_BF16, GLA_F32
 
-__all__ = ["fwd_chunked", "fwd_chunked_fixed_decay", "bwd_chunked", "decode_step",
+__all__ = ["fwd_chunked", "fwd_chunked_fixed_decay", "fwd_chunked_noalloc", "bwd_chunked",
+           "decode_step",
            "decode_step_slots", "mixer_epilogue", "decode_mixer", "head_rms_weights",
            "workspace_size",
            "GLAError", "library_path"]
@@ -91,8 +93,17 @@ def fwd_chunked_fixed_decay(q, k, v, log_lambda, S0=None, cu_seqlens=None, chunk
                 o, S_T, workspace, fixed_decay=True)
 
 
+def fwd_chunked_noalloc(q, k, v, g, S0=None, cu_seqlens=None, chunk_size: int = 64,
+                        out_dtype=None, output_final_state: bool = True, o=None, S_T=None):
+    """fwd_chunked through gla_fwd_chunked_noalloc: the library's fixed per-GPU
+    scratch instead of a workspace (nothing is allocated for it; pass o and
+    S_T to allocate nothing at all). Returns (o, S_T)."""
+    return _fwd(q, k, v, g, S0, cu_seqlens, chunk_size, out_dtype, output_final_state, o, S_T,
+                None, fixed_decay=False, noalloc=True)
+
+
 def _fwd(q, k, v, g, S0, cu_seqlens, chunk_size, out_dtype, output_final_state, o, S_T,
-         workspace, fixed_decay):
+         workspace, fixed_decay, noalloc=False):
     torch = _torch()
     lib = _lib.load()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or g.dim() != (1 if fixed_decay else 3):
@@ -121,11 +132,17 @@ def _fwd(q, k, v, g, S0, cu_seqlens, chunk_size, out_dtype, output_final_state, 
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _require(S_T, "S_T", torch.float32, dev)
     in_code = _dtype_code(q.dtype)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    if noalloc:
+        st = lib.gla_fwd_chunked_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0),
+                                         _ptr(cu_seqlens), _ptr(o), _ptr(S_T), B, T, H, dk, dv,
+                                         N, chunk_size, in_code, _dtype_code(out_dtype), stream)
+        _lib.check(st, "gla_fwd_chunked_noalloc")
+        return o, S_T
     ws_bytes = int(lib.gla_fwd_chunked_workspace_size(B, T, H, dk, dv, N, chunk_size,
                                                       int(cu_seqlens is not None), in_code))
     if ws_bytes > 0 and (workspace is None or workspace.numel() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev).cuda_stream
     fn = lib.gla_fwd_chunked_fixed_decay if fixed_decay else lib.gla_fwd_chunked
     st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T),
             B, T, H, dk, dv, N, chunk_size, in_code, _dtype_code(out_dtype),

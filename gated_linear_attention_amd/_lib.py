@@ -42,6 +42,10 @@ def load():
     lib.gla_fwd_chunked_workspace_size.restype = ctypes.c_size_t
     lib.gla_fwd_chunked.argtypes = [vp] * 8 + [i] * 7 + [i, i, vp, ctypes.c_size_t, vp]
     lib.gla_fwd_chunked.restype = i
+    lib.gla_fwd_chunked_noalloc.argtypes = [vp] * 8 + [i] * 7 + [i, i, vp]
+    lib.gla_fwd_chunked_noalloc.restype = i
+    lib.gla_fwd_chunked_noalloc_max_scratch.argtypes = []
+    lib.gla_fwd_chunked_noalloc_max_scratch.restype = ctypes.c_size_t
     lib.gla_fwd_chunked_fixed_decay.argtypes = lib.gla_fwd_chunked.argtypes
     lib.gla_fwd_chunked_fixed_decay.restype = i
     lib.gla_bwd_chunked_workspace_size.argtypes = [i] * 9

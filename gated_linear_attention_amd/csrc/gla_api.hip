@@ -300,13 +300,12 @@ size_t gla_fwd_chunked_workspace_size(int B, int T, int H, int dk, int dv, int n
 
 namespace {
 
-// Argument checks of both forward entry points, then the forward.
-gla_status fwd_checked(const void *q, const void *k, const void *v, const float *g,
-                       const float *S0, const int32_t *cu_seqlens, void *o, float *S_T, int B,
-                       int T, int H, int dk, int dv, int num_seqs, int chunk_size,
-                       gla_dtype in_dtype, gla_dtype out_dtype, void *workspace,
-                       size_t workspace_bytes, void *stream_, bool fixed_decay) {
-  hipStream_t stream = static_cast<hipStream_t>(stream_);
+// Argument checks of the forward entry points (GLA_OK: valid).
+gla_status fwd_validate(const void *q, const void *k, const void *v, const float *g,
+                        const float *S0, const int32_t *cu_seqlens, void *o, float *S_T, int B,
+                        int T, int H, int dk, int dv, int num_seqs, int chunk_size,
+                        gla_dtype in_dtype, gla_dtype out_dtype, const void *workspace,
+                        bool fixed_decay) {
   if (B < 0 || T < 0 || H < 0 || num_seqs < 0) return GLA_ERR_INVALID_ARGUMENT;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
   const bool has_cu = cu_seqlens != nullptr;
@@ -334,9 +333,22 @@ gla_status fwd_checked(const void *q, const void *k, const void *v, const float 
        overlaps(S_T, bytes_S, k, bytes_qk) || overlaps(S_T, bytes_S, v, bytes_v) ||
        overlaps(S_T, bytes_S, g, bytes_g)))
     return GLA_ERR_INVALID_ARGUMENT;
+  return GLA_OK;
+}
 
-  return gla::fwd_core(q, k, v, g, S0, cu_seqlens, o, S_T, B, T, H, dk, dv, N, chunk_size,
-                       in_dtype, out_dtype, workspace, workspace_bytes, stream, fixed_decay);
+// Argument checks, then the forward.
+gla_status fwd_checked(const void *q, const void *k, const void *v, const float *g,
+                       const float *S0, const int32_t *cu_seqlens, void *o, float *S_T, int B,
+                       int T, int H, int dk, int dv, int num_seqs, int chunk_size,
+                       gla_dtype in_dtype, gla_dtype out_dtype, void *workspace,
+                       size_t workspace_bytes, void *stream_, bool fixed_decay) {
+  const gla_status st = fwd_validate(q, k, v, g, S0, cu_seqlens, o, S_T, B, T, H, dk, dv,
+                                     num_seqs, chunk_size, in_dtype, out_dtype, workspace,
+                                     fixed_decay);
+  if (st != GLA_OK || H == 0 || num_seqs == 0) return st;
+  return gla::fwd_core(q, k, v, g, S0, cu_seqlens, o, S_T, B, T, H, dk, dv, num_seqs,
+                       chunk_size, in_dtype, out_dtype, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream_), fixed_decay);
 }
 
 }  // namespace
@@ -350,6 +362,56 @@ gla_status gla_fwd_chunked(const void *q, const void *k, const void *v, const fl
                            size_t workspace_bytes, void *stream) {
   return fwd_checked(q, k, v, g, S0, cu_seqlens, o, S_T, B, T, H, dk, dv, num_seqs, chunk_size,
                      in_dtype, out_dtype, workspace, workspace_bytes, stream, false);
+}
+
+}  // extern "C"
+
+// Scratch of gla_fwd_chunked_noalloc: one fixed array per GPU, held by the
+// loaded library until the process ends. Host code never uses the array's
+// name as an address: each device's address comes from hipGetSymbolAddress
+// once, with that device current, and is kept per device.
+static constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, or nullptr if it cannot be had.
+void *scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);  // racing threads store the same
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gla_fwd_chunked_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
+
+gla_status gla_fwd_chunked_noalloc(const void *q, const void *k, const void *v, const float *g,
+                                   const float *S0, const int32_t *cu_seqlens, void *o,
+                                   float *S_T, int B, int T, int H, int dk, int dv,
+                                   int num_seqs, int chunk_size, gla_dtype in_dtype,
+                                   gla_dtype out_dtype, void *stream) {
+  // the checks of gla_fwd_chunked (no workspace to check), then the scratch
+  gla_status st = fwd_validate(q, k, v, g, S0, cu_seqlens, o, S_T, B, T, H, dk, dv, num_seqs,
+                               chunk_size, in_dtype, out_dtype, nullptr, false);
+  if (st != GLA_OK || H == 0 || num_seqs == 0) return st;
+  const size_t need =
+      fwd_workspace(B, T, H, dk, dv, num_seqs, chunk_size, cu_seqlens != nullptr, in_dtype);
+  if (need > kNoAllocScratchBytes) return GLA_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (need > 0 && !(ws = scratch_ptr())) return GLA_ERR_HIP;
+  return gla::fwd_core(q, k, v, g, S0, cu_seqlens, o, S_T, B, T, H, dk, dv, num_seqs,
+                       chunk_size, in_dtype, out_dtype, ws, need, static_cast<hipStream_t>(stream),
+                       false);
 }
 
 gla_status gla_fwd_chunked_fixed_decay(const void *q, const void *k, const void *v,

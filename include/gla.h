@@ -115,6 +115,31 @@ gla_status gla_fwd_chunked(const void *q, const void *k, const void *v, const fl
                            size_t workspace_bytes, void *stream);
 
 /*
+ * gla_fwd_chunked without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Same arguments, results, checks and errors as
+ * gla_fwd_chunked, minus workspace / workspace_bytes: the scratch the call
+ * needs (gla_fwd_chunked_workspace_size for the same sizes; 0 for dense
+ * batches that fill the GPU) comes from a fixed array of
+ * gla_fwd_chunked_noalloc_max_scratch() bytes (64 MiB) that the library holds
+ * on each GPU it runs on until the process ends. A call that needs more
+ * returns GLA_ERR_WORKSPACE before anything is enqueued (use
+ * gla_fwd_chunked with a workspace then). The call allocates nothing (no
+ * hipMalloc, no library allocation); its first call on a device looks up
+ * that device's address of the array. Every call on one GPU shares the
+ * array: calls that may overlap in time on one GPU (other streams, other
+ * host threads) race and must be ordered by the caller. Nothing in it needs
+ * to start zeroed; its contents after a call are undefined.
+ */
+size_t gla_fwd_chunked_noalloc_max_scratch(void);
+
+gla_status gla_fwd_chunked_noalloc(const void *q, const void *k, const void *v, const float *g,
+                                   const float *S0, const int32_t *cu_seqlens, void *o,
+                                   float *S_T, int B, int T, int H, int dk, int dv,
+                                   int num_seqs, int chunk_size, gla_dtype in_dtype,
+                                   gla_dtype out_dtype, void *stream);
+
+/*
  * The same forward for fixed per-head decays (Laplace 3B on AWS Trainium2,
  * "Decay schedule": each head's decay is set at initialisation on a
  * geometric schedule and not learned), so there is no per-token gate stream:

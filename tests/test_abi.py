@@ -22,6 +22,8 @@ def test_header_declares_the_boundary():
                                   "gla_decode_mixer", "gla_decode_step", "gla_decode_step_slots",
                                   "gla_fwd_chunked",
                                   "gla_fwd_chunked_fixed_decay",
+                                  "gla_fwd_chunked_noalloc",
+                                  "gla_fwd_chunked_noalloc_max_scratch",
                                   "gla_fwd_chunked_workspace_size", "gla_mixer_epilogue",
                                   "gla_status_string"]
 
@@ -286,3 +288,34 @@ def test_binding_refuses_host_tensors():
                  lambda: gla.bwd_chunked(q, q, q, g, q)):
         with pytest.raises(ValueError, match="GPU memory"):
             call()
+
+
+def test_noalloc_forward_checks_before_any_launch():
+    """gla_fwd_chunked_noalloc: the forward's argument checks, then its fixed
+    scratch: a call that needs more than the library holds is refused with
+    GLA_ERR_WORKSPACE before anything is enqueued (host logic only: no call
+    here reaches the GPU)."""
+    lib = _lib.load()
+    cap = lib.gla_fwd_chunked_noalloc_max_scratch()
+    assert cap == 64 << 20
+    G = 1 << 40  # fake, 16-byte-aligned device addresses: never dereferenced
+    P = [FAKE + i * G for i in range(8)]
+
+    def call(B=1, T=64, H=1, dk=64, dv=64, N=1, C=64, ind=_lib.GLA_BF16, cu=None, q=None):
+        p = list(P)
+        if cu is not None:
+            p[5] = cu
+        if q is not None:
+            p[0] = q
+        return lib.gla_fwd_chunked_noalloc(*p, B, T, H, dk, dv, N, C, ind, _lib.GLA_F32, None)
+
+    assert call(B=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(q=FAKE + 4) == _lib.GLA_ERR_INVALID_ARGUMENT       # misaligned
+    assert call(dk=32) == _lib.GLA_ERR_UNSUPPORTED
+    assert call(C=32) == _lib.GLA_ERR_UNSUPPORTED
+    assert call(H=0) == _lib.GLA_OK                                # nothing to do
+    # one 4M-token sequence over 64 heads: its segment states need far more
+    # than the fixed scratch
+    need = lib.gla_fwd_chunked_workspace_size(1, 1 << 22, 64, 128, 128, 1, 64, 0, _lib.GLA_BF16)
+    assert need > cap
+    assert call(T=1 << 22, H=64, dk=128, dv=128) == _lib.GLA_ERR_WORKSPACE
