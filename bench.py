@@ -81,6 +81,39 @@ def time_launches(fn, steps, stream):
     return wall, sum(per) / len(per)
 
 
+def pair_error(x, ref, cu=None, state=False):
+    """Largest normwise error, max |x - ref| / max |ref|, over (sequence, head)
+    pairs: of a token-major tensor [B, T, H, ...] (packed spans cu[n] ..
+    cu[n+1] when cu is given), or with state=True of [N, H, ...]."""
+    import numpy as np
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if state:
+        blocks = [(x[n, h], ref[n, h]) for n in range(x.shape[0]) for h in range(x.shape[1])]
+    else:
+        spans = ([(b, 0, x.shape[1]) for b in range(x.shape[0])] if cu is None else
+                 [(0, int(cu[n]), int(cu[n + 1])) for n in range(len(cu) - 1)])
+        blocks = [(x[b, s_:e, h], ref[b, s_:e, h]) for b, s_, e in spans if e > s_
+                  for h in range(x.shape[2])]
+    worst = 0.0
+    for a, r in blocks:
+        if not np.all(np.isfinite(a)):
+            return float("inf")
+        scale = np.abs(r).max()
+        d = np.abs(a - r).max()
+        worst = max(worst, float(d / scale if scale > 0 else d))
+    return worst
+
+
+def host_cores():
+    """Cores this process may run on, and the machine's count."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count()
+    return {"nproc": avail, "cpu_count": os.cpu_count()}
+
+
 def percentiles_ms(per):
     """median, p10, p90 of per-launch times (ms), as bench.py reports them."""
     n = len(per)
@@ -105,12 +138,12 @@ def warm_up(fn, steps, seconds):
 
 # kernel that runs the headline forward at each chunk size, and the sources
 # whose hash keys its committed counter record
+# (bf16 inputs run every chunk size as 64-token chunks on one kernel)
 FWD_KERNELS = {
     64: ("chunk_bf16_w8_kernel<128,4,float,false,false,false>",
          ["chunk_bf16_w8.hip", "bf16_blocks.h", "gla_common.h"]),
-    128: ("chunk_bf16_kernel<128,128,float,false,false>",
-          ["chunk_bf16.hip", "bf16_blocks.h", "gla_common.h"]),
 }
+FWD_KERNELS[128] = FWD_KERNELS[64]
 
 
 def bench_forward(args):
@@ -185,6 +218,12 @@ def bench_forward(args):
     warm_up(step_bf16_out, 10, 0.2)
     wall3, kern_ms3 = time_launches(step_bf16_out, args.steps, stream)
     alg_bytes16 = alg_bytes - tok_heads * dv * 2
+    # outputs of input set 0 at both chunk sizes, for the parity check
+    outs = {}
+    for c in (C, C2):
+        step_at(c)(0)
+        torch.cuda.synchronize()
+        outs[c] = (o.cpu().numpy(), S_T.cpu().numpy())
     res = {
         "tokens": tokens,
         "ms_per_step": ms_per_step,
@@ -215,7 +254,7 @@ def bench_forward(args):
                  "dense_tile_util": round(dense_tile_flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                  "peak_tflops": BF16_PEAK_TFLOPS},
     }
-    return res, host_set0
+    return res, host_set0, outs
 
 
 def bench_backward(args):
@@ -245,6 +284,9 @@ def bench_backward(args):
     warm_up(step, 3, min(args.warm_seconds, 0.5))
     steps = max(5, args.steps // 5)
     wall, kern_ms = time_launches(step, steps, stream)
+    got = [x.cpu().numpy() for x in gla.bwd_chunked(tq, tk, tv, tlg, tdo, chunk_size=C,
+                                                    need_dS0=False, workspace=ws)[:4]]
+    bench_backward.parity_inputs = (q, k, v, lg, dO, got)
     tok_heads = B * T * H
     # read q, k, v, dO (bf16) and the gates once, write dq, dk, dv (fp32) and dg once
     alg_bytes = tok_heads * (2 * dk + 2 * dk + 2 * dv + 2 * dv + 4 + 4 * dk + 4 * dk + 4 * dv + 4)
@@ -277,16 +319,24 @@ def bench_decode(args):
     D = synth.DECODE
     N, H, dk, dv, steps = D["N"], D["H"], D["dk"], D["dv"], D["steps"]
     dev = torch.device("cuda:0")
-    S = torch.from_numpy(synth.make_decode_state(N, H, dk, dv, seed=D["state_seed"])).to(dev)
+    S_host = synth.make_decode_state(N, H, dk, dv, seed=D["state_seed"])
+    S = torch.from_numpy(S_host).to(dev)
     qs, ks, vs, gs = [], [], [], []
+    host_steps = []  # the first steps' inputs, for the parity check and the oracle's time
     for s in range(steps):
         q, k, v, lg = synth.make_decode_step_inputs(N, H, dk, dv, seed=D["step_seed_base"] + s)
+        if s < 3:
+            host_steps.append((q, k, v, lg))
         qs.append(torch.from_numpy(q).to(torch.bfloat16).to(dev))
         ks.append(torch.from_numpy(k).to(torch.bfloat16).to(dev))
         vs.append(torch.from_numpy(v).to(torch.bfloat16).to(dev))
         gs.append(torch.from_numpy(lg).to(dev))
     o = torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # the first step from the initial state, kept for the parity check (every pair)
+    gla.decode_step(qs[0], ks[0], vs[0], gs[0], S, o=o)
+    torch.cuda.synchronize()
+    bench_decode.parity_inputs = (S_host, host_steps, o.cpu().numpy(), S.cpu().numpy())
 
     def step(i):
         gla.decode_step(qs[i % steps], ks[i % steps], vs[i % steps], gs[i % steps], S, o=o)
@@ -318,7 +368,7 @@ def bench_decode(args):
         "unit": "GB/s",
         "ms_per_step": 1e3 * wall / steps,
         "kernel_ms": kern_ms,
-        "tokens_per_s": N / (1e-3 * wall / steps),
+        "tokens_per_s": round(N / (wall / steps), 1),
         "config": {"workload": "decode 1280 sequences x 16 heads", "N": N, "H": H, "dk": dk,
                    "dv": dv, "chained_steps": steps, "in_dtype": "bf16", "state": "f32 in place"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
@@ -388,6 +438,13 @@ def bench_prefill(args):
     alg = tok_heads * (2 * dk + 2 * dk + 2 * dv + 4 + 4 * dv) + 2 * B * H * dk * dv * 4
     out = {"config": {"workload": "prefill_64k", "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
                       "S0": "N(0, 0.02^2)"}, "algorithmic_bytes": alg}
+    # a head sample (one per host core, spread over the heads) whose inputs and
+    # outputs the oracle checks and whose oracle run is timed
+    n_s = max(1, min(H, host_cores()["nproc"]))
+    hs = list(range(0, H, H // n_s))[:n_s]
+    hsel = lambda x: x[:, :, hs].float().cpu().numpy()
+    sample = {"heads": hs, "inputs": (hsel(q), hsel(k), hsel(v), lg[:, :, hs].cpu().numpy(),
+                                      S0[:, hs].cpu().numpy(), None), "outputs": {}}
     for C in (64, 128):
         ws = torch.empty(max(1, gla.workspace_size(B, T, H, dk, dv, B, C)), dtype=torch.uint8,
                          device=dev)
@@ -405,6 +462,8 @@ def bench_prefill(args):
         out[f"c{C}"] = {"call_ms": round(call_ms, 4), "tokens_per_s": round(B * T / (wall / steps), 1),
                         "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                         "segments_per_sequence": segs, **percentiles_ms(time_launches.last)}
+        sample["outputs"][C] = (o[:, :, hs].cpu().numpy(), S_T[:, hs].cpu().numpy())
+    bench_prefill.sample = sample
     return out
 
 
@@ -444,6 +503,11 @@ def bench_varlen(args):
     qd, kd, vd, lgd = (x[:, :Bd * 2048].reshape((Bd, 2048) + tuple(x.shape[2:])) for x in (q, k, v, lg))
     od = torch.empty((Bd, 2048, H, dv), dtype=torch.float32, device=dev)
     STd = torch.empty((Bd, H, dk, dv), device=dev)
+    # a head sample over every sequence for the oracle (check and timing)
+    hs = [0, H // 3, 2 * H // 3, H - 1]
+    hsel = lambda x: x[:, :, hs].float().cpu().numpy()
+    sample = {"heads": hs, "inputs": (hsel(q), hsel(k), hsel(v), lg[:, :, hs].cpu().numpy(),
+                                      S0[:, hs].cpu().numpy(), cu_h), "outputs": {}}
     for C in (64, 128):
         ws = torch.empty(max(1, gla.workspace_size(1, total, H, dk, dv, N, C, True)),
                          dtype=torch.uint8, device=dev)
@@ -472,6 +536,9 @@ def bench_varlen(args):
                         "efficiency_vs_dense": round(tps / tps_d, 4),
                         "critical_path_chunks": crit,
                         "balanced_chunks_per_cu": round(balanced, 1), **pct}
+        # o holds this chunk size's result (the dense comparison writes od)
+        sample["outputs"][C] = (o[:, :, hs].cpu().numpy(), S_T[:, hs].cpu().numpy())
+    bench_varlen.sample = sample
     return out
 
 
@@ -510,10 +577,13 @@ def bench_laplace(args):
                 "gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
     fwd = {}
+    lap_out = {}
     for C in (64, 128):
         fwd[f"fixed_decay_c{C}"] = timed(
             lambda i, C=C: gla.fwd_chunked_fixed_decay(tq, tk, tv, lam, chunk_size=C, o=o,
                                                        S_T=S_T), alg_fixed)
+        lap_out[C] = (o.cpu().numpy(), S_T.cpu().numpy())
+    bench_laplace.parity_inputs = ((q, k, v, lg), lap_out)
     fwd["token_gates_c64"] = timed(
         lambda i: gla.fwd_chunked(tq, tk, tv, tlg, chunk_size=64, o=o, S_T=S_T), alg_gates)
 
@@ -570,8 +640,8 @@ def bench_laplace(args):
                    "H": H, "dk": dk, "dv": dv, "in_dtype": "bf16", "out_dtype": "f32",
                    "decays": "fixed geometric schedule, half-lives 1 .. 2048 tokens"},
         "forward": fwd,
-        "forward_kernel": {"c64": "chunk_bf16_w8_kernel<96,6,float,false,false,false>",
-                           "c128": "chunk_bf16_kernel<128,96,float,false,false>"},
+        "forward_kernel": "chunk_bf16_w8_kernel<96,6,float,false,false,false> "
+                          "(both chunk sizes run as 64-token chunks)",
         "forward_algorithmic_bytes": alg_fixed,
         "backward": bwd,
         "epilogue": epi,
@@ -730,6 +800,103 @@ def cpu_baseline(host_set, target_s=10.0, min_wall=3.0):
                                f"{n1} runs, {t_one:.2f} s"}
 
 
+def _timed(fn):
+    t0 = time.perf_counter()
+    r = fn()
+    return r, time.perf_counter() - t0
+
+
+def oracle_legs(fwd_outs, host_set, chunk):
+    """The fp64 C oracle against the GPU results of the benchmarked configs
+    (the largest normwise error over (sequence, head) pairs), and its own time
+    on the same inputs as a CPU baseline per config. Every pair is checked for
+    train_2k (both chunk sizes), the train_2k backward, laplace_2k and the
+    first decode step (all 20,480 pairs); prefill_64k and varlen_64 on a head
+    sample over every token (their inputs are drawn on the device)."""
+    import numpy as np
+
+    from oracle import c_oracle
+
+    parity, cpu = {}, {}
+    cores = host_cores()
+    q, k, v, lg = host_set
+    B, T, H, _ = q.shape
+    (o_ref, S_ref, used), el = _timed(lambda: c_oracle.fwd(q, k, v, lg, None, None, nthreads=0))
+    for c, (o, ST) in fwd_outs.items():
+        parity[f"train_2k_c{c}"] = {"o": pair_error(o, o_ref), "S_T": pair_error(ST, S_ref, state=True),
+                                    "pairs": B * H}
+    cpu["train_2k_all_heads"] = {"value": round(B * T / el, 1), "unit": "tokens/s",
+                                 "threads": used, "seconds": round(el, 2)}
+    del o_ref, S_ref
+    bi = getattr(bench_backward, "parity_inputs", None)
+    if bi is not None:
+        bq, bk, bv, blg, bdo, got = bi
+        (ref, el) = _timed(lambda: c_oracle.bwd(bq, bk, bv, blg, bdo, None, None, None,
+                                                 nthreads=0))
+        parity[f"train_2k_backward_c{chunk}"] = {
+            "dq": pair_error(got[0], ref[0]), "dk": pair_error(got[1], ref[1]),
+            "dv": pair_error(got[2], ref[2]),
+            "dlog_g": float(np.abs(got[3] - ref[3]).max() / np.abs(ref[3]).max()),
+            "pairs": B * H, "note": "dlog_g normwise over the whole tensor"}
+        cpu["train_2k_backward_all_heads"] = {"value": round(B * T / el, 1), "unit": "tokens/s",
+                                              "threads": ref[5], "seconds": round(el, 2)}
+        del ref, bi
+        bench_backward.parity_inputs = None
+    di = getattr(bench_decode, "parity_inputs", None)
+    if di is not None:
+        S0h, steps_in, o1, S1 = di
+        S_ref = S0h.astype(np.float64)
+        (res, el) = _timed(lambda: c_oracle.decode(*steps_in[0], S_ref, nthreads=0))
+        N, Hd = S0h.shape[:2]
+        parity["decode_step1"] = {"o": pair_error(o1, res[0], state=True),
+                                  "S": pair_error(S1, S_ref, state=True), "pairs": N * Hd}
+        times = [el]
+        for st in steps_in[1:]:
+            times.append(_timed(lambda st=st: c_oracle.decode(*st, S_ref, nthreads=0))[1])
+        per = sum(times) / len(times)
+        state_bytes = 2 * S0h.nbytes
+        cpu["decode_1280x16"] = {"value": round(N / per, 1), "unit": "tokens/s",
+                                 "state_gbs": round(state_bytes / per / 1e9, 2),
+                                 "ms_per_step": round(1e3 * per, 1), "threads": res[1],
+                                 "sample": f"all {N * Hd} (sequence, head) pairs, {len(times)} "
+                                           f"chained steps (the benchmark chains 100)"}
+        del S_ref, di
+        bench_decode.parity_inputs = None
+    for name, fn in (("prefill_64k", bench_prefill), ("varlen_64", bench_varlen)):
+        smp = getattr(fn, "sample", None)
+        if smp is None:
+            continue
+        sq, sk, sv, slg, sS0, cu = smp["inputs"]
+        (res, el) = _timed(lambda: c_oracle.fwd(sq, sk, sv, slg, sS0, cu, nthreads=0))
+        for c, (o, ST) in smp["outputs"].items():
+            parity[f"{name}_c{c}"] = {"o": pair_error(o, res[0], cu),
+                                      "S_T": pair_error(ST, res[1], state=True),
+                                      "heads": smp["heads"]}
+        ntok = sq.shape[1]
+        H_full = {"prefill_64k": 32, "varlen_64": 16}[name]
+        cpu[name] = {"value": round(ntok * len(smp["heads"]) / el / H_full, 1),
+                     "unit": "tokens/s", "threads": res[2], "seconds": round(el, 2),
+                     "sample": f"{len(smp['heads'])} of {H_full} heads x every token "
+                               f"({ntok}); value scaled to tokens/s of a {H_full}-head layer"}
+        del res, smp
+        fn.sample = None
+    li = getattr(bench_laplace, "parity_inputs", None)
+    if li is not None:
+        (lq, lk, lv, llg), outs = li
+        (res, el) = _timed(lambda: c_oracle.fwd(lq, lk, lv, llg, None, None, nthreads=0))
+        for c, (o, ST) in outs.items():
+            parity[f"laplace_2k_c{c}"] = {"o": pair_error(o, res[0]),
+                                          "S_T": pair_error(ST, res[1], state=True),
+                                          "pairs": lq.shape[0] * lq.shape[2]}
+        cpu["laplace_2k_all_heads"] = {"value": round(lq.shape[0] * lq.shape[1] / el, 1),
+                                       "unit": "tokens/s", "threads": res[2],
+                                       "seconds": round(el, 2)}
+        del res, li
+        bench_laplace.parity_inputs = None
+    cpu.update(cores)
+    return parity, cpu
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -786,7 +953,7 @@ def main():
         return
 
     log("forward: building inputs")
-    fwd, host_set = bench_forward(args)
+    fwd, host_set, fwd_outs = bench_forward(args)
     log(f"forward: {fwd['value']:.4g} tokens/s, kernel {fwd['kernel_ms']:.4f} ms")
     bwd = None
     if not args.no_backward:
@@ -819,10 +986,16 @@ def main():
         layers = bench_decode_layers(args)
         log(f"decode layers: {layers}")
     cpu = None
+    log("parity: the fp64 oracle on the benchmarked configs")
+    parity, per_config = oracle_legs(fwd_outs, host_set, args.chunk)
+    log(f"parity: {parity}")
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the fp64 oracle")
         cpu = cpu_baseline(host_set)
         cpu["gpu_over_cpu"] = round(fwd["value"] / cpu["value"], 1)
+        cpu.update({"nproc": per_config["nproc"], "cpu_count": per_config["cpu_count"],
+                    "per_config": {k_: v_ for k_, v_ in per_config.items()
+                                   if k_ not in ("nproc", "cpu_count")}})
         log(f"cpu baseline: {cpu['value']} tokens/s on {cpu['cores']} threads")
 
     line = {
@@ -853,6 +1026,7 @@ def main():
         "laplace": lap,
         "decode_layers": layers,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(line), flush=True)
 

@@ -7,7 +7,7 @@
 namespace gla {
 
 
-constexpr int kBfSlice = 64;  // state columns per workgroup (4 wavefronts x 16)
+constexpr int kBfSlice = 64;  // state columns per workgroup slice (four column groups of 16)
 
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;

@@ -1,28 +1,51 @@
-// Chunked GLA forward, bf16 inputs, 64-token chunks, eight wavefronts per
-// workgroup (two per SIMD).
+// Chunked GLA forward for bf16 inputs on the CDNA4 matrix cores: 64-token
+// chunks, eight wavefronts per workgroup (two per SIMD).
 //
-// The algebra is the chunked form of Laplace 3B on AWS Trainium2
-// (automationscribe.com/?p=7116), "Challenge 1", as in chunk_bf16.hip:
-//   O = diag(e^{b}) Q S + ((Q K^T) .* D) V,   S <- e^{b_last} S + K^T (e^{b_last - b} . V).
+// Laplace 3B on AWS Trainium2 (automationscribe.com/?p=7116), "Challenge 1":
+// within each chunk the output is decay-masked linear attention over the
+// chunk plus the query's read of the running state; chunks are independent
+// except for the state, which advances by the decay compounded over the
+// chunk. With b_i the in-chunk inclusive cumulative log-gate:
+//
+//   O = diag(e^{b}) Q S + ((Q K^T) .* D) V,   D_ij = e^{b_i - b_j} (j <= i)
+//   S <- e^{b_last} S + K^T (e^{b_last - b} . V)
+//
+// D is evaluated per element as the exponential of a difference (never as a
+// product e^{b_i} e^{-b_j}, which overflows for strong decay). The page's
+// chunks are 128 tokens, matched to Trainium2's 128 SBUF partitions; here the
+// tile is 64 tokens (a 128-token chunk is two 64-token chunks in exact
+// arithmetic), which lets the Q, K and V tiles double-buffer in LDS.
 //
 // Decomposition: one 512-thread workgroup per (work item, head, 64-column
-// slice of the state), like the four-wavefront kernel, but each wavefront
-// owns half as much: wavefront (c, r) (c = w & 3, r = w >> 2) holds state rows
-// [r d_k/2, (r+1) d_k/2) of columns 16c .. 16c+15 in its accumulators. Per
-// chunk it
+// slice of the state); a work item is a run of one sequence's tokens, walked
+// chunk by chunk with the fp32 state slice in the matrix-core accumulators for
+// the whole run. Wavefront (c, r) (c = w & 3, r = w >> 2) holds state rows
+// [r d_k/2, (r+1) d_k/2) of columns 16c .. 16c+15. Per chunk it
 //   * computes its share of the lower-triangular score tiles into P (LDS);
 //   * computes the state read over its half of d_k for all 64 rows,
 //     O^T_part = S_half^T Q_half^T, and hands the rows it does not own to its
 //     partner (c, 1-r) through LDS;
 //   * after the one mid-chunk barrier, adds the partner's half for its own 32
 //     rows, scales them by e^{b_i}, adds V^T P^T for those rows, and stores
-//     them one chunk later (16-byte row pieces);
+//     them at the chunk's end (16-byte row pieces);
 //   * advances its half of the state: S_half <- gamma S_half + K_half^T (kappa . V).
-// Each wavefront's dependency chain is half as long as with four wavefronts,
-// and two wavefronts per SIMD let one's MFMA, VALU and LDS work overlap the
-// other's waits. Data movement (HBM -> LDS buffer loads into swizzled,
-// double-buffered tiles; LDS transpose reads; hi/lo bf16 splits of P, S and
-// kappa . V) is the same as in chunk_bf16.hip.
+// Each wavefront's dependency chain is short, and two wavefronts per SIMD let
+// one's MFMA, VALU and LDS work overlap the other's waits.
+//
+// Data movement: Q, K (64 x d_k) and the V slice are copied HBM -> LDS with
+// buffer loads that write LDS directly (16 bytes per lane, no register
+// staging); rows past the end of the run fall outside the buffer descriptor's
+// range and arrive as zeros. Tiles are row-major with the 16-byte column
+// chunks of row r XOR-swizzled by r, so that operand reads of 16 consecutive
+// rows hit distinct LDS banks, and double-buffered: chunk n+1 streams in while
+// chunk n computes. Operands that need the chunk dimension as the reduction
+// index (K^T for the state update, V for P V) are read with the LDS transpose
+// read (ds_read_b64_tr_b16), so no transposed copies are kept.
+//
+// Accuracy: bf16 inputs are exact operands; every value rounded on its way
+// into an MFMA (P, S, kappa . V) is split into hi = bf16(x) and lo =
+// bf16(x - hi) and both parts are multiplied, which keeps about 16 significant
+// bits with fp32 accumulation.
 //
 // The same kernel serves the 96 x 192 heads of Laplace 3B ("GLA mixer") with
 // six column groups: twelve wavefronts (three per SIMD) over a 96-column slice,
@@ -61,7 +84,7 @@ struct W8Lds {
 
 // HBM -> LDS copy of one chunk into stage st, done by the wavefronts of row
 // half 0 (the others, whose chain per chunk is longer, only store outputs).
-// Tiles are swizzled as in ChunkLoader (chunk_bf16.hip). The row pointers
+// Tiles are swizzled as described at the top of this file. The row pointers
 // advance by one chunk per next() call, so a chunk costs a few scalar adds and
 // one clamp of the descriptor ranges. The log-gates go to a three-slot ring
 // two chunks ahead of their use.
@@ -852,11 +875,12 @@ static hipError_t launch_w8_d(const uint16_t *q, const uint16_t *k, const uint16
                                        slots, slot_gamma, stream);
 }
 
-hipError_t launch_chunk_bf16_c64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                 const float *g, const float *S0, float *S_T, void *o,
-                                 bool out_bf16, const FwdDims &d, const WorkItem *items,
-                                 const int *n_items, int grid_items, float *slots,
-                                 float *slot_gamma, bool state_pass, hipStream_t stream) {
+hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const float *g, const float *S0, float *S_T, void *o, bool out_bf16,
+                             const FwdDims &d, const WorkItem *items, const int *n_items,
+                             int grid_items, float *slots, float *slot_gamma, bool state_pass,
+                             hipStream_t stream) {
+  if (d.C != kW8C) return hipErrorInvalidValue;  // the planner runs bf16 inputs at chunk 64
   if (d.dk == 96)  // 96 x 192 heads: two slices of six column groups
     return launch_w8_d<96, 6>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
                               slots, slot_gamma, state_pass, stream);

@@ -44,6 +44,15 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int round_up(long x, int m) { return (int)(((x + m - 1) / m) * m); }
 
+// The chunk the kernels run at. The bf16 matrix-core kernel tiles 64 tokens:
+// a 128-token chunk of the chunked form equals two 64-token chunks in exact
+// arithmetic (the state advance composes), and at 64 tokens the Q, K, V tiles
+// double-buffer in LDS while at 128 they do not; so chunk_size 128 runs as
+// 64-token chunks there. The fp32 kernel runs either size as asked.
+int kernel_chunk(gla_dtype in_dtype, bool f32_kernel, int chunk_size) {
+  return in_dtype == GLA_BF16 && !f32_kernel ? 64 : chunk_size;
+}
+
 // State columns one workgroup of the forward owns (the column "slice"): 96 for
 // the twelve-wavefront bf16 kernel (d_k = 96, chunk 64), else 64 (bf16) or 32.
 int slice_width(gla_dtype in_dtype, int dk, int C) {
@@ -214,6 +223,7 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
   d.dk = dk;
   d.dv = dv;
   d.N = N;
+  chunk_size = kernel_chunk(in_dtype, f32_kernel, chunk_size);
   d.C = chunk_size;
   d.gts = fixed_decay ? 0 : H;
   d.rev = rev;
@@ -268,6 +278,7 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
 size_t fwd_workspace(int B, int T, int H, int dk, int dv, int N, int chunk_size, bool has_cu,
                      gla_dtype in_dtype, bool f32_kernel) {
   PlanLayout lay;
+  chunk_size = kernel_chunk(in_dtype, f32_kernel, chunk_size);
   if (!make_plan(B, T, H, dk, dv, N, chunk_size, has_cu, f32_kernel ? GLA_F32 : in_dtype, lay))
     return 0;
   return lay.total_bytes;
@@ -439,7 +450,8 @@ bool bwd_f32_kernel(int dk, int dv) { return dk == 96 && dv == 192; }
 // The dv run of those heads is a 96 x 192 forward: on the twelve-wavefront
 // bf16 kernel for bf16 inputs at chunk 64, otherwise with the dq and dk runs.
 bool bwd_dv_f32_kernel(int dk, int dv, int C, gla_dtype in_dtype) {
-  return bwd_f32_kernel(dk, dv) && !(in_dtype == GLA_BF16 && C == 64);
+  (void)C;  // the bf16 kernels run every chunk size as 64-token chunks
+  return bwd_f32_kernel(dk, dv) && in_dtype != GLA_BF16;
 }
 
 // Workspace layout of the backward (all offsets 256-byte aligned).
@@ -465,7 +477,7 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int N, int C, bool has
   L.stt = take(mat);
   L.a0 = take(mat);
   const bool f32k = bwd_f32_kernel(dk, dv);
-  L.fused_dots = in_dtype == GLA_BF16 && C == 64 && !f32k;
+  L.fused_dots = in_dtype == GLA_BF16 && !f32k;  // the 64-token kernel's row dots
   const size_t parts = L.fused_dots ? (size_t)(dk / 16) * ntok * 4 : 0;
   L.dqp = take(parts);
   L.dkp = take(parts);

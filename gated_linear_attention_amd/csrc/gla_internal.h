@@ -108,14 +108,8 @@ hipError_t launch_chunk_f32(const void *q, const void *k, const void *v, const f
                             int grid_items, float *slots, float *slot_gamma, bool state_pass,
                             hipStream_t stream);
 
-// bf16 inputs, 64-token chunks: eight-wavefront kernel (chunk_bf16_w8.hip).
-hipError_t launch_chunk_bf16_c64(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                 const float *g, const float *S0, float *S_T, void *o,
-                                 bool out_bf16, const FwdDims &d, const WorkItem *items,
-                                 const int *n_items, int grid_items, float *slots,
-                                 float *slot_gamma, bool state_pass, hipStream_t stream);
-
-// bf16 inputs on the matrix cores, fp32 accumulation and state.
+// bf16 inputs on the matrix cores, fp32 accumulation and state: the eight-
+// (twelve-) wavefront kernel of chunk_bf16_w8.hip, 64-token chunks (d.C = 64).
 hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                              const float *g, const float *S0, float *S_T, void *o, bool out_bf16,
                              const FwdDims &d, const WorkItem *items, const int *n_items,
