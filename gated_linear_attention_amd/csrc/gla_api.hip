@@ -32,159 +32,6 @@ int cu_count() {
   return n;
 }
 
-bool supported_head_dim(int d) { return d == 64 || d == 128; }
-
-// (d_k, d_v) pairs of the forward and decode: any of {64, 128} x {64, 128},
-// and Laplace 3B's 96 x 192 heads.
-bool fwd_dims(int dk, int dv) {
-  return (supported_head_dim(dk) && supported_head_dim(dv)) || (dk == 96 && dv == 192);
-}
-
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-int round_up(long x, int m) { return (int)(((x + m - 1) / m) * m); }
-
-// The chunk the kernels run at. The bf16 matrix-core kernel tiles 64 tokens:
-// a 128-token chunk of the chunked form equals two 64-token chunks in exact
-// arithmetic (the state advance composes), and at 64 tokens the Q, K, V tiles
-// double-buffer in LDS while at 128 they do not; so chunk_size 128 runs as
-// 64-token chunks there. The fp32 kernel runs either size as asked.
-int kernel_chunk(gla_dtype in_dtype, bool f32_kernel, int chunk_size) {
-  return in_dtype == GLA_BF16 && !f32_kernel ? 64 : chunk_size;
-}
-
-// State columns one workgroup of the forward owns (the column "slice"): 96 for
-// the twelve-wavefront bf16 kernel (d_k = 96, chunk 64), else 64 (bf16) or 32.
-int slice_width(gla_dtype in_dtype, int dk, int C) {
-  if (in_dtype != GLA_BF16) return 32;
-  return dk == 96 && C == 64 ? 96 : 64;
-}
-
-// Tokens per work item. A dense batch with enough (sequence, head, slice)
-// work units to cover every CU runs each sequence whole; otherwise sequences
-// are split into about ceil(CUs / units) segments. A packed batch caps
-// segments at its per-CU share of the work, so no single long sequence sets
-// the critical path. GLA_SEG_LEN overrides the choice (tuning only; the
-// result does not depend on it beyond rounding).
-int choose_seg_len(int B, int T, int H, int dk, int dv, int N, int C, bool has_cu,
-                   gla_dtype in_dtype) {
-  long L;
-  const char *env = std::getenv("GLA_SEG_LEN");
-  const int n_slices = dv / slice_width(in_dtype, dk, C);
-  if (env && std::atoi(env) > 0) {
-    L = std::atoi(env);
-  } else if (!has_cu) {
-    const long units = (long)B * H * n_slices;
-    // workgroups to aim for: one per CU on the bf16 kernels, four on the
-    // fp32 one (two fit per CU, and it is bound by latency, not bandwidth),
-    // except with 192-dim keys (the 96 x 192 backward's dq and dk runs), whose
-    // chunks carry enough work that a split costs more than it hides
-    // (laplace_2k backward: 3.82 ms whole against 4.04 ms in three segments)
-    const long target = (long)cu_count() * (in_dtype == GLA_BF16 || dk == 192 ? 1 : 4);
-    if (units >= target) {
-      L = T;
-    } else {
-      const long nseg = (target + units - 1) / units;
-      L = (T + nseg - 1) / nseg;
-    }
-    if (in_dtype == GLA_BF16) {
-      // A split adds three launches (plan, state pass, combine) and a combine
-      // chain that is sequential in the segments of a sequence, so on the
-      // matrix-core kernels short segments do not pay: a sequence of at most
-      // 8 chunks (chunk 64) or 2 (chunk 128) runs whole, and at chunk 64
-      // segments keep about sqrt(chunks) / 1.7 chunks (measured on MI355X for
-      // 256 - 4,096 tokens and 1 - 64 work units; the fp32 kernel, several
-      // times slower per chunk, always gains from the split).
-      const long chunks = ((long)T + C - 1) / C;
-      if (chunks <= (C == 64 ? 8 : 2)) {
-        L = T;
-      } else if (C == 64) {
-        const long seg_chunks = std::max(1L, std::lround(std::sqrt((double)chunks) / 1.7));
-        L = std::max(L, seg_chunks * C);
-      }
-    }
-  } else {
-    // the dense rule's per-CU target, 192-dim keys included
-    const long work = (long)T * H * n_slices;
-    L = work / ((long)cu_count() * (in_dtype == GLA_BF16 || dk == 192 ? 1 : 4));
-    if (in_dtype == GLA_BF16 && C == 64 && N > 0) {
-      // the segment floor of dense batches, from the mean sequence length
-      // (the lengths themselves stay on the device)
-      const double mean_chunks = (double)T / N / C;
-      const long seg_chunks = std::max(1L, std::lround(std::sqrt(mean_chunks) / 1.7));
-      L = std::max(L, seg_chunks * C);
-    }
-  }
-  L = round_up(L < C ? C : L, C);
-  const long cap = round_up(T < C ? C : T, C);
-  if (L > cap) L = cap;
-  if (L > 65536) L = 65536;  // bounds the scheduler's sort buckets
-  return (int)L;
-}
-
-// Whether the forward needs the device-side planner, and its workspace layout.
-bool make_plan(int B, int T, int H, int dk, int dv, int N, int C, bool has_cu,
-               gla_dtype in_dtype, PlanLayout &lay) {
-  std::memset(&lay, 0, sizeof(lay));
-  const int L = choose_seg_len(B, T, H, dk, dv, N, C, has_cu, in_dtype);
-  lay.seg_len = L;
-  long seg_items;  // (a bound on) the non-last segments, each one state-pass run
-  if (!has_cu) {
-    const int nseg = T > 0 ? (T + L - 1) / L : 1;
-    if (nseg <= 1) return false;
-    seg_items = (long)B * (nseg - 1);
-  } else {
-    seg_items = T / L;  // segments that can be full length
-  }
-  // The state pass runs each non-last segment in n_sub pieces so that it has
-  // at least about four workgroups per CU (pieces of at least 8 chunks); the
-  // combine then chains the pieces. GLA_STATE_SUB overrides n_sub (tuning and
-  // tests; results do not depend on it beyond rounding).
-  int want = 1;
-  if (seg_items > 0) {
-    const long units = seg_items * H * (dv / slice_width(in_dtype, dk, C));
-    want = (int)((4L * cu_count() + units - 1) / units);
-    want = std::min(want, std::max(1, L / (8 * C)));
-  }
-  const char *env = std::getenv("GLA_STATE_SUB");
-  if (env && std::atoi(env) > 0) want = std::atoi(env);
-  want = std::max(1, std::min(want, L / C));
-  lay.sub_len = round_up((L + want - 1) / want, C);
-  lay.n_sub = (L + lay.sub_len - 1) / lay.sub_len;
-  if (!has_cu) {
-    lay.max_items = (int)(seg_items + B);
-    lay.max_state_items = (int)(seg_items * lay.n_sub);
-    lay.max_multi = B;
-    lay.max_slots = (int)(seg_items * lay.n_sub + B);
-  } else {
-    lay.max_items = (int)(N + seg_items);
-    lay.max_state_items = (int)(seg_items * lay.n_sub);
-    lay.max_multi = (int)seg_items;
-    lay.max_slots = (int)(seg_items * (lay.n_sub + 1));
-  }
-  size_t off = 0;
-  lay.off_header = off;
-  off = align256(off + sizeof(PlanHeader));
-  lay.off_items = off;
-  off = align256(off + sizeof(WorkItem) * (size_t)lay.max_items);
-  lay.off_state_items = off;
-  off = align256(off + sizeof(WorkItem) * (size_t)lay.max_state_items);
-  lay.off_multi = off;
-  off = align256(off + sizeof(MultiSeq) * (size_t)lay.max_multi);
-  lay.off_slots = off;
-  off = align256(off + sizeof(float) * (size_t)lay.max_slots * H * dk * dv);
-  lay.off_slot_gamma = off;
-  off = align256(off + sizeof(float) * (size_t)lay.max_slots * H);
-  lay.total_bytes = off;
-  return true;
-}
-
-bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
-  if (!a || !b || na == 0 || nb == 0) return false;
-  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-  return x < y + nb && y < x + na;
-}
-
 size_t dtype_size(gla_dtype t) { return t == GLA_BF16 ? 2 : 4; }
 
 // Tensors that the kernels read or write in 8- or 16-byte pieces, or copy
@@ -231,7 +78,7 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
   d.dot_part = dot ? dot->part : nullptr;
   d.dot_stride = dot ? dot->stride : 0;
   PlanLayout lay;
-  const bool planned = make_plan(B, T, H, dk, dv, N, chunk_size, has_cu,
+  const bool planned = make_plan(B, T, H, dk, dv, N, chunk_size, has_cu, cu_count(),
                                  f32_kernel ? GLA_F32 : in_dtype, lay);
   if (planned && (!workspace || workspace_bytes < lay.total_bytes)) return GLA_ERR_WORKSPACE;
 
@@ -279,7 +126,8 @@ size_t fwd_workspace(int B, int T, int H, int dk, int dv, int N, int chunk_size,
                      gla_dtype in_dtype, bool f32_kernel) {
   PlanLayout lay;
   chunk_size = kernel_chunk(in_dtype, f32_kernel, chunk_size);
-  if (!make_plan(B, T, H, dk, dv, N, chunk_size, has_cu, f32_kernel ? GLA_F32 : in_dtype, lay))
+  if (!make_plan(B, T, H, dk, dv, N, chunk_size, has_cu, cu_count(),
+                 f32_kernel ? GLA_F32 : in_dtype, lay))
     return 0;
   return lay.total_bytes;
 }

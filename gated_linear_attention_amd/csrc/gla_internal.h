@@ -6,57 +6,9 @@
 #include <stdint.h>
 
 #include "gla.h"
+#include "plan_host.h"
 
 namespace gla {
-
-// One unit of chunked-forward work for one (head, dv-slice): a run of tokens
-// [tok_begin, tok_end) of sequence `seq` on the flattened time axis (row b of
-// a dense batch starts at b*T). `state_in` < 0 starts from S0[seq] (zeros if
-// S0 is NULL); otherwise from workspace state slot `state_in`. In the
-// output pass, `state_out` < 0 writes the final state to S_T[seq] and
-// `state_out` == kNoStateOut writes nothing; in the state pass it is the slot
-// that receives the segment's local state and total log-decay.
-struct WorkItem {
-  int tok_begin;
-  int tok_end;
-  int seq;
-  int state_in;
-  int state_out;
-  int seq_begin, seq_end;  // the whole sequence's tokens (time-reversed runs map through them)
-  int pad;
-};
-constexpr int kNoStateOut = -2;
-
-// A sequence split into segments: its chain of `nslot` state slots starts at
-// slot_base (slot_base holds S0; slot_base + b the state after b state items,
-// each a sub-segment of sub_len tokens of a non-last segment; segment s starts
-// from slot_base + s * (sub-segments per segment)).
-struct MultiSeq {
-  int seq;
-  int slot_base;
-  int nslot;
-  int pad;
-};
-
-struct PlanHeader {
-  int n_items;        // output-pass items
-  int n_state_items;  // state-pass items (all non-last segments)
-  int n_multi;        // sequences with more than one segment
-  int pad;
-};
-
-// Workspace layout of a planned forward (all offsets 256-byte aligned).
-struct PlanLayout {
-  int seg_len;          // tokens per segment (multiple of the chunk size)
-  int sub_len;          // tokens per state-pass item (divides the segment into n_sub pieces)
-  int n_sub;            // state-pass items per non-last segment
-  int max_items;        // bound on output-pass items
-  int max_state_items;  // bound on state-pass items
-  int max_multi;        // bound on split sequences
-  int max_slots;        // bound on state slots
-  size_t off_header, off_items, off_state_items, off_multi, off_slots, off_slot_gamma;
-  size_t total_bytes;
-};
 
 // dims of the flattened problem
 struct FwdDims {
