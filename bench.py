@@ -588,8 +588,8 @@ def bench_laplace(args):
         lambda i: gla.fwd_chunked(tq, tk, tv, tlg, chunk_size=64, o=o, S_T=S_T), alg_gates)
 
     # the backward on the same inputs (the decays as a per-token gate stream, dO
-    # drawn like v, dS_T = 0); its dq and dk runs have 192-dim keys and run on
-    # the fp32-arithmetic kernel, the dv run on the twelve-wavefront kernel
+    # drawn like v, dS_T = 0); every run on the twelve-wavefront kernel, the dq
+    # and dk runs' 192-dim keys as two 96-dim halves
     gen = torch.Generator(device=dev).manual_seed(w.seed + 4)
     tdo = torch.randn((B, T, H, dv), generator=gen, device=dev).to(torch.bfloat16)
     bws = torch.empty(gla._lib.load().gla_bwd_chunked_workspace_size(B, T, H, dk, dv, B, 64, 0,
@@ -599,9 +599,11 @@ def bench_laplace(args):
     bwd = timed(lambda i: gla.bwd_chunked(tq, tk, tv, tlg, tdo, chunk_size=64, need_dS0=False,
                                           workspace=bws), alg_bwd)
     bwd.update({"algorithmic_bytes": alg_bwd, "chunk": 64,
-                "kernels": "chunk_f32_kernel<64,192,float,false,false,bf16> (dq), "
-                           "chunk_bf16_w8_kernel<96,6,float,false,true,false> (dv), "
-                           "chunk_f32_kernel<64,192,float,false,true,bf16> (dk), gate kernels"})
+                "kernels": "chunk_bf16_w8_kernel<96,6,float,false,false,false> (dq: the "
+                           "192-dim keys as two 96-dim halves, head groups of two), "
+                           "chunk_bf16_w8_kernel<96,6,float,false,true,false> (dv; dk: the "
+                           "same split, time-reversed), gate kernels (halves summed with "
+                           "the gate dots)"})
     del tdo, bws
 
     # the mixer epilogue on the forward's output: fp32 o, bf16 q, k, v and gate

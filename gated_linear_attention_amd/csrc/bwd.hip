@@ -44,12 +44,15 @@ __global__ __launch_bounds__(256) void transpose_kernel(const float *__restrict_
 }
 
 // dB[p, h] = q.dq - k.dk for every token row (32 lanes per row, 4 elements
-// per lane per step, 8 rows per workgroup).
+// per lane per step, 8 rows per workgroup). With dq2 / dk2 (the second key
+// halves of split-key runs), dq += dq2 and dk += dk2 first (written back).
 template <typename Tin>
 __global__ __launch_bounds__(256) void gate_dot_kernel(const Tin *__restrict__ q,
                                                        const Tin *__restrict__ k,
-                                                       const float *__restrict__ dq,
-                                                       const float *__restrict__ dk,
+                                                       float *__restrict__ dq,
+                                                       float *__restrict__ dk,
+                                                       const float *__restrict__ dq2,
+                                                       const float *__restrict__ dk2,
                                                        float *__restrict__ dB, long rows, int DK) {
   const long row = (long)blockIdx.x * 8 + threadIdx.x / 32;
   const int l = threadIdx.x % 32;
@@ -57,8 +60,15 @@ __global__ __launch_bounds__(256) void gate_dot_kernel(const Tin *__restrict__ q
   if (row < rows) {
     const size_t base = (size_t)row * DK;
     for (int i = 4 * l; i < DK; i += 128) {
-      const f32x4 a = load4_as_f32(q + base + i), b = *reinterpret_cast<const f32x4 *>(dq + base + i);
-      const f32x4 c = load4_as_f32(k + base + i), d = *reinterpret_cast<const f32x4 *>(dk + base + i);
+      const f32x4 a = load4_as_f32(q + base + i), c = load4_as_f32(k + base + i);
+      f32x4 b = *reinterpret_cast<const f32x4 *>(dq + base + i);
+      f32x4 d = *reinterpret_cast<const f32x4 *>(dk + base + i);
+      if (dq2) {
+        b += *reinterpret_cast<const f32x4 *>(dq2 + base + i);
+        d += *reinterpret_cast<const f32x4 *>(dk2 + base + i);
+        *reinterpret_cast<f32x4 *>(dq + base + i) = b;
+        *reinterpret_cast<f32x4 *>(dk + base + i) = d;
+      }
       acc += (a[0] * b[0] + a[1] * b[1]) + (a[2] * b[2] + a[3] * b[3]) -
              ((c[0] * d[0] + c[1] * d[1]) + (c[2] * d[2] + c[3] * d[3]));
     }
@@ -224,22 +234,23 @@ hipError_t launch_transpose(const float *in, float *out, int count, int rows, in
   return hipSuccess;
 }
 
-hipError_t launch_dgate(const void *q, const void *k, const float *dq, const float *dk,
-                        const float *lg, const float *ST_t, const float *dST_t, const float *A0,
-                        float *dl, float *dS0, const int32_t *cu, int N, int T, int H, int DK,
-                        int DV, bool in_bf16, const float *dq_part, const float *dk_part,
-                        int n_part, hipStream_t stream) {
+hipError_t launch_dgate(const void *q, const void *k, float *dq, float *dk, const float *lg,
+                        const float *ST_t, const float *dST_t, const float *A0, float *dl,
+                        float *dS0, const int32_t *cu, int N, int T, int H, int DK, int DV,
+                        bool in_bf16, const float *dq_part, const float *dk_part, int n_part,
+                        hipStream_t stream, const float *dq2, const float *dk2) {
+  if ((dq2 == nullptr) != (dk2 == nullptr) || (dq2 && n_part != 0)) return hipErrorInvalidValue;
   const long rows = (long)(cu ? T : (long)N * T) * H;  // token rows of the batch
   if (rows > 0 && n_part == 0) {
     const dim3 grid((unsigned)((rows + 7) / 8)), block(256);
     if (in_bf16)
       hipLaunchKernelGGL(gate_dot_kernel<uint16_t>, grid, block, 0, stream,
                          static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k), dq,
-                         dk, dl, rows, DK);
+                         dk, dq2, dk2, dl, rows, DK);
     else
       hipLaunchKernelGGL(gate_dot_kernel<float>, grid, block, 0, stream,
-                         static_cast<const float *>(q), static_cast<const float *>(k), dq, dk, dl,
-                         rows, DK);
+                         static_cast<const float *>(q), static_cast<const float *>(k), dq, dk, dq2,
+                         dk2, dl, rows, DK);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

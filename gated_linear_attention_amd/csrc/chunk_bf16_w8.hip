@@ -118,27 +118,29 @@ struct W8Loader {
   int se_sum, seq_b, n_ld, n_g;
   static constexpr int kFar = 0x7fff0000;  // an offset past any descriptor range
 
+  // q and k have H heads (h is this workgroup's); v and the gates have HR =
+  // H / (head group) heads, of which this workgroup's is hr (see the kernel).
   __device__ __forceinline__ void init(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                       const float *lg, int t0, int H, int gts, int h, int DV,
-                                       int col0, int sb = 0, int se = 0) {
+                                       const float *lg, int t0, int H, int HR, int gts, int h,
+                                       int hr, int DV, int col0, int sb = 0, int se = 0) {
     if constexpr (REV) {
       qh = q + (size_t)h * DK;
       kh = k + (size_t)h * DK;
-      vh = v + (size_t)h * DV + col0;
-      gh = lg + h;
+      vh = v + (size_t)hr * DV + col0;
+      gh = lg + hr;
       se_sum = sb + se;
       seq_b = sb;
     }
     const size_t tok0 = (size_t)t0 * H + h;
     qp = q + tok0 * DK;
     kp = k + tok0 * DK;
-    vp = v + tok0 * DV + col0;
-    gp = lg + (size_t)t0 * gts + h;
+    vp = v + ((size_t)t0 * HR + hr) * DV + col0;
+    gp = lg + (size_t)t0 * gts + hr;
     qk_step = (size_t)C * H * DK;
-    v_step = (size_t)C * H * DV;
+    v_step = (size_t)C * HR * DV;
     g_step = (size_t)C * gts;
     qk_row = (uint32_t)H * DK * 2;
-    v_row = (uint32_t)H * DV * 2;
+    v_row = (uint32_t)HR * DV * 2;
     g_row = (uint32_t)gts * 4;
   }
   // Descriptors for the tile chunk that starts at token t0 (the one after the
@@ -325,6 +327,14 @@ struct W8Wave {
 // outputs' shape): each wavefront sums o * x over its 16 columns per row and
 // writes part[((slice * NCG + column group) * H + h) * part_stride + token]
 // (part_stride = tokens; a wavefront's 16 rows are 64 contiguous bytes).
+//
+// Head groups (hg > 1): q, k, S0, S_T and the state slots have H heads, and
+// v, the gates and the outputs H / hg: head h reads values and gates of head
+// h / hg and writes its outputs to o (h % hg == 0) or o2 (otherwise). The
+// backward uses hg = 2 to run a forward whose 192-dim keys are split into two
+// 96-dim halves (the scores and the state rows separate over key dimensions,
+// so the two halves' outputs add): a [.., 192] tensor is [.., 2, 96], and a
+// 192 x 96 state is two stacked 96 x 96 ones.
 template <int DK, int NCG, typename Tout, bool SP, bool REV = false, bool DOT = false>
 __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
@@ -332,7 +342,7 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
     float *__restrict__ ST, Tout *__restrict__ o, const WorkItem *__restrict__ items,
     const int *__restrict__ n_items, float *__restrict__ slots, float *__restrict__ slot_gamma,
     int T, int H, int gts, int DV, int n_pairs, const uint16_t *__restrict__ xd,
-    float *__restrict__ dpart, long part_stride) {
+    float *__restrict__ dpart, long part_stride, int hg, Tout *__restrict__ o2) {
   using Wv = W8Wave<DK, NCG, SP>;
   using LDS = typename Wv::LDS;
   using Loader = W8Loader<DK, NCG, SP, REV>;
@@ -360,6 +370,8 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
     pair = L0 / n_slices;
   }
   const int it = pair / H, h = pair % H;
+  const int HR = H / hg, hr = h / hg;             // values', gates' and outputs' heads
+  Tout *const ow = hg > 1 && h % hg ? o2 : o;     // this head's output tensor
   if (items && it >= *n_items) return;
   const WorkItem w = bf_item_for(items, it, T);
 
@@ -429,7 +441,7 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
   // complete in order, so this wavefront's loads are waited for first (issued
   // long before, they have landed); the barrier that opens the next chunk then
   // lets just these stores stay in flight.
-  const size_t rs16 = (size_t)16 * H * DV;
+  const size_t rs16 = (size_t)16 * HR * DV;
   auto mem_row = [&](int t) -> size_t {
     return (size_t)(REV ? w.seq_begin + w.seq_end - 1 - t : t);
   };
@@ -460,11 +472,11 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
     }
     if constexpr (REV) {  // logical row t is memory row sb + se - 1 - t
       const int se1 = w.seq_begin + w.seq_end - 1 - tc - ln;
-      Tout *ob = o + ((size_t)h) * DV + col0 + wcol + 4 * lg4;
-      if (16 * mi0 + ln < nc) store4_from_f32(ob + (size_t)(se1 - 16 * mi0) * H * DV, own[0]);
-      if (16 * mi1 + ln < nc) store4_from_f32(ob + (size_t)(se1 - 16 * mi1) * H * DV, own[1]);
+      Tout *ob = ow + ((size_t)hr) * DV + col0 + wcol + 4 * lg4;
+      if (16 * mi0 + ln < nc) store4_from_f32(ob + (size_t)(se1 - 16 * mi0) * HR * DV, own[0]);
+      if (16 * mi1 + ln < nc) store4_from_f32(ob + (size_t)(se1 - 16 * mi1) * HR * DV, own[1]);
     } else {
-      Tout *ob = o + ((size_t)(tc + ln) * H + h) * DV + col0 + wcol + 4 * lg4;
+      Tout *ob = ow + ((size_t)(tc + ln) * HR + hr) * DV + col0 + wcol + 4 * lg4;
       if (16 * mi0 + ln < nc) store4_from_f32(ob + mi0 * rs16, own[0]);
       if (16 * mi1 + ln < nc) store4_from_f32(ob + mi1 * rs16, own[1]);
     }
@@ -474,7 +486,7 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
 
   Loader ld;
   int t0 = w.tok_begin;
-  ld.init(q, k, v, lg, t0, H, gts, h, DV, col0, w.seq_begin, w.seq_end);
+  ld.init(q, k, v, lg, t0, H, HR, gts, h, hr, DV, col0, w.seq_begin, w.seq_end);
   ld.next(t0, w.tok_end, 0);
   ld.k_part(s, wave, lane);
   ld.q_part(s, wave, lane);
@@ -822,7 +834,7 @@ static hipError_t launch_w8_t(const uint16_t *q, const uint16_t *k, const uint16
   hipLaunchKernelGGL((chunk_bf16_w8_kernel<DK, NCG, Tout, SP, REV, DOT>), dim3(blocks),
                      dim3(128 * NCG), 0, stream, q, k, v, g, S0, S_T, static_cast<Tout *>(o),
                      items, n_items, slots, slot_gamma, d.T, d.H, d.gts, d.dv, (int)pairs,
-                     d.dot_x, d.dot_part, d.dot_stride);
+                     d.dot_x, d.dot_part, d.dot_stride, d.hg, static_cast<Tout *>(d.o2));
   return hipGetLastError();
 }
 
@@ -881,6 +893,7 @@ hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_
                              int grid_items, float *slots, float *slot_gamma, bool state_pass,
                              hipStream_t stream) {
   if (d.C != kW8C) return hipErrorInvalidValue;  // the planner runs bf16 inputs at chunk 64
+  if (d.hg != 1 && (d.dot_x || d.H % d.hg || !d.o2)) return hipErrorInvalidValue;
   if (d.dk == 96)  // 96 x 192 heads: two slices of six column groups
     return launch_w8_d<96, 6>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
                               slots, slot_gamma, state_pass, stream);

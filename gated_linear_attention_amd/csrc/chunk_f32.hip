@@ -383,6 +383,7 @@ hipError_t launch_chunk_f32(const void *q, const void *k, const void *v, const f
                             const FwdDims &d, const WorkItem *items, const int *n_items,
                             int grid_items, float *slots, float *slot_gamma, bool state_pass,
                             hipStream_t stream) {
+  if (d.hg != 1) return hipErrorInvalidValue;  // head groups: the bf16 kernel only
   if (d.dot_x) return hipErrorInvalidValue;  // row dots: bf16 chunk-64 kernel only
   if (in_bf16) {
     const auto *qb = static_cast<const uint16_t *>(q), *kb = static_cast<const uint16_t *>(k),

@@ -61,7 +61,8 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
                     const int32_t *cu_seqlens, void *o, float *S_T, int B, int T, int H, int dk,
                     int dv, int N, int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
                     void *workspace, size_t workspace_bytes, hipStream_t stream,
-                    bool fixed_decay, bool rev, const DotOut *dot, bool f32_kernel) {
+                    bool fixed_decay, bool rev, const DotOut *dot, bool f32_kernel,
+                    int head_group, void *o2) {
   const bool has_cu = cu_seqlens != nullptr;
   FwdDims d;
   d.B = B;
@@ -72,7 +73,9 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
   d.N = N;
   chunk_size = kernel_chunk(in_dtype, f32_kernel, chunk_size);
   d.C = chunk_size;
-  d.gts = fixed_decay ? 0 : H;
+  d.gts = fixed_decay ? 0 : H / head_group;  // the gates have the real heads
+  d.hg = head_group;
+  d.o2 = o2;
   d.rev = rev;
   d.dot_x = dot ? static_cast<const uint16_t *>(dot->x) : nullptr;
   d.dot_part = dot ? dot->part : nullptr;
@@ -302,10 +305,18 @@ bool bwd_dv_f32_kernel(int dk, int dv, int C, gla_dtype in_dtype) {
   return bwd_f32_kernel(dk, dv) && in_dtype != GLA_BF16;
 }
 
+// bf16 inputs with 96 x 192 heads: the dq and dk runs (192-dim keys, 96-dim
+// values) run on the twelve-wavefront kernel as two 96-dim key halves, head
+// groups of two, whose outputs add.
+bool bwd_split_keys(int dk, int dv, gla_dtype in_dtype) {
+  return dk == 96 && dv == 192 && in_dtype == GLA_BF16;
+}
+
 // Workspace layout of the backward (all offsets 256-byte aligned).
 struct BwdLayout {
-  size_t s0t, dstt, stt, a0, dqp, dkp, fws, total, fws_bytes;
+  size_t s0t, dstt, stt, a0, dqp, dkp, dq2, dk2, fws, total, fws_bytes;
   bool fused_dots;  // dq and dk passes write partial q.dq, k.dk (bf16, chunk 64)
+  bool split;       // dq, dk runs in two key halves (dq2, dk2: the second halves)
 };
 
 BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int N, int C, bool has_cu,
@@ -325,11 +336,15 @@ BwdLayout bwd_layout(int B, int T, int H, int dk, int dv, int N, int C, bool has
   L.stt = take(mat);
   L.a0 = take(mat);
   const bool f32k = bwd_f32_kernel(dk, dv);
+  L.split = bwd_split_keys(dk, dv, in_dtype);
   L.fused_dots = in_dtype == GLA_BF16 && !f32k;  // the 64-token kernel's row dots
   const size_t parts = L.fused_dots ? (size_t)(dk / 16) * ntok * 4 : 0;
   L.dqp = take(parts);
   L.dkp = take(parts);
-  const size_t f1 = fwd_workspace(B, T, H, dv, dk, N, C, has_cu, in_dtype, f32k);
+  L.dq2 = take(L.split ? ntok * dk * 4 : 0);
+  L.dk2 = take(L.split ? ntok * dk * 4 : 0);
+  const size_t f1 = L.split ? fwd_workspace(B, T, 2 * H, dk, dk, N, C, has_cu, in_dtype, false)
+                            : fwd_workspace(B, T, H, dv, dk, N, C, has_cu, in_dtype, f32k);
   const size_t f2 = fwd_workspace(B, T, H, dk, dv, N, C, has_cu, in_dtype,
                                   bwd_dv_f32_kernel(dk, dv, C, in_dtype));
   L.fws_bytes = f1 > f2 ? f1 : f2;
@@ -404,7 +419,9 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   const DotOut dq_dot{q, reinterpret_cast<float *>(ws + L.dqp), (long)B * T};
   const DotOut dk_dot{k, reinterpret_cast<float *>(ws + L.dkp), (long)B * T};
   const bool fuse = L.fused_dots;
-  const bool f32k = bwd_f32_kernel(DK, DV);
+  const bool f32k = bwd_f32_kernel(DK, DV) && !L.split;
+  float *dq2 = L.split ? reinterpret_cast<float *>(ws + L.dq2) : nullptr;
+  float *dk2 = L.split ? reinterpret_cast<float *>(ws + L.dk2) : nullptr;
   // transposed initial states
   if ((S0 && launch_transpose(S0, s0t, N * H, DK, DV, stream) != hipSuccess) ||
       (dS_T && launch_transpose(dS_T, dstt, N * H, DK, DV, stream) != hipSuccess))
@@ -412,8 +429,14 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   gla_status st;
   // dq: forward with (q, k, v) = (dO, v, k) on the transposed state; its final
   // state is S_T^T
-  st = fwd_core(dO, v, k, g, s0t, cu_seqlens, dq, stt, B, T, H, DV, DK, N, chunk_size, in_dtype,
-                GLA_F32, fws, L.fws_bytes, stream, false, false, fuse ? &dq_dot : nullptr, f32k);
+  if (L.split)  // 192-dim keys as two 96-dim halves: heads of [.., 2, 96], states [2, 96, 96]
+    st = fwd_core(dO, v, k, g, s0t, cu_seqlens, dq, stt, B, T, 2 * H, DK, DK, N, chunk_size,
+                  in_dtype, GLA_F32, fws, L.fws_bytes, stream, false, false, nullptr, false, 2,
+                  dq2);
+  else
+    st = fwd_core(dO, v, k, g, s0t, cu_seqlens, dq, stt, B, T, H, DV, DK, N, chunk_size,
+                  in_dtype, GLA_F32, fws, L.fws_bytes, stream, false, false,
+                  fuse ? &dq_dot : nullptr, f32k);
   if (st != GLA_OK) return st;
   // dv: the reversed-time run with (q, k, v) = (k, q, dO) from dS_T; ends in A_0
   st = fwd_core(k, q, dO, g, dS_T, cu_seqlens, dv, a0, B, T, H, DK, DV, N, chunk_size, in_dtype,
@@ -421,13 +444,19 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
                 bwd_dv_f32_kernel(DK, DV, chunk_size, in_dtype));
   if (st != GLA_OK) return st;
   // dk: the reversed-time run with (q, k, v) = (v, dO, q) from dS_T^T
-  st = fwd_core(v, dO, q, g, dstt, cu_seqlens, dk, nullptr, B, T, H, DV, DK, N, chunk_size,
-                in_dtype, GLA_F32, fws, L.fws_bytes, stream, false, true,
-                fuse ? &dk_dot : nullptr, f32k);
+  if (L.split)
+    st = fwd_core(v, dO, q, g, dstt, cu_seqlens, dk, nullptr, B, T, 2 * H, DK, DK, N, chunk_size,
+                  in_dtype, GLA_F32, fws, L.fws_bytes, stream, false, true, nullptr, false, 2,
+                  dk2);
+  else
+    st = fwd_core(v, dO, q, g, dstt, cu_seqlens, dk, nullptr, B, T, H, DV, DK, N, chunk_size,
+                  in_dtype, GLA_F32, fws, L.fws_bytes, stream, false, true,
+                  fuse ? &dk_dot : nullptr, f32k);
   if (st != GLA_OK) return st;
   if (launch_dgate(q, k, dq, dk, g, stt, dstt, a0, dg, dS0, cu_seqlens, N, T, H, DK, DV,
                    in_dtype == GLA_BF16, fuse ? dq_dot.part : nullptr,
-                   fuse ? dk_dot.part : nullptr, fuse ? DK / 16 : 0, stream) != hipSuccess)
+                   fuse ? dk_dot.part : nullptr, fuse ? DK / 16 : 0, stream, dq2,
+                   dk2) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;
 }

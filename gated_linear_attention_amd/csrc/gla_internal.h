@@ -25,6 +25,11 @@ struct FwdDims {
   const uint16_t *dot_x;
   float *dot_part;
   long dot_stride;
+  // head groups (bf16 kernel only): H counts the heads of q, k and the states;
+  // v, the gates and the outputs have H / hg heads, and heads with h % hg != 0
+  // write their outputs to o2 (see chunk_bf16_w8_kernel)
+  int hg = 1;
+  void *o2 = nullptr;
 };
 
 // Row dot products requested from a forward run (see FwdDims::dot_x).
@@ -77,7 +82,7 @@ gla_status fwd_core(const void *q, const void *k, const void *v, const float *g,
                     int dv, int N, int chunk_size, gla_dtype in_dtype, gla_dtype out_dtype,
                     void *workspace, size_t workspace_bytes, hipStream_t stream,
                     bool fixed_decay = false, bool rev = false, const DotOut *dot = nullptr,
-                    bool f32_kernel = false);
+                    bool f32_kernel = false, int head_group = 1, void *o2 = nullptr);
 // f32_kernel: run the fp32 kernel whatever in_dtype is (its workspace plan differs).
 size_t fwd_workspace(int B, int T, int H, int dk, int dv, int N, int chunk_size, bool has_cu,
                      gla_dtype in_dtype, bool f32_kernel = false);
@@ -87,11 +92,15 @@ hipError_t launch_transpose(const float *in, float *out, int count, int rows, in
 // The gate gradient dl (reverse cumulative sums of q.dq - k.dk per sequence)
 // and dS0. With n_part > 0 the dots come from the forward runs' partial sums
 // dq_part / dk_part; otherwise they are formed from q, dq, k, dk first.
-hipError_t launch_dgate(const void *q, const void *k, const float *dq, const float *dk,
-                        const float *lg, const float *ST_t, const float *dST_t, const float *A0,
-                        float *dl, float *dS0, const int32_t *cu, int N, int T, int H, int DK,
-                        int DV, bool in_bf16, const float *dq_part, const float *dk_part,
-                        int n_part, hipStream_t stream);
+// With dq2 / dk2 (the second key halves of a split-key run: head groups of
+// two, see FwdDims::hg), dq += dq2 and dk += dk2 first, in the same pass as
+// the dots.
+hipError_t launch_dgate(const void *q, const void *k, float *dq, float *dk, const float *lg,
+                        const float *ST_t, const float *dST_t, const float *A0, float *dl,
+                        float *dS0, const int32_t *cu, int N, int T, int H, int DK, int DV,
+                        bool in_bf16, const float *dq_part, const float *dk_part, int n_part,
+                        hipStream_t stream, const float *dq2 = nullptr,
+                        const float *dk2 = nullptr);
 
 // One decode step with the mixer epilogue fused (decode.hip): S (or the pool
 // entries slots[n], as launch_decode) updated in place, z written; o is not.
