@@ -354,14 +354,28 @@ def bench_decode(args):
     pool = torch.empty((P, H, dk, dv), dtype=torch.float32, device=dev).normal_(0.0, 0.02)
     perm = np.random.default_rng(D["state_seed"]).permutation(P)[:N].astype(np.int32)
     slots = torch.from_numpy(perm).to(dev)
+    # the slot-sorted streaming order: one small launch per step, shared by
+    # every layer of the step (timed on its own below)
+    order = gla.slot_order(slots, P)
 
     def step_slots(i):
+        gla.decode_step_slots(qs[i % steps], ks[i % steps], vs[i % steps], gs[i % steps], pool,
+                              slots, o=o, order=order)
+
+    def step_slots_given(i):  # the requests streamed in the batch's own (random) order
         gla.decode_step_slots(qs[i % steps], ks[i % steps], vs[i % steps], gs[i % steps], pool,
                               slots, o=o)
 
     warm_up(step_slots, 10, min(args.warm_seconds, 0.5))
     wall_s, kern_ms_s = time_launches(step_slots, steps, stream)
     gbs_s = alg_bytes / (kern_ms_s * 1e-3) / 1e9
+    warm_up(step_slots_given, 10, 0.0)
+    _, kern_ms_g = time_launches(step_slots_given, steps, stream)
+    ord_buf = torch.empty_like(order)
+    _, kern_ms_o = time_launches(
+        lambda i: gla._lib.check(gla._lib.load().gla_decode_slot_order(
+            slots.data_ptr(), N, P, ord_buf.data_ptr(), stream.cuda_stream), "slot order"),
+        steps, stream)
     return {
         "metric": "decode-step state HBM GB/s",
         "value": round(gbs, 1),
@@ -377,7 +391,11 @@ def bench_decode(args):
                      "kernel": "decode_step_kernel<128,128,bf16,float>"},
         "pool_slots": {"pool": P, "requests": N, "kernel_ms": round(kern_ms_s, 4),
                        "gbs": round(gbs_s, 1), "frac": round(gbs_s / HBM_PEAK_GBS, 4),
-                       "entry": "gla_decode_step_slots"},
+                       "entry": "gla_decode_step_slots with the gla_decode_slot_order order",
+                       "order_kernel_ms": round(kern_ms_o, 4),
+                       "given_order_kernel_ms": round(kern_ms_g, 4),
+                       "given_order_frac": round(alg_bytes / (kern_ms_g * 1e-3) / 1e9
+                                                 / HBM_PEAK_GBS, 4)},
     }
 
 
@@ -690,9 +708,10 @@ def bench_decode_layers(args, layers=24, batches=(20, 1280)):
         z = [torch.empty((N, H, dv), dtype=bf, device=dev) for _ in range(layers)]
 
         def step(i=0):
+            order = gla.slot_order(slots, N)  # once per step, for every layer
             for l in range(layers):
                 q, k, v, g = qkv[l]
-                gla.decode_step_slots(q, k, v, lg, pools[l], slots, o=o[l])
+                gla.decode_step_slots(q, k, v, lg, pools[l], slots, o=o[l], order=order)
                 gla.mixer_epilogue(o[l], q, k, v, g, ta, rms_w, 1e-6, z=z[l])
 
         warm_up(step, 3, min(args.warm_seconds, 0.3))
@@ -716,9 +735,11 @@ def bench_decode_layers(args, layers=24, batches=(20, 1280)):
         replay = (time.perf_counter() - t0) / steps
         # the same step with the fused decode + epilogue: one kernel per layer
         def step_fused(i=0):
+            order = gla.slot_order(slots, N)
             for l in range(layers):
                 q, k, v, g = qkv[l]
-                gla.decode_mixer(q, k, v, lg, pools[l], g, ta, rms_w, 1e-6, slots=slots, z=z[l])
+                gla.decode_mixer(q, k, v, lg, pools[l], g, ta, rms_w, 1e-6, slots=slots, z=z[l],
+                                 order=order)
 
         warm_up(step_fused, 3, min(args.warm_seconds, 0.3))
         torch.cuda.synchronize()

@@ -9,9 +9,10 @@ device memory and the current HIP stream.
     o, S_T = fwd_chunked_noalloc(q, k, v, g, S0=None, cu_seqlens=None)  # no workspace
     dq, dk, dv, dg, dS0 = bwd_chunked(q, k, v, g, dO, S0=None, cu_seqlens=None, dS_T=None)
     o = decode_step(q, k, v, g, S)          # S updated in place
-    o = decode_step_slots(q, k, v, g, S_pool, slots)   # S_pool[slots] updated in place
+    order = slot_order(slots, P)            # once per step: the slot-sorted streaming order
+    o = decode_step_slots(q, k, v, g, S_pool, slots, order=order)   # S_pool[slots] in place
     z = mixer_epilogue(o, q, k, v, g_out, a, rms_w, eps)  # self-augmentation, RMSNorm, SiLU gate
-    z = decode_mixer(q, k, v, g, S, g_out, a, rms_w, eps, slots=None)  # decode + epilogue, fused
+    z = decode_mixer(q, k, v, g, S, g_out, a, rms_w, eps, slots=None, order=None)  # fused
 
 Shapes follow the C ABI: q, k [B, T, H, dk]; v [B, T, H, dv]; g [B, T, H]
 fp32 natural-log gates; S0 / S_T [N, H, dk, dv] fp32; cu_seqlens int32 [N+1]
@@ -24,7 +25,8 @@ from ._lib import GLAError, GLA_BF16, GLA_F32
 
 __all__ = ["fwd_chunked", "fwd_chunked_fixed_decay", "fwd_chunked_noalloc", "bwd_chunked",
            "decode_step",
-           "decode_step_slots", "mixer_epilogue", "decode_mixer", "head_rms_weights",
+           "decode_step_slots", "slot_order", "mixer_epilogue", "decode_mixer",
+           "head_rms_weights",
            "workspace_size",
            "GLAError", "library_path"]
 
@@ -225,10 +227,28 @@ def decode_step(q, k, v, g, S, out_dtype=None, o=None):
     return o
 
 
-def decode_step_slots(q, k, v, g, S_pool, slots, out_dtype=None, o=None):
+def slot_order(slots, P):
+    """The slot-sorted streaming order (int32 [2, N] on the device: the
+    requests by ascending slot, padded lanes last, then their slots) of a
+    serving batch whose requests use pool entries slots (int32 [N]) of a
+    P-entry pool: computed on the GPU, once per step, and passed to every
+    layer's decode_step_slots / decode_mixer."""
+    torch = _torch()
+    lib = _lib.load()
+    _require(slots, "slots", torch.int32, slots.device, align=4)
+    N = slots.numel()
+    order = torch.empty((2, N), dtype=torch.int32, device=slots.device)
+    stream = torch.cuda.current_stream(slots.device).cuda_stream
+    st = lib.gla_decode_slot_order(_ptr(slots), N, int(P), _ptr(order), stream)
+    _lib.check(st, "gla_decode_slot_order")
+    return order
+
+
+def decode_step_slots(q, k, v, g, S_pool, slots, out_dtype=None, o=None, order=None):
     """Decode step over a pool of states: request n reads and updates
     S_pool[slots[n]] ([P, H, dk, dv] fp32, in place); slots (int32 [N], on the
-    device) outside [0, P) mark padded lanes (no state touched, o = 0). Returns o."""
+    device) outside [0, P) mark padded lanes (no state touched, o = 0). order
+    (int32 [2, N], from slot_order) sets the streaming order only. Returns o."""
     torch = _torch()
     lib = _lib.load()
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or g.dim() != 2 or S_pool.dim() != 4:
@@ -243,7 +263,9 @@ def decode_step_slots(q, k, v, g, S_pool, slots, out_dtype=None, o=None):
     _require(g, "g", torch.float32, dev, align=4)
     _require(S_pool, "S_pool", torch.float32, dev)
     _require(slots, "slots", torch.int32, dev, align=4)
-    if tuple(S_pool.shape[1:]) != (H, dk, dv) or tuple(g.shape) != (N, H) or slots.numel() != N:
+    _require(order, "order", torch.int32, dev, align=4)
+    if (tuple(S_pool.shape[1:]) != (H, dk, dv) or tuple(g.shape) != (N, H) or slots.numel() != N
+            or (order is not None and tuple(order.shape) != (2, N))):
         raise ValueError("inconsistent decode shapes")
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if o is None:
@@ -251,7 +273,7 @@ def decode_step_slots(q, k, v, g, S_pool, slots, out_dtype=None, o=None):
     _require(o, "o", out_dtype, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = lib.gla_decode_step_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S_pool), _ptr(slots),
-                                   _ptr(o), N, P, H, dk, dv, _dtype_code(q.dtype),
+                                   _ptr(order), _ptr(o), N, P, H, dk, dv, _dtype_code(q.dtype),
                                    _dtype_code(out_dtype), stream)
     _lib.check(st, "gla_decode_step_slots")
     return o
@@ -309,10 +331,11 @@ def mixer_epilogue(o, q, k, v, g, a, rms_w, eps: float = 1e-6, out_dtype=None, z
 
 
 def decode_mixer(q, k, v, g, S, g_out, a, rms_w, eps: float = 1e-6, slots=None,
-                 out_dtype=None, z=None):
+                 out_dtype=None, z=None, order=None):
     """One decode step with the mixer epilogue fused: S (dense [N, H, dk, dv],
-    or a pool [P, H, dk, dv] addressed by int32 slots [N]) is updated in place
-    and z = epilogue(o) is returned; o itself is not materialised."""
+    or a pool [P, H, dk, dv] addressed by int32 slots [N], streamed in the
+    optional order from slot_order) is updated in place and z = epilogue(o)
+    is returned; o itself is not materialised."""
     torch = _torch()
     lib = _lib.load()
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or g.dim() != 2 or S.dim() != 4:
@@ -326,6 +349,9 @@ def decode_mixer(q, k, v, g, S, g_out, a, rms_w, eps: float = 1e-6, slots=None,
         _require(x, name, dt, dev)
     _require(g, "g", torch.float32, dev, align=4)
     _require(slots, "slots", torch.int32, dev, align=4)
+    _require(order, "order", torch.int32, dev, align=4)
+    if order is not None and (slots is None or tuple(order.shape) != (2, N)):
+        raise ValueError("order needs slots and one entry per request")
     if (tuple(S.shape[1:]) != (H, dk, dv) or tuple(g.shape) != (N, H)
             or tuple(g_out.shape) != (N, H, dv) or tuple(a.shape) != (H, dk)
             or tuple(rms_w.shape) != (H, dv) or (slots is None and S.shape[0] != N)
@@ -338,7 +364,7 @@ def decode_mixer(q, k, v, g, S, g_out, a, rms_w, eps: float = 1e-6, slots=None,
     _require(z, "z", out_dtype, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     st = lib.gla_decode_mixer(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S), _ptr(slots),
-                              S.shape[0], _ptr(g_out), _ptr(a), _ptr(rms_w), float(eps), _ptr(z),
+                              _ptr(order), S.shape[0], _ptr(g_out), _ptr(a), _ptr(rms_w), float(eps), _ptr(z),
                               N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype), stream)
     _lib.check(st, "gla_decode_mixer")
     return z

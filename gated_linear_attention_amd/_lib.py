@@ -54,11 +54,13 @@ def load():
     lib.gla_bwd_chunked.restype = i
     lib.gla_decode_step.argtypes = [vp] * 6 + [i] * 4 + [i, i, vp]
     lib.gla_decode_step.restype = i
-    lib.gla_decode_step_slots.argtypes = [vp] * 7 + [i] * 5 + [i, i, vp]
+    lib.gla_decode_step_slots.argtypes = [vp] * 8 + [i] * 5 + [i, i, vp]
     lib.gla_decode_step_slots.restype = i
     lib.gla_mixer_epilogue.argtypes = [vp] * 7 + [ctypes.c_float, vp] + [i] * 4 + [i, i, i, vp]
     lib.gla_mixer_epilogue.restype = i
-    lib.gla_decode_mixer.argtypes = ([vp] * 6 + [i] + [vp] * 3 + [ctypes.c_float, vp] + [i] * 4
+    lib.gla_decode_slot_order.argtypes = [vp, i, i, vp, vp]
+    lib.gla_decode_slot_order.restype = i
+    lib.gla_decode_mixer.argtypes = ([vp] * 7 + [i] + [vp] * 3 + [ctypes.c_float, vp] + [i] * 4
                                      + [i, i, vp])
     lib.gla_decode_mixer.restype = i
     _lib = lib

@@ -481,19 +481,32 @@ gla_status gla_decode_step(const void *q, const void *k, const void *v, const fl
       overlaps(S, bS, k, bq) || overlaps(S, bS, v, bv) || overlaps(S, bS, g, bg))
     return GLA_ERR_INVALID_ARGUMENT;
   const hipError_t err = launch_decode(q, k, v, g, S, o, N, H, dk, dv, in_dtype == GLA_BF16,
-                                       out_dtype == GLA_BF16, nullptr, 0, cu_count(), stream);
+                                       out_dtype == GLA_BF16, nullptr, nullptr, 0, cu_count(),
+                                       stream);
   return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
-gla_status gla_decode_step_slots(const void *q, const void *k, const void *v, const float *g,
-                                 float *S_pool, const int32_t *slots, void *o, int N, int P,
-                                 int H, int dk, int dv, gla_dtype in_dtype, gla_dtype out_dtype,
+gla_status gla_decode_slot_order(const int32_t *slots, int N, int P, int32_t *order,
                                  void *stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (N < 0 || P < 0) return GLA_ERR_INVALID_ARGUMENT;
+  if (P > kMaxOrderPool) return GLA_ERR_UNSUPPORTED;
+  if (N == 0) return GLA_OK;
+  if (!slots || !order || !all_al4({slots, order})) return GLA_ERR_INVALID_ARGUMENT;
+  if (overlaps(order, (size_t)N * 8, slots, (size_t)N * 4)) return GLA_ERR_INVALID_ARGUMENT;
+  return launch_slot_order(slots, N, P, order, stream) == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
+gla_status gla_decode_step_slots(const void *q, const void *k, const void *v, const float *g,
+                                 float *S_pool, const int32_t *slots, const int32_t *order,
+                                 void *o, int N, int P, int H, int dk, int dv, gla_dtype in_dtype,
+                                 gla_dtype out_dtype, void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (N < 0 || P < 0 || H < 0) return GLA_ERR_INVALID_ARGUMENT;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
   if (!fwd_dims(dk, dv)) return GLA_ERR_UNSUPPORTED;
-  if (!all_al16({q, k, v, S_pool, o}) || !all_al4({g, slots})) return GLA_ERR_INVALID_ARGUMENT;
+  if (!all_al16({q, k, v, S_pool, o}) || !all_al4({g, slots, order}))
+    return GLA_ERR_INVALID_ARGUMENT;
   const size_t pairs = (size_t)N * H;
   if (pairs == 0) return GLA_OK;
   if (pairs > (size_t)INT_MAX || (size_t)P * H > (size_t)INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
@@ -504,10 +517,11 @@ gla_status gla_decode_step_slots(const void *q, const void *k, const void *v, co
   if (overlaps(o, bo, q, bq) || overlaps(o, bo, k, bq) || overlaps(o, bo, v, bv) ||
       overlaps(o, bo, g, bg) || overlaps(o, bo, S_pool, bS) || overlaps(o, bo, slots, bs) ||
       overlaps(S_pool, bS, q, bq) || overlaps(S_pool, bS, k, bq) || overlaps(S_pool, bS, v, bv) ||
-      overlaps(S_pool, bS, g, bg) || overlaps(S_pool, bS, slots, bs))
+      overlaps(S_pool, bS, g, bg) || overlaps(S_pool, bS, slots, bs) ||
+      overlaps(o, bo, order, order ? 2 * bs : 0) || overlaps(S_pool, bS, order, order ? 2 * bs : 0))
     return GLA_ERR_INVALID_ARGUMENT;
   const hipError_t err = launch_decode(q, k, v, g, S_pool, o, N, H, dk, dv, in_dtype == GLA_BF16,
-                                       out_dtype == GLA_BF16, slots, P, cu_count(), stream);
+                                       out_dtype == GLA_BF16, slots, order, P, cu_count(), stream);
   return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
@@ -543,7 +557,8 @@ gla_status gla_mixer_epilogue(const void *o, const void *q, const void *k, const
 }
 
 gla_status gla_decode_mixer(const void *q, const void *k, const void *v, const float *g,
-                            float *S, const int32_t *slots, int P, const void *g_out,
+                            float *S, const int32_t *slots, const int32_t *order, int P,
+                            const void *g_out,
                             const float *a, const float *rms_w, float eps, void *z, int N, int H,
                             int dk, int dv, gla_dtype in_dtype, gla_dtype out_dtype,
                             void *stream_) {
@@ -552,7 +567,8 @@ gla_status gla_decode_mixer(const void *q, const void *k, const void *v, const f
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GLA_ERR_INVALID_ARGUMENT;
   if (!(eps >= 0.f) || eps > 3.4e38f) return GLA_ERR_INVALID_ARGUMENT;
   if (!fwd_dims(dk, dv)) return GLA_ERR_UNSUPPORTED;
-  if (!all_al16({q, k, v, S, g_out, a, rms_w, z}) || !all_al4({g, slots}))
+  if (order && !slots) return GLA_ERR_INVALID_ARGUMENT;
+  if (!all_al16({q, k, v, S, g_out, a, rms_w, z}) || !all_al4({g, slots, order}))
     return GLA_ERR_INVALID_ARGUMENT;
   const size_t pairs = (size_t)N * H;
   if (pairs == 0) return GLA_OK;
@@ -564,13 +580,14 @@ gla_status gla_decode_mixer(const void *q, const void *k, const void *v, const f
   const size_t bq = pairs * dk * es, bv = pairs * dv * es, bg = pairs * 4;
   const size_t bS = n_states * dk * dv * 4, bz = pairs * dv * dtype_size(out_dtype);
   const size_t ba = (size_t)H * dk * 4, bw = (size_t)H * dv * 4, bs = slots ? (size_t)N * 4 : 0;
-  const void *ins[] = {q, k, v, g, g_out, a, rms_w, slots};
-  const size_t nins[] = {bq, bq, bv, bg, bv, ba, bw, bs};
-  for (int i = 0; i < 8; ++i)
+  const void *ins[] = {q, k, v, g, g_out, a, rms_w, slots, order};
+  const size_t nins[] = {bq, bq, bv, bg, bv, ba, bw, bs, order ? 2 * bs : 0};
+  for (int i = 0; i < 9; ++i)
     if (overlaps(z, bz, ins[i], nins[i]) || overlaps(S, bS, ins[i], nins[i]))
       return GLA_ERR_INVALID_ARGUMENT;
   if (overlaps(z, bz, S, bS)) return GLA_ERR_INVALID_ARGUMENT;
-  MixerArgs m{q, k, v, g, S, g_out, a, rms_w, eps, z, slots, slots ? P : 0, H, (long)pairs};
+  MixerArgs m{q, k, v, g, S, g_out, a, rms_w, eps, z, slots, slots ? P : 0, H, (long)pairs,
+              ReqMap{order, N, 1, 0, 1}};
   const hipError_t err =
       launch_decode_mixer(m, dk, dv, in_dtype == GLA_BF16, out_dtype == GLA_BF16, stream);
   return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;

@@ -43,9 +43,40 @@ struct DotOut {
 // for slots[n] in [0, P), and a padded lane (no state touched, o = 0) else.
 // Batches with fewer than two (sequence, head) pairs per CU (n_cu CUs) split
 // each pair's columns over several workgroups.
+// Launch position -> request of the decode kernels (decode.hip): order[j]
+// when the caller passed the slot-sorted order (order [2, n]: the requests,
+// then their slots), else groups of gs requests with group g at position
+// (g * stride) % ng (requests past ng * gs in place).
+struct ReqMap {
+  const int32_t *order;
+  int n, gs, ng, stride;
+  __device__ __forceinline__ int operator()(int j) const {  // -1: not a request
+    if (order) {
+      const int r = order[j];
+      return r >= 0 && r < n ? r : -1;
+    }
+    if (j >= gs * ng) return j;
+    const int g = j / gs;
+    return gs * (int)(((long)g * stride) % ng) + (j - g * gs);
+  }
+  // the pool slot of position j (request r): from the order's second row, a
+  // load that does not wait for the first
+  __device__ __forceinline__ int slot(int j, const int32_t *slots, int r) const {
+    return order ? order[n + j] : slots[r];
+  }
+};
+ReqMap make_req_map(const int32_t *order, int n, long bytes_per_request);
+
+// The largest pool gla_decode_slot_order sorts (one LDS counter per entry).
+constexpr int kMaxOrderPool = 32768;
+hipError_t launch_slot_order(const int32_t *slots, int N, int P, int32_t *order,
+                             hipStream_t stream);
+
+// order: the slot-sorted request order (with slots only), or null.
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g, float *S,
                          void *o, int N, int H, int dk, int dv, bool in_bf16, bool out_bf16,
-                         const int32_t *slots, int P, int n_cu, hipStream_t stream);
+                         const int32_t *slots, const int32_t *order, int P, int n_cu,
+                         hipStream_t stream);
 
 // s0_copy: the output pass writes S_T over S0, so the first segment of a
 // split sequence reads a copy of S0 that the combine leaves in the chain's
@@ -115,6 +146,7 @@ struct MixerArgs {
   const int32_t *slots;
   int P, H;
   long pairs;
+  ReqMap map;  // map.order: the slot-sorted request order, or null
 };
 hipError_t launch_decode_mixer(const MixerArgs &m, int dk, int dv, bool in_bf16, bool out_bf16,
                                hipStream_t stream);

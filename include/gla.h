@@ -227,11 +227,34 @@ gla_status gla_decode_step(const void *q, const void *k, const void *v, const fl
  *   slots  [N] int32 DEVICE array; a slot outside [0, P) (e.g. -1) marks a
  *          padded lane: no state is read or written and o[n] is set to 0.
  *          Valid slots must be distinct (two requests on one slot race).
+ *   order  [2, N] int32 DEVICE array or NULL: the order in which the
+ *          requests' states are streamed, as gla_decode_slot_order writes it
+ *          for these slots (row 0 the requests, row 1 their slots, which the
+ *          step then reads in place of slots[]). The results do not depend
+ *          on it; the time does: states streamed in slot order run near the
+ *          dense step's rate, states in a random slot order about 6% slower.
+ *          Entries of row 0 outside [0, N) are skipped; anything but a
+ *          permutation of 0 .. N-1 there leaves outputs unwritten or updates
+ *          a state twice.
  *   q, k, v, g, o, N, H, dk, dv, dtypes as gla_decode_step.
  */
 gla_status gla_decode_step_slots(const void *q, const void *k, const void *v, const float *g,
-                                 float *S_pool, const int32_t *slots, void *o, int N, int P,
-                                 int H, int dk, int dv, gla_dtype in_dtype, gla_dtype out_dtype,
+                                 float *S_pool, const int32_t *slots, const int32_t *order,
+                                 void *o, int N, int P, int H, int dk, int dv, gla_dtype in_dtype,
+                                 gla_dtype out_dtype, void *stream);
+
+/*
+ * The streaming order for a serving batch (Laplace 3B on AWS Trainium2,
+ * "Inference optimization": the engine decodes a batch of sequences whose
+ * states sit in fixed pool slots): order[0][0 .. N-1] = the requests 0 .. N-1
+ * sorted by slots[n] ascending, padded lanes (slots outside [0, P)) last, and
+ * order[1][i] = slots[order[0][i]]. Every layer of a step uses the same
+ * slots, so one call per step serves all of them. One workgroup; device
+ * arrays slots [N] and order [2, N] (must not overlap). P <= 32768, else
+ * GLA_ERR_UNSUPPORTED (pass order = NULL to the decode calls instead).
+ * Requests sharing a slot are ordered arbitrarily.
+ */
+gla_status gla_decode_slot_order(const int32_t *slots, int N, int P, int32_t *order,
                                  void *stream);
 
 /*
@@ -268,7 +291,8 @@ gla_status gla_mixer_epilogue(const void *o, const void *q, const void *k, const
  * One decode step with the token-mixer epilogue fused (Laplace 3B on AWS
  * Trainium2, "GLA mixer" and "Inference optimization"): the state update of
  * gla_decode_step (slots == NULL: S is [N, H, dk, dv]) or of
- * gla_decode_step_slots (slots != NULL: S is the pool [P, H, dk, dv]), then
+ * gla_decode_step_slots (slots != NULL: S is the pool [P, H, dk, dv]; order
+ * as there, NULL without slots), then
  * gla_mixer_epilogue's arithmetic on the readout, in one kernel; the readout
  * o itself is not written.
  *
@@ -281,7 +305,8 @@ gla_status gla_mixer_epilogue(const void *o, const void *q, const void *k, const
  * overlap the inputs.
  */
 gla_status gla_decode_mixer(const void *q, const void *k, const void *v, const float *g,
-                            float *S, const int32_t *slots, int P, const void *g_out,
+                            float *S, const int32_t *slots, const int32_t *order, int P,
+                            const void *g_out,
                             const float *a, const float *rms_w, float eps, void *z, int N, int H,
                             int dk, int dv, gla_dtype in_dtype, gla_dtype out_dtype,
                             void *stream);

@@ -19,7 +19,8 @@ def header_functions():
 
 def test_header_declares_the_boundary():
     assert header_functions() == ["gla_bwd_chunked", "gla_bwd_chunked_workspace_size",
-                                  "gla_decode_mixer", "gla_decode_step", "gla_decode_step_slots",
+                                  "gla_decode_mixer", "gla_decode_slot_order", "gla_decode_step",
+                                  "gla_decode_step_slots",
                                   "gla_fwd_chunked",
                                   "gla_fwd_chunked_fixed_decay",
                                   "gla_fwd_chunked_noalloc",
@@ -164,8 +165,9 @@ def test_decode_slots_rejects_bad_arguments_before_launch():
     lib = _lib.load()
     def call(q=FAKE, k=FAKE + G, v=FAKE + 2 * G, g=FAKE + 3 * G, S=FAKE + 4 * G,
              slots=FAKE + 40 * G, o=FAKE + 41 * G, N=4, P=8, H=2, dk=64, dv=64,
-             ind=_lib.GLA_BF16, outd=_lib.GLA_F32):
-        return lib.gla_decode_step_slots(q, k, v, g, S, slots, o, N, P, H, dk, dv, ind, outd, None)
+             ind=_lib.GLA_BF16, outd=_lib.GLA_F32, order=None):
+        return lib.gla_decode_step_slots(q, k, v, g, S, slots, order, o, N, P, H, dk, dv, ind,
+                                         outd, None)
     assert call(N=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call(P=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call(ind=3) == _lib.GLA_ERR_INVALID_ARGUMENT
@@ -174,7 +176,26 @@ def test_decode_slots_rejects_bad_arguments_before_launch():
     assert call(S=None) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call(o=FAKE + 4 * G + 64) == _lib.GLA_ERR_INVALID_ARGUMENT   # o inside the pool
     assert call(slots=FAKE + 4 * G + 64) == _lib.GLA_ERR_INVALID_ARGUMENT  # slots inside the pool
+    assert call(order=FAKE + 4 * G + 64) == _lib.GLA_ERR_INVALID_ARGUMENT  # order inside the pool
+    assert call(order=FAKE + 41 * G) == _lib.GLA_ERR_INVALID_ARGUMENT      # order under o
+    assert call(order=FAKE + 42 * G + 2) == _lib.GLA_ERR_INVALID_ARGUMENT  # misaligned
     assert call(N=0) == _lib.GLA_OK
+    assert call(N=0, order=FAKE + 42 * G) == _lib.GLA_OK
+
+
+def test_slot_order_rejects_bad_arguments_before_launch():
+    lib = _lib.load()
+    G = 1 << 30
+    S, O = FAKE, FAKE + G
+    call = lambda s=S, n=4, P=8, o=O: lib.gla_decode_slot_order(s, n, P, o, None)
+    assert call(n=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(P=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(P=32769) == _lib.GLA_ERR_UNSUPPORTED   # one LDS counter per pool entry
+    assert call(s=None) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(o=None) == _lib.GLA_ERR_INVALID_ARGUMENT
+    assert call(o=S + 8) == _lib.GLA_ERR_INVALID_ARGUMENT   # order over the slots
+    assert call(o=O + 2) == _lib.GLA_ERR_INVALID_ARGUMENT   # misaligned
+    assert call(n=0, s=None, o=None) == _lib.GLA_OK
 
 
 def test_epilogue_rejects_bad_arguments_before_launch():
@@ -205,10 +226,11 @@ def test_decode_mixer_rejects_bad_arguments_before_launch():
     F32, BF = _lib.GLA_F32, _lib.GLA_BF16
     q, k, v, g, S, go, a, w, z = (FAKE + (i << 30) for i in range(9))
 
-    def call(N=4, H=2, dk=64, dv=64, eps=1e-6, slots=None, P=0, zz=None, ind=BF, ptrs=None):
+    def call(N=4, H=2, dk=64, dv=64, eps=1e-6, slots=None, P=0, zz=None, ind=BF, ptrs=None,
+             order=None):
         p = ptrs or (q, k, v, g, S)
-        return lib.gla_decode_mixer(*p, slots, P, go, a, w, eps, zz or z, N, H, dk, dv, ind,
-                                    F32, None)
+        return lib.gla_decode_mixer(*p, slots, order, P, go, a, w, eps, zz or z, N, H, dk, dv,
+                                    ind, F32, None)
     assert call(N=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call(eps=-1.0) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call(ind=9) == _lib.GLA_ERR_INVALID_ARGUMENT
@@ -219,6 +241,8 @@ def test_decode_mixer_rejects_bad_arguments_before_launch():
     assert call(zz=S + 64) == _lib.GLA_ERR_INVALID_ARGUMENT       # z inside the state
     assert call(zz=go) == _lib.GLA_ERR_INVALID_ARGUMENT           # z over the gate stream
     assert call(ptrs=(q, k, v, g, q + 16)) == _lib.GLA_ERR_INVALID_ARGUMENT  # S over q
+    assert call(order=FAKE + (11 << 30)) == _lib.GLA_ERR_INVALID_ARGUMENT   # order without slots
+    assert call(slots=FAKE + (10 << 30), P=8, order=S + 64) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call(H=0) == _lib.GLA_OK
 
 
@@ -259,7 +283,8 @@ def test_misaligned_pointers_rejected_before_launch():
     for i in [0, 1, 2, 4, 5]:
         assert dec([x + 8 * (j == i) for j, x in enumerate(ptr)]) == BAD, i
     slots = FAKE + 40 * G
-    dsl = lambda p, s: lib.gla_decode_step_slots(*p[:5], s, p[5], 4, 8, 2, 64, 64, BF, F32, None)
+    dsl = lambda p, s: lib.gla_decode_step_slots(*p[:5], s, None, p[5], 4, 8, 2, 64, 64, BF, F32,
+                                                 None)
     assert dsl(ptr, slots + 2) == BAD
     assert dsl([x + 8 * (j == 4) for j, x in enumerate(ptr)], slots) == BAD  # the pool
 
@@ -271,7 +296,7 @@ def test_misaligned_pointers_rejected_before_launch():
 
     q, k, v, g, S, go, a, w, z = (FAKE + (i << 30) for i in range(9))
     mix = lambda q=q, S=S, go=go, z=z, g=g: lib.gla_decode_mixer(
-        q, k, v, g, S, None, 0, go, a, w, 1e-6, z, 4, 2, 64, 64, BF, F32, None)
+        q, k, v, g, S, None, None, 0, go, a, w, 1e-6, z, 4, 2, 64, 64, BF, F32, None)
     assert mix(q=q + 8) == BAD and mix(S=S + 4) == BAD and mix(go=go + 2) == BAD
     assert mix(z=z + 8) == BAD and mix(g=g + 2) == BAD
 
