@@ -140,8 +140,8 @@ def warm_up(fn, steps, seconds):
 # whose hash keys its committed counter record
 # (bf16 inputs run every chunk size as 64-token chunks on one kernel)
 FWD_KERNELS = {
-    64: ("chunk_bf16_w8_kernel<128,4,float,false,false,false>",
-         ["chunk_bf16_w8.hip", "bf16_blocks.h", "gla_common.h"]),
+    64: ("chunk_bf16_ws_kernel<float>",
+         ["chunk_bf16_ws.hip", "bf16_blocks.h", "tile_loader.h", "gla_common.h"]),
 }
 FWD_KERNELS[128] = FWD_KERNELS[64]
 

@@ -115,8 +115,53 @@ __device__ __forceinline__ u32x2 lds_tr16_nowait(const uint16_t *p) {
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
   return r;
 }
+// Plain LDS reads and a store issued as inline assembly, for code that has LDS
+// direct loads in flight to other buffers (see lds_tr16_nowait); a read's
+// result must pass through lds_wait() before use.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char *)p);
+}
+__device__ __forceinline__ u32x4 lds_ld128(const void *p) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+  return r;
+}
+__device__ __forceinline__ uint32_t lds_ld32(const void *p) {
+  uint32_t r;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+  return r;
+}
+__device__ __forceinline__ void lds_st128(void *p, const f32x4 &v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_st32(void *p, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+// Wait until at most n (0, 1, 10 or 11; anything else waits for all) of this
+// wavefront's vector-memory operations are outstanding.
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+  if (n == 11) asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+  else if (n == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 // Wait for this wavefront's LDS reads; the operands are tied so that their
 // users cannot be scheduled above the wait.
+__device__ __forceinline__ void lds_wait(u32x4 &a) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a));
+}
+__device__ __forceinline__ void lds_wait(uint32_t &a) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a));
+}
+__device__ __forceinline__ void lds_wait(uint32_t &a, uint32_t &b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void lds_wait(uint32_t &a, uint32_t &b, uint32_t &c) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c));
+}
+__device__ __forceinline__ void lds_wait(u32x4 &a, u32x4 &b, u32x4 &c, u32x4 &d) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
 __device__ __forceinline__ void lds_wait(u32x4 &a, u32x4 &b) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
 }

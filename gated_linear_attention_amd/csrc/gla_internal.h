@@ -104,6 +104,15 @@ hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_
                              int grid_items, float *slots, float *slot_gamma, bool state_pass,
                              hipStream_t stream);
 
+// The output pass for 128-dim keys on the wavefront-specialised kernel of
+// chunk_bf16_ws.hip (d.C = 64, d.dv a multiple of 64, no head groups, no
+// reversal or dot products); launch_chunk_bf16 routes there.
+hipError_t launch_chunk_bf16_ws(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const float *g, const float *S0, float *S_T, void *o,
+                                bool out_bf16, const FwdDims &d, const WorkItem *items,
+                                const int *n_items, int grid_items, const float *slots,
+                                hipStream_t stream);
+
 // The chunked forward after argument checks (gla_api.hip), and its workspace.
 // g is log_g [.., T, H], or with fixed_decay one log-decay per head [H]. rev
 // runs every sequence in reversed time (FwdDims::rev): o is written in the
