@@ -69,7 +69,8 @@ struct WsLds {
 };
 
 // LLVM's raw buffer loads into registers (offsets at or past the descriptor's
-// range read as 0).
+// range read as 0); the last argument is the cache policy (kNonTemporal: nt).
+constexpr int kNonTemporal = 2;
 __device__ i32x4 raw_buffer_load_b128(i32x4 rsrc, int voffset, int soffset, int aux) __asm(
     "llvm.amdgcn.raw.buffer.load.v4i32");
 __device__ float raw_buffer_load_f32(i32x4 rsrc, int voffset, int soffset, int aux) __asm(
@@ -128,7 +129,8 @@ struct WsStager {
     for (int i = 0; i < 2; ++i) {
       const int r = (2 * iw + i) * 8 + lane / 8;
       const int vo = r * v_row + (((lane % 8) ^ (r & 7)) << 4);
-      vv[i] = __builtin_bit_cast(u32x4, raw_buffer_load_b128(rv, vo, 0, 0));
+      // V is read by this workgroup alone: a non-temporal load (cache policy nt)
+      vv[i] = __builtin_bit_cast(u32x4, raw_buffer_load_b128(rv, vo, 0, kNonTemporal));
     }
     qp += qk_step;
     kp += qk_step;
