@@ -85,8 +85,15 @@ __device__ float raw_buffer_load_f32(i32x4 rsrc, int voffset, int soffset, int a
 // reads the swizzled chunk, the LDS side is linear); the last one also loads
 // the log-gates, three chunks ahead. Rows past the end of the run lie past
 // the descriptor's range and read as zeros.
+//
+// REV (time-reversed run, the backward's adjoint recurrence): logical token t
+// of a sequence [sb, se) is memory row sb + se - 1 - t, so a chunk's rows are
+// read bottom-up into the same LDS layout, and the gate at logical position
+// u = t - sb is the log-gate of memory row se - u (u >= 1; 0 at u = 0).
+template <bool REV>
 struct WsStager {
   static constexpr int C = kW8C, DK = kWsDK, SW = kWsSW;
+  static constexpr int kFar = 0x7fff0000;  // an offset past any descriptor range
   const uint16_t *qp, *kp, *vp;  // first row (this head / slice) of the next chunk to load
   const float *gp;               // first gate of the next gate chunk to load
   size_t qk_step, v_step, g_step;
@@ -94,10 +101,22 @@ struct WsStager {
   u32x4 kq[8], vv[2];             // staged K (0..3) and Q (4..7) blocks, V blocks
   float gx;                       // staged log-gate
   bool active, g_active;
+  // REV: head / slice bases, sb + se and the sequence start
+  const uint16_t *qh, *kh, *vh;
+  const float *gh;
+  int se_sum, seq_b;
 
   __device__ __forceinline__ void init(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                        const float *lg, int t0, int H, int gts, int h, int DV,
-                                       int col0) {
+                                       int col0, int sb, int se) {
+    if constexpr (REV) {
+      qh = q + (size_t)h * DK;
+      kh = k + (size_t)h * DK;
+      vh = v + (size_t)h * DV + col0;
+      gh = lg + h;
+      se_sum = sb + se;
+      seq_b = sb;
+    }
     const size_t tok0 = (size_t)t0 * H + h;
     qp = q + tok0 * DK;
     kp = k + tok0 * DK;
@@ -115,20 +134,29 @@ struct WsStager {
     active = t0 < tok_end;
     if (!active) return;
     const uint32_t last = (uint32_t)(min(C, tok_end - t0) - 1);
+    const int n_ld = (int)last + 1;
+    if constexpr (REV) {  // lowest memory row of the chunk: sb + se - t0 - n
+      const size_t lo = (size_t)(se_sum - t0 - n_ld);
+      qp = qh + lo * (qk_row / 2);
+      kp = kh + lo * (qk_row / 2);
+      vp = vh + lo * (v_row / 2);
+    }
     const i32x4 rk = make_rsrc(kp, last * qk_row + DK * 2);
     const i32x4 rq = make_rsrc(qp, last * qk_row + DK * 2);
     const i32x4 rv = make_rsrc(vp, last * v_row + SW * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (4 * iw + i) * 4 + lane / 16;
-      const int vo = row * qk_row + (((lane % 16) ^ (row & 15)) << 4);
+      int vo = (REV ? n_ld - 1 - row : row) * qk_row + (((lane % 16) ^ (row & 15)) << 4);
+      if (REV && row >= n_ld) vo = kFar;
       kq[i] = __builtin_bit_cast(u32x4, raw_buffer_load_b128(rk, vo, 0, 0));
       kq[4 + i] = __builtin_bit_cast(u32x4, raw_buffer_load_b128(rq, vo, 0, 0));
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = (2 * iw + i) * 8 + lane / 8;
-      const int vo = r * v_row + (((lane % 8) ^ (r & 7)) << 4);
+      int vo = (REV ? n_ld - 1 - r : r) * v_row + (((lane % 8) ^ (r & 7)) << 4);
+      if (REV && r >= n_ld) vo = kFar;
       // V is read by this workgroup alone: a non-temporal load (cache policy nt)
       vv[i] = __builtin_bit_cast(u32x4, raw_buffer_load_b128(rv, vo, 0, kNonTemporal));
     }
@@ -154,6 +182,13 @@ struct WsStager {
     g_active = t0 < tok_end;
     if (!g_active) return;
     const uint32_t last = (uint32_t)(min(C, tok_end - t0) - 1);
+    if constexpr (REV) {  // rows se - u for u = t0 - sb + n - 1 .. t0 - sb; u = 0 is out of range
+      const int n_g = (int)last + 1;
+      const i32x4 rg = make_rsrc(gh + (size_t)(se_sum - t0 - n_g + 1) * (g_row / 4),
+                                 last * g_row + (t0 == seq_b ? 0 : 4));
+      gx = raw_buffer_load_f32(rg, lane < n_g ? (n_g - 1 - lane) * g_row : kFar, 0, 0);
+      return;
+    }
     gx = raw_buffer_load_f32(make_rsrc(gp, last * g_row + 4), lane * g_row, 0, 0);
     gp += g_step;
   }
@@ -246,13 +281,18 @@ __device__ __forceinline__ void ws_intra(const uint16_t *sq, const uint16_t *sk,
 
 }  // namespace
 
-template <typename Tout>
+// REV: the time-reversed run (see WsStager). DOT: also the row dot products
+// of the outputs with x (a bf16 tensor of the outputs' shape): each state
+// wavefront sums o * x over its 16 columns per row and writes
+// part[((slice * 4 + column group) * H + h) * part_stride + token].
+template <typename Tout, bool REV, bool DOT>
 __global__ __launch_bounds__(512) void chunk_bf16_ws_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ lg, const float *__restrict__ S0,
     float *__restrict__ ST, Tout *__restrict__ o, const WorkItem *__restrict__ items,
     const int *__restrict__ n_items, const float *__restrict__ slots, int T, int H, int gts,
-    int DV, int n_pairs) {
+    int DV, int n_pairs, const uint16_t *__restrict__ xd, float *__restrict__ dpart,
+    long part_stride) {
   constexpr int C = kW8C, DK = kWsDK, SW = kWsSW, XP = kWsXP;
   __shared__ WsLds s;
 
@@ -306,11 +346,11 @@ __global__ __launch_bounds__(512) void chunk_bf16_ws_kernel(
 
   const int t0 = w.tok_begin;
   const int NC = (w.tok_end - t0 + C - 1) / C;  // chunks of this run
-  WsStager sg;
+  WsStager<REV> sg;
   if (!state_wave) {
     // chunk 0 and the gates of chunks 0, 1 straight into LDS; chunk 1 and the
     // gates of chunk 2 staged for the first step
-    sg.init(q, k, v, lg, t0, H, gts, h, DV, col0);
+    sg.init(q, k, v, lg, t0, H, gts, h, DV, col0, w.seq_begin, w.seq_end);
     sg.load(t0, w.tok_end, iw, lane);
     sg.commit(s, 0, iw, lane);
     sg.load(t0 + C, w.tok_end, iw, lane);
@@ -329,6 +369,10 @@ __global__ __launch_bounds__(512) void chunk_bf16_ws_kernel(
   }
   barrier_lds();
 
+  // memory row of logical token t
+  auto mem_row = [&](int t) -> size_t {
+    return (size_t)(REV ? w.seq_begin + w.seq_end - 1 - t : t);
+  };
   if (state_wave) {
     f32x4 qs_prev[4] = {};  // e^{b} Q S of the previous chunk, this wavefront's columns
     for (int ci = 0; ci <= NC; ++ci) {
@@ -339,6 +383,20 @@ __global__ __launch_bounds__(512) void chunk_bf16_ws_kernel(
       const uint16_t *sk = s.k[st];
       const uint16_t *sv = s.v[st];
       f32x4 qs_cur[4];
+      // x row pieces matching chunk ci - 1's outputs (DOT), loaded now so that
+      // they land while the state is read and advanced
+      u32x2 xv[4] = {};
+      if constexpr (DOT) {
+        if (ci > 0) {
+          const int tp = t0 + (ci - 1) * C;
+          const int np = min(C, w.tok_end - tp);
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            if (16 * m + ln < np)
+              xv[m] = *reinterpret_cast<const u32x2 *>(
+                  xd + (mem_row(tp + 16 * m + ln) * H + h) * DV + col0 + 16 * c + 4 * lg4);
+        }
+      }
       if (cur) {
         // ---- state read for this wavefront's 16 columns, all 64 rows:
         // part[m][r] = sum_d S[d][16 c + 4 lg4 + r] Q[16 m + ln][d]. A = S^T
@@ -435,13 +493,32 @@ __global__ __launch_bounds__(512) void chunk_bf16_ws_kernel(
       if (ci > 0) {
         const int tp = t0 + (ci - 1) * C;
         const int np = min(C, w.tok_end - tp);
-        Tout *ob = o + ((size_t)(tp + ln) * H + h) * DV + col0 + 16 * c + 4 * lg4;
-        const size_t rs16 = (size_t)16 * H * DV;
+        Tout *ob = o + (size_t)h * DV + col0 + 16 * c + 4 * lg4;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const f32x4 pv =
               *reinterpret_cast<const f32x4 *>(&s.y[st ^ 1][(16 * m + ln) * XP + 16 * c + 4 * lg4]);
-          if (16 * m + ln < np) store4_from_f32(ob + m * rs16, qs_prev[m] + pv);
+          const f32x4 out = qs_prev[m] + pv;
+          const size_t mr = mem_row(tp + 16 * m + ln);
+          if (16 * m + ln < np) store4_from_f32(ob + mr * H * DV, out);
+          if constexpr (DOT) {
+            const u32x2 xw = xv[m];
+            float d = out[0] * __uint_as_float(xw.x << 16) +
+                      out[1] * __uint_as_float(xw.x & 0xffff0000u) +
+                      out[2] * __uint_as_float(xw.y << 16) +
+                      out[3] * __uint_as_float(xw.y & 0xffff0000u);
+            // the sum over the row's four lane groups: swapping a value with
+            // itself across 16-lane rows (then 32-lane halves) and adding the
+            // two results gives d[l] + d[l ^ 16] (then + d[l ^ 32]) everywhere
+            const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(d),
+                                                              __float_as_uint(d), false, false);
+            d = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+            const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(d),
+                                                              __float_as_uint(d), false, false);
+            d = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+            if (lg4 == 0 && 16 * m + ln < np)
+              dpart[((size_t)(slice * 4 + c) * H + h) * part_stride + mr] = d;
+          }
         }
       }
       if (cur) {
@@ -500,24 +577,42 @@ __global__ __launch_bounds__(512) void chunk_bf16_ws_kernel(
   }
 }
 
+template <typename Tout, bool REV, bool DOT>
+static void launch_ws_t(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                        const float *S0, float *S_T, void *o, const FwdDims &d,
+                        const WorkItem *items, const int *n_items, long blocks, long pairs,
+                        const float *slots, hipStream_t stream) {
+  hipLaunchKernelGGL((chunk_bf16_ws_kernel<Tout, REV, DOT>), dim3(blocks), dim3(512), 0, stream,
+                     q, k, v, g, S0, S_T, static_cast<Tout *>(o), items, n_items, slots, d.T,
+                     d.H, d.gts, d.dv, (int)pairs, d.dot_x, d.dot_part, d.dot_stride);
+}
+
 hipError_t launch_chunk_bf16_ws(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                 const float *g, const float *S0, float *S_T, void *o,
                                 bool out_bf16, const FwdDims &d, const WorkItem *items,
                                 const int *n_items, int grid_items, const float *slots,
                                 hipStream_t stream) {
-  if (d.C != kW8C || d.dk != kWsDK || d.dv % kWsSW || d.hg != 1 || d.rev || d.dot_x)
-    return hipErrorInvalidValue;
+  if (d.C != kW8C || d.dk != kWsDK || d.dv % kWsSW || d.hg != 1) return hipErrorInvalidValue;
+  // the reversed and dot-product runs are the backward's: per-token gates, fp32 outputs
+  if ((d.rev || d.dot_x) && (out_bf16 || d.gts == 0)) return hipErrorInvalidValue;
   const long pairs = (long)grid_items * d.H;
   const long blocks = pairs * (d.dv / kWsSW);
   if (blocks == 0) return hipSuccess;
-  if (out_bf16)
-    hipLaunchKernelGGL(chunk_bf16_ws_kernel<uint16_t>, dim3(blocks), dim3(512), 0, stream, q, k,
-                       v, g, S0, S_T, static_cast<uint16_t *>(o), items, n_items, slots, d.T, d.H,
-                       d.gts, d.dv, (int)pairs);
+  if (d.rev && d.dot_x)
+    launch_ws_t<float, true, true>(q, k, v, g, S0, S_T, o, d, items, n_items, blocks, pairs,
+                                   slots, stream);
+  else if (d.rev)
+    launch_ws_t<float, true, false>(q, k, v, g, S0, S_T, o, d, items, n_items, blocks, pairs,
+                                    slots, stream);
+  else if (d.dot_x)
+    launch_ws_t<float, false, true>(q, k, v, g, S0, S_T, o, d, items, n_items, blocks, pairs,
+                                    slots, stream);
+  else if (out_bf16)
+    launch_ws_t<uint16_t, false, false>(q, k, v, g, S0, S_T, o, d, items, n_items, blocks, pairs,
+                                        slots, stream);
   else
-    hipLaunchKernelGGL(chunk_bf16_ws_kernel<float>, dim3(blocks), dim3(512), 0, stream, q, k, v,
-                       g, S0, S_T, static_cast<float *>(o), items, n_items, slots, d.T, d.H, d.gts,
-                       d.dv, (int)pairs);
+    launch_ws_t<float, false, false>(q, k, v, g, S0, S_T, o, d, items, n_items, blocks, pairs,
+                                     slots, stream);
   return hipGetLastError();
 }
 

@@ -105,8 +105,9 @@ hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_
                              hipStream_t stream);
 
 // The output pass for 128-dim keys on the wavefront-specialised kernel of
-// chunk_bf16_ws.hip (d.C = 64, d.dv a multiple of 64, no head groups, no
-// reversal or dot products); launch_chunk_bf16 routes there.
+// chunk_bf16_ws.hip (d.C = 64, d.dv a multiple of 64, no head groups;
+// reversed and dot-product runs with per-token gates and fp32 outputs);
+// launch_chunk_bf16 routes there.
 hipError_t launch_chunk_bf16_ws(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                 const float *g, const float *S0, float *S_T, void *o,
                                 bool out_bf16, const FwdDims &d, const WorkItem *items,
