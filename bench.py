@@ -666,7 +666,8 @@ def bench_laplace(args):
         "backward": bwd,
         "epilogue": epi,
         "forward_traffic_c64": measured_traffic("chunk_fwd_bf16_laplace_2k_c64",
-                                                FWD_KERNELS[64][1]),
+                                                ["chunk_bf16_w8.hip", "bf16_blocks.h",
+                                                 "tile_loader.h", "gla_common.h"]),
         "decode": {"N": N, "kernel_ms": round(kern_ms, 5), "gbs": round(gbs, 1),
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg_dec,
                    "traffic": measured_traffic("decode_step_laplace_1280x16",
