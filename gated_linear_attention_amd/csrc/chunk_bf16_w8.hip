@@ -741,12 +741,15 @@ hipError_t launch_chunk_bf16(const uint16_t *q, const uint16_t *k, const uint16_
                              hipStream_t stream) {
   if (d.C != kW8C) return hipErrorInvalidValue;  // the planner runs bf16 inputs at chunk 64
   if (d.hg != 1 && (d.dot_x || d.H % d.hg || !d.o2)) return hipErrorInvalidValue;
-  // the output pass of 128-dim keys (forward and the backward's runs): the
-  // wavefront-specialised kernel
+  // 128-dim keys (forward and the backward's runs, and their state passes):
+  // the wavefront-specialised kernels
   if (!state_pass && d.dk == 128 && d.dv % 64 == 0 && d.hg == 1 &&
       !((d.rev || d.dot_x) && (out_bf16 || d.gts == 0)))
     return launch_chunk_bf16_ws(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
                                 slots, stream);
+  if (state_pass && d.dk == 128 && d.dv % 64 == 0 && d.hg == 1)
+    return launch_chunk_bf16_ws_state(k, v, g, d, items, n_items, grid_items, slots, slot_gamma,
+                                      stream);
   if (d.dk == 96)  // 96 x 192 heads: two slices of six column groups
     return launch_w8_d<96, 6>(q, k, v, g, S0, S_T, o, out_bf16, d, items, n_items, grid_items,
                               slots, slot_gamma, state_pass, stream);

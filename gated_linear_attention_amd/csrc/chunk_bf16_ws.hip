@@ -90,7 +90,9 @@ __device__ float raw_buffer_load_f32(i32x4 rsrc, int voffset, int soffset, int a
 // of a sequence [sb, se) is memory row sb + se - 1 - t, so a chunk's rows are
 // read bottom-up into the same LDS layout, and the gate at logical position
 // u = t - sb is the log-gate of memory row se - u (u >= 1; 0 at u = 0).
-template <bool REV>
+//
+// QL = false (the state pass): K and V only.
+template <bool REV, bool QL = true>
 struct WsStager {
   static constexpr int C = kW8C, DK = kWsDK, SW = kWsSW;
   static constexpr int kFar = 0x7fff0000;  // an offset past any descriptor range
@@ -142,7 +144,7 @@ struct WsStager {
       vp = vh + lo * (v_row / 2);
     }
     const i32x4 rk = make_rsrc(kp, last * qk_row + DK * 2);
-    const i32x4 rq = make_rsrc(qp, last * qk_row + DK * 2);
+    const i32x4 rq = QL ? make_rsrc(qp, last * qk_row + DK * 2) : rk;
     const i32x4 rv = make_rsrc(vp, last * v_row + SW * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -150,7 +152,7 @@ struct WsStager {
       int vo = (REV ? n_ld - 1 - row : row) * qk_row + (((lane % 16) ^ (row & 15)) << 4);
       if (REV && row >= n_ld) vo = kFar;
       kq[i] = __builtin_bit_cast(u32x4, raw_buffer_load_b128(rk, vo, 0, 0));
-      kq[4 + i] = __builtin_bit_cast(u32x4, raw_buffer_load_b128(rq, vo, 0, 0));
+      if constexpr (QL) kq[4 + i] = __builtin_bit_cast(u32x4, raw_buffer_load_b128(rq, vo, 0, 0));
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -165,12 +167,14 @@ struct WsStager {
     vp += v_step;
   }
   // Write the staged chunk into stage st.
-  __device__ __forceinline__ void commit(WsLds &s, int st, int iw, int lane) {
+  template <typename L>
+  __device__ __forceinline__ void commit(L &s, int st, int iw, int lane) {
     if (!active) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       *reinterpret_cast<u32x4 *>(&s.k[st][(4 * iw + i) * 512 + 8 * lane]) = kq[i];
-      *reinterpret_cast<u32x4 *>(&s.q[st][(4 * iw + i) * 512 + 8 * lane]) = kq[4 + i];
+      if constexpr (QL)
+        *reinterpret_cast<u32x4 *>(&s.q[st][(4 * iw + i) * 512 + 8 * lane]) = kq[4 + i];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -192,15 +196,17 @@ struct WsStager {
     gx = raw_buffer_load_f32(make_rsrc(gp, last * g_row + 4), lane * g_row, 0, 0);
     gp += g_step;
   }
-  __device__ __forceinline__ void gate_commit(WsLds &s, int slot, int lane) {
+  template <typename L>
+  __device__ __forceinline__ void gate_commit(L &s, int slot, int lane) {
     if (g_active) s.lgb[slot][lane] = gx;
   }
 };
 
 // The decay arrays of a chunk from its log-gates (x = this lane's, 0 past the
 // end of the run): a reset gate enters the prefix sums as 0 and cuts every
-// product of gates that spans it.
-__device__ __forceinline__ void ws_gates(WsGates &g, float x, int lane) {
+// product of gates that spans it. Returns the chunk's total log-decay (-inf if
+// it holds a reset).
+__device__ __forceinline__ float ws_gates(WsGates &g, float x, int lane) {
   const bool rst = is_reset(x);
   const uint64_t rm = __builtin_amdgcn_ballot_w64(rst);
   const float incl = wave_inclusive_scan(rst ? 0.f : x);
@@ -213,6 +219,7 @@ __device__ __forceinline__ void ws_gates(WsGates &g, float x, int lane) {
   g.lam[lane] = ri < 0 ? fast_exp2(b2) : 0.f;
   g.kap[lane] = lane < rl ? 0.f : fast_exp2(b2last - b2);
   if (lane == 0) g.gam = rl < 0 ? fast_exp2(b2last) : 0.f;
+  return rl < 0 ? total : -__builtin_huge_valf();
 }
 
 // The attention term of one chunk for query row block R (rows 16 R .. 16 R +
@@ -577,6 +584,160 @@ __global__ __launch_bounds__(512) void chunk_bf16_ws_kernel(
   }
 }
 
+// The state pass of a split sequence on the same layout: each work item (a
+// piece of a segment) runs the state recurrence from zero, S <- e^{b_last} S +
+// K^T (kappa . V) chunk by chunk, and leaves its final state in its slot and
+// its total log-decay (-inf if it holds a reset) beside it, for the combine to
+// chain. No queries, no outputs: the four state wavefronts only advance the
+// state; the four others copy K and V two chunks ahead and prepare the decay
+// arrays. Without Q, the attention term and the hand-over, a workgroup needs
+// 50 KB of LDS and at most 128 VGPRs a lane, so two run on a CU.
+struct WsSpLds {
+  uint16_t k[2][kW8C * kWsDK];
+  uint16_t v[2][kW8C * kWsSW];
+  float lgb[3][kW8C];
+  WsGates g[2];
+};
+
+template <bool REV>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void
+chunk_bf16_ws_state_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                           const float *__restrict__ lg, const WorkItem *__restrict__ items,
+                           const int *__restrict__ n_items, float *__restrict__ slots,
+                           float *__restrict__ slot_gamma, int T, int H, int gts, int DV,
+                           int n_pairs) {
+  constexpr int C = kW8C, DK = kWsDK, SW = kWsSW;
+  __shared__ WsSpLds s;
+
+  // Block -> (pair = item * H + head, column slice); slices of a pair share an XCD.
+  const int n_slices = DV / SW;
+  const int per_round = 8 * n_slices;
+  const int full = (n_pairs * n_slices) / per_round * per_round;
+  int pair, slice;
+  const int L0 = blockIdx.x;
+  if (L0 < full) {
+    const int xcd = L0 % 8, kk = L0 / 8;
+    slice = kk % n_slices;
+    pair = (kk / n_slices) * 8 + xcd;
+  } else {
+    slice = L0 % n_slices;
+    pair = L0 / n_slices;
+  }
+  const int it = pair / H, h = pair % H;
+  if (it >= *n_items) return;
+  const WorkItem w = items[it];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+  const int ln = lane % 16, lg4 = lane / 16;
+  const bool state_wave = wave < 4;
+  const int c = wave & 3;   // state: column group of 16
+  const int iw = wave - 4;  // index among the copying wavefronts
+  const int col0 = slice * SW;
+  const int t0 = w.tok_begin;
+  const int NC = (w.tok_end - t0 + C - 1) / C;
+
+  WsStager<REV, false> sg;
+  float lsum = 0.f;  // wavefront 4: the item's total log-decay
+  if (!state_wave) {
+    sg.init(k, k, v, lg, t0, H, gts, h, DV, col0, w.seq_begin, w.seq_end);
+    sg.load(t0, w.tok_end, iw, lane);
+    sg.commit(s, 0, iw, lane);
+    sg.load(t0 + C, w.tok_end, iw, lane);
+    if (iw == 3) {
+      sg.gate_load(t0, w.tok_end, lane);
+      sg.gate_commit(s, 0, lane);
+      sg.gate_load(t0 + C, w.tok_end, lane);
+      sg.gate_commit(s, 1, lane);
+      sg.gate_load(t0 + 2 * C, w.tok_end, lane);
+    }
+  }
+  barrier_lds();
+  if (wave == 4 && NC > 0) {
+    const float x = s.lgb[0][lane];
+    lsum += ws_gates(s.g[0], lane < w.tok_end - t0 ? x : 0.f, lane);
+  }
+  barrier_lds();
+
+  if (state_wave) {
+    // S_acc[t][r] = S[16 t + 4 lg4 + r][col0 + 16 c + ln]
+    f32x4 S_acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) S_acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ci = 0; ci < NC; ++ci) {
+      const int st = ci & 1;
+      const WsGates &G = s.g[st];
+      const uint16_t *sk = s.k[st];
+      const uint16_t *sv = s.v[st];
+      const float gam = G.gam;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) S_acc[t] *= gam;
+      // S += K^T (kappa . V) over keys 32 kb .. 32 kb + 31: B = kappa . V
+      // (hi, lo; slot 8 lg4 + e <-> key 32 kb + 8 lg4 + e, column 16 c + ln),
+      // A = K^T (the same key slots, row d = 16 t + ln)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int r0 = 32 * kb + 8 * lg4 + (ln >> 2);
+        const int cc = 16 * c + 4 * (ln & 3);
+        const u32x2 x0 = lds_tr16(&sv[v_off(r0, cc)]);
+        const u32x2 x1 = lds_tr16(&sv[v_off(r0 + 4, cc)]);
+        u32x4 kt[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const u32x2 a0 = lds_tr16(&sk[qk_off<DK>(r0, 16 * t + 4 * (ln & 3))]);
+          const u32x2 a1 = lds_tr16(&sk[qk_off<DK>(r0 + 4, 16 * t + 4 * (ln & 3))]);
+          kt[t] = u32x4{a0.x, a0.y, a1.x, a1.y};
+        }
+        const u32x4 vf = u32x4{x0.x, x0.y, x1.x, x1.y};
+        const f32x4 kap0 = *reinterpret_cast<const f32x4 *>(&G.kap[32 * kb + 8 * lg4]);
+        const f32x4 kap1 = *reinterpret_cast<const f32x4 *>(&G.kap[32 * kb + 8 * lg4 + 4]);
+        u32x4 kv_h, kv_l;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const uint32_t vw = vf[e2];
+          const float v0 = __uint_as_float(vw << 16), v1 = __uint_as_float(vw & 0xffff0000u);
+          const f32x4 &kk = e2 < 2 ? kap0 : kap1;
+          uint32_t hh, ll;
+          split_pk_bf16(kk[2 * (e2 & 1)] * v0, kk[2 * (e2 & 1) + 1] * v1, hh, ll);
+          kv_h[e2] = hh;
+          kv_l[e2] = ll;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S_acc[t] = mfma16(kt[t], kv_h, S_acc[t]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S_acc[t] = mfma16(kt[t], kv_l, S_acc[t]);
+        // one half's operands at a time (two workgroups share a CU: 128 VGPRs)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // chunk ci + 1's tiles and decay arrays are ready
+      barrier_lds();
+    }
+    float *sout = slots + ((size_t)w.state_out * H + h) * ((size_t)DK * DV);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sout[(size_t)(16 * t + 4 * lg4 + r) * DV + col0 + 16 * c + ln] = S_acc[t][r];
+    return;
+  }
+
+  // copying wavefronts
+  for (int ci = 0; ci < NC; ++ci) {
+    const int tc = t0 + ci * C;
+    const int st = ci & 1;
+    sg.commit(s, st ^ 1, iw, lane);
+    if (iw == 3) sg.gate_commit(s, (ci + 2) % 3, lane);
+    sg.load(tc + 2 * C, w.tok_end, iw, lane);
+    if (iw == 3) sg.gate_load(tc + 3 * C, w.tok_end, lane);
+    if (wave == 4 && ci + 1 < NC) {
+      const float x = s.lgb[(ci + 1) % 3][lane];
+      lsum += ws_gates(s.g[st ^ 1], lane < w.tok_end - tc - C ? x : 0.f, lane);
+    }
+    barrier_lds();
+  }
+  if (wave == 4 && slice == 0 && lane == 0) slot_gamma[(size_t)w.state_out * H + h] = lsum;
+}
+
 template <typename Tout, bool REV, bool DOT>
 static void launch_ws_t(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                         const float *S0, float *S_T, void *o, const FwdDims &d,
@@ -613,6 +774,24 @@ hipError_t launch_chunk_bf16_ws(const uint16_t *q, const uint16_t *k, const uint
   else
     launch_ws_t<float, false, false>(q, k, v, g, S0, S_T, o, d, items, n_items, blocks, pairs,
                                      slots, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_bf16_ws_state(const uint16_t *k, const uint16_t *v, const float *g,
+                                      const FwdDims &d, const WorkItem *items, const int *n_items,
+                                      int grid_items, float *slots, float *slot_gamma,
+                                      hipStream_t stream) {
+  if (d.C != kW8C || d.dk != kWsDK || d.dv % kWsSW || d.hg != 1 || !items)
+    return hipErrorInvalidValue;
+  const long pairs = (long)grid_items * d.H;
+  const long blocks = pairs * (d.dv / kWsSW);
+  if (blocks == 0) return hipSuccess;
+  if (d.rev)
+    hipLaunchKernelGGL((chunk_bf16_ws_state_kernel<true>), dim3(blocks), dim3(512), 0, stream, k,
+                       v, g, items, n_items, slots, slot_gamma, d.T, d.H, d.gts, d.dv, (int)pairs);
+  else
+    hipLaunchKernelGGL((chunk_bf16_ws_state_kernel<false>), dim3(blocks), dim3(512), 0, stream, k,
+                       v, g, items, n_items, slots, slot_gamma, d.T, d.H, d.gts, d.dv, (int)pairs);
   return hipGetLastError();
 }
 

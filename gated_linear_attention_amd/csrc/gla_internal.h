@@ -113,6 +113,11 @@ hipError_t launch_chunk_bf16_ws(const uint16_t *q, const uint16_t *k, const uint
                                 bool out_bf16, const FwdDims &d, const WorkItem *items,
                                 const int *n_items, int grid_items, const float *slots,
                                 hipStream_t stream);
+// The state pass (split sequences' pieces) for 128-dim keys on the same layout.
+hipError_t launch_chunk_bf16_ws_state(const uint16_t *k, const uint16_t *v, const float *g,
+                                      const FwdDims &d, const WorkItem *items, const int *n_items,
+                                      int grid_items, float *slots, float *slot_gamma,
+                                      hipStream_t stream);
 
 // The chunked forward after argument checks (gla_api.hip), and its workspace.
 // g is log_g [.., T, H], or with fixed_decay one log-decay per head [H]. rev
