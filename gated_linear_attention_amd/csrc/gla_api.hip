@@ -153,7 +153,7 @@ const char *gla_status_string(gla_status s) {
 size_t gla_fwd_chunked_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
                                       int chunk_size, int has_cu_seqlens, gla_dtype in_dtype) {
   if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !fwd_dims(dk, dv) ||
-      (chunk_size != 64 && chunk_size != 128) || !valid_dtype(in_dtype))
+      !supported_chunk(chunk_size) || !valid_dtype(in_dtype))
     return 0;
   return fwd_workspace(B, T, H, dk, dv, num_seqs, chunk_size, has_cu_seqlens != 0, in_dtype);
 }
@@ -174,7 +174,7 @@ gla_status fwd_validate(const void *q, const void *k, const void *v, const float
   if (has_cu ? (B != 1) : (num_seqs != B)) return GLA_ERR_INVALID_ARGUMENT;
   if ((long)B * T > INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
   if (!fwd_dims(dk, dv)) return GLA_ERR_UNSUPPORTED;
-  if (chunk_size != 64 && chunk_size != 128) return GLA_ERR_UNSUPPORTED;
+  if (!supported_chunk(chunk_size)) return GLA_ERR_UNSUPPORTED;
   if (!all_al16({q, k, v, o, S0, S_T, workspace}) || !all_al4({g, cu_seqlens}))
     return GLA_ERR_INVALID_ARGUMENT;
   const int N = num_seqs;
@@ -360,7 +360,7 @@ extern "C" {
 size_t gla_bwd_chunked_workspace_size(int B, int T, int H, int dk, int dv, int num_seqs,
                                       int chunk_size, int has_cu_seqlens, gla_dtype in_dtype) {
   if (B < 0 || T < 0 || H <= 0 || num_seqs < 0 || !bwd_dims(dk, dv) ||
-      (chunk_size != 64 && chunk_size != 128) || !valid_dtype(in_dtype))
+      !supported_chunk(chunk_size) || !valid_dtype(in_dtype))
     return 0;
   return bwd_layout(B, T, H, dk, dv, num_seqs, chunk_size, has_cu_seqlens != 0, in_dtype).total;
 }
@@ -379,7 +379,7 @@ gla_status gla_bwd_chunked(const void *q, const void *k, const void *v, const fl
   if (has_cu ? (B != 1) : (num_seqs != B)) return GLA_ERR_INVALID_ARGUMENT;
   if ((long)B * T > INT_MAX) return GLA_ERR_INVALID_ARGUMENT;
   if (!bwd_dims(DK, DV)) return GLA_ERR_UNSUPPORTED;
-  if (chunk_size != 64 && chunk_size != 128) return GLA_ERR_UNSUPPORTED;
+  if (!supported_chunk(chunk_size)) return GLA_ERR_UNSUPPORTED;
   if (!all_al16({q, k, v, dO, S0, dS_T, dq, dk, dv, dS0, workspace}) ||
       !all_al4({g, dg, cu_seqlens}))
     return GLA_ERR_INVALID_ARGUMENT;

@@ -78,13 +78,19 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 inline int round_up(long x, int m) { return (int)(((x + m - 1) / m) * m); }
 
-// The chunk the kernels run at. The bf16 matrix-core kernel tiles 64 tokens:
-// a 128-token chunk of the chunked form equals two 64-token chunks in exact
-// arithmetic (the state advance composes), and at 64 tokens the Q, K, V tiles
-// double-buffer in LDS while at 128 they do not; so chunk_size 128 runs as
-// 64-token chunks there. The fp32 kernel runs either size as asked.
+// Chunk sizes of the chunked form the calls accept (Laplace 3B on AWS
+// Trainium2: 128-token chunks in "Challenge 1", 256 discussed in "Challenge 3").
+inline bool supported_chunk(int c) { return c == 64 || c == 128 || c == 256; }
+
+// The chunk the kernels run at. A chunk of C tokens of the chunked form equals
+// C / C' consecutive chunks of C' tokens in exact arithmetic (the state
+// advance composes). The bf16 matrix-core kernel tiles 64 tokens, whose Q, K,
+// V tiles double-buffer in LDS (at 128 they do not), so it runs every chunk
+// size as 64-token chunks; the fp32 kernel runs 64 and 128 as asked and 256 as
+// two chunks of 128.
 inline int kernel_chunk(gla_dtype in_dtype, bool f32_kernel, int chunk_size) {
-  return in_dtype == GLA_BF16 && !f32_kernel ? 64 : chunk_size;
+  if (in_dtype == GLA_BF16 && !f32_kernel) return 64;
+  return chunk_size > 128 ? 128 : chunk_size;  // a 256-token chunk is two of 128
 }
 
 // State columns one workgroup of the forward owns (the column "slice"): 96 for

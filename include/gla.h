@@ -40,7 +40,7 @@
  *    treated the same way: g_t = 0 exactly. No decay product that spans a
  *    reset is formed, so a reset never turns into NaN; the backward returns
  *    dlog_g = 0 at a reset and no gradient crosses it.
- *  - Supported sizes: d_k, d_v in {64, 128}; chunk_size in {64, 128}. The
+ *  - Supported sizes: d_k, d_v in {64, 128}; chunk_size in {64, 128, 256}. The
  *    forward, the backward and the decode steps also take (d_k, d_v) =
  *    (96, 192), the head shape of Laplace 3B ("GLA mixer"). Anything else
  *    returns GLA_ERR_UNSUPPORTED.
@@ -97,8 +97,12 @@ const char *gla_status_string(gla_status s);
  *              same pointer as S0 (each state is read before it is written);
  *              any other overlap with an input is undefined.
  *   num_seqs   N (must equal B when cu_seqlens is NULL).
- *   chunk_size 64 or 128: the chunk length C of the chunked form. Results
- *              agree across chunk sizes up to rounding.
+ *   chunk_size 64, 128 or 256: the chunk length C of the chunked form
+ *              ("Challenge 1" chunks by 128 tokens; "Challenge 3" weighs
+ *              256). Results agree across chunk sizes up to rounding: a chunk
+ *              of C tokens equals consecutive shorter chunks in exact
+ *              arithmetic, and the kernels run bf16 inputs as 64-token chunks
+ *              and fp32 inputs as chunks of min(C, 128) tokens.
  *   in_dtype   GLA_BF16 (MFMA path, fp32 accumulation and fp32 state) or
  *              GLA_F32 (fp32 arithmetic throughout).
  *   workspace  device scratch of at least gla_fwd_chunked_workspace_size()

@@ -206,6 +206,12 @@ def pin_chunked(impl, seed=6, T=70, chunks=(1, 3, 16, 64, 70, 128)):
     return worst
 
 
+def pin_chunked_256(impl, seed=16):
+    """The 256-token chunk (Laplace 3B on AWS Trainium2, "Challenge 3") over 600
+    tokens: two whole chunks and a ragged tail of 88."""
+    return pin_chunked(impl, seed=seed, T=600, chunks=(256,))
+
+
 # -------------------------------------------------------------- invariants
 def pin_continuation(impl, seed=7, T=40, T1=17):
     q, k, v, lg, S0 = rand_inputs(seed, B=2, T=T, H=2, dk=4, dv=5)
@@ -254,6 +260,7 @@ ALL_PINS = {
     "geometric_scalar": pin_geometric_scalar,
     "reset": pin_reset,
     "chunked": pin_chunked,
+    "chunked_256": pin_chunked_256,
     "continuation": pin_continuation,
     "varlen": pin_varlen,
     "linearity": pin_linearity,

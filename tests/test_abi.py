@@ -67,6 +67,8 @@ def test_fwd_rejects_bad_arguments_before_launch():
     assert _fwd(dk=192, dv=96, **P) == _lib.GLA_ERR_UNSUPPORTED
     assert _fwd(dk=96, dv=192, B=0, N=0, **P) == _lib.GLA_OK  # the Laplace head shape is accepted
     assert _fwd(C=32, **P) == _lib.GLA_ERR_UNSUPPORTED
+    assert _fwd(C=512, **P) == _lib.GLA_ERR_UNSUPPORTED
+    assert _fwd(C=256, H=0, **P) == _lib.GLA_OK  # 256-token chunks are accepted
     assert _fwd(**{**P, "q": None}) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert _fwd(**{**P, "o": P["q"] + 64}) == _lib.GLA_ERR_INVALID_ARGUMENT  # o overlaps q
     assert _fwd(cu=FAKE + (5 << 30), B=2, N=2, **P) == _lib.GLA_ERR_INVALID_ARGUMENT
@@ -80,7 +82,7 @@ def test_fixed_decay_fwd_rejects_bad_arguments_before_launch():
              o=FAKE + (4 << 30), H=8)
     assert _fwd(True, B=-1, **P) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert _fwd(True, dk=96, **P) == _lib.GLA_ERR_UNSUPPORTED
-    assert _fwd(True, C=256, **P) == _lib.GLA_ERR_UNSUPPORTED
+    assert _fwd(True, C=512, **P) == _lib.GLA_ERR_UNSUPPORTED
     assert _fwd(True, **{**P, "g": None}) == _lib.GLA_ERR_INVALID_ARGUMENT
     # log_lambda holds H = 8 floats: an o that starts at its fifth overlaps it
     assert _fwd(True, **{**P, "o": P["g"] + 16}) == _lib.GLA_ERR_INVALID_ARGUMENT
@@ -145,7 +147,7 @@ def test_bwd_rejects_bad_arguments_before_launch():
     assert _bwd(ind=5, **P, **W) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert _bwd(N=2, **P, **W) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert _bwd(dkd=96, **P, **W) == _lib.GLA_ERR_UNSUPPORTED
-    assert _bwd(C=256, **P, **W) == _lib.GLA_ERR_UNSUPPORTED
+    assert _bwd(C=512, **P, **W) == _lib.GLA_ERR_UNSUPPORTED
     assert _bwd(**{**P, "dO": None}, **W) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert _bwd(**{**P, "dg": None}, **W) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert _bwd(**{**P, "dq": P["q"] + 64}, **W) == _lib.GLA_ERR_INVALID_ARGUMENT  # output on input

@@ -82,13 +82,13 @@ def test_bwd_bf16_shapes(dk, dv, T):
     check_bwd(*_inputs(_shape(dk, dv), 500 + T + dk + dv, B=2, T=T, H=2), "bf16", tight=1e-4)
 
 
-@pytest.mark.parametrize("C", [64, 128])
+@pytest.mark.parametrize("C", [64, 128, 256])
 def test_bwd_chunk_sizes(C):
     gu.say(f"bwd bf16 C={C}")
     check_bwd(*_inputs(_shape(128, 128), 600, B=2, T=333, H=2), "bf16", C=C, tight=1e-4)
 
 
-@pytest.mark.parametrize("C", [64, 128])
+@pytest.mark.parametrize("C", [64, 128, 256])
 def test_bwd_f32_tiny_workload(C):
     """The fp32 workload's shape (B=1, H=2, T=256, d=64), with upstream gradients."""
     gu.say(f"bwd fp32 tiny C={C}")

@@ -74,7 +74,7 @@ def check_full_size(name, tight):
 W = synth.WORKLOADS
 
 
-@pytest.mark.parametrize("C", [64, 128])
+@pytest.mark.parametrize("C", [64, 128, 256])
 def test_tiny_f32_workload(C):
     """B=1, H=2, T=256, d=64, fp32 inputs, S0 = 0."""
     gu.say(f"tiny fp32 workload C={C}")
@@ -84,7 +84,7 @@ def test_tiny_f32_workload(C):
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
 @pytest.mark.parametrize("T", [64, 300, 1])
-@pytest.mark.parametrize("C", [64, 128])
+@pytest.mark.parametrize("C", [64, 128, 256])
 def test_bf16_shapes(dk, dv, T, C):
     """Several tiles, a ragged tail chunk, a single token; nonzero S0."""
     gu.say(f"bf16 dk={dk} dv={dv} T={T} C={C}")
@@ -94,7 +94,7 @@ def test_bf16_shapes(dk, dv, T, C):
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
-@pytest.mark.parametrize("C", [64, 128])
+@pytest.mark.parametrize("C", [64, 128, 256])
 def test_f32_shapes(dk, dv, C):
     gu.say(f"f32 dk={dk} dv={dv} C={C}")
     w = synth.Workload("t", B=2, T=333, H=2, dk=dk, dv=dv, dtype="f32", gate_bias=2.0,

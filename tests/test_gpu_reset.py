@@ -34,12 +34,15 @@ def plant(lg, where, value=NEG_INF):
 
 def dense_resets(T, C):
     """Reset positions of a dense batch of 2 sequences x 3 heads: sequence 0,
-    head 0 at its first token, mid-chunk, on chunk boundaries of both chunk
-    sizes, twice in a row and on its last token; sequence 1, head 1 over a
-    whole chunk; head 2 none (heads are independent)."""
+    head 0 at its first token, mid-chunk, on chunk boundaries of every chunk
+    size, twice in a row and on its last token; sequence 1, head 1 over a
+    whole chunk (or to the end of the sequence); head 2 none (heads are
+    independent)."""
     w = [(0, 0, 0), (0, 37, 0), (0, 64, 0), (0, 128, 0), (0, 100, 0), (0, 101, 0),
          (0, T - 1, 0)]
-    w += [(1, t, 1) for t in range(C, 2 * C)]
+    if T > 256:
+        w += [(0, 256, 0)]
+    w += [(1, t, 1) for t in range(C, min(2 * C, T))]
     w += [(1, 5, 0)]
     return w
 
@@ -73,7 +76,7 @@ def check_fwd(q, k, v, lg, S0, cu, dtype, C, tight=None, alias=False):
 
 @pytest.mark.parametrize("value", [NEG_INF, -200.0, -1e30])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("C", [64, 128])
+@pytest.mark.parametrize("C", [64, 128, 256])
 def test_reset_forward_dense(C, dtype, value):
     gu.say(f"reset fwd dense C={C} {dtype} value={value}")
     T = 300
