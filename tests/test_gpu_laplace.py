@@ -91,13 +91,15 @@ def test_fixed_decay_equals_broadcast_gates(dk, dv, dtype, C):
     check(q, k, v, lg, S0, cu, dtype, C=C)
 
 
+@pytest.mark.parametrize("dk,dv", [(96, 192), (128, 128)])
 @pytest.mark.parametrize("C", [64, 128])
-def test_fixed_decay_varlen_split(C, monkeypatch):
+def test_fixed_decay_varlen_split(C, dk, dv, monkeypatch):
     """Packed sequences split into segments: the state pass sums the fixed
-    decays over each segment's own tokens only."""
-    gu.say(f"fixed decay varlen + split C={C}")
+    decays over each segment's own tokens only (96 x 192 heads on the
+    twelve-wavefront state pass, 128 x 128 on the K-and-V-only one)."""
+    gu.say(f"fixed decay varlen + split C={C} {dk}x{dv}")
     monkeypatch.setenv("GLA_SEG_LEN", "192" if C == 64 else "256")
-    w = synth.Workload("t", B=1, T=0, H=16, dk=96, dv=192, dtype="bf16", gate_bias=0.0,
+    w = synth.Workload("t", B=1, T=0, H=16, dk=dk, dv=dv, dtype="bf16", gate_bias=0.0,
                        s0_std=0.02, chunk=C, seed=36, fixed_decay=True)
     q, k, v, lg, S0, cu = synth.make_forward_inputs(w, lengths=[700, 0, 37, 321, 129, 1])
     lam = synth.fixed_log_decays(16)
