@@ -117,10 +117,26 @@ __global__ __launch_bounds__(256) void gate_scan_kernel(
   __shared__ float xs[2048];
   __shared__ unsigned char fs[2048];
 
-  // <dS_T, S_T>
+  // <dS_T, S_T> in 16-byte pieces (d_k d_v is a multiple of 1024), four a
+  // round with all loads issued first
+  const size_t n4 = mat / 4;
   float fro = 0.f;
-  if (dST_t)
-    for (size_t i = tid; i < mat; i += 256) fro += dST_t[base + i] * ST_t[base + i];
+  if (dST_t) {
+    const f32x4 *a4 = reinterpret_cast<const f32x4 *>(dST_t + base);
+    const f32x4 *b4 = reinterpret_cast<const f32x4 *>(ST_t + base);
+    for (size_t i0 = tid; i0 < n4; i0 += 1024) {
+      f32x4 a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const size_t i = i0 + 256 * u;
+        a[u] = i < n4 ? a4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+        b[u] = i < n4 ? b4[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        fro += (a[u][0] * b[u][0] + a[u][1] * b[u][1]) + (a[u][2] * b[u][2] + a[u][3] * b[u][3]);
+    }
+  }
   red[tid] = fro;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
@@ -137,7 +153,17 @@ __global__ __launch_bounds__(256) void gate_scan_kernel(
       const float l0 = lg[(size_t)s * H + h];
       g0 = is_reset(l0) ? 0.f : fast_exp2(l0 * kLog2e);
     }
-    for (size_t i = tid; i < mat; i += 256) dS0[base + i] = g0 * A0[base + i];
+    const f32x4 *a4 = reinterpret_cast<const f32x4 *>(A0 + base);
+    f32x4 *d4 = reinterpret_cast<f32x4 *>(dS0 + base);
+    for (size_t i0 = tid; i0 < n4; i0 += 1024) {
+      f32x4 a[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        a[u] = i0 + 256 * u < n4 ? a4[i0 + 256 * u] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + 256 * u < n4) d4[i0 + 256 * u] = g0 * a[u];
+    }
   }
 
   // tiles of 8 tokens per thread, last tile first; carry = the running sum
@@ -240,6 +266,7 @@ hipError_t launch_dgate(const void *q, const void *k, float *dq, float *dk, cons
                         bool in_bf16, const float *dq_part, const float *dk_part, int n_part,
                         hipStream_t stream, const float *dq2, const float *dk2) {
   if ((dq2 == nullptr) != (dk2 == nullptr) || (dq2 && n_part != 0)) return hipErrorInvalidValue;
+  if (((long)DK * DV) % 1024) return hipErrorInvalidValue;  // the scan's 16-byte state pieces
   const long rows = (long)(cu ? T : (long)N * T) * H;  // token rows of the batch
   if (rows > 0 && n_part == 0) {
     const dim3 grid((unsigned)((rows + 7) / 8)), block(256);
