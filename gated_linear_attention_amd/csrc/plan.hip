@@ -15,6 +15,8 @@
 // before it plus the segment's own contribution from a zero state (Laplace 3B
 // on AWS Trainium2, "Challenge 1": the state advances by the decay compounded
 // over a chunk; a segment is a run of chunks).
+#include <algorithm>
+
 #include "gla_common.h"
 #include "gla_internal.h"
 
@@ -184,6 +186,65 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
   }
 }
 
+// The same plan for a dense batch (no cu_seqlens) with at least two segments
+// per sequence: every sequence has T tokens, so every sequence has the same
+// segments and the plan is a closed form, written by one thread per
+// (sequence, segment) without the histogram and scans. Full segments come
+// first (longest first, as the counting sort orders them), then the last
+// segments; slots, state items and split sequences in sequence order, as in
+// plan_kernel.
+__global__ __launch_bounds__(256) void plan_dense_kernel(int N, int T, int L, int Ls, int n_sub,
+                                                         int s0_copy,
+                                                         PlanHeader *__restrict__ hdr,
+                                                         WorkItem *__restrict__ items,
+                                                         WorkItem *__restrict__ sitems,
+                                                         MultiSeq *__restrict__ multi) {
+  const int nseg = (T + L - 1) / L;  // >= 2
+  const int per_seq_slots = (nseg - 1) * n_sub + 1;
+  const long total = (long)N * nseg;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    hdr->n_items = (int)total;
+    hdr->n_state_items = N * (nseg - 1) * n_sub;
+    hdr->n_multi = N;
+  }
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (long)gridDim.x * blockDim.x) {
+    const int n = (int)(i / nseg), s = (int)(i % nseg);
+    const int start = n * T;
+    const int slot_base = n * per_seq_slots;
+    const int tb = start + s * L;
+    const int te = min(tb + L, start + T);
+    WorkItem it;
+    it.tok_begin = tb;
+    it.tok_end = te;
+    it.seq = n;
+    it.state_in = (s > 0 || s0_copy) ? slot_base + s * n_sub : -1;
+    it.state_out = (s == nseg - 1) ? -1 : kNoStateOut;
+    it.seq_begin = start;
+    it.seq_end = start + T;
+    it.pad = 0;
+    items[s < nseg - 1 ? n * (nseg - 1) + s : N * (nseg - 1) + n] = it;
+    if (s < nseg - 1) {
+      for (int j = 0; j < n_sub; ++j) {
+        WorkItem si = it;
+        si.tok_begin = tb + j * Ls;
+        si.tok_end = min(tb + (j + 1) * Ls, te);
+        si.state_in = -1;
+        si.state_out = slot_base + s * n_sub + j + 1;
+        sitems[(n * (nseg - 1) + s) * n_sub + j] = si;
+      }
+    }
+    if (s == 0) {
+      MultiSeq m;
+      m.seq = n;
+      m.slot_base = slot_base;
+      m.nslot = per_seq_slots;
+      m.pad = 0;
+      multi[n] = m;
+    }
+  }
+}
+
 // Chain the state pieces: from S0 (or 0) as the state before piece 0, for b >= 1
 //   slot[base+b] = exp(gamma[base+b]) * slot[base+b-1] + slot[base+b]
 // where the state pass left piece b-1's local state and total log-decay in
@@ -235,6 +296,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 hipError_t launch_plan(const int32_t *cu_seqlens, const FwdDims &d, const PlanLayout &lay,
                        bool s0_copy, void *workspace, hipStream_t stream) {
   char *ws = static_cast<char *>(workspace);
+  if (!cu_seqlens) {  // dense: the closed-form plan (make_plan plans only split batches)
+    const long total = (long)d.N * ((d.T + lay.seg_len - 1) / lay.seg_len);
+    const int blocks = (int)std::min<long>((total + 255) / 256, 1024);
+    hipLaunchKernelGGL(plan_dense_kernel, dim3(blocks), dim3(256), 0, stream, d.N, d.T,
+                       lay.seg_len, lay.sub_len, lay.n_sub, (int)s0_copy,
+                       reinterpret_cast<PlanHeader *>(ws + lay.off_header),
+                       reinterpret_cast<WorkItem *>(ws + lay.off_items),
+                       reinterpret_cast<WorkItem *>(ws + lay.off_state_items),
+                       reinterpret_cast<MultiSeq *>(ws + lay.off_multi));
+    return hipGetLastError();
+  }
   const int nb = lay.seg_len / d.C + 1;
   const size_t lds = sizeof(int) * (3 * nb + 32);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), lds, stream, cu_seqlens, d.N, d.T,
