@@ -298,8 +298,8 @@ hipError_t launch_plan(const int32_t *cu_seqlens, const FwdDims &d, const PlanLa
   char *ws = static_cast<char *>(workspace);
   if (!cu_seqlens) {  // dense: the closed-form plan (make_plan plans only split batches)
     const long total = (long)d.N * ((d.T + lay.seg_len - 1) / lay.seg_len);
-    if (total == 0) return hipSuccess;
-    const int blocks = (int)std::min<long>((total + 255) / 256, 1024);
+    // at least one block: it writes the header (an empty plan has no items)
+    const int blocks = (int)std::max<long>(1, std::min<long>((total + 255) / 256, 1024));
     hipLaunchKernelGGL(plan_dense_kernel, dim3(blocks), dim3(256), 0, stream, d.N, d.T,
                        lay.seg_len, lay.sub_len, lay.n_sub, (int)s0_copy,
                        reinterpret_cast<PlanHeader *>(ws + lay.off_header),
