@@ -199,7 +199,15 @@ __global__ __launch_bounds__(256) void plan_dense_kernel(int N, int T, int L, in
                                                          WorkItem *__restrict__ items,
                                                          WorkItem *__restrict__ sitems,
                                                          MultiSeq *__restrict__ multi) {
-  const int nseg = (T + L - 1) / L;  // >= 2
+  const int nseg = (T + L - 1) / L;  // >= 2 where the host plans
+  if (nseg < 2) {  // nothing to split: an empty plan
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      hdr->n_items = 0;
+      hdr->n_state_items = 0;
+      hdr->n_multi = 0;
+    }
+    return;
+  }
   const int per_seq_slots = (nseg - 1) * n_sub + 1;
   const long total = (long)N * nseg;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
