@@ -304,8 +304,9 @@ def bench_backward(args):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": alg_bytes,
-                     "note": "whole gla_bwd_chunked call: three chunked-forward runs plus "
-                             "reversal, transpose and gate-gradient kernels"},
+                     "note": "whole gla_bwd_chunked call: three chunked-forward runs on "
+                             "chunk_bf16_ws_kernel (dq with q.dq partials, dv and dk in "
+                             "reversed time, dk with k.dk partials) and the gate scan"},
     }
 
 
