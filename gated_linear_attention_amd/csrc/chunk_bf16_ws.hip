@@ -640,6 +640,7 @@ chunk_bf16_ws_state_kernel(const uint16_t *__restrict__ k, const uint16_t *__res
   WsStager<REV, false> sg;
   float lsum = 0.f;  // wavefront 4: the item's total log-decay
   if (!state_wave) {
+    // (no queries: k stands in for the unused q pointer)
     sg.init(k, k, v, lg, t0, H, gts, h, DV, col0, w.seq_begin, w.seq_end);
     sg.load(t0, w.tok_end, iw, lane);
     sg.commit(s, 0, iw, lane);
