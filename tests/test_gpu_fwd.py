@@ -191,6 +191,32 @@ def test_forced_state_pieces(seg, sub, C, varlen, monkeypatch):
     check(*synth.make_forward_inputs(w, lengths=lengths), "bf16", C=C, tight=2e-5)
 
 
+@pytest.mark.parametrize("dtype,dk,dv,T", [("bf16", 128, 128, 700), ("bf16", 64, 64, 640),
+                                          ("f32", 64, 64, 500)])
+@pytest.mark.parametrize("alias", [False, True])
+def test_dense_plan_equals_packed_plan(dtype, dk, dv, T, alias, monkeypatch):
+    """A dense batch is planned in closed form, a packed one by the counting
+    sort: the same sequences with the same segment length and pieces, once
+    dense and once as cu_seqlens of equal lengths, give the same outputs and
+    final states bit for bit (the item order differs, the arithmetic of an
+    item does not)."""
+    gu.say(f"dense plan vs packed plan {dtype} {dk}x{dv} T={T} alias={alias}")
+    monkeypatch.setenv("GLA_SEG_LEN", "256")
+    monkeypatch.setenv("GLA_STATE_SUB", "2")
+    w = synth.Workload("t", B=3, T=T, H=2, dk=dk, dv=dv, dtype=dtype, gate_bias=3.0,
+                       s0_std=0.03, chunk=64, seed=37)
+    q, k, v, lg, S0, cu = synth.make_forward_inputs(w)
+    assert cu is None
+    o_d, S_d = run_gpu(q, k, v, lg, S0, None, dtype, alias=alias)
+    B = q.shape[0]
+    flat = lambda x: x.reshape((1, B * T) + x.shape[2:])
+    cu_p = (np.arange(B + 1) * T).astype(np.int32)
+    o_p, S_p = run_gpu(flat(q), flat(k), flat(v), flat(lg), S0, cu_p, dtype, alias=alias)
+    np.testing.assert_array_equal(o_d.reshape(o_p.shape), o_p)
+    np.testing.assert_array_equal(S_d, S_p)
+    check(q, k, v, lg, S0, None, dtype, tight=2e-5 if dtype == "bf16" else None)
+
+
 def test_forced_state_pieces_f32(monkeypatch):
     gu.say("state pieces fp32")
     monkeypatch.setenv("GLA_SEG_LEN", "256")
