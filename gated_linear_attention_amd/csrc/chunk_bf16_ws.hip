@@ -353,14 +353,27 @@ __global__ __launch_bounds__(512) void chunk_bf16_ws_kernel(
 
   const int t0 = w.tok_begin;
   const int NC = (w.tok_end - t0 + C - 1) / C;  // chunks of this run
-  WsStager<REV> sg;
+  // BAL: wavefront 4 (row block 0, the lightest attention term) also copies
+  // the tile share of wavefront 7 (row block 3, the heaviest), so that the
+  // SIMDs' loads even out; the forward only (the backward's reversed and
+  // dot-product runs measured slower with it)
+  constexpr bool BAL = !REV && !DOT;
+  WsStager<REV> sg, sg2;
   if (!state_wave) {
     // chunk 0 and the gates of chunks 0, 1 straight into LDS; chunk 1 and the
     // gates of chunk 2 staged for the first step
     sg.init(q, k, v, lg, t0, H, gts, h, DV, col0, w.seq_begin, w.seq_end);
-    sg.load(t0, w.tok_end, iw, lane);
-    sg.commit(s, 0, iw, lane);
-    sg.load(t0 + C, w.tok_end, iw, lane);
+    if (!BAL || iw != 3) {
+      sg.load(t0, w.tok_end, iw, lane);
+      sg.commit(s, 0, iw, lane);
+      sg.load(t0 + C, w.tok_end, iw, lane);
+    }
+    if (BAL && iw == 0) {
+      sg2.init(q, k, v, lg, t0, H, gts, h, DV, col0, w.seq_begin, w.seq_end);
+      sg2.load(t0, w.tok_end, 3, lane);
+      sg2.commit(s, 0, 3, lane);
+      sg2.load(t0 + C, w.tok_end, 3, lane);
+    }
     if (iw == 3) {
       sg.gate_load(t0, w.tok_end, lane);
       sg.gate_commit(s, 0, lane);
@@ -559,9 +572,11 @@ __global__ __launch_bounds__(512) void chunk_bf16_ws_kernel(
     // ---- chunk ci + 1 (loaded last step) into the other stage, the gates
     // of chunk ci + 2 into the ring; then load chunk ci + 2 and the gates of
     // chunk ci + 3
-    sg.commit(s, st ^ 1, iw, lane);
+    if (!BAL || iw != 3) sg.commit(s, st ^ 1, iw, lane);
+    if (BAL && iw == 0) sg2.commit(s, st ^ 1, 3, lane);
     if (iw == 3) sg.gate_commit(s, (ci + 2) % 3, lane);
-    sg.load(tc + 2 * C, w.tok_end, iw, lane);
+    if (!BAL || iw != 3) sg.load(tc + 2 * C, w.tok_end, iw, lane);
+    if (BAL && iw == 0) sg2.load(tc + 2 * C, w.tok_end, 3, lane);
     if (iw == 3) sg.gate_load(tc + 3 * C, w.tok_end, lane);
 
     if (cur) {
