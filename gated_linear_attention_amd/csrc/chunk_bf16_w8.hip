@@ -361,8 +361,11 @@ __global__ __launch_bounds__(128 * NCG) void chunk_bf16_w8_kernel(
   // score tiles: tile `wave` (with four column groups every wavefront, and
   // tiles 8 and 9 also for wavefronts 4 and 5; with six, wavefronts 0 .. 9),
   // lower triangle of 16x16 tiles, row-major
-  const bool has_tile = NCG == 4 || wave < 10;
-  const int ti1 = tile_ti(has_tile ? wave : 0), tj1 = tile_tj(has_tile ? wave : 0);
+  // six column groups: the ten tiles on waves 0-3 and 6-11, so that the
+  // loading waves 4 and 5 (SIMDs 0 and 1) carry no tile
+  const bool has_tile = NCG == 4 || wave < 4 || wave >= 6;
+  const int tidx = NCG == 4 || wave < 4 ? wave : wave - 2;
+  const int ti1 = tile_ti(has_tile ? tidx : 0), tj1 = tile_tj(has_tile ? tidx : 0);
   const bool two_tiles = NCG == 4 && (wave == 4 || wave == 5);
   const int ti2 = 3, tj2 = wave - 2;
 
