@@ -355,9 +355,10 @@ def bench_decode(args):
     pool = torch.empty((P, H, dk, dv), dtype=torch.float32, device=dev).normal_(0.0, 0.02)
     perm = np.random.default_rng(D["state_seed"]).permutation(P)[:N].astype(np.int32)
     slots = torch.from_numpy(perm).to(dev)
-    # the slot-sorted streaming order: one small launch per step, shared by
+    # the streaming order over the pool (4 MiB blocks of entries at a stride,
+    # slot order within a block): one small launch per step, shared by
     # every layer of the step (timed on its own below)
-    order = gla.slot_order(slots, P)
+    order = gla.slot_order(slots, P, H * dk * dv * 4)
 
     def step_slots(i):
         gla.decode_step_slots(qs[i % steps], ks[i % steps], vs[i % steps], gs[i % steps], pool,
@@ -375,7 +376,8 @@ def bench_decode(args):
     ord_buf = torch.empty_like(order)
     _, kern_ms_o = time_launches(
         lambda i: gla._lib.check(gla._lib.load().gla_decode_slot_order(
-            slots.data_ptr(), N, P, ord_buf.data_ptr(), stream.cuda_stream), "slot order"),
+            slots.data_ptr(), N, P, H * dk * dv * 4, ord_buf.data_ptr(), stream.cuda_stream),
+            "slot order"),
         steps, stream)
     return {
         "metric": "decode-step state HBM GB/s",
@@ -710,7 +712,7 @@ def bench_decode_layers(args, layers=24, batches=(20, 1280)):
         z = [torch.empty((N, H, dv), dtype=bf, device=dev) for _ in range(layers)]
 
         def step(i=0):
-            order = gla.slot_order(slots, N)  # once per step, for every layer
+            order = gla.slot_order(slots, N, H * dk * dv * 4)  # once per step, for every layer
             for l in range(layers):
                 q, k, v, g = qkv[l]
                 gla.decode_step_slots(q, k, v, lg, pools[l], slots, o=o[l], order=order)
@@ -737,7 +739,7 @@ def bench_decode_layers(args, layers=24, batches=(20, 1280)):
         replay = (time.perf_counter() - t0) / steps
         # the same step with the fused decode + epilogue: one kernel per layer
         def step_fused(i=0):
-            order = gla.slot_order(slots, N)
+            order = gla.slot_order(slots, N, H * dk * dv * 4)
             for l in range(layers):
                 q, k, v, g = qkv[l]
                 gla.decode_mixer(q, k, v, lg, pools[l], g, ta, rms_w, 1e-6, slots=slots, z=z[l],

@@ -9,7 +9,7 @@ device memory and the current HIP stream.
     o, S_T = fwd_chunked_noalloc(q, k, v, g, S0=None, cu_seqlens=None)  # no workspace
     dq, dk, dv, dg, dS0 = bwd_chunked(q, k, v, g, dO, S0=None, cu_seqlens=None, dS_T=None)
     o = decode_step(q, k, v, g, S)          # S updated in place
-    order = slot_order(slots, P)            # once per step: the slot-sorted streaming order
+    order = slot_order(slots, P, H * dk * dv * 4)  # once per step: the pool's streaming order
     o = decode_step_slots(q, k, v, g, S_pool, slots, order=order)   # S_pool[slots] in place
     z = mixer_epilogue(o, q, k, v, g_out, a, rms_w, eps)  # self-augmentation, RMSNorm, SiLU gate
     z = decode_mixer(q, k, v, g, S, g_out, a, rms_w, eps, slots=None, order=None)  # fused
@@ -227,19 +227,22 @@ def decode_step(q, k, v, g, S, out_dtype=None, o=None):
     return o
 
 
-def slot_order(slots, P):
-    """The slot-sorted streaming order (int32 [2, N] on the device: the
-    requests by ascending slot, padded lanes last, then their slots) of a
-    serving batch whose requests use pool entries slots (int32 [N]) of a
-    P-entry pool: computed on the GPU, once per step, and passed to every
-    layer's decode_step_slots / decode_mixer."""
+def slot_order(slots, P, slot_bytes=0):
+    """The streaming order (int32 [2, N] on the device: the requests in pool
+    order, padded lanes last, then their slots) of a serving batch whose
+    requests use pool entries slots (int32 [N]) of a P-entry pool whose
+    entries are slot_bytes each (H * dk * dv * 4; 0 for plain slot order):
+    computed on the GPU, once per step, and passed to every layer's
+    decode_step_slots / decode_mixer."""
     torch = _torch()
     lib = _lib.load()
     _require(slots, "slots", torch.int32, slots.device, align=4)
+    if slot_bytes < 0:
+        raise ValueError("slot_bytes must be >= 0")
     N = slots.numel()
     order = torch.empty((2, N), dtype=torch.int32, device=slots.device)
     stream = torch.cuda.current_stream(slots.device).cuda_stream
-    st = lib.gla_decode_slot_order(_ptr(slots), N, int(P), _ptr(order), stream)
+    st = lib.gla_decode_slot_order(_ptr(slots), N, int(P), int(slot_bytes), _ptr(order), stream)
     _lib.check(st, "gla_decode_slot_order")
     return order
 

@@ -58,7 +58,7 @@ def load():
     lib.gla_decode_step_slots.restype = i
     lib.gla_mixer_epilogue.argtypes = [vp] * 7 + [ctypes.c_float, vp] + [i] * 4 + [i, i, i, vp]
     lib.gla_mixer_epilogue.restype = i
-    lib.gla_decode_slot_order.argtypes = [vp, i, i, vp, vp]
+    lib.gla_decode_slot_order.argtypes = [vp, i, i, ctypes.c_size_t, vp, vp]
     lib.gla_decode_slot_order.restype = i
     lib.gla_decode_mixer.argtypes = ([vp] * 7 + [i] + [vp] * 3 + [ctypes.c_float, vp] + [i] * 4
                                      + [i, i, vp])

@@ -28,8 +28,9 @@
 // sorted 481 us; groups of four consecutive requests, the groups at a stride
 // of three, 448-454 us; 96 x 192 heads, 1.125 MiB a request: launch order
 // fastest, 538 us, groups of four 553 us). So position j serves request
-// map(j): the slot-sorted order that gla_decode_slot_order writes, when the
-// caller passes one, and for a dense batch whose requests tile 4 MiB exactly,
+// map(j): the order that gla_decode_slot_order writes, when the caller passes
+// one (the pool's 4 MiB blocks of entries at the same stride, slot order
+// within a block), and for a dense batch whose requests tile 4 MiB exactly,
 // groups of 4 MiB at a stride coprime with their count (a permutation for
 // every N); otherwise launch order.
 #include <algorithm>
@@ -40,21 +41,31 @@
 
 namespace gla {
 
+// The stride at which groups are visited: the first of 3, 5, 7, ... coprime
+// with the group count (1, i.e. in place, below three groups or if none is).
+static int group_stride(int ng) {
+  if (ng < 3) return 1;
+  for (int a : {3, 5, 7, 11, 13, 17, 19, 23})
+    if (std::gcd(a, ng) == 1) return a;
+  return 1;
+}
+
+// States per 4 MiB group: only where a request's (or pool entry's) states tile
+// 4 MiB exactly (96 x 192 heads, 1.125 MiB a request, stream fastest in launch
+// order); 0 otherwise.
+static int group_size(long bytes_per_state) {
+  const long group = 4l << 20;
+  if (bytes_per_state <= 0 || bytes_per_state > group || group % bytes_per_state) return 0;
+  return (int)(group / bytes_per_state);
+}
+
 ReqMap make_req_map(const int32_t *order, int n, long bytes_per_request) {
   ReqMap m{order, n, 1, 0, 1};
-  // groups of whole 4 MiB: only where the requests' states tile 4 MiB exactly
-  // (96 x 192 heads, 1.125 MiB a request, stream fastest in launch order)
-  const long group = 4l << 20;
-  if (order || n <= 0 || bytes_per_request <= 0 || group % bytes_per_request) return m;
-  m.gs = (int)(group / bytes_per_request);
+  const int gs = group_size(bytes_per_request);
+  if (order || n <= 0 || gs == 0) return m;
+  m.gs = gs;
   m.ng = n / m.gs;
-  for (int a : {3, 5, 7, 11, 13, 17, 19, 23}) {
-    if (std::gcd(a, m.ng) == 1) {
-      m.stride = a;
-      break;
-    }
-  }
-  if (m.ng < 3) m.stride = 1;
+  m.stride = group_stride(m.ng);
   return m;
 }
 
@@ -457,18 +468,33 @@ hipError_t launch_decode_mixer(const MixerArgs &m_in, int dk, int dv, bool in_bf
   return hipErrorInvalidValue;
 }
 
-// The slot-sorted processing order for gla_decode_step_slots and
-// gla_decode_mixer (order [2, N]: the requests, then their slots, so that a
-// decode workgroup reads its slot without waiting for its request index):
-// a counting sort of the requests by slot in one workgroup,
-// with a counter per pool entry and one for the padded lanes (slots outside
-// [0, P)), which go last. Requests on the same slot (a caller error: their
-// updates race) are placed in any order; the result is a permutation of
-// 0 .. N-1 for every input.
+// The processing order for gla_decode_step_slots and gla_decode_mixer (order
+// [2, N]: the requests, then their slots, so that a decode workgroup reads its
+// slot without waiting for its request index): a counting sort of the
+// requests by the key of their slot in one workgroup, with a counter per pool
+// entry and one for the padded lanes (slots outside [0, P)), which go last.
+// The key streams the pool the way the dense step streams a batch: the pool
+// in blocks of gs entries (4 MiB of states), block b at rank b * s^-1 mod nb
+// so that consecutive ranks are s blocks apart, slot order within a block,
+// and the slots past the last whole block after every block, in slot order
+// (gs = 0: slot order throughout). 1,280 requests on random slots of a
+// 2,048-entry pool of 1 MiB states: 471 us against 478 us per step in plain
+// slot order. The key is a permutation of 0 .. P-1. Requests on the same slot
+// (a caller error: their updates race) are placed in any order; the result is
+// a permutation of 0 .. N-1 for every input.
 constexpr int kOrderThreads = 1024;
 
+struct OrderKey {
+  int gs, nb, inv;  // entries per block, whole blocks, inverse of the stride mod nb
+  __device__ __forceinline__ int operator()(int sl) const {
+    if (gs == 0 || sl >= gs * nb) return sl;
+    const int b = sl / gs;
+    return (int)(((long)b * inv) % nb) * gs + sl % gs;
+  }
+};
+
 __global__ __launch_bounds__(kOrderThreads) void slot_order_kernel(const int32_t *__restrict__ slots,
-                                                                   int N, int P,
+                                                                   int N, int P, OrderKey key,
                                                                    int32_t *__restrict__ order) {
   extern __shared__ uint32_t cnt[];  // P + 1 counters
   __shared__ uint32_t wsum[kOrderThreads / 64];
@@ -478,7 +504,7 @@ __global__ __launch_bounds__(kOrderThreads) void slot_order_kernel(const int32_t
   __syncthreads();
   for (int n = t; n < N; n += kOrderThreads) {
     const int sl = slots[n];
-    atomicAdd(&cnt[sl >= 0 && sl < P ? sl : P], 1u);
+    atomicAdd(&cnt[sl >= 0 && sl < P ? key(sl) : P], 1u);
   }
   __syncthreads();
   // exclusive prefix sum over the K counters: each thread a run of consecutive
@@ -506,19 +532,30 @@ __global__ __launch_bounds__(kOrderThreads) void slot_order_kernel(const int32_t
   __syncthreads();
   for (int n = t; n < N; n += kOrderThreads) {
     const int sl = slots[n];
-    const uint32_t pos = atomicAdd(&cnt[sl >= 0 && sl < P ? sl : P], 1u);
+    const uint32_t pos = atomicAdd(&cnt[sl >= 0 && sl < P ? key(sl) : P], 1u);
     order[pos] = n;
     order[N + pos] = sl;
   }
 }
 
-hipError_t launch_slot_order(const int32_t *slots, int N, int P, int32_t *order,
+hipError_t launch_slot_order(const int32_t *slots, int N, int P, long slot_bytes, int32_t *order,
                              hipStream_t stream) {
   if (N == 0) return hipSuccess;
   if (P < 0 || P > kMaxOrderPool) return hipErrorInvalidValue;
+  OrderKey key{group_size(slot_bytes), 0, 0};
+  if (key.gs > 0) {
+    key.nb = P / key.gs;
+    const int s = group_stride(key.nb);
+    for (int a = 1; s > 1 && a < key.nb; ++a)  // s^-1 mod nb (s and nb coprime)
+      if ((long)s * a % key.nb == 1) {
+        key.inv = a;
+        break;
+      }
+    if (key.inv == 0) key = OrderKey{0, 0, 0};  // fewer than three blocks: slot order
+  }
   const size_t lds = (size_t)(P + 1) * sizeof(uint32_t);
   hipLaunchKernelGGL(slot_order_kernel, dim3(1), dim3(kOrderThreads), lds, stream, slots, N, P,
-                     order);
+                     key, order);
   return hipGetLastError();
 }
 

@@ -486,15 +486,17 @@ gla_status gla_decode_step(const void *q, const void *k, const void *v, const fl
   return err == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
-gla_status gla_decode_slot_order(const int32_t *slots, int N, int P, int32_t *order,
-                                 void *stream_) {
+gla_status gla_decode_slot_order(const int32_t *slots, int N, int P, size_t slot_bytes,
+                                 int32_t *order, void *stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (N < 0 || P < 0) return GLA_ERR_INVALID_ARGUMENT;
   if (P > kMaxOrderPool) return GLA_ERR_UNSUPPORTED;
   if (N == 0) return GLA_OK;
   if (!slots || !order || !all_al4({slots, order})) return GLA_ERR_INVALID_ARGUMENT;
   if (overlaps(order, (size_t)N * 8, slots, (size_t)N * 4)) return GLA_ERR_INVALID_ARGUMENT;
-  return launch_slot_order(slots, N, P, order, stream) == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+  // entries above 4 MiB form no blocks (slot order); the clamp keeps the size a long
+  const long sb = slot_bytes > ((size_t)1 << 40) ? 0 : (long)slot_bytes;
+  return launch_slot_order(slots, N, P, sb, order, stream) == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
 gla_status gla_decode_step_slots(const void *q, const void *k, const void *v, const float *g,

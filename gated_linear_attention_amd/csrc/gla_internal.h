@@ -69,10 +69,10 @@ ReqMap make_req_map(const int32_t *order, int n, long bytes_per_request);
 
 // The largest pool gla_decode_slot_order sorts (one LDS counter per entry).
 constexpr int kMaxOrderPool = 32768;
-hipError_t launch_slot_order(const int32_t *slots, int N, int P, int32_t *order,
+hipError_t launch_slot_order(const int32_t *slots, int N, int P, long slot_bytes, int32_t *order,
                              hipStream_t stream);
 
-// order: the slot-sorted request order (with slots only), or null.
+// order: the pool-order request order (with slots only), or null.
 hipError_t launch_decode(const void *q, const void *k, const void *v, const float *g, float *S,
                          void *o, int N, int H, int dk, int dv, bool in_bf16, bool out_bf16,
                          const int32_t *slots, const int32_t *order, int P, int n_cu,

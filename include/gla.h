@@ -235,7 +235,7 @@ gla_status gla_decode_step(const void *q, const void *k, const void *v, const fl
  *          requests' states are streamed, as gla_decode_slot_order writes it
  *          for these slots (row 0 the requests, row 1 their slots, which the
  *          step then reads in place of slots[]). The results do not depend
- *          on it; the time does: states streamed in slot order run near the
+ *          on it; the time does: states streamed in that order run near the
  *          dense step's rate, states in a random slot order about 6% slower.
  *          Entries of row 0 outside [0, N) are skipped; anything but a
  *          permutation of 0 .. N-1 there leaves outputs unwritten or updates
@@ -251,15 +251,22 @@ gla_status gla_decode_step_slots(const void *q, const void *k, const void *v, co
  * The streaming order for a serving batch (Laplace 3B on AWS Trainium2,
  * "Inference optimization": the engine decodes a batch of sequences whose
  * states sit in fixed pool slots): order[0][0 .. N-1] = the requests 0 .. N-1
- * sorted by slots[n] ascending, padded lanes (slots outside [0, P)) last, and
- * order[1][i] = slots[order[0][i]]. Every layer of a step uses the same
- * slots, so one call per step serves all of them. One workgroup; device
- * arrays slots [N] and order [2, N] (must not overlap). P <= 32768, else
- * GLA_ERR_UNSUPPORTED (pass order = NULL to the decode calls instead).
- * Requests sharing a slot are ordered arbitrarily.
+ * sorted by the pool position of their slot, padded lanes (slots outside
+ * [0, P)) last, and order[1][i] = slots[order[0][i]]. slot_bytes is the size
+ * of one pool entry (H * dk * dv * 4). Where it divides 4 MiB and the pool
+ * holds at least three whole 4 MiB blocks of entries, the pool is streamed
+ * the way the dense decode step streams a batch: block by block, consecutive
+ * blocks in the order s apart (block b at rank b * s^-1 mod the block count,
+ * s the first of 3, 5, 7, ... coprime with it), slot order within a block,
+ * and the entries past the last whole block after all blocks; otherwise
+ * (slot_bytes 0, other sizes, small pools) plain ascending slot order. Every
+ * layer of a step uses the same slots, so one call per step serves all of
+ * them. One workgroup; device arrays slots [N] and order [2, N] (must not
+ * overlap). P <= 32768, else GLA_ERR_UNSUPPORTED (pass order = NULL to the
+ * decode calls instead). Requests sharing a slot are ordered arbitrarily.
  */
-gla_status gla_decode_slot_order(const int32_t *slots, int N, int P, int32_t *order,
-                                 void *stream);
+gla_status gla_decode_slot_order(const int32_t *slots, int N, int P, size_t slot_bytes,
+                                 int32_t *order, void *stream);
 
 /*
  * Token-mixer epilogue around the readout (Laplace 3B on AWS Trainium2,

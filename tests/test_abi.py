@@ -189,7 +189,7 @@ def test_slot_order_rejects_bad_arguments_before_launch():
     lib = _lib.load()
     G = 1 << 30
     S, O = FAKE, FAKE + G
-    call = lambda s=S, n=4, P=8, o=O: lib.gla_decode_slot_order(s, n, P, o, None)
+    call = lambda s=S, n=4, P=8, o=O, b=1 << 20: lib.gla_decode_slot_order(s, n, P, b, o, None)
     assert call(n=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call(P=-1) == _lib.GLA_ERR_INVALID_ARGUMENT
     assert call(P=32769) == _lib.GLA_ERR_UNSUPPORTED   # one LDS counter per pool entry

@@ -7,14 +7,22 @@ the dense step streams its requests in groups. The order changes which
 workgroup serves which request, never the arithmetic of a request, so:
 
 * gla_decode_slot_order returns a permutation of 0 .. N-1 that lists the
-  valid slots ascending (unique for distinct slots) and the padded lanes
-  last, and beside it each position's slot;
+  valid slots in the pool's streaming order (unique for distinct slots) and
+  the padded lanes last, and beside it each position's slot. The streaming
+  order, as the header states it: where an entry's size divides 4 MiB and
+  the pool holds three or more whole 4 MiB blocks, the blocks in the
+  sequence 0, s, 2s, ... (mod the block count; s the first of 3, 5, 7, ...
+  coprime with it), slots ascending within a block, then the entries past
+  the last whole block ascending; otherwise slots ascending. The test walks
+  that block sequence itself (no modular inverse);
 * a step with the order gives bit for bit the outputs and pool of the same
   step without it (slot decode and the fused decode + epilogue);
 * the dense step at batch sizes that leave a tail after the last whole group,
   or whose group count shares a factor with the first strides, still serves
   every request exactly once (every pair checked against the fp64 oracle).
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -25,14 +33,37 @@ from oracle import gla_oracle as orc
 pytestmark = pytest.mark.gpu
 
 
-def _order(slots, P):
+def _order(slots, P, slot_bytes=0):
     import gated_linear_attention_amd as gla
-    return gu.host(gla.slot_order(gu.dev(np.asarray(slots, np.int32)), P)).astype(np.int64)
+    return gu.host(gla.slot_order(gu.dev(np.asarray(slots, np.int32)), P, slot_bytes)).astype(
+        np.int64)
 
 
-def _check_order(slots, P, order2):
-    """order2 [2, N]: a permutation of the requests (valid slots ascending,
-    padded lanes last), then each position's slot."""
+def _pool_rank(P, slot_bytes):
+    """Rank of every pool entry in the streaming order: the blocks' visiting
+    sequence 0, s, 2s, ... walked step by step."""
+    rank = np.arange(P, dtype=np.int64)
+    group = 4 << 20
+    if slot_bytes <= 0 or slot_bytes > group or group % slot_bytes:
+        return rank
+    gs = group // slot_bytes
+    nb = P // gs
+    strides = [a for a in (3, 5, 7, 11, 13, 17, 19, 23) if math.gcd(a, nb) == 1]
+    if nb < 3 or not strides:
+        return rank
+    s = strides[0]
+    b, seen = 0, set()
+    for j in range(nb):  # j-th block visited: j * s mod nb
+        assert b not in seen
+        seen.add(b)
+        rank[b * gs:(b + 1) * gs] = j * gs + np.arange(gs)
+        b = (b + s) % nb
+    return rank
+
+
+def _check_order(slots, P, order2, slot_bytes=0):
+    """order2 [2, N]: a permutation of the requests (valid slots in the
+    pool's streaming order, padded lanes last), then each position's slot."""
     slots = np.asarray(slots, np.int64)
     N = len(slots)
     assert order2.shape == (2, N)
@@ -43,13 +74,15 @@ def _check_order(slots, P, order2):
     nv = int(valid.sum())
     head = order[:nv]
     assert np.all(valid[head]) and not np.any(valid[order[nv:]])  # padded lanes last
-    assert np.all(np.diff(slots[head]) >= 0)                     # slots ascending
+    rank = _pool_rank(P, slot_bytes)
+    assert np.all(np.diff(rank[slots[head]]) >= 0)               # streaming order
 
 
+@pytest.mark.parametrize("slot_bytes", [0, 1 << 20])
 @pytest.mark.parametrize("N,P,pad", [(1, 1, 0), (5, 8, 2), (1280, 2048, 0), (1280, 2048, 37),
                                      (5000, 32768, 11), (3000, 3000, 0), (700, 256, 0)])
-def test_slot_order_lists_requests_by_slot(N, P, pad):
-    gu.say(f"slot order N={N} P={P} padded={pad}")
+def test_slot_order_lists_requests_in_pool_order(N, P, pad, slot_bytes):
+    gu.say(f"slot order N={N} P={P} padded={pad} entry {slot_bytes} B")
     rng = np.random.default_rng(N + P)
     if N <= P:
         slots = rng.permutation(P)[:N]
@@ -60,10 +93,34 @@ def test_slot_order_lists_requests_by_slot(N, P, pad):
         lanes = rng.choice(N, size=pad, replace=False)
         slots[lanes[: pad // 2]] = -1
         slots[lanes[pad // 2:]] = P + rng.integers(0, 5, size=pad - pad // 2)
-    order = _order(slots, P)
-    _check_order(slots, P, order)
+    order = _order(slots, P, slot_bytes)
+    _check_order(slots, P, order, slot_bytes)
     if N <= P and not pad:  # distinct slots: the order is unique
-        np.testing.assert_array_equal(order[0], np.argsort(slots, kind="stable"))
+        rank = _pool_rank(P, slot_bytes)
+        np.testing.assert_array_equal(order[0], np.argsort(rank[slots], kind="stable"))
+
+
+@pytest.mark.parametrize("P,slot_bytes,blocks", [
+    (2050, 1 << 20, 512),     # 512 blocks of four, stride 3, a tail of two entries
+    (60, 1 << 20, 15),        # 15 blocks: 3 and 5 share a factor with it, stride 7
+    (32768, 64 << 10, 512),   # 64 KiB entries, blocks of 64
+    (400, 32 << 10, 3),       # three blocks of 128 (the fewest that are strided), tail 16
+    (8, 1 << 20, 0),          # two whole blocks: slot order
+    (3000, 3 << 20, 0),       # 3 MiB entries do not tile 4 MiB: slot order
+    (3000, 8 << 20, 0),       # larger than a block: slot order
+    (3000, (1 << 20) + 4, 0)])
+def test_slot_order_block_cases(P, slot_bytes, blocks):
+    """Every slot of the pool requested once, in a random batch order: the
+    order is the streaming order itself."""
+    gu.say(f"slot order over a whole pool P={P}, entry {slot_bytes} B, {blocks} blocks")
+    slots = np.random.default_rng(P).permutation(P).astype(np.int64)
+    order = _order(slots, P, slot_bytes)
+    _check_order(slots, P, order, slot_bytes)
+    rank = _pool_rank(P, slot_bytes)
+    if blocks == 0:
+        np.testing.assert_array_equal(rank, np.arange(P))
+    np.testing.assert_array_equal(np.sort(rank), np.arange(P))
+    np.testing.assert_array_equal(rank[order[1]], np.arange(P))
 
 
 def test_slot_order_all_padded_and_empty():
@@ -98,8 +155,8 @@ def test_slot_decode_with_order_is_bit_identical(N, P, H, dk, dv):
     rng = np.random.default_rng(N)
     slots = rng.permutation(P)[:N].astype(np.int64)
     slots[::17] = -1
-    order = gla.slot_order(gu.dev(slots.astype(np.int32)), P)
-    _check_order(slots, P, gu.host(order).astype(np.int64))
+    order = gla.slot_order(gu.dev(slots.astype(np.int32)), P, H * dk * dv * 4)
+    _check_order(slots, P, gu.host(order).astype(np.int64), H * dk * dv * 4)
     o_a, pool_a = _slot_step(N, P, H, dk, dv, slots, None)
     o_b, pool_b = _slot_step(N, P, H, dk, dv, slots, order)
     for a, b in zip(o_a, o_b):
@@ -116,7 +173,8 @@ def test_decode_mixer_with_order_is_bit_identical(dk, dv):
     slots = rng.permutation(P)[:N].astype(np.int64)
     slots[3::50] = -1
     sl = gu.dev(slots.astype(np.int32))
-    order = gla.slot_order(sl, P)
+    order = gla.slot_order(sl, P, H * dk * dv * 4)
+    _check_order(slots, P, gu.host(order).astype(np.int64), H * dk * dv * 4)
     a, tw, tier = synth.make_epilogue_params(H, dk, dv, seed=3, n_tiers=2)
     w = gla.head_rms_weights(gu.dev(tw), gu.dev(tier))
     q, k, v, lg = synth.make_decode_step_inputs(N, H, dk, dv, seed=77)
