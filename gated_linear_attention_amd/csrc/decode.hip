@@ -50,6 +50,20 @@ static int group_stride(int ng) {
   return 1;
 }
 
+// a^-1 mod m for a, m coprime and m >= 2 (extended Euclid); 0 if none exists.
+static int inverse_mod(int a, int m) {
+  long r0 = m, r1 = a % m, t0 = 0, t1 = 1;
+  while (r1 != 0) {
+    const long qt = r0 / r1, r2 = r0 - qt * r1, t2 = t0 - qt * t1;
+    r0 = r1;
+    r1 = r2;
+    t0 = t1;
+    t1 = t2;
+  }
+  if (r0 != 1) return 0;
+  return (int)((t0 % m + m) % m);
+}
+
 // States per 4 MiB group: only where a request's (or pool entry's) states tile
 // 4 MiB exactly (96 x 192 heads, 1.125 MiB a request, stream fastest in launch
 // order); 0 otherwise.
@@ -546,11 +560,7 @@ hipError_t launch_slot_order(const int32_t *slots, int N, int P, long slot_bytes
   if (key.gs > 0) {
     key.nb = P / key.gs;
     const int s = group_stride(key.nb);
-    for (int a = 1; s > 1 && a < key.nb; ++a)  // s^-1 mod nb (s and nb coprime)
-      if ((long)s * a % key.nb == 1) {
-        key.inv = a;
-        break;
-      }
+    if (s > 1) key.inv = inverse_mod(s, key.nb);
     if (key.inv == 0) key = OrderKey{0, 0, 0};  // fewer than three blocks: slot order
   }
   const size_t lds = (size_t)(P + 1) * sizeof(uint32_t);
