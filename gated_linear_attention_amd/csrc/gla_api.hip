@@ -292,8 +292,9 @@ namespace {
 
 // Head shapes of the backward: (d_k, d_v) in {64, 128}^2 on the forward
 // kernels of the input type, and the Laplace 96 x 192 heads, whose dq and dk
-// runs are forwards with 192-dim keys: those run on the fp32 kernel (which
-// reads bf16 inputs too), the dv run with them.
+// runs are forwards with 192-dim keys: with bf16 inputs those run as two
+// 96-dim key halves (bwd_split_keys below), with fp32 inputs on the fp32
+// kernel, the dv run with them.
 bool bwd_dims(int dk, int dv) {
   return (supported_head_dim(dk) && supported_head_dim(dv)) || (dk == 96 && dv == 192);
 }
