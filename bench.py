@@ -58,17 +58,24 @@ def measured_traffic(kernel_key, sources):
 
 
 def time_launches(fn, steps, stream):
-    """Run fn(i) for i in range(steps) on `stream` twice: the timed pass (wall
-    clock between synchronisations, nothing else enqueued), then a pass with a
-    HIP event pair recorded on that stream around each launch. Returns (wall
-    seconds of the timed pass, mean per-launch GPU ms from the events)."""
+    """Run fn(i) for i in range(steps) on `stream` twice. The timed pass:
+    back-to-back calls with nothing else enqueued, timed by the wall clock
+    between synchronisations and by one HIP event pair recorded on that stream
+    around all of them. Then a pass with an event pair around each call, for
+    the per-call distribution (time_launches.last, sorted; each pair adds its
+    own few microseconds of event overhead). Returns (wall seconds of the timed
+    pass, mean GPU ms per call from the timed pass's event pair)."""
     import torch
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
         fn(i)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    region_ms = e0.elapsed_time(e1) / steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     for i in range(steps):
@@ -78,7 +85,7 @@ def time_launches(fn, steps, stream):
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in ev]
     time_launches.last = sorted(per)
-    return wall, sum(per) / len(per)
+    return wall, region_ms
 
 
 def pair_error(x, ref, cu=None, state=False):
