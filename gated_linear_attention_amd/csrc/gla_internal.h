@@ -44,8 +44,8 @@ struct DotOut {
 // Batches with fewer than two (sequence, head) pairs per CU (n_cu CUs) split
 // each pair's columns over several workgroups.
 // Launch position -> request of the decode kernels (decode.hip): order[j]
-// when the caller passed the slot-sorted order (order [2, n]: the requests,
-// then their slots), else groups of gs requests with group g at position
+// when the caller passed gla_decode_slot_order's order (order [2, n]: the
+// requests, then their slots), else groups of gs requests with group g at position
 // (g * stride) % ng (requests past ng * gs in place).
 struct ReqMap {
   const int32_t *order;
@@ -161,7 +161,7 @@ struct MixerArgs {
   const int32_t *slots;
   int P, H;
   long pairs;
-  ReqMap map;  // map.order: the slot-sorted request order, or null
+  ReqMap map;  // map.order: gla_decode_slot_order's request order, or null
 };
 hipError_t launch_decode_mixer(const MixerArgs &m, int dk, int dv, bool in_bf16, bool out_bf16,
                                hipStream_t stream);
